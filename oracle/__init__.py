@@ -1,0 +1,301 @@
+"""ctypes binding of the fp64 CPU oracle (liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product package.  The oracle
+computes the Stable LatentMoE layer forward from its plain definition (see
+oracle.h for the steps and the pages they follow).  Inputs are raw storage
+arrays (float32, uint16 bf16 bits, uint8 e4m3 codes with fp32 block scales);
+a "shape" is any object with the attributes d, latent, n_experts, top_k,
+expert_inter, n_shared, shared_inter, beta, beta_u, rms_eps.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32, BF16, FP8 = 0, 1, 2
+GIVEN, BATCH = 0, 1
+
+_NP_DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): FP8}
+
+
+class OrcMat(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_void_p), ("n_mats", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class OrcShape(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("latent", ctypes.c_int64),
+                ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
+                ("expert_inter", ctypes.c_int64), ("n_shared", ctypes.c_int64),
+                ("shared_inter", ctypes.c_int64), ("beta", ctypes.c_double),
+                ("beta_u", ctypes.c_double), ("rms_eps", ctypes.c_double)]
+
+
+class OrcWeights(ctypes.Structure):
+    _fields_ = [("w_router", OrcMat), ("router_bias", ctypes.c_void_p),
+                ("w_down_proj", OrcMat), ("w_gate", OrcMat), ("w_up", OrcMat),
+                ("w_down", OrcMat), ("gamma", ctypes.c_void_p), ("w_up_proj", OrcMat),
+                ("sh_gate", OrcMat), ("sh_up", OrcMat), ("sh_down", OrcMat)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        P, I64, D, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int32
+        sig = {
+            "orc_bf16_to_double": ([ctypes.c_uint16], D),
+            "orc_e4m3_to_double": ([ctypes.c_uint8], D),
+            "orc_decode": ([P, I64, I64, I64], D),
+            "orc_matvec": ([P, I64, P, P], None),
+            "orc_sigmoid": ([D], D),
+            "orc_phi": ([D, D], D),
+            "orc_psi": ([D, D], D),
+            "orc_router_logits": ([P, P, P, P, I64, P], ctypes.c_int),
+            "orc_quantile": ([P, I64, I64, I64, P], ctypes.c_int),
+            "orc_topk": ([P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+            "orc_dispatch": ([P, I64, I64, I64, P, P, P, P], ctypes.c_int),
+            "orc_expert": ([P, P, P, P, I64, P, P], ctypes.c_int),
+            "orc_combine_norm": ([P, P, P, P, P, P], ctypes.c_int),
+            "orc_shared": ([P, P, P, P], ctypes.c_int),
+            "orc_output": ([P, P, P, P, P], ctypes.c_int),
+            "orc_forward": ([P, P, P, I64, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dt=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a) if dt is None else np.asarray(a, dtype=dt))
+    return a
+
+
+def shape_of(cfg) -> OrcShape:
+    g = lambda n, dflt=0: getattr(cfg, n, dflt)
+    return OrcShape(g("d"), g("latent"), g("n_experts"), g("top_k"), g("expert_inter"),
+                    g("n_shared"), g("shared_inter"), float(g("beta", 4.0)),
+                    float(g("beta_u", 25.0)), float(g("rms_eps", 1e-6)))
+
+
+class Mat:
+    """Keeps the arrays behind an OrcMat alive."""
+
+    def __init__(self, data: np.ndarray, scale: np.ndarray | None = None, n_mats=None,
+                 rows=None, cols=None):
+        self.data = np.ascontiguousarray(data)
+        self.scale = None if scale is None else np.ascontiguousarray(scale, np.float32)
+        dt = _NP_DT[self.data.dtype]
+        if data.ndim == 3:
+            n_mats, rows, cols = data.shape
+        elif data.ndim == 2:
+            n_mats, rows, cols = 1, data.shape[0], data.shape[1]
+        self.c = OrcMat(self.data.ctypes.data, dt,
+                        None if self.scale is None else self.scale.ctypes.data,
+                        n_mats, rows, cols)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class Weights:
+    """Oracle view of a layer given as a dict of raw-storage arrays (the
+    key names of the GPU ABI's weight set)."""
+
+    def __init__(self, layer: dict):
+        def m(name):
+            if layer.get(name) is None:
+                return None
+            return Mat(layer[name], layer.get("scale:" + name))
+        self.mats = {n: m(n) for n in ("w_router", "w_down_proj", "w_gate", "w_up", "w_down",
+                                       "w_up_proj", "sh_gate", "sh_up", "sh_down")}
+        self.bias = _c(layer.get("router_bias"), np.float32)
+        self.gamma = _c(layer.get("gamma"), np.float32)
+        def cm(n):
+            return self.mats[n].c if self.mats[n] is not None else OrcMat()
+        self.c = OrcWeights(cm("w_router"),
+                            None if self.bias is None else self.bias.ctypes.data,
+                            cm("w_down_proj"), cm("w_gate"), cm("w_up"), cm("w_down"),
+                            None if self.gamma is None else self.gamma.ctypes.data,
+                            cm("w_up_proj"), cm("sh_gate"), cm("sh_up"), cm("sh_down"))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+# ---- scalar functions ----------------------------------------------------------
+
+def sigmoid(z):
+    return lib().orc_sigmoid(float(z))
+
+
+def phi(g, beta=4.0):
+    return lib().orc_phi(float(g), float(beta))
+
+
+def psi(u, beta_u=25.0):
+    return lib().orc_psi(float(u), float(beta_u))
+
+
+def bf16_to_double(bits):
+    return lib().orc_bf16_to_double(int(bits))
+
+
+def e4m3_to_double(code):
+    return lib().orc_e4m3_to_double(int(code))
+
+
+def matvec(mat: Mat, vec, index=0):
+    vec = _c(vec, np.float64)
+    out = np.empty(mat.c.rows, np.float64)
+    lib().orc_matvec(mat.ref, index, _ptr(vec), _ptr(out))
+    return out
+
+
+# ---- steps ----------------------------------------------------------------------
+
+def router_logits(cfg, w: Weights, x: np.ndarray, rows=None) -> np.ndarray:
+    """fp64 logits [n_rows][E] of the listed token rows of x (raw storage [bt][d])."""
+    xm = Mat(x)
+    if rows is None:
+        n = x.shape[0]
+        rp = None
+    else:
+        rp = np.ascontiguousarray(rows, np.int64)
+        n = rp.size
+    out = np.empty((n, cfg.n_experts), np.float64)
+    rc = lib().orc_router_logits(ctypes.byref(shape_of(cfg)), w.ref, xm.ref, _ptr(rp), n,
+                                 _ptr(out))
+    if rc:
+        raise ValueError("orc_router_logits rejected its arguments")
+    return out
+
+
+def quantile(z32: np.ndarray, m: int) -> np.ndarray:
+    z32 = _c(z32, np.float32)
+    bt, E = z32.shape
+    out = np.empty(E, np.float32)
+    if lib().orc_quantile(_ptr(z32), bt, E, m, _ptr(out)):
+        raise ValueError("orc_quantile rejected its arguments")
+    return out
+
+
+def topk(z32: np.ndarray, k: int, alpha=None, z64=None):
+    z32 = _c(z32, np.float32)
+    alpha = _c(alpha, np.float32)
+    z64 = _c(z64, np.float64)
+    bt, E = z32.shape
+    idx = np.empty((bt, k), np.int32)
+    w = np.empty((bt, k), np.float64)
+    if lib().orc_topk(_ptr(z32), _ptr(alpha), _ptr(z64), bt, E, k, _ptr(idx), _ptr(w)):
+        raise ValueError("orc_topk rejected its arguments")
+    return idx, w
+
+
+def dispatch(idx: np.ndarray, n_experts: int):
+    idx = _c(idx, np.int32)
+    bt, k = idx.shape
+    counts = np.empty(n_experts, np.int32)
+    offsets = np.empty(n_experts + 1, np.int32)
+    perm = np.empty(bt * k, np.int32)
+    inv = np.empty(bt * k, np.int32)
+    if lib().orc_dispatch(_ptr(idx), bt, k, n_experts, _ptr(counts), _ptr(offsets),
+                          _ptr(perm), _ptr(inv)):
+        raise ValueError("orc_dispatch rejected its arguments")
+    return counts, offsets, perm, inv
+
+
+def expert(cfg, gate: Mat, up: Mat, down: Mat, x_lat, index=0) -> np.ndarray:
+    x_lat = _c(x_lat, np.float64)
+    o = np.empty(cfg.latent, np.float64)
+    if lib().orc_expert(ctypes.byref(shape_of(cfg)), gate.ref, up.ref, down.ref, index,
+                        _ptr(x_lat), _ptr(o)):
+        raise ValueError("orc_expert rejected its arguments")
+    return o
+
+
+def combine_norm(cfg, o: np.ndarray, w, gamma=None):
+    o = _c(o, np.float64)
+    w = _c(w, np.float64)
+    gamma = _c(gamma, np.float32)
+    ylat = np.empty(cfg.latent, np.float64)
+    n = np.empty(cfg.latent, np.float64)
+    if lib().orc_combine_norm(ctypes.byref(shape_of(cfg)), _ptr(o), _ptr(w), _ptr(gamma),
+                              _ptr(ylat), _ptr(n)):
+        raise ValueError("orc_combine_norm rejected its arguments")
+    return ylat, n
+
+
+def shared(cfg, w: Weights, x_t) -> np.ndarray:
+    x_t = _c(x_t, np.float64)
+    out = np.empty(cfg.d, np.float64)
+    if lib().orc_shared(ctypes.byref(shape_of(cfg)), w.ref, _ptr(x_t), _ptr(out)):
+        raise ValueError("orc_shared rejected its arguments")
+    return out
+
+
+def output(cfg, w: Weights, n, x_t) -> np.ndarray:
+    n = _c(n, np.float64)
+    x_t = _c(x_t, np.float64)
+    y = np.empty(cfg.d, np.float64)
+    if lib().orc_output(ctypes.byref(shape_of(cfg)), w.ref, _ptr(n), _ptr(x_t), _ptr(y)):
+        raise ValueError("orc_output rejected its arguments")
+    return y
+
+
+def decode(arr: np.ndarray, scale=None) -> np.ndarray:
+    """Exact fp64 value of a raw-storage matrix or stack (uses the oracle's decoders)."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    m = Mat(a if a.ndim >= 2 else a.reshape(1, -1), scale)
+    rows = m.c.n_mats * m.c.rows
+    out = np.empty((rows, m.c.cols), np.float64)
+    for i in range(rows):
+        for c in range(m.c.cols):
+            out[i, c] = lib().orc_decode(m.ref, i // m.c.rows, i % m.c.rows, c)
+    return out.reshape(a.shape)
+
+
+def forward(cfg, layer: dict, cutoff: int = BATCH, alpha=None):
+    """Whole layer on every token of layer['x'] (small shapes).  Returns a dict."""
+    w = Weights(layer)
+    x = Mat(layer["x"])
+    bt = layer["x"].shape[0]
+    E, k, P = cfg.n_experts, cfg.top_k, bt * cfg.top_k
+    alpha = _c(alpha, np.float32)
+    out = dict(z32=np.empty((bt, E), np.float32), zeta=np.empty(E, np.float32),
+               idx=np.empty((bt, k), np.int32), w=np.empty((bt, k), np.float64),
+               counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
+               perm=np.empty(P, np.int32), inv_perm=np.empty(P, np.int32),
+               y=np.empty((bt, cfg.d), np.float64))
+    rc = lib().orc_forward(ctypes.byref(shape_of(cfg)), w.ref, x.ref, bt, cutoff, _ptr(alpha),
+                           *(_ptr(out[n]) for n in ("z32", "zeta", "idx", "w", "counts",
+                                                    "offsets", "perm", "inv_perm", "y")))
+    if rc:
+        raise ValueError("orc_forward rejected its arguments")
+    return out

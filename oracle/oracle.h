@@ -1,0 +1,135 @@
+/*
+ * oracle.h -- plain, slow fp64 CPU oracle of the Stable LatentMoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path never
+ * does.  It shares no code with the GPU library.
+ *
+ * What it computes (the plain definition of the layer):
+ *   Kimi K3 Stable LatentMoE as described on tech.news18a.com
+ *   "KimiK3的StableLatentMoE架构解析" (module structure, figure 1; forward flow,
+ *   figure 2; the three stability techniques: SiTU-GLU, RMSNorm before up,
+ *   Quantile Balancing) and on mkdocs.reaper.mx "Vue d'ensemble de
+ *   l'architecture" (per-token path, steps c-g; parameter budget table).
+ *
+ *   1. logits z[t][e] = sum_i x[t][i] W_r[e][i] + b[e];  scores s = sigmoid(z)
+ *   2. cutoff (BATCH mode): zeta[e] = m-th largest of column e of fp32 z,
+ *      m = clamp(ceil(bt*k/E), 1, bt); GIVEN mode uses a caller's alpha.
+ *   3. r = fp32(z) - alpha in fp32; per token the k experts of largest r
+ *      (equal r: lower expert id first), listed in ascending expert id;
+ *      combine weight w = s at the chosen expert (not renormalised).
+ *   4. dispatch: per-expert counts, exclusive offsets, pairs p = t*k + j
+ *      ordered by (expert asc, token asc), and the inverse permutation.
+ *   5. x_lat = W_down_proj x                                     (d -> L)
+ *   6. per pair: o = W_d,e (phi(W_g,e x_lat) * psi(W_u,e x_lat))  (width L)
+ *   7. y_lat = sum_j w_j o_j (j ascending);  n = y_lat / sqrt(mean(y_lat^2) + eps) * gamma
+ *   8. y = W_up_proj n + sum_{j < S} W_ds,j (phi(W_gs,j x) * psi(W_us,j x))
+ *   phi(g) = sigmoid(g) * beta * tanh(g / beta),  psi(u) = beta_u * tanh(u / beta_u)
+ *
+ * Every dot product is accumulated in fp64 in index order.  Inputs are
+ * decoded exactly: fp32 and bf16 widen, an fp8 e4m3fn code times its fp32
+ * 128x128 block scale is exact in fp64.
+ *
+ * Parity pins (tests/test_oracle_pins.py): closed forms, invariants and
+ * brute force as listed there.  The layer output as a whole is pinned only
+ * through those properties: the pages print no worked numeric example of
+ * it.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8E4M3 = 2 };
+enum { ORC_CUTOFF_GIVEN = 0, ORC_CUTOFF_BATCH = 1 };
+
+/* n_mats matrices of rows x cols, row-major, raw storage.  For ORC_FP8E4M3,
+ * scale holds [n_mats][rows/128][cols/128] fp32 block scales. */
+typedef struct {
+  const void *data;
+  int32_t dtype;
+  const float *scale;
+  int64_t n_mats, rows, cols;
+} orc_mat;
+
+typedef struct {
+  int64_t d, latent, n_experts, top_k, expert_inter, n_shared, shared_inter;
+  double beta, beta_u, rms_eps;
+} orc_shape;
+
+typedef struct {
+  orc_mat w_router;                 /* [1][E][d] */
+  const float *router_bias;         /* [E] or NULL */
+  orc_mat w_down_proj;              /* [1][L][d] */
+  orc_mat w_gate, w_up;             /* [E][I][L] */
+  orc_mat w_down;                   /* [E][L][I] */
+  const float *gamma;               /* [L] */
+  orc_mat w_up_proj;                /* [1][d][L] */
+  orc_mat sh_gate, sh_up;           /* [S][I_s][d] */
+  orc_mat sh_down;                  /* [S][d][I_s] */
+} orc_weights;
+
+/* One element, decoded exactly. */
+double orc_decode(const orc_mat *m, int64_t mat, int64_t r, int64_t c);
+double orc_bf16_to_double(uint16_t bits);
+double orc_e4m3_to_double(uint8_t code);
+
+/* out[r] = sum_c M[mat][r][c] in[c], fp64, c ascending. */
+void orc_matvec(const orc_mat *m, int64_t mat, const double *in, double *out);
+
+double orc_sigmoid(double z);
+double orc_phi(double g, double beta);
+double orc_psi(double u, double beta_u);
+
+/* Step 1 for the token rows listed (rows == NULL: rows 0..n_rows-1).
+ * x is [bt][d] raw storage.  z_out [n_rows][E] fp64. */
+int orc_router_logits(const orc_shape *s, const orc_weights *w, const orc_mat *x,
+                      const int64_t *rows, int64_t n_rows, double *z_out);
+
+/* Step 2: zeta[e] = m-th largest of z32[.][e] over bt tokens. */
+int orc_quantile(const float *z32, int64_t bt, int64_t n_experts, int64_t m, float *zeta);
+
+/* Step 3.  z32 [bt][E] fp32 logits, alpha [E] (NULL: 0), z64 [bt][E] fp64 logits
+ * for the combine weights (NULL: the fp32 logits are used).  idx [bt][k]
+ * ascending expert ids, w [bt][k]. */
+int orc_topk(const float *z32, const float *alpha, const double *z64, int64_t bt,
+             int64_t n_experts, int64_t k, int32_t *idx, double *w);
+
+/* Step 4. offsets has E+1 entries. */
+int orc_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
+                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm);
+
+/* Step 6 for one pair: o = W_d[e] (phi(W_g[e] xl) * psi(W_u[e] xl)).  The
+ * three orc_mat may hold all experts (mat = e) or just one (mat = 0). */
+int orc_expert(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
+               const orc_mat *w_down, int64_t mat, const double *x_lat, double *o);
+
+/* Step 7 for one token: o [k][L] expert outputs in slot order, w [k]. */
+int orc_combine_norm(const orc_shape *s, const double *o, const double *w,
+                     const float *gamma, double *y_lat, double *n);
+
+/* Shared experts on one token: out [d] = sum_j W_ds,j (phi(W_gs,j x) psi(W_us,j x)). */
+int orc_shared(const orc_shape *s, const orc_weights *w, const double *x_t, double *out);
+
+/* Step 8 for one token: y = W_up_proj n + shared(x). */
+int orc_output(const orc_shape *s, const orc_weights *w, const double *n,
+               const double *x_t, double *y);
+
+/* The whole layer on bt tokens (small shapes).  Outputs may be NULL except y.
+ * alpha_given: GIVEN-mode cutoffs (NULL: 0).  z32 [bt][E], zeta [E] (BATCH),
+ * idx [bt][k], wts [bt][k], counts [E], offsets [E+1], perm/inv_perm [bt*k],
+ * y [bt][d] fp64. */
+int orc_forward(const orc_shape *s, const orc_weights *w, const orc_mat *x, int64_t bt,
+                int32_t cutoff_mode, const float *alpha_given, float *z32_out,
+                float *zeta_out, int32_t *idx_out, double *wts_out, int32_t *counts,
+                int32_t *offsets, int32_t *perm, int32_t *inv_perm, double *y);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ORACLE_H */

@@ -1,0 +1,356 @@
+"""Seeded synthetic workloads for the Stable LatentMoE layer.
+
+This module generates inputs only: token activations, layer weights, fp8 block
+scales, Zipf logit offsets and routing-index fixtures.  It holds none of the
+layer's arithmetic.  The host generator (``libsynth_host.so``, gcc) and the
+device generator (``libsynth_dev.so``, hipcc) expand the same counter-based
+Philox-4x32-10 definition in ``synth_rng.h`` and produce identical bits, so the
+GPU path can have a 60 GB layer written straight into HBM while the CPU oracle
+regenerates any slice of it (one expert, a few token rows) on the host.
+
+Workload shapes follow the five layer configurations of the Kimi K3 Stable
+LatentMoE (tech.news18a.com "KimiK3的StableLatentMoE架构解析", forward-flow
+figure 2; mkdocs.reaper.mx "Vue d'ensemble de l'architecture", per-token path
+steps c-g and the parameter-budget table).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+F32, BF16, FP8 = 0, 1, 2
+NORMAL, DYADIC = 0, 1
+NORMAL_INT_STD = 107022.329313
+NORMAL_INT_MAX = 524280
+FP8_MAX = 448.0
+FP8_BLOCK = 128
+
+DTYPE_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8}
+NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1}
+
+# Tensor ids: distinct Philox counter words per tensor.
+TID = {
+    "x": 1, "w_router": 2, "w_down_proj": 3, "w_gate": 4, "w_up": 5, "w_down": 6,
+    "w_up_proj": 7, "sh_gate": 8, "sh_up": 9, "sh_down": 10,
+}
+SCALE_TID_BASE = 100  # block scales of tensor t use id SCALE_TID_BASE + TID[t]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    bt: int
+    d: int
+    latent: int
+    n_experts: int
+    top_k: int
+    expert_inter: int
+    n_shared: int
+    shared_inter: int
+    act: str = "bf16"
+    weight: str = "bf16"
+    router: str = "bf16"
+    bias: str = "zero"          # "zero" or "zipf1.1"
+    cutoff: str = "given"       # benchmark cutoff mode: "given" (alpha = 0) or "batch"
+    beta: float = 4.0
+    beta_u: float = 25.0
+    rms_eps: float = 1e-6
+
+    # ---- derived sizes -------------------------------------------------
+    @property
+    def pairs(self) -> int:
+        return self.bt * self.top_k
+
+    @property
+    def quantile_rank(self) -> int:
+        """m = clamp(ceil(bt*k/E), 1, bt)."""
+        m = -(-self.bt * self.top_k // self.n_experts)
+        return max(1, min(m, self.bt))
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs of one forward (2 per multiply-add of every GEMM)."""
+        bt, d, L, E = self.bt, self.d, self.latent, self.n_experts
+        return (2 * bt * d * E + 2 * bt * d * L + 2 * self.pairs * 3 * L * self.expert_inter
+                + 2 * bt * L * d + 2 * bt * 3 * d * self.n_shared * self.shared_inter)
+
+    def with_(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+CONFIGS: Dict[str, Config] = {
+    "tiny_fp32": Config("tiny_fp32", bt=64, d=256, latent=64, n_experts=16, top_k=2,
+                        expert_inter=64, n_shared=1, shared_inter=128,
+                        act="f32", weight="f32", router="f32", cutoff="batch"),
+    "mid_bf16": Config("mid_bf16", bt=4096, d=2048, latent=512, n_experts=64, top_k=8,
+                       expert_inter=512, n_shared=2, shared_inter=1024, cutoff="given"),
+    "k3_decode_bf16": Config("k3_decode_bf16", bt=64, d=7168, latent=3584, n_experts=896,
+                             top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
+                             cutoff="given"),
+    "k3_prefill_bf16": Config("k3_prefill_bf16", bt=16384, d=7168, latent=3584,
+                              n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                              shared_inter=3072, bias="zipf1.1", cutoff="batch"),
+    "k3_prefill_fp8": Config("k3_prefill_fp8", bt=8192, d=7168, latent=3584, n_experts=896,
+                             top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
+                             weight="fp8", router="bf16", cutoff="batch"),
+}
+
+
+# ---- tensor catalogue -------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    name: str
+    shape: tuple          # storage shape, row-major, weights [out][in]
+    dtype: int
+    fan_in: int           # sets sigma = 1/sqrt(fan_in) for weights
+    mat_rows: int         # rows / cols of one matrix (block scales tile these)
+    mat_cols: int
+    n_mats: int
+
+    @property
+    def numel(self) -> int:
+        return int(np.prod(self.shape))
+
+    @property
+    def nbytes(self) -> int:
+        return self.numel * ELEM_BYTES[self.dtype]
+
+    @property
+    def n_scale_blocks(self) -> int:
+        return self.n_mats * (self.mat_rows // FP8_BLOCK) * (self.mat_cols // FP8_BLOCK)
+
+
+def specs(cfg: Config) -> Dict[str, Spec]:
+    d, L, E, I, S, Is = (cfg.d, cfg.latent, cfg.n_experts, cfg.expert_inter, cfg.n_shared,
+                         cfg.shared_inter)
+    a, w, r = DTYPE_NAMES[cfg.act], DTYPE_NAMES[cfg.weight], DTYPE_NAMES[cfg.router]
+    return {
+        "x": Spec("x", (cfg.bt, d), a, 1, cfg.bt, d, 1),
+        "w_router": Spec("w_router", (E, d), r, d, E, d, 1),
+        "w_down_proj": Spec("w_down_proj", (L, d), w, d, L, d, 1),
+        "w_gate": Spec("w_gate", (E, I, L), w, L, I, L, E),
+        "w_up": Spec("w_up", (E, I, L), w, L, I, L, E),
+        "w_down": Spec("w_down", (E, L, I), w, I, L, I, E),
+        "w_up_proj": Spec("w_up_proj", (d, L), w, L, d, L, 1),
+        "sh_gate": Spec("sh_gate", (S, Is, d), w, d, Is, d, S),
+        "sh_up": Spec("sh_up", (S, Is, d), w, d, Is, d, S),
+        "sh_down": Spec("sh_down", (S, d, Is), w, S * Is, d, Is, S),
+    }
+
+
+WEIGHT_NAMES = ("w_router", "w_down_proj", "w_gate", "w_up", "w_down", "w_up_proj",
+                "sh_gate", "sh_up", "sh_down")
+FP8_NAMES = ("w_down_proj", "w_gate", "w_up", "w_down", "w_up_proj", "sh_gate", "sh_up",
+             "sh_down")
+
+
+def dyadic_router_shift(d: int) -> int:
+    """q such that dyadic router weights k * 2^-q (|k| <= 8) against dyadic
+    tokens (|x| <= 2) give logits of roughly unit spread."""
+    return int(round(math.log2(math.sqrt(d * 2 * 24))))
+
+
+def draw_params(cfg: Config, name: str, routing: str = "normal"):
+    """(kind, scale, range) of the draw that fills tensor `name`."""
+    sp = specs(cfg)[name]
+    if routing == "dyadic" and name == "x":
+        return DYADIC, 1.0, 2
+    if routing == "dyadic" and name == "w_router":
+        return DYADIC, 2.0 ** -dyadic_router_shift(cfg.d), 8
+    if sp.dtype == FP8:
+        return NORMAL, FP8_MAX / NORMAL_INT_MAX, 0
+    sigma = 1.0 if name == "x" else 1.0 / math.sqrt(sp.fan_in)
+    return NORMAL, float(np.float32(sigma / NORMAL_INT_STD)), 0
+
+
+def scale_base(cfg: Config, name: str) -> float:
+    """Centre of the fp8 block scales of `name`: dequantised codes then have
+    standard deviation ~ 1/sqrt(fan_in)."""
+    sp = specs(cfg)[name]
+    sigma = 1.0 / math.sqrt(sp.fan_in)
+    return sigma * (NORMAL_INT_MAX / FP8_MAX) / NORMAL_INT_STD
+
+
+# ---- native libraries ---------------------------------------------------------
+
+_host = None
+_dev = None
+
+
+def lib_host():
+    global _host
+    if _host is None:
+        path = os.path.join(HERE, "libsynth_host.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.synth_fill_host.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_int32]
+        lib.synth_fill_host.restype = ctypes.c_int
+        lib.synth_philox_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_normal_int_host.argtypes = [ctypes.c_uint64, ctypes.c_uint32,
+                                              ctypes.c_uint64]
+        lib.synth_normal_int_host.restype = ctypes.c_int32
+        lib.synth_bf16_host.argtypes = [ctypes.c_float]
+        lib.synth_bf16_host.restype = ctypes.c_uint16
+        lib.synth_e4m3_host.argtypes = [ctypes.c_float]
+        lib.synth_e4m3_host.restype = ctypes.c_uint8
+        lib.synth_block_scales_host.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.c_uint64, ctypes.c_uint32,
+                                                ctypes.c_double]
+        lib.synth_zipf_offsets_host.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.c_double]
+        lib.synth_routing_host.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
+                                           ctypes.c_int64]
+        _host = lib
+    return _host
+
+
+def lib_dev():
+    global _dev
+    if _dev is None:
+        path = os.path.join(HERE, "libsynth_dev.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.synth_fill_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_float, ctypes.c_int32,
+                                          ctypes.c_void_p]
+        lib.synth_fill_device.restype = ctypes.c_int
+        _dev = lib
+    return _dev
+
+
+# ---- host-side generation -------------------------------------------------------
+
+def host_fill(dtype: int, n: int, seed: int, tid: int, offset: int, kind: int, scale: float,
+              rng: int) -> np.ndarray:
+    out = np.empty(n, dtype=NP_STORAGE[dtype])
+    rc = lib_host().synth_fill_host(out.ctypes.data, dtype, n, seed, tid, offset, kind,
+                                    scale, rng)
+    if rc != 0:
+        raise ValueError("synth_fill_host rejected its arguments")
+    return out
+
+
+def host_tensor(cfg: Config, name: str, seed: int = 0, routing: str = "normal",
+                start: int = 0, count: Optional[int] = None) -> np.ndarray:
+    """Raw storage (float32 / uint16 bf16 bits / uint8 e4m3 codes) of elements
+    start..start+count of tensor `name`, flat."""
+    sp = specs(cfg)[name]
+    if count is None:
+        count = sp.numel - start
+    kind, scale, rng = draw_params(cfg, name, routing)
+    return host_fill(sp.dtype, count, seed, TID[name], start, kind, scale, rng)
+
+
+def host_matrix(cfg: Config, name: str, index: int = 0, seed: int = 0,
+                routing: str = "normal") -> np.ndarray:
+    """Matrix `index` (an expert, a shared expert) of tensor `name`, 2-D raw storage."""
+    sp = specs(cfg)[name]
+    n = sp.mat_rows * sp.mat_cols
+    return host_tensor(cfg, name, seed, routing, index * n, n).reshape(sp.mat_rows,
+                                                                      sp.mat_cols)
+
+
+def host_rows(cfg: Config, name: str, rows, seed: int = 0, routing: str = "normal"):
+    """Selected rows of a 2-D tensor (e.g. token rows of x), raw storage."""
+    sp = specs(cfg)[name]
+    cols = sp.shape[-1]
+    return np.stack([host_tensor(cfg, name, seed, routing, int(r) * cols, cols)
+                     for r in rows]) if len(rows) else np.zeros((0, cols),
+                                                                 NP_STORAGE[sp.dtype])
+
+
+def host_scales(cfg: Config, name: str, seed: int = 0) -> Optional[np.ndarray]:
+    """fp32 block scales [n_mats][rows/128][cols/128] of an fp8 tensor, else None."""
+    sp = specs(cfg)[name]
+    if sp.dtype != FP8:
+        return None
+    out = np.empty(sp.n_scale_blocks, dtype=np.float32)
+    rc = lib_host().synth_block_scales_host(out.ctypes.data, out.size, seed,
+                                            SCALE_TID_BASE + TID[name],
+                                            scale_base(cfg, name))
+    if rc != 0:
+        raise ValueError("synth_block_scales_host rejected its arguments")
+    return out.reshape(sp.n_mats, sp.mat_rows // FP8_BLOCK, sp.mat_cols // FP8_BLOCK)
+
+
+def router_bias(cfg: Config) -> Optional[np.ndarray]:
+    """Per-expert logit offsets, or None for a bias-free router."""
+    if cfg.bias == "zero":
+        return None
+    if cfg.bias.startswith("zipf"):
+        s = float(cfg.bias[4:])
+        out = np.empty(cfg.n_experts, dtype=np.float32)
+        lib_host().synth_zipf_offsets_host(out.ctypes.data, cfg.n_experts, s)
+        return out
+    raise ValueError(cfg.bias)
+
+
+def gamma(cfg: Config) -> np.ndarray:
+    return np.ones(cfg.latent, dtype=np.float32)
+
+
+def routing_fixture(bt: int, k: int, n_experts: int, seed: int = 0, hot: int = 0,
+                    tid: int = 50) -> np.ndarray:
+    """[bt][k] int32 expert ids, distinct and ascending per token."""
+    out = np.empty((bt, k), dtype=np.int32)
+    rc = lib_host().synth_routing_host(out.ctypes.data, bt, k, n_experts, seed, tid, hot)
+    if rc != 0:
+        raise ValueError("synth_routing_host rejected its arguments")
+    return out
+
+
+def host_layer(cfg: Config, seed: int = 0, routing: str = "normal") -> dict:
+    """Every tensor of a (small) layer on the host, raw storage, shaped."""
+    out = {}
+    for name, sp in specs(cfg).items():
+        out[name] = host_tensor(cfg, name, seed, routing).reshape(sp.shape)
+        sc = host_scales(cfg, name, seed)
+        if sc is not None:
+            out["scale:" + name] = sc
+    out["router_bias"] = router_bias(cfg)
+    out["gamma"] = gamma(cfg)
+    return out
+
+
+# ---- device-side generation (needs torch with a GPU) -------------------------------
+
+def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cuda",
+                 names=None) -> dict:
+    """Every tensor of the layer generated directly in device memory (torch
+    tensors of the raw storage dtype).  Same bits as host_layer()."""
+    import torch
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8}
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, sp in specs(cfg).items():
+        if names is not None and name not in names:
+            continue
+        t = torch.empty(sp.shape, dtype=tdt[sp.dtype], device=device)
+        kind, scale, rng = draw_params(cfg, name, routing)
+        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()), sp.dtype, sp.numel,
+                                         seed, TID[name], 0, kind, scale, rng,
+                                         ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"synth_fill_device failed ({rc}) for {name}")
+        out[name] = t
+        sc = host_scales(cfg, name, seed)
+        if sc is not None:
+            out["scale:" + name] = torch.from_numpy(sc).to(device)
+    b = router_bias(cfg)
+    out["router_bias"] = None if b is None else torch.from_numpy(b).to(device)
+    out["gamma"] = torch.from_numpy(gamma(cfg)).to(device)
+    return out

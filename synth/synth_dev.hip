@@ -1,0 +1,58 @@
+// synth_dev.hip -- device (gfx950) generator of seeded synthetic layer inputs.
+//
+// Writes a tensor straight into device memory with the same bits as
+// synth_fill_host() in synth_host.c (both expand synth_rng.h), so a
+// 60 GB layer is generated in HBM without a host copy, while the CPU side can
+// regenerate any slice of it.  Holds no arithmetic of the MoE layer.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "synth_rng.h"
+
+#define SYNTH_API extern "C" __attribute__((visibility("default")))
+
+template <int DT>
+__global__ void __launch_bounds__(256) synth_fill_kernel(void *out, int64_t n, uint64_t seed,
+                                                         uint32_t tensor_id, int64_t offset,
+                                                         int kind, float scale, int32_t range) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float v = synth_value(seed, tensor_id, (uint64_t)(offset + i), kind, scale, range);
+    if (DT == SYNTH_F32) ((float *)out)[i] = v;
+    else if (DT == SYNTH_BF16) ((uint16_t *)out)[i] = synth_f32_to_bf16(v);
+    else ((uint8_t *)out)[i] = synth_f32_to_e4m3(v);
+  }
+}
+
+// Device twin of synth_fill_host.  `out` is a device pointer with room for n
+// elements of dtype.  Enqueued on `stream`; returns 0, -1 on a bad argument,
+// -4 if the launch failed.
+SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
+                                uint32_t tensor_id, int64_t offset, int kind, float scale,
+                                int32_t range, hipStream_t stream) {
+  if (n < 0 || offset < 0) return -1;
+  if (n == 0) return 0;
+  if (!out) return -1;
+  if (kind != SYNTH_NORMAL && kind != SYNTH_DYADIC) return -1;
+  if (kind == SYNTH_DYADIC && range < 0) return -1;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  dim3 grid((unsigned)blocks), block(256);
+  switch (dtype) {
+    case SYNTH_F32:
+      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_F32>, grid, block, 0, stream, out, n, seed,
+                         tensor_id, offset, kind, scale, range);
+      break;
+    case SYNTH_BF16:
+      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_BF16>, grid, block, 0, stream, out, n, seed,
+                         tensor_id, offset, kind, scale, range);
+      break;
+    case SYNTH_FP8E4M3:
+      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_FP8E4M3>, grid, block, 0, stream, out, n,
+                         seed, tensor_id, offset, kind, scale, range);
+      break;
+    default:
+      return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
