@@ -1,0 +1,154 @@
+/*
+ * moe.h -- C ABI of the Stable LatentMoE layer forward on one MI355X (gfx950).
+ *
+ * The layer (Kimi K3 "Stable LatentMoE"): tech.news18a.com
+ * "KimiK3的StableLatentMoE架构解析" -- module structure (figure 1: router,
+ * down_proj, experts, latent_norm, up_proj, shared), forward flow (figure 2),
+ * SiTU-GLU (first technique), RMSNorm before up (second technique),
+ * Quantile Balancing (third technique); mkdocs.reaper.mx "Vue d'ensemble de
+ * l'architecture" -- per-token path steps c-g and the parameter-budget
+ * table (d = 7168, L = 3584, 896 experts, top 16, 2 shared experts).
+ *
+ * For a batch of bt token rows x[bt][d] the library computes
+ *   z = x W_r^T + b                       router logits (fp32), s = sigmoid(z)
+ *   alpha = batch cutoffs (BATCH) or the caller's (GIVEN)
+ *   per token: the top_k experts of largest z - alpha (ties: lower id)
+ *   x_lat = x W_down_proj^T               (d -> latent)
+ *   o_p   = W_d,e (phi(W_g,e x_lat) * psi(W_u,e x_lat)) per (token, expert) pair
+ *   n     = RMSNorm(sum_j s_j o_j) * gamma
+ *   y     = n W_up_proj^T + sum_{j<S} W_ds,j (phi(W_gs,j x) * psi(W_us,j x))
+ * with phi(g) = sigmoid(g) beta tanh(g/beta), psi(u) = beta_u tanh(u/beta_u).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers on the current HIP device, row-major;
+ *    weight matrices are [out][in].  Structs and scalars are host memory.
+ *  - The caller owns and allocates every buffer, including the workspace of
+ *    moe_workspace_bytes() bytes (256-byte aligned).  The library allocates
+ *    no device memory and never synchronises the host: work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and is complete when
+ *    that stream is.  Inputs are read-only; outputs are fully overwritten.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    error nothing is enqueued and a negative moe_status is returned.
+ *    Asynchronous device faults surface at the caller's next synchronisation.
+ *  - Calls that share a workspace must be ordered on one stream.
+ *  - NaN or Inf inputs are not supported (results unspecified).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL where required, negative size, bad enum */
+  MOE_ERR_UNSUPPORTED = -2, /* shape or dtype combination not implemented */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL, too small or misaligned */
+  MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8E4M3_B128 = 2 /* OCP e4m3fn codes + fp32 scale per 128x128 block */
+} moe_dtype;
+
+/* Quantile Balancing cutoff (tech.news18a.com page, third technique): BATCH
+ * takes alpha[e] = the m-th largest fp32 logit of expert e over the batch,
+ * m = clamp(ceil(bt*top_k/E), 1, bt), so each expert's load is driven to
+ * bt*top_k/E; GIVEN takes a caller-held alpha (e.g. a running estimate). */
+typedef enum { MOE_CUTOFF_GIVEN = 0, MOE_CUTOFF_BATCH = 1 } moe_cutoff_mode;
+
+typedef struct moe_config {
+  int64_t d;            /* model width (7168 for K3) */
+  int64_t latent;       /* latent width L of the routed path (3584) */
+  int64_t n_experts;    /* E routed experts (896), 1 <= E <= 1024 */
+  int64_t top_k;        /* k experts per token (16), 1 <= k <= min(E, 64) */
+  int64_t expert_inter; /* I, routed expert intermediate width (3072) */
+  int64_t n_shared;     /* S shared experts (2), 0 <= S <= 4 */
+  int64_t shared_inter; /* I_s per shared expert (3072) */
+  float beta;           /* SiTU gate cap (4) */
+  float beta_u;         /* SiTU up-branch cap (25) */
+  float rms_eps;        /* latent RMSNorm epsilon (1e-6) */
+  int32_t act_dtype;    /* x and y: MOE_F32 or MOE_BF16 */
+  int32_t weight_dtype; /* W_down_proj, experts, W_up_proj, shared: MOE_F32 (with f32
+                           act), MOE_BF16 or MOE_FP8E4M3_B128 (with bf16 act) */
+  int32_t router_dtype; /* W_r: equal to act_dtype */
+  int32_t cutoff_mode;  /* moe_cutoff_mode */
+} moe_config;
+/* Shape limits: bf16/fp8 paths need d, latent, expert_inter, shared_inter
+ * multiples of 64 (of 128 with fp8 weights); else MOE_ERR_UNSUPPORTED. */
+
+typedef struct moe_weights {
+  const void *w_router;      /* [E][d] router_dtype */
+  const float *router_bias;  /* [E] logit offsets, or NULL (= 0) */
+  const float *cutoff;       /* [E] GIVEN-mode alpha in logit units, or NULL (= 0) */
+  const void *w_down_proj;   /* [L][d] */
+  const void *w_gate;        /* [E][I][L] */
+  const void *w_up;          /* [E][I][L] */
+  const void *w_down;        /* [E][L][I] */
+  const float *latent_gamma; /* [L] RMSNorm gain */
+  const void *w_up_proj;     /* [d][L] */
+  const void *sh_gate;       /* [S][I_s][d] */
+  const void *sh_up;         /* [S][I_s][d] */
+  const void *sh_down;       /* [S][d][I_s] */
+  /* MOE_FP8E4M3_B128 only (else NULL): fp32 block scales, one per 128x128
+   * block of each [out][in] matrix, laid out [matrices][out/128][in/128]. */
+  const float *s_down_proj, *s_gate, *s_up, *s_down, *s_up_proj, *s_sh_gate, *s_sh_up,
+      *s_sh_down;
+} moe_weights;
+
+/* Router results.  The router "computes scores and indices" (tech.news18a.com
+ * page, figure 2).  topk_idx lists each token's experts in ascending id;
+ * topk_w is sigmoid(z) of each (the bias included, the cutoff excluded, not
+ * renormalised). */
+typedef struct moe_route_out {
+  int32_t *topk_idx; /* [bt][k] required */
+  float *topk_w;     /* [bt][k] required */
+  float *cutoff;     /* [E] optional: the alpha used (the batch quantile in BATCH mode) */
+  float *logits;     /* [bt][E] optional: fp32 z */
+} moe_route_out;
+
+/* Grouping of (token, expert) pairs p = t*k + j by expert -- the single-GPU
+ * form of the dispatch exchange (mkdocs.reaper.mx page, section
+ * "Vérification de compréhension": dispatch and combine per MoE layer). */
+typedef struct moe_dispatch_out {
+  int32_t *counts;   /* [E] pairs per expert */
+  int32_t *offsets;  /* [E+1] exclusive prefix sum of counts */
+  int32_t *perm;     /* [bt*k] pair ids ordered by (expert asc, token asc) */
+  int32_t *inv_perm; /* [bt*k] position of pair p in perm */
+} moe_dispatch_out;
+
+/* Device bytes of workspace moe_route / moe_dispatch / moe_forward need for
+ * bt tokens (the maximum of the three); 0 for an invalid config. */
+size_t moe_workspace_bytes(const moe_config *cfg, int64_t bt);
+
+/* Router: logits, cutoffs and top-k of bt tokens x[bt][d] (act_dtype). */
+moe_status moe_route(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
+                     moe_route_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch of given routing indices topk_idx[bt][k] (each in [0, E), distinct
+ * and ascending per token).  All four outputs are required. */
+moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int64_t bt,
+                        moe_dispatch_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole layer: y[bt][d] (act_dtype).  route / disp may be NULL; when given
+ * they receive the routing and dispatch of this call.  The shared experts
+ * run on shared_stream (NULL: on `stream`) and are joined into `stream`
+ * before the output projection. */
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
+                       void *y, moe_route_out *route, moe_dispatch_out *disp, void *ws,
+                       size_t ws_bytes, void *stream, void *shared_stream);
+
+/* Static text for a status code. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

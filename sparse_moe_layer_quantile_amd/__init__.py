@@ -1,0 +1,224 @@
+"""Stable LatentMoE layer forward on one MI355X (gfx950).
+
+Python binding of ``libmoe.so``, the C ABI declared in ``include/moe.h``:
+``moe_workspace_bytes``, ``moe_route``, ``moe_dispatch``, ``moe_forward``,
+``moe_status_str``.  This module only marshals arguments: every step of the
+layer runs in the library's HIP kernels.  PyTorch provides device memory and
+streams (``tensor.data_ptr()``, ``torch.cuda.current_stream()``).  There is no
+fallback: if the library is missing the import of this module fails.
+
+The layer (Kimi K3 Stable LatentMoE): tech.news18a.com
+"KimiK3的StableLatentMoE架构解析" figures 1-2 and its three techniques;
+mkdocs.reaper.mx "Vue d'ensemble de l'architecture", per-token steps c-g.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_FP8E4M3_B128 = 0, 1, 2
+CUTOFF_GIVEN, CUTOFF_BATCH = 0, 1
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128}
+CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH}
+
+_P = ctypes.c_void_p
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("latent", ctypes.c_int64),
+                ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
+                ("expert_inter", ctypes.c_int64), ("n_shared", ctypes.c_int64),
+                ("shared_inter", ctypes.c_int64), ("beta", ctypes.c_float),
+                ("beta_u", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("router_dtype", ctypes.c_int32), ("cutoff_mode", ctypes.c_int32)]
+
+
+WEIGHT_FIELDS = ("w_router", "router_bias", "cutoff", "w_down_proj", "w_gate", "w_up",
+                 "w_down", "latent_gamma", "w_up_proj", "sh_gate", "sh_up", "sh_down",
+                 "s_down_proj", "s_gate", "s_up", "s_down", "s_up_proj", "s_sh_gate",
+                 "s_sh_up", "s_sh_down")
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in WEIGHT_FIELDS]
+
+
+class MoeRouteOut(ctypes.Structure):
+    _fields_ = [("topk_idx", _P), ("topk_w", _P), ("cutoff", _P), ("logits", _P)]
+
+
+class MoeDispatchOut(ctypes.Structure):
+    _fields_ = [("counts", _P), ("offsets", _P), ("perm", _P), ("inv_perm", _P)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    CP = ctypes.POINTER
+    lib.moe_workspace_bytes.argtypes = [CP(MoeConfig), ctypes.c_int64]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route.argtypes = [CP(MoeConfig), CP(MoeWeights), _P, ctypes.c_int64,
+                              CP(MoeRouteOut), _P, ctypes.c_size_t, _P]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_dispatch.argtypes = [CP(MoeConfig), _P, ctypes.c_int64, CP(MoeDispatchOut), _P,
+                                 ctypes.c_size_t, _P]
+    lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [CP(MoeConfig), CP(MoeWeights), _P, ctypes.c_int64, _P,
+                                CP(MoeRouteOut), CP(MoeDispatchOut), _P, ctypes.c_size_t, _P,
+                                _P]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
+            "moe_status_str")
+
+
+def status_str(status: int) -> str:
+    return LIB.moe_status_str(int(status)).decode()
+
+
+def make_config(d, latent, n_experts, top_k, expert_inter, n_shared, shared_inter,
+                beta=4.0, beta_u=25.0, rms_eps=1e-6, act="bf16", weight="bf16", router=None,
+                cutoff="batch") -> MoeConfig:
+    router = act if router is None else router
+    return MoeConfig(d, latent, n_experts, top_k, expert_inter, n_shared, shared_inter, beta,
+                     beta_u, rms_eps, DTYPES[act], DTYPES[weight], DTYPES[router],
+                     CUTOFFS[cutoff])
+
+
+# ---- pointer-level calls (ints are device addresses; 0 = NULL) --------------------
+
+def workspace_bytes(cfg: MoeConfig, bt: int) -> int:
+    return int(LIB.moe_workspace_bytes(ctypes.byref(cfg), bt))
+
+
+def moe_route(cfg, weights: MoeWeights, x: int, bt: int, out: MoeRouteOut, ws: int,
+              ws_bytes: int, stream: int) -> int:
+    return LIB.moe_route(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None), bt,
+                         ctypes.byref(out), _P(ws or None), ws_bytes, _P(stream or None))
+
+
+def moe_dispatch(cfg, topk_idx: int, bt: int, out: MoeDispatchOut, ws: int, ws_bytes: int,
+                 stream: int) -> int:
+    return LIB.moe_dispatch(ctypes.byref(cfg), _P(topk_idx or None), bt, ctypes.byref(out),
+                            _P(ws or None), ws_bytes, _P(stream or None))
+
+
+def moe_forward(cfg, weights: MoeWeights, x: int, bt: int, y: int, route, disp, ws: int,
+                ws_bytes: int, stream: int, shared_stream: int = 0) -> int:
+    return LIB.moe_forward(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None), bt,
+                           _P(y or None), ctypes.byref(route) if route is not None else None,
+                           ctypes.byref(disp) if disp is not None else None, _P(ws or None),
+                           ws_bytes, _P(stream or None), _P(shared_stream or None))
+
+
+# ---- torch-tensor convenience layer (memory and streams only) -----------------------
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def weights_struct(tensors: dict) -> MoeWeights:
+    """MoeWeights from a dict of device tensors keyed by the moe_weights field
+    names (missing keys -> NULL)."""
+    return MoeWeights(*(_ptr(tensors.get(n)) for n in WEIGHT_FIELDS))
+
+
+class StableLatentMoE:
+    """One layer: a config and its device-resident weights.  The caller's
+    tensors are borrowed, not copied."""
+
+    def __init__(self, cfg: MoeConfig, tensors: dict):
+        self.cfg = cfg
+        self.tensors = dict(tensors)
+        self.w = weights_struct(self.tensors)
+        self._ws = None
+
+    def workspace(self, bt: int):
+        import torch
+        need = workspace_bytes(self.cfg, bt)
+        if need == 0 and bt > 0:
+            raise MoeError(-2, "moe_workspace_bytes")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def route(self, x, want_logits=False):
+        import torch
+        bt = x.shape[0]
+        E, k = self.cfg.n_experts, self.cfg.top_k
+        dev = x.device
+        idx = torch.empty((bt, k), dtype=torch.int32, device=dev)
+        w = torch.empty((bt, k), dtype=torch.float32, device=dev)
+        cut = torch.empty(E, dtype=torch.float32, device=dev)
+        logits = torch.empty((bt, E), dtype=torch.float32, device=dev) if want_logits else None
+        out = MoeRouteOut(idx.data_ptr(), w.data_ptr(), cut.data_ptr(), _ptr(logits))
+        ws = self.workspace(bt)
+        st = moe_route(self.cfg, self.w, _ptr(x), bt, out, ws.data_ptr(), ws.numel(),
+                       torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise MoeError(st, "moe_route")
+        return dict(idx=idx, w=w, cutoff=cut, logits=logits)
+
+    def dispatch(self, idx):
+        import torch
+        bt = idx.shape[0]
+        E, P = self.cfg.n_experts, idx.numel()
+        dev = idx.device
+        res = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(P, dtype=torch.int32, device=dev),
+                   inv_perm=torch.empty(P, dtype=torch.int32, device=dev))
+        out = MoeDispatchOut(*(res[n].data_ptr() for n in ("counts", "offsets", "perm",
+                                                           "inv_perm")))
+        ws = self.workspace(bt)
+        st = moe_dispatch(self.cfg, idx.data_ptr(), bt, out, ws.data_ptr(), ws.numel(),
+                          torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise MoeError(st, "moe_dispatch")
+        return res
+
+    def forward(self, x, shared_stream=None, return_routing=False, out=None):
+        import torch
+        bt = x.shape[0]
+        E, k, P = self.cfg.n_experts, self.cfg.top_k, x.shape[0] * self.cfg.top_k
+        dev = x.device
+        y = out if out is not None else torch.empty((bt, self.cfg.d), dtype=x.dtype, device=dev)
+        route = disp = None
+        extra = {}
+        if return_routing:
+            extra = dict(idx=torch.empty((bt, k), dtype=torch.int32, device=dev),
+                         w=torch.empty((bt, k), dtype=torch.float32, device=dev),
+                         cutoff=torch.empty(E, dtype=torch.float32, device=dev),
+                         logits=torch.empty((bt, E), dtype=torch.float32, device=dev),
+                         counts=torch.empty(E, dtype=torch.int32, device=dev),
+                         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                         perm=torch.empty(P, dtype=torch.int32, device=dev),
+                         inv_perm=torch.empty(P, dtype=torch.int32, device=dev))
+            route = MoeRouteOut(*(extra[n].data_ptr() for n in ("idx", "w", "cutoff",
+                                                                "logits")))
+            disp = MoeDispatchOut(*(extra[n].data_ptr() for n in ("counts", "offsets", "perm",
+                                                                  "inv_perm")))
+        ws = self.workspace(bt)
+        st = moe_forward(self.cfg, self.w, _ptr(x), bt, y.data_ptr(), route, disp,
+                         ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream,
+                         shared_stream.cuda_stream if shared_stream is not None else 0)
+        if st != 0:
+            raise MoeError(st, "moe_forward")
+        return (y, extra) if return_routing else y

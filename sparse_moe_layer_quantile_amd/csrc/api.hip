@@ -1,0 +1,419 @@
+// api.hip -- the C ABI declared in include/moe.h: argument validation,
+// workspace planning and the launch sequence of the Stable LatentMoE forward.
+//
+// Launch order of moe_forward (tech.news18a.com "KimiK3的StableLatentMoE架构解析",
+// figure 2: two parallel paths from the flattened x; mkdocs.reaper.mx "Vue
+// d'ensemble de l'architecture", per-token steps c-g):
+//   shared_stream: shared gate/up + SiTU -> hs                    (step g, part 1)
+//   stream:        router logits -> cutoffs -> top-k -> dispatch  (step c)
+//                  x_lat = x W_down_proj^T                        (step d)
+//                  grouped gate/up + SiTU -> h (gathered rows)    (step e)
+//                  grouped down, x routing weight -> o            (step e)
+//                  combine + latent RMSNorm -> n                  (step f)
+//                  join(shared_stream)
+//                  y = [n | hs] [W_up_proj | W_ds,0 | W_ds,1]^T   (steps f, g; the final sum)
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "gemm.h"
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t elem_size(int32_t dt) {
+  switch (dt) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 2;
+    case MOE_FP8E4M3_B128: return 1;
+  }
+  return 0;
+}
+
+struct Plan {
+  int path = PATH_BF16;
+  bool fp8 = false;
+  int64_t act_bytes = 2;
+  // byte offsets into the workspace
+  size_t z, zT, alpha, idx, w, counts, offsets, tile_offsets, perm, inv_perm, masks, xlat, h, o,
+      n, hs, total;
+};
+
+moe_status check_config(const moe_config *c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->d <= 0 || c->latent <= 0 || c->n_experts <= 0 || c->top_k <= 0 ||
+      c->expert_inter <= 0 || c->n_shared < 0 || (c->n_shared > 0 && c->shared_inter <= 0))
+    return MOE_ERR_INVALID_ARG;
+  if (c->cutoff_mode != MOE_CUTOFF_GIVEN && c->cutoff_mode != MOE_CUTOFF_BATCH)
+    return MOE_ERR_INVALID_ARG;
+  if (elem_size(c->act_dtype) == 0 || elem_size(c->weight_dtype) == 0 ||
+      elem_size(c->router_dtype) == 0)
+    return MOE_ERR_INVALID_ARG;
+  if (!(c->beta > 0.0f) || !(c->beta_u > 0.0f) || !(c->rms_eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (c->n_experts > 1024 || c->top_k > c->n_experts || c->top_k > 64 || c->n_shared > 4)
+    return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_F32) {
+    if (c->weight_dtype != MOE_F32 || c->router_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  } else if (c->act_dtype == MOE_BF16) {
+    if (c->router_dtype != MOE_BF16 || c->weight_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  const int64_t q = c->weight_dtype == MOE_FP8E4M3_B128 ? 128 : 64;
+  if (c->d % 64 || c->latent % q || c->expert_inter % q || (c->n_shared && c->shared_inter % q))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
+  if (c->latent > 4096) return MOE_ERR_UNSUPPORTED;  // combine stages a latent row per wave in LDS
+  return MOE_OK;
+}
+
+moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
+  moe_status st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (bt < 0) return MOE_ERR_INVALID_ARG;
+  if (bt * c->top_k > INT32_MAX || bt > INT32_MAX / 64) return MOE_ERR_UNSUPPORTED;
+  p->path = c->act_dtype == MOE_F32 ? PATH_F32 : PATH_BF16;
+  p->fp8 = c->weight_dtype == MOE_FP8E4M3_B128;
+  p->act_bytes = elem_size(c->act_dtype);
+  const int64_t E = c->n_experts, k = c->top_k, P = bt * k, L = c->latent;
+  const int64_t nb = (bt + 63) / 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  p->z = take(4 * bt * E);
+  p->zT = take(4 * bt * E);
+  p->alpha = take(4 * E);
+  p->idx = take(4 * P);
+  p->w = take(4 * P);
+  p->counts = take(4 * E);
+  p->offsets = take(4 * (E + 1));
+  p->tile_offsets = take(4 * (E + 1));
+  p->perm = take(4 * P);
+  p->inv_perm = take(4 * P);
+  p->masks = take(8 * E * nb);
+  p->xlat = take(p->act_bytes * bt * L);
+  p->h = take(p->act_bytes * P * c->expert_inter);
+  p->o = take(p->act_bytes * P * L);
+  p->n = take(p->act_bytes * bt * L);
+  p->hs = take(p->act_bytes * bt * c->n_shared * c->shared_inter);
+  p->total = off + kAlign;
+  return MOE_OK;
+}
+
+moe_status check_ws(const Plan &p, void *ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < p.total - kAlign || (reinterpret_cast<uintptr_t>(ws) % kAlign))
+    return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts) {
+  if (!w || !w->w_router) return false;
+  if (c->cutoff_mode == MOE_CUTOFF_GIVEN) { /* cutoff may be NULL */ }
+  if (!need_experts) return true;
+  if (!w->w_down_proj || !w->w_gate || !w->w_up || !w->w_down || !w->latent_gamma ||
+      !w->w_up_proj)
+    return false;
+  if (c->n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return false;
+  if (c->weight_dtype == MOE_FP8E4M3_B128) {
+    if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
+    if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;
+  }
+  return true;
+}
+
+GemmArgs base_args(const moe_config *c) {
+  GemmArgs a = {};
+  a.beta = c->beta;
+  a.inv_beta = 1.0f / c->beta;
+  a.beta_u = c->beta_u;
+  a.inv_beta_u = 1.0f / c->beta_u;
+  return a;
+}
+
+#define MOE_TRY_HIP(expr)                        \
+  do {                                           \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// Router: logits (+ transposed copy for the batch quantile), cutoffs, top-k.
+moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, const void *x,
+                     int64_t bt, float *z, int32_t *idx, float *wts, float *cutoff_out, void *ws,
+                     hipStream_t s) {
+  const int64_t E = c->n_experts;
+  const bool batch = c->cutoff_mode == MOE_CUTOFF_BATCH;
+  float *zT = at<float>(ws, p.zT);
+  GemmArgs a = base_args(c);
+  a.M = bt;
+  a.N = E;
+  a.nseg = 1;
+  a.seg[0] = GemmSeg{x, c->d, w->w_router, c->d, nullptr, c->d};
+  a.out = z;
+  a.ldo = E;
+  a.out_t = batch ? zT : nullptr;
+  a.bias = w->router_bias;
+  const int bm = gemm_bm(p.path);
+  MOE_TRY_HIP(gemm_launch(a, p.path, GK_ROUTER, false, (bt + bm - 1) / bm, s));
+  const float *alpha;
+  if (batch) {
+    int64_t m = (bt * c->top_k + E - 1) / E;
+    m = m < 1 ? 1 : (m > bt ? bt : m);
+    float *zeta = cutoff_out ? cutoff_out : at<float>(ws, p.alpha);
+    MOE_TRY_HIP(launch_quantile(zT, bt, E, m, zeta, s));
+    alpha = zeta;
+  } else {
+    alpha = w->cutoff;
+    if (cutoff_out) MOE_TRY_HIP(launch_copy_or_zero_f32(cutoff_out, w->cutoff, E, s));
+  }
+  MOE_TRY_HIP(launch_topk(z, alpha, bt, E, c->top_k, idx, wts, s));
+  return MOE_OK;
+}
+
+// One pool of events per process for the two-stream join.
+std::mutex g_ev_mu;
+std::vector<std::pair<int, hipEvent_t>> g_ev_free;
+
+hipError_t ev_get(hipEvent_t *ev) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(g_ev_mu);
+    for (size_t i = 0; i < g_ev_free.size(); ++i)
+      if (g_ev_free[i].first == dev) {
+        *ev = g_ev_free[i].second;
+        g_ev_free.erase(g_ev_free.begin() + i);
+        return hipSuccess;
+      }
+  }
+  return hipEventCreateWithFlags(ev, hipEventDisableTiming);
+}
+
+void ev_put(hipEvent_t ev) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  g_ev_free.emplace_back(dev, ev);
+}
+
+}  // namespace
+
+MOE_API size_t moe_workspace_bytes(const moe_config *cfg, int64_t bt) {
+  Plan p;
+  if (make_plan(cfg, bt, &p) != MOE_OK) return 0;
+  return p.total - kAlign;
+}
+
+MOE_API const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+MOE_API moe_status moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
+                             int64_t bt, moe_route_out *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  Plan p;
+  moe_status st = make_plan(cfg, bt, &p);
+  if (st != MOE_OK) return st;
+  if (!check_weights(cfg, w, false) || !out || !out->topk_idx || !out->topk_w)
+    return MOE_ERR_INVALID_ARG;
+  if (bt > 0 && !x) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bt == 0) {
+    if (out->cutoff && cfg->cutoff_mode == MOE_CUTOFF_GIVEN)
+      MOE_TRY_HIP(launch_copy_or_zero_f32(out->cutoff, w->cutoff, cfg->n_experts, s));
+    return MOE_OK;
+  }
+  float *z = out->logits ? out->logits : at<float>(ws, p.z);
+  return run_route(cfg, p, w, x, bt, z, out->topk_idx, out->topk_w, out->cutoff, ws, s);
+}
+
+MOE_API moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int64_t bt,
+                                moe_dispatch_out *out, void *ws, size_t ws_bytes,
+                                void *stream) {
+  Plan p;
+  moe_status st = make_plan(cfg, bt, &p);
+  if (st != MOE_OK) return st;
+  if (!out || !out->counts || !out->offsets || !out->perm || !out->inv_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (bt > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(launch_dispatch(topk_idx, bt, cfg->top_k, cfg->n_experts, gemm_bm(p.path),
+                              at<uint64_t>(ws, p.masks), out->counts, out->offsets,
+                              at<int32_t>(ws, p.tile_offsets), out->perm, out->inv_perm, s));
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
+                               int64_t bt, void *y, moe_route_out *route,
+                               moe_dispatch_out *disp, void *ws, size_t ws_bytes, void *stream,
+                               void *shared_stream) {
+  Plan p;
+  moe_status st = make_plan(cfg, bt, &p);
+  if (st != MOE_OK) return st;
+  if (!check_weights(cfg, w, true)) return MOE_ERR_INVALID_ARG;
+  if (bt > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  if (route && (!route->topk_idx || !route->topk_w)) return MOE_ERR_INVALID_ARG;
+  if (disp && (!disp->counts || !disp->offsets || !disp->perm || !disp->inv_perm))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t ss = shared_stream ? static_cast<hipStream_t>(shared_stream) : s;
+  if (bt == 0) return MOE_OK;
+
+  const int64_t E = cfg->n_experts, k = cfg->top_k, P = bt * k, d = cfg->d, L = cfg->latent;
+  const int64_t I = cfg->expert_inter, S = cfg->n_shared, Is = cfg->shared_inter;
+  const int bm = gemm_bm(p.path);
+  const bool fp8 = p.fp8;
+  const int64_t dense_mt = (bt + bm - 1) / bm;
+
+  // ---- shared experts: gate/up + SiTU on the second stream -----------------------
+  hipEvent_t ev_x = nullptr, ev_sh = nullptr;
+  const bool two_streams = S > 0 && ss != s;
+  void *hs = at<void>(ws, p.hs);
+  if (S > 0) {
+    if (two_streams) {
+      if (ev_get(&ev_x) != hipSuccess || ev_get(&ev_sh) != hipSuccess) return MOE_ERR_HIP;
+      MOE_TRY_HIP(hipEventRecord(ev_x, s));
+      MOE_TRY_HIP(hipStreamWaitEvent(ss, ev_x, 0));
+    }
+    GemmArgs a = base_args(cfg);
+    a.M = bt;
+    a.N = S * Is;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{x, d, w->sh_gate, d, w->s_sh_gate, d};
+    a.b_up = w->sh_up;
+    a.bscale_up = w->s_sh_up;
+    a.out = hs;
+    a.ldo = S * Is;
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, fp8, dense_mt, ss));
+    if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_sh, ss));
+  }
+
+  // ---- routing -----------------------------------------------------------------
+  float *z = (route && route->logits) ? route->logits : at<float>(ws, p.z);
+  int32_t *idx = route ? route->topk_idx : at<int32_t>(ws, p.idx);
+  float *wts = route ? route->topk_w : at<float>(ws, p.w);
+  st = run_route(cfg, p, w, x, bt, z, idx, wts, route ? route->cutoff : nullptr, ws, s);
+  if (st != MOE_OK) return st;
+
+  // ---- dispatch -----------------------------------------------------------------
+  int32_t *counts = disp ? disp->counts : at<int32_t>(ws, p.counts);
+  int32_t *offsets = disp ? disp->offsets : at<int32_t>(ws, p.offsets);
+  int32_t *perm = disp ? disp->perm : at<int32_t>(ws, p.perm);
+  int32_t *inv_perm = disp ? disp->inv_perm : at<int32_t>(ws, p.inv_perm);
+  int32_t *tile_offsets = at<int32_t>(ws, p.tile_offsets);
+  MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, bm, at<uint64_t>(ws, p.masks), counts, offsets,
+                              tile_offsets, perm, inv_perm, s));
+
+  // ---- x_lat = x W_down_proj^T ---------------------------------------------------
+  void *xlat = at<void>(ws, p.xlat);
+  {
+    GemmArgs a = base_args(cfg);
+    a.M = bt;
+    a.N = L;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, w->s_down_proj, d};
+    a.out = xlat;
+    a.ldo = L;
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
+  }
+
+  // ---- routed experts ---------------------------------------------------------------
+  const int64_t grouped_mt = (P + bm - 1) / bm + E;
+  void *h = at<void>(ws, p.h);
+  void *o = at<void>(ws, p.o);
+  {
+    GemmArgs a = base_args(cfg);
+    a.M = P;
+    a.N = I;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{xlat, L, w->w_gate, L, w->s_gate, L};
+    a.b_up = w->w_up;
+    a.bscale_up = w->s_up;
+    a.offsets = offsets;
+    a.tile_offsets = tile_offsets;
+    a.n_experts = (int32_t)E;
+    a.b_estride = I * L;
+    a.s_estride = fp8 ? (I / 128) * (L / 128) : 0;
+    a.gather = perm;
+    a.gather_div = (int32_t)k;
+    a.out = h;
+    a.ldo = I;
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, fp8, grouped_mt, s));
+  }
+  {
+    GemmArgs a = base_args(cfg);
+    a.M = P;
+    a.N = L;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{h, I, w->w_down, I, w->s_down, I};
+    a.offsets = offsets;
+    a.tile_offsets = tile_offsets;
+    a.n_experts = (int32_t)E;
+    a.b_estride = L * I;
+    a.s_estride = fp8 ? (L / 128) * (I / 128) : 0;
+    a.row_w = wts;
+    a.row_perm = perm;
+    a.out = o;
+    a.ldo = L;
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_DOWN, fp8, grouped_mt, s));
+  }
+
+  // ---- combine + latent RMSNorm -------------------------------------------------------
+  void *nrm = at<void>(ws, p.n);
+  MOE_TRY_HIP(launch_combine_norm(o, p.path == PATH_BF16, inv_perm, bt, k, L,
+                                  w->latent_gamma, cfg->rms_eps, nrm, s));
+
+  // ---- y = n W_up_proj^T + sum_j hs_j W_ds,j^T ------------------------------------------
+  if (two_streams) {
+    MOE_TRY_HIP(hipStreamWaitEvent(s, ev_sh, 0));
+    ev_put(ev_x);
+    ev_put(ev_sh);
+  }
+  {
+    GemmArgs a = base_args(cfg);
+    a.M = bt;
+    a.N = d;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{nrm, L, w->w_up_proj, L, w->s_up_proj, L};
+    const int64_t esz = elem_size(cfg->weight_dtype);
+    for (int64_t j = 0; j < S; ++j) {
+      GemmSeg &g = a.seg[a.nseg++];
+      g.a = static_cast<const char *>(hs) + p.act_bytes * j * Is;
+      g.lda = S * Is;
+      g.b = static_cast<const char *>(w->sh_down) + esz * j * d * Is;
+      g.ldb = Is;
+      g.bscale = fp8 ? w->s_sh_down + j * (d / 128) * (Is / 128) : nullptr;
+      g.k = Is;
+    }
+    a.out = y;
+    a.ldo = d;
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
+  }
+  return MOE_OK;
+}

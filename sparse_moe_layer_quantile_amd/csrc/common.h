@@ -1,0 +1,75 @@
+// common.h -- shared device helpers of the gfx950 MoE kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+namespace moe {
+
+// ---- bf16 storage ------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+// Round to nearest even; finite inputs only.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- fp8 e4m3fn (OCP) -> fp32, from the format definition --------------------
+// 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+// subnormals m * 2^-9.  NaN (S.1111.111) is not expected in weights.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t sign = (code & 0x80u) << 24;
+  const uint32_t em = code & 0x7Fu;
+  float v;
+  if (em >= 0x08u) {
+    v = __uint_as_float(((em >> 3) + 120u) << 23 | (em & 7u) << 20);
+  } else {
+    v = (float)em * (1.0f / 512.0f);
+  }
+  return __uint_as_float(__float_as_uint(v) | sign);
+}
+
+// ---- elementary functions (from their definitions via exp) ------------------
+// exp(x) = 2^(x log2 e) on the hardware exp2 unit.
+__device__ __forceinline__ float exp_fast(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+// sigmoid(x) = 1 / (1 + e^-x)
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_fast(1.0f + exp_fast(-x)); }
+// tanh(x) = sign(x) (1 - e^-2|x|) / (1 + e^-2|x|)
+__device__ __forceinline__ float tanh_f(float x) {
+  const float e = exp_fast(-2.0f * fabsf(x));
+  return copysignf((1.0f - e) * rcp_fast(1.0f + e), x);
+}
+// SiTU-GLU factors: phi(g) = sigmoid(g) beta tanh(g / beta), psi(u) = beta_u tanh(u / beta_u)
+__device__ __forceinline__ float situ(float g, float u, float beta, float inv_beta,
+                                      float beta_u, float inv_beta_u) {
+  const float phi = sigmoid_f(g) * beta * tanh_f(g * inv_beta);
+  const float psi = beta_u * tanh_f(u * inv_beta_u);
+  return phi * psi;
+}
+
+// Order-preserving map of an fp32 value to uint32 (larger value -> larger
+// key); -0 is folded onto +0 so that equal values give equal keys.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+}  // namespace moe

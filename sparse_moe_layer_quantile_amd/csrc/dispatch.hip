@@ -1,0 +1,154 @@
+// dispatch.hip -- grouping of (token, expert) pairs by expert.
+//
+// On one GPU the dispatch exchange of the MoE layer (mkdocs.reaper.mx "Vue
+// d'ensemble de l'architecture", section "Vérification de compréhension":
+// one dispatch and one combine per MoE layer) becomes a permutation of the
+// pair list into expert-contiguous segments, which GroupedExperts then runs
+// as one grouped GEMM (tech.news18a.com "KimiK3的StableLatentMoE架构解析",
+// figure 1: experts packed by group for memory locality).
+//
+// Deterministic stable counting sort, no order-dependent atomics:
+//   1. per block of 64 tokens, an LDS bitmask per expert of the tokens that
+//      chose it (ds_or_b64); popcounts add into counts[e] (integer sums);
+//   2. one workgroup scans counts -> offsets, and ceil(counts / tile_bm) ->
+//      the first M-tile of each expert for the grouped GEMMs;
+//   3. one workgroup per expert walks its masks in token order: a prefix
+//      over the blocks' popcounts places every pair at its stable position.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ void __launch_bounds__(256) dispatch_mask_kernel(const int32_t *__restrict__ idx,
+                                                            int64_t bt, int k, int E, int nb,
+                                                            uint64_t *__restrict__ masks,
+                                                            int32_t *__restrict__ counts) {
+  extern __shared__ uint64_t bits[];  // [E]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) bits[e] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int ntok = (int)min((int64_t)64, bt - t0);
+  for (int p = tid; p < ntok * k; p += 256) {
+    const int tl = p / k;
+    const int e = idx[t0 * k + p];
+    if (e >= 0 && e < E) atomicOr((unsigned long long *)&bits[e], 1ull << tl);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    const uint64_t m = bits[e];
+    masks[(int64_t)e * nb + blockIdx.x] = m;
+    const int c = __popcll(m);
+    if (c) atomicAdd(&counts[e], c);
+  }
+}
+
+// One workgroup of 1024 threads; E <= 1024.
+__global__ void __launch_bounds__(1024) dispatch_scan_kernel(const int32_t *__restrict__ counts,
+                                                             int E, int tile_bm,
+                                                             int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ tile_offsets) {
+  __shared__ int32_t wsum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t c = tid < E ? counts[tid] : 0;
+  const int32_t tc = (c + tile_bm - 1) / tile_bm;
+  int32_t a = c, b = tc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t oa = __shfl_up(a, off, 64), ob = __shfl_up(b, off, 64);
+    if (lane >= off) { a += oa; b += ob; }
+  }
+  if (lane == 63) { wsum[0][wave] = a; wsum[1][wave] = b; }
+  __syncthreads();
+  int32_t pa = 0, pb = 0;
+  for (int w = 0; w < wave; ++w) { pa += wsum[0][w]; pb += wsum[1][w]; }
+  a += pa;
+  b += pb;
+  if (tid < E) {
+    offsets[tid + 1] = a;
+    tile_offsets[tid + 1] = b;
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    tile_offsets[0] = 0;
+  }
+}
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int32_t v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256) dispatch_scatter_kernel(
+    const uint64_t *__restrict__ masks, int nb, const int32_t *__restrict__ idx, int k,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv_perm) {
+  __shared__ int32_t wsum[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t *mk = masks + (int64_t)e * nb;
+  int32_t run = offsets[e];
+  for (int b0 = 0; b0 < nb; b0 += 256) {
+    const int b = b0 + tid;
+    uint64_t m = b < nb ? mk[b] : 0ull;
+    const int32_t c = __popcll(m);
+    int32_t incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) before += wsum[w];
+      total += wsum[w];
+    }
+    int32_t pos = run + before + incl - c;
+    while (m) {
+      const int tl = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int64_t t = (int64_t)b * 64 + tl;
+      const int j = lower_bound_i32(idx + t * k, k, e);
+      const int32_t p = (int32_t)(t * k + j);
+      perm[pos] = p;
+      inv_perm[p] = pos;
+      ++pos;
+    }
+    run += total;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
+                           int tile_bm, uint64_t *masks, int32_t *counts, int32_t *offsets,
+                           int32_t *tile_offsets, int32_t *perm, int32_t *inv_perm,
+                           hipStream_t s) {
+  const int E = (int)n_experts;
+  hipError_t err = launch_zero_i32(counts, E, s);
+  if (err != hipSuccess) return err;
+  const int nb = (int)((bt + 63) / 64);
+  if (nb > 0) {
+    hipLaunchKernelGGL(dispatch_mask_kernel, dim3(nb), dim3(256), sizeof(uint64_t) * E, s, idx,
+                       bt, (int)k, E, nb, masks, counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, tile_bm,
+                     offsets, tile_offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (nb > 0) {
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, masks, nb, idx,
+                       (int)k, offsets, perm, inv_perm);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace moe

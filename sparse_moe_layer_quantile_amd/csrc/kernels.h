@@ -1,0 +1,51 @@
+// kernels.h -- internal launch interface between the C ABI (api.hip) and the
+// kernels.  Every launcher enqueues on the given stream and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct GemmArgs;
+
+enum GemmPath { PATH_BF16 = 0, PATH_F32 = 1 };
+enum GemmKind {
+  GK_ROUTER = 0,       // z = A B^T + bias -> fp32 (+ transposed copy)
+  GK_DENSE = 1,        // C = A B^T (K may be split over segments)
+  GK_DENSE_SITU = 2,   // h = SiTU(A Bg^T, A Bu^T)
+  GK_EXPERT_SITU = 3,  // grouped + gathered A, SiTU epilogue
+  GK_EXPERT_DOWN = 4,  // grouped, epilogue scales row p by its routing weight
+};
+
+int gemm_bm(int path);
+int gemm_bn_out(int path, bool dual);
+hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int64_t m_tiles,
+                       hipStream_t s);
+
+// ---- routing ------------------------------------------------------------------
+// zT [E][bt] fp32 -> alpha[e] = m-th largest of row e.
+hipError_t launch_quantile(const float *zT, int64_t bt, int64_t n_experts, int64_t m,
+                           float *alpha, hipStream_t s);
+// z [bt][E] fp32, alpha [E] or NULL -> idx [bt][k] ascending, w [bt][k] = sigmoid(z).
+hipError_t launch_topk(const float *z, const float *alpha, int64_t bt, int64_t n_experts,
+                       int64_t k, int32_t *idx, float *w, hipStream_t s);
+// dst[i] = src ? src[i] : 0 for i < n.
+hipError_t launch_copy_or_zero_f32(float *dst, const float *src, int64_t n, hipStream_t s);
+hipError_t launch_zero_i32(int32_t *dst, int64_t n, hipStream_t s);
+
+// ---- dispatch -------------------------------------------------------------------
+// masks: [E][ceil(bt/64)] u64 scratch; counts must be zeroed first.
+hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
+                           int tile_bm, uint64_t *masks, int32_t *counts, int32_t *offsets,
+                           int32_t *tile_offsets, int32_t *perm, int32_t *inv_perm,
+                           hipStream_t s);
+
+// ---- combine + latent RMSNorm ---------------------------------------------------
+// o [P][L] (act) rows already scaled by their routing weight; n [bt][L] (act).
+hipError_t launch_combine_norm(const void *o, bool bf16, const int32_t *inv_perm, int64_t bt,
+                               int64_t k, int64_t L, const float *gamma, float eps, void *n,
+                               hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,198 @@
+"""Parity harness: GPU path (through the C ABI) against the fp64 CPU oracle.
+
+Comparison rules:
+  * routing indices, dispatch counts / offsets / permutations: bit-exact.  A
+    token whose expert set differs is accepted only as a near tie: the GPU's
+    set must be a valid top-k of the oracle's cutoff-adjusted scores
+    sigmoid(z - alpha) within TIE_BAND, and such tokens are logged.
+  * floating-point outputs: normwise max relative error
+    max|y - y_ref| / max|y_ref| within TOL[dtype] (bf16 2e-2, fp8-weight 6e-2,
+    fp32 1e-4), on the tokens whose routing matches.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+import synth
+
+TIE_BAND = 1e-6
+TOL = {"bf16": 2e-2, "fp8": 6e-2, "f32": 1e-4}
+
+ABI_NAME = {"w_router": "w_router", "router_bias": "router_bias", "w_down_proj": "w_down_proj",
+            "w_gate": "w_gate", "w_up": "w_up", "w_down": "w_down", "gamma": "latent_gamma",
+            "w_up_proj": "w_up_proj", "sh_gate": "sh_gate", "sh_up": "sh_up",
+            "sh_down": "sh_down"}
+SCALE_ABI = {"w_down_proj": "s_down_proj", "w_gate": "s_gate", "w_up": "s_up",
+             "w_down": "s_down", "w_up_proj": "s_up_proj", "sh_gate": "s_sh_gate",
+             "sh_up": "s_sh_up", "sh_down": "s_sh_down"}
+
+
+def tol_of(cfg) -> float:
+    if cfg.act == "f32":
+        return TOL["f32"]
+    return TOL["fp8"] if cfg.weight == "fp8" else TOL["bf16"]
+
+
+def abi_config(cfg, cutoff=None):
+    import sparse_moe_layer_quantile_amd as moe
+    return moe.make_config(cfg.d, cfg.latent, cfg.n_experts, cfg.top_k, cfg.expert_inter,
+                           cfg.n_shared, cfg.shared_inter, cfg.beta, cfg.beta_u, cfg.rms_eps,
+                           act=cfg.act, weight=cfg.weight, router=cfg.router,
+                           cutoff=cutoff or cfg.cutoff)
+
+
+def device_layer(cfg, seed=0, routing="normal", cutoff=None, alpha=None, names=None):
+    """(StableLatentMoE, x) with every tensor (or those in `names`) generated
+    in device memory."""
+    import torch
+    import sparse_moe_layer_quantile_amd as moe
+    lay = synth.device_layer(cfg, seed, routing, names=names)
+    t = {}
+    for k, v in lay.items():
+        if k == "x" or v is None:
+            continue
+        if k.startswith("scale:"):
+            t[SCALE_ABI[k[6:]]] = v
+        else:
+            t[ABI_NAME[k]] = v
+    if alpha is not None:
+        t["cutoff"] = torch.as_tensor(np.asarray(alpha, np.float32), device="cuda")
+    layer = moe.StableLatentMoE(abi_config(cfg, cutoff), t)
+    torch.cuda.synchronize()
+    return layer, lay.get("x")
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def y_to_f64(y):
+    import torch
+    return y.detach().to(torch.float64).cpu().numpy()
+
+
+def normwise_err(y, ref) -> float:
+    den = float(np.abs(ref).max())
+    return float(np.abs(y - ref).max()) / (den if den > 0 else 1.0)
+
+
+def sigmoid64(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))
+
+
+def routing_mismatches(idx_gpu, idx_ref, z32_ref, alpha_ref, band=TIE_BAND):
+    """Tokens whose expert sets differ, and those among them that are not near
+    ties of the oracle's cutoff-adjusted scores."""
+    diff = np.nonzero((idx_gpu != idx_ref).any(1))[0]
+    bad = []
+    for t in diff:
+        r = (z32_ref[t] - (alpha_ref if alpha_ref is not None else 0)).astype(np.float32)
+        s = sigmoid64(r)
+        chosen = np.zeros(len(s), bool)
+        chosen[idx_gpu[t]] = True
+        if len(set(idx_gpu[t].tolist())) != idx_gpu.shape[1]:
+            bad.append(int(t))
+            continue
+        lo = s[chosen].min()
+        hi = s[~chosen].max() if (~chosen).any() else -np.inf
+        if lo < hi - band:
+            bad.append(int(t))
+    return [int(t) for t in diff], bad
+
+
+def check_dispatch_valid(idx, counts, offsets, perm, inv_perm, n_experts):
+    """Properties every correct dispatch of idx has (used where the routing
+    legitimately differs from the oracle's by a near tie)."""
+    k = idx.shape[1]
+    flat = idx.reshape(-1)
+    assert (counts == np.bincount(flat, minlength=n_experts)).all()
+    assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+    assert (np.sort(perm) == np.arange(flat.size)).all()
+    assert (inv_perm[perm] == np.arange(flat.size)).all()
+    e_sorted = flat[perm]
+    assert (np.diff(e_sorted) >= 0).all()
+    tok = perm // k
+    same = np.diff(e_sorted) == 0
+    assert (np.diff(tok)[same] > 0).all()
+
+
+# ---- oracle reference for sampled tokens of a large layer --------------------------
+
+def oracle_routing_full(cfg, seed=0, routing="normal", cutoff=None, alpha=None, x=None):
+    """Full-batch oracle routing (steps 1-4): needs every token's logits."""
+    lay = {"w_router": synth.host_tensor(cfg, "w_router", seed, routing).reshape(
+        cfg.n_experts, cfg.d), "router_bias": synth.router_bias(cfg)}
+    if x is None:
+        x = synth.host_tensor(cfg, "x", seed, routing).reshape(cfg.bt, cfg.d)
+    w = oracle.Weights(lay)
+    z64 = oracle.router_logits(cfg, w, x)
+    z32 = z64.astype(np.float32)
+    mode = cutoff or cfg.cutoff
+    if mode == "batch":
+        a = oracle.quantile(z32, cfg.quantile_rank)
+    else:
+        a = np.zeros(cfg.n_experts, np.float32) if alpha is None else np.asarray(alpha,
+                                                                                  np.float32)
+    idx, wts = oracle.topk(z32, cfg.top_k, alpha=a, z64=z64)
+    counts, offsets, perm, inv = oracle.dispatch(idx, cfg.n_experts)
+    return dict(z64=z64, z32=z32, alpha=a, idx=idx, w=wts, counts=counts, offsets=offsets,
+                perm=perm, inv_perm=inv, x=x)
+
+
+def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None):
+    """Oracle y (fp64) of the listed tokens given their routing (steps 5-8),
+    regenerating each touched expert's matrices on the host."""
+    sp = synth.specs(cfg)
+    mats = {}
+    for n in ("w_down_proj", "w_up_proj", "sh_gate", "sh_up", "sh_down"):
+        mats[n] = synth.host_tensor(cfg, n, seed, routing).reshape(sp[n].shape)
+        sc = synth.host_scales(cfg, n, seed)
+        if sc is not None:
+            mats["scale:" + n] = sc
+    mats["gamma"] = synth.gamma(cfg)
+    w = oracle.Weights(mats)
+    if x is None:
+        xrows = synth.host_rows(cfg, "x", tokens, seed, routing)
+    else:
+        xrows = x[tokens]
+    xd = oracle.decode(xrows)
+    xlat = np.stack([oracle.matvec(w.mats["w_down_proj"], xd[i]) for i in range(len(tokens))])
+    k = cfg.top_k
+    o = np.zeros((len(tokens), k, cfg.latent))
+    by_expert = {}
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            by_expert.setdefault(int(idx[t, j]), []).append((i, j))
+    esc = {n: synth.host_scales(cfg, n, seed) for n in ("w_gate", "w_up", "w_down")}
+    for e, pairs in sorted(by_expert.items()):
+        g, u, dn = (oracle.Mat(synth.host_matrix(cfg, n, e, seed, routing),
+                               None if esc[n] is None else esc[n][e])
+                    for n in ("w_gate", "w_up", "w_down"))
+        for i, j in pairs:
+            o[i, j] = oracle.expert(cfg, g, u, dn, xlat[i])
+    ys = []
+    for i, t in enumerate(tokens):
+        _, n = oracle.combine_norm(cfg, o[i], wts[t], mats["gamma"])
+        ys.append(oracle.output(cfg, w, n, xd[i]))
+    return np.stack(ys)
+
+
+# ---- smoke -------------------------------------------------------------------------------
+
+def smoke_check():
+    """One small forward on cuda:0 through the C ABI, checked against the oracle."""
+    import torch
+    cfg = synth.CONFIGS["tiny_fp32"]
+    layer, x = device_layer(cfg, seed=0)
+    y, r = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(cfg, synth.host_layer(cfg, 0), cutoff=oracle.BATCH)
+    diff, bad = routing_mismatches(to_np(r["idx"]), ref["idx"], ref["z32"], ref["zeta"])
+    assert not bad, f"routing differs from the oracle beyond near ties: tokens {bad}"
+    keep = np.setdiff1d(np.arange(cfg.bt), diff)
+    err = normwise_err(y_to_f64(y)[keep], ref["y"][keep])
+    assert err <= tol_of(cfg), f"normwise error {err:.3e} above {tol_of(cfg)}"
+    print(f"smoke ok: {cfg.name} bt={cfg.bt} normwise err {err:.2e}", flush=True)
