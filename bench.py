@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the Stable LatentMoE layer forward on one MI355X.
+
+One step = one full forward of the layer (router logits, quantile cutoffs,
+top-k, dispatch, W_down_proj, grouped SiTU-GLU experts, combine + latent
+RMSNorm, output projection with the shared experts) over one batch of
+synthetic tokens already resident in HBM, through the C ABI (moe_forward).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
+with HIP events on its own stream inside the timed loop) and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--config k3_prefill_bf16] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "LatentMoE layer tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+
+
+def phase_work(cfg, touched: int) -> dict:
+    """Algorithmic FLOPs and HBM bytes of each phase of one forward.
+
+    Bytes count each operand once: weights actually needed (every touched
+    expert once), activations in, results out."""
+    bt, d, L, E, k = cfg.bt, cfg.d, cfg.latent, cfg.n_experts, cfg.top_k
+    I, S, Is = cfg.expert_inter, cfg.n_shared, cfg.shared_inter
+    P = bt * k
+    ab = 4 if cfg.act == "f32" else 2
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight]
+    rb = {"f32": 4, "bf16": 2}[cfg.router]
+    sc = (lambda r, c: (r // 128) * (c // 128) * 4) if cfg.weight == "fp8" else (lambda r, c: 0)
+    batch = cfg.cutoff == "batch"
+    return {
+        "shared_gateup": (2 * bt * d * 2 * S * Is,
+                          bt * d * ab + 2 * S * (Is * d * wb + sc(Is, d)) + bt * S * Is * ab),
+        "router_logits": (2 * bt * d * E, bt * d * ab + E * d * rb + bt * E * 4 * (2 if batch else 1)),
+        "cutoff": (0, bt * E * 4 if batch else 0),
+        "topk": (0, bt * E * 4 + P * 8),
+        "dispatch": (0, P * 4 + P * 8),
+        "down_proj": (2 * bt * d * L, bt * d * ab + L * d * wb + sc(L, d) + bt * L * ab),
+        "expert_gateup": (2 * P * 2 * L * I,
+                          touched * 2 * (I * L * wb + sc(I, L)) + bt * L * ab + P * I * ab),
+        "expert_down": (2 * P * L * I, touched * (L * I * wb + sc(L, I)) + P * I * ab + P * L * ab),
+        "combine_norm": (0, P * L * ab + bt * L * ab),
+        "output": (2 * bt * (L + S * Is) * d,
+                   bt * (L + S * Is) * ab + d * (L + S * Is) * wb + sc(d, L) + S * sc(d, Is)
+                   + bt * d * ab),
+    }
+
+
+def roofline_of(name, flops, nbytes, ms):
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = flops / (ms * 1e-3) / 1e12
+        out = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+               "frac": ach / PEAK_BF16_TFLOPS}
+    else:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        out = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": ach / PEAK_HBM_GBS}
+    out.update({"traffic": None, "kernel": name, "ms": ms, "algorithmic_flops": flops,
+                "algorithmic_bytes": nbytes,
+                "mfma_frac": flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                "hbm_frac": nbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9)})
+    return out
+
+
+def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
+    """The fp64 CPU oracle on a bounded sample of the same workload."""
+    import oracle
+    import synth
+    from tests import parity
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if cfg.bt * cfg.flops() / cfg.bt <= 2e11:  # small layers: the whole oracle forward
+        lay = synth.host_layer(cfg, seed)
+        t0 = time.perf_counter()
+        oracle.forward(cfg, lay, cutoff=oracle.BATCH if cfg.cutoff == "batch" else oracle.GIVEN)
+        dt = time.perf_counter() - t0
+        return {"value": cfg.bt / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"whole forward of all {cfg.bt} tokens ({dt:.1f} s)"}
+    rng = np.random.default_rng(seed)
+    tokens = np.sort(rng.choice(cfg.bt, size=min(n_tokens, cfg.bt), replace=False))
+    sp = synth.specs(cfg)
+    mats = {n: synth.host_tensor(cfg, n, seed).reshape(sp[n].shape)
+            for n in ("w_router", "w_down_proj", "w_up_proj", "sh_gate", "sh_up", "sh_down")}
+    for n in ("w_down_proj", "w_up_proj", "sh_gate", "sh_up", "sh_down"):
+        s = synth.host_scales(cfg, n, seed)
+        if s is not None:
+            mats["scale:" + n] = s
+    mats["router_bias"] = synth.router_bias(cfg)
+    mats["gamma"] = synth.gamma(cfg)
+    w = oracle.Weights(mats)
+    xrows = synth.host_rows(cfg, "x", tokens, seed)
+    timed = 0.0
+    # router logits + top-k of the sample
+    t0 = time.perf_counter()
+    z64 = oracle.router_logits(cfg, w, xrows)
+    z32 = z64.astype(np.float32)
+    timed += time.perf_counter() - t0
+    # batch quantile over a full-size logit matrix, amortised over the batch
+    q = 0.0
+    if cfg.cutoff == "batch":
+        zfull = rng.standard_normal((cfg.bt, cfg.n_experts), dtype=np.float32)
+        t0 = time.perf_counter()
+        alpha = oracle.quantile(zfull, cfg.quantile_rank)
+        q = time.perf_counter() - t0
+        del zfull
+    else:
+        alpha = np.zeros(cfg.n_experts, np.float32)
+    t0 = time.perf_counter()
+    idx, wts = oracle.topk(z32, cfg.top_k, alpha=alpha, z64=z64)
+    xd = oracle.decode(xrows)
+    xlat = np.stack([oracle.matvec(w.mats["w_down_proj"], xd[i]) for i in range(len(tokens))])
+    timed += time.perf_counter() - t0
+    # experts, expert-major; regenerating an expert's matrices is not timed
+    o = np.zeros((len(tokens), cfg.top_k, cfg.latent))
+    by_e = {}
+    for i in range(len(tokens)):
+        for j in range(cfg.top_k):
+            by_e.setdefault(int(idx[i, j]), []).append((i, j))
+    esc = {n: synth.host_scales(cfg, n, seed) for n in ("w_gate", "w_up", "w_down")}
+    for e, pairs in by_e.items():
+        g, u, dn = (oracle.Mat(synth.host_matrix(cfg, n, e, seed),
+                               None if esc[n] is None else esc[n][e])
+                    for n in ("w_gate", "w_up", "w_down"))
+        t0 = time.perf_counter()
+        for i, j in pairs:
+            o[i, j] = oracle.expert(cfg, g, u, dn, xlat[i])
+        timed += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(len(tokens)):
+        _, n = oracle.combine_norm(cfg, o[i], wts[i], mats["gamma"])
+        oracle.output(cfg, w, n, xd[i])
+    timed += time.perf_counter() - t0
+    per_token = timed / len(tokens) + q / cfg.bt
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{len(tokens)} of {cfg.bt} tokens through router logits, top-k, "
+                       f"W_down, {cfg.top_k} experts, combine+RMSNorm, W_up and shared "
+                       f"experts ({timed:.1f} s), plus the batch quantile over a full "
+                       f"{cfg.bt}x{cfg.n_experts} logit matrix ({q:.2f} s) amortised per "
+                       f"token; extrapolated to tokens/s")}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="k3_prefill_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-stream", action="store_true", help="shared experts on the main stream")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import sparse_moe_layer_quantile_amd as moe
+    from tests import parity
+
+    cfg = synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    layer, x = parity.device_layer(cfg, seed=args.seed)
+    y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
+    side = None if args.one_stream else torch.cuda.Stream()
+
+    # routing of this batch: experts touched (for the algorithmic byte count)
+    _, r = layer.forward(x, shared_stream=side, return_routing=True, out=y)
+    counts = r["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    del r
+
+    for _ in range(args.warmup):
+        layer.forward(x, shared_stream=side, out=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, shared_stream=side, out=y)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+
+    # the same loop again with per-phase HIP events on each phase's stream
+    moe.profile_enable(True)
+    for _ in range(args.steps):
+        layer.forward(x, shared_stream=side, out=y)
+    torch.cuda.synchronize()
+    phases = moe.profile_read()
+    moe.profile_enable(False)
+
+    work = phase_work(cfg, touched)
+    dom = max(phases, key=lambda n: phases[n][0])
+    roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0])
+    layer_flops = cfg.flops()
+    line = {
+        "metric": METRIC,
+        "value": cfg.bt * args.steps / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "bt": cfg.bt, "d": cfg.d, "latent": cfg.latent,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "expert_inter": cfg.expert_inter, "n_shared": cfg.n_shared,
+                   "shared_inter": cfg.shared_inter, "weights": cfg.weight,
+                   "cutoff": cfg.cutoff, "router_bias": cfg.bias,
+                   "parallelism": "1 GPU"},
+        "roofline": roof,
+        "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                  "experts_touched": touched,
+                  "weight_gb": sum(sp.nbytes for n, sp in synth.specs(cfg).items() if n != "x")
+                  / 1e9},
+        "phases_ms": {n: round(v[0], 4) for n, v in phases.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

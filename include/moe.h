@@ -147,6 +147,20 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
 /* Static text for a status code. */
 const char *moe_status_str(int status);
 
+/* ---- Measurement support (not part of the layer) ----------------------------
+ * While enabled, moe_forward records a timing hipEvent pair around each of its
+ * phases on the stream that phase runs on (the shared experts on
+ * shared_stream).  moe_profile_read waits for the recorded events, returns the
+ * average milliseconds per call of each phase and clears the record.  Phases:
+ * 0 shared gate/up, 1 router logits, 2 cutoffs, 3 top-k, 4 dispatch,
+ * 5 W_down_proj, 6 expert gate/up, 7 expert down, 8 combine + RMSNorm,
+ * 9 output projection.  Events are created by the library and kept for reuse
+ * (no device memory).  Not thread-safe against concurrent forwards. */
+#define MOE_N_PHASES 10
+moe_status moe_profile_enable(int on);
+moe_status moe_profile_read(double *ms_avg, int64_t *calls); /* arrays of MOE_N_PHASES */
+const char *moe_profile_phase_name(int phase);
+
 #ifdef __cplusplus
 }
 #endif

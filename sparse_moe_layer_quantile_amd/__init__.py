@@ -80,13 +80,21 @@ def _load():
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_profile_enable.argtypes = [ctypes.c_int]
+    lib.moe_profile_enable.restype = ctypes.c_int
+    lib.moe_profile_read.argtypes = [_P, _P]
+    lib.moe_profile_read.restype = ctypes.c_int
+    lib.moe_profile_phase_name.argtypes = [ctypes.c_int]
+    lib.moe_profile_phase_name.restype = ctypes.c_char_p
     return lib
 
 
 LIB = _load()
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
-            "moe_status_str")
+            "moe_status_str", "moe_profile_enable", "moe_profile_read",
+            "moe_profile_phase_name")
+N_PHASES = 10
 
 
 def status_str(status: int) -> str:
@@ -126,6 +134,21 @@ def moe_forward(cfg, weights: MoeWeights, x: int, bt: int, y: int, route, disp, 
                            _P(y or None), ctypes.byref(route) if route is not None else None,
                            ctypes.byref(disp) if disp is not None else None, _P(ws or None),
                            ws_bytes, _P(stream or None), _P(shared_stream or None))
+
+
+def profile_enable(on: bool) -> None:
+    """Per-phase HIP-event timing of moe_forward (measurement support)."""
+    LIB.moe_profile_enable(1 if on else 0)
+
+
+def profile_read() -> dict:
+    """{phase name: (average ms per call, calls)} since profiling was enabled."""
+    ms = (ctypes.c_double * N_PHASES)()
+    calls = (ctypes.c_int64 * N_PHASES)()
+    st = LIB.moe_profile_read(ms, calls)
+    if st != 0:
+        raise MoeError(st, "moe_profile_read")
+    return {LIB.moe_profile_phase_name(i).decode(): (ms[i], calls[i]) for i in range(N_PHASES)}
 
 
 # ---- torch-tensor convenience layer (memory and streams only) -----------------------

@@ -152,6 +152,53 @@ GemmArgs base_args(const moe_config *c) {
     if ((expr) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
+// ---- phase timing (measurement support) -------------------------------------------
+enum Phase {
+  PH_SHARED = 0, PH_ROUTER, PH_CUTOFF, PH_TOPK, PH_DISPATCH, PH_DOWN_PROJ, PH_EXPERT_GATEUP,
+  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT
+};
+const char *kPhaseNames[MOE_N_PHASES] = {
+    "shared_gateup", "router_logits", "cutoff", "topk", "dispatch", "down_proj",
+    "expert_gateup", "expert_down", "combine_norm", "output"};
+
+struct Profiler {
+  bool on = false;
+  std::mutex mu;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[MOE_N_PHASES];
+  std::vector<hipEvent_t> pool;
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event pair around its lifetime on `s` while profiling is on.
+struct PhaseScope {
+  hipEvent_t b = nullptr, e = nullptr;
+  hipStream_t s;
+  int ph;
+  PhaseScope(int phase, hipStream_t stream) : s(stream), ph(phase) {
+    if (!g_prof.on) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    b = prof_event();
+    e = prof_event();
+    if (b && e && hipEventRecord(b, s) != hipSuccess) b = nullptr;
+  }
+  ~PhaseScope() {
+    if (!b || !e) return;
+    const bool ok = hipEventRecord(e, s) == hipSuccess;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (ok) g_prof.rec[ph].emplace_back(b, e);
+  }
+};
+
 // Router: logits (+ transposed copy for the batch quantile), cutoffs, top-k.
 moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, const void *x,
                      int64_t bt, float *z, int32_t *idx, float *wts, float *cutoff_out, void *ws,
@@ -169,19 +216,28 @@ moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, c
   a.out_t = batch ? zT : nullptr;
   a.bias = w->router_bias;
   const int bm = gemm_bm(p.path);
-  MOE_TRY_HIP(gemm_launch(a, p.path, GK_ROUTER, false, (bt + bm - 1) / bm, s));
-  const float *alpha;
-  if (batch) {
-    int64_t m = (bt * c->top_k + E - 1) / E;
-    m = m < 1 ? 1 : (m > bt ? bt : m);
-    float *zeta = cutoff_out ? cutoff_out : at<float>(ws, p.alpha);
-    MOE_TRY_HIP(launch_quantile(zT, bt, E, m, zeta, s));
-    alpha = zeta;
-  } else {
-    alpha = w->cutoff;
-    if (cutoff_out) MOE_TRY_HIP(launch_copy_or_zero_f32(cutoff_out, w->cutoff, E, s));
+  {
+    PhaseScope ph(PH_ROUTER, s);
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_ROUTER, false, (bt + bm - 1) / bm, s));
   }
-  MOE_TRY_HIP(launch_topk(z, alpha, bt, E, c->top_k, idx, wts, s));
+  const float *alpha;
+  {
+    PhaseScope ph(PH_CUTOFF, s);
+    if (batch) {
+      int64_t m = (bt * c->top_k + E - 1) / E;
+      m = m < 1 ? 1 : (m > bt ? bt : m);
+      float *zeta = cutoff_out ? cutoff_out : at<float>(ws, p.alpha);
+      MOE_TRY_HIP(launch_quantile(zT, bt, E, m, zeta, s));
+      alpha = zeta;
+    } else {
+      alpha = w->cutoff;
+      if (cutoff_out) MOE_TRY_HIP(launch_copy_or_zero_f32(cutoff_out, w->cutoff, E, s));
+    }
+  }
+  {
+    PhaseScope ph(PH_TOPK, s);
+    MOE_TRY_HIP(launch_topk(z, alpha, bt, E, c->top_k, idx, wts, s));
+  }
   return MOE_OK;
 }
 
@@ -213,6 +269,42 @@ void ev_put(hipEvent_t ev) {
 }
 
 }  // namespace
+
+MOE_API moe_status moe_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = on != 0;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_profile_read(double *ms_avg, int64_t *calls) {
+  if (!ms_avg || !calls) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  moe_status st = MOE_OK;
+  for (int p = 0; p < MOE_N_PHASES; ++p) {
+    double sum = 0.0;
+    int64_t n = 0;
+    for (auto &be : g_prof.rec[p]) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(be.second) != hipSuccess ||
+          hipEventElapsedTime(&ms, be.first, be.second) != hipSuccess) {
+        st = MOE_ERR_HIP;
+      } else {
+        sum += ms;
+        ++n;
+      }
+      g_prof.pool.push_back(be.first);
+      g_prof.pool.push_back(be.second);
+    }
+    g_prof.rec[p].clear();
+    ms_avg[p] = n ? sum / (double)n : 0.0;
+    calls[p] = n;
+  }
+  return st;
+}
+
+MOE_API const char *moe_profile_phase_name(int phase) {
+  return (phase >= 0 && phase < MOE_N_PHASES) ? kPhaseNames[phase] : "";
+}
 
 MOE_API size_t moe_workspace_bytes(const moe_config *cfg, int64_t bt) {
   Plan p;
@@ -310,6 +402,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.bscale_up = w->s_sh_up;
     a.out = hs;
     a.ldo = S * Is;
+    PhaseScope ph(PH_SHARED, ss);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, fp8, dense_mt, ss));
     if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_sh, ss));
   }
@@ -327,8 +420,11 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   int32_t *perm = disp ? disp->perm : at<int32_t>(ws, p.perm);
   int32_t *inv_perm = disp ? disp->inv_perm : at<int32_t>(ws, p.inv_perm);
   int32_t *tile_offsets = at<int32_t>(ws, p.tile_offsets);
-  MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, bm, at<uint64_t>(ws, p.masks), counts, offsets,
-                              tile_offsets, perm, inv_perm, s));
+  {
+    PhaseScope ph(PH_DISPATCH, s);
+    MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, bm, at<uint64_t>(ws, p.masks), counts, offsets,
+                                tile_offsets, perm, inv_perm, s));
+  }
 
   // ---- x_lat = x W_down_proj^T ---------------------------------------------------
   void *xlat = at<void>(ws, p.xlat);
@@ -340,6 +436,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, w->s_down_proj, d};
     a.out = xlat;
     a.ldo = L;
+    PhaseScope ph(PH_DOWN_PROJ, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
   }
 
@@ -364,6 +461,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.gather_div = (int32_t)k;
     a.out = h;
     a.ldo = I;
+    PhaseScope ph(PH_EXPERT_GATEUP, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, fp8, grouped_mt, s));
   }
   {
@@ -381,13 +479,17 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.row_perm = perm;
     a.out = o;
     a.ldo = L;
+    PhaseScope ph(PH_EXPERT_DOWN, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_DOWN, fp8, grouped_mt, s));
   }
 
   // ---- combine + latent RMSNorm -------------------------------------------------------
   void *nrm = at<void>(ws, p.n);
-  MOE_TRY_HIP(launch_combine_norm(o, p.path == PATH_BF16, inv_perm, bt, k, L,
-                                  w->latent_gamma, cfg->rms_eps, nrm, s));
+  {
+    PhaseScope ph(PH_COMBINE, s);
+    MOE_TRY_HIP(launch_combine_norm(o, p.path == PATH_BF16, inv_perm, bt, k, L,
+                                    w->latent_gamma, cfg->rms_eps, nrm, s));
+  }
 
   // ---- y = n W_up_proj^T + sum_j hs_j W_ds,j^T ------------------------------------------
   if (two_streams) {
@@ -413,6 +515,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     }
     a.out = y;
     a.ldo = d;
+    PhaseScope ph(PH_OUTPUT, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
   }
   return MOE_OK;

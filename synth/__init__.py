@@ -167,7 +167,7 @@ def draw_params(cfg: Config, name: str, routing: str = "normal"):
         return DYADIC, 2.0 ** -dyadic_router_shift(cfg.d), 8
     if sp.dtype == FP8:
         return NORMAL, FP8_MAX / NORMAL_INT_MAX, 0
-    sigma = 1.0 if name == "x" else 1.0 / math.sqrt(sp.fan_in)
+    sigma = 1.0 if (name == "x" or sp.fan_in == 0) else 1.0 / math.sqrt(sp.fan_in)
     return NORMAL, float(np.float32(sigma / NORMAL_INT_STD)), 0
 
 
@@ -175,7 +175,7 @@ def scale_base(cfg: Config, name: str) -> float:
     """Centre of the fp8 block scales of `name`: dequantised codes then have
     standard deviation ~ 1/sqrt(fan_in)."""
     sp = specs(cfg)[name]
-    sigma = 1.0 / math.sqrt(sp.fan_in)
+    sigma = 1.0 / math.sqrt(max(sp.fan_in, 1))
     return sigma * (NORMAL_INT_MAX / FP8_MAX) / NORMAL_INT_STD
 
 

@@ -1,0 +1,82 @@
+"""GPU parity at the full K3 layer shapes (d=7168, L=3584, 896 experts, top 16,
+I=3072, 2 shared experts of 3072), in the launch configuration the benchmark
+times (two streams).  Routing is checked on every token against the full-batch
+oracle; the layer output on every token (decode) or on a seeded sample of
+tokens the oracle computes one by one (prefill)."""
+import numpy as np
+import pytest
+
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _run_k3(cfg_name, n_sample, seed=0):
+    cfg = synth.CONFIGS[cfg_name]
+    say("k3 parity", cfg.name, "bt", cfg.bt, "sample", n_sample)
+    layer, x = parity.device_layer(cfg, seed=seed)
+    side = torch.cuda.Stream()
+    y, r = layer.forward(x, shared_stream=side, return_routing=True)
+    torch.cuda.synchronize()
+    yg = parity.y_to_f64(y)
+    got = {n: parity.to_np(v) for n, v in r.items()}
+    del layer, x, y, r
+    torch.cuda.empty_cache()
+    say("  gpu done; oracle routing")
+    ref = parity.oracle_routing_full(cfg, seed=seed)
+    dz = np.abs(got["logits"].astype(np.float64) - ref["z64"]).max()
+    say(f"  max |z - z_ref| = {dz:.3e}")
+    assert dz <= 1e-5
+    assert np.abs(got["cutoff"] - ref["alpha"]).max() <= dz
+    diff, bad = parity.routing_mismatches(got["idx"], ref["idx"], ref["z32"], ref["alpha"])
+    say(f"  near-tie tokens {len(diff)}: {diff[:8]}")
+    assert not bad, f"routing beyond the near-tie band on tokens {bad[:8]}"
+    if not diff:
+        for n in ("counts", "offsets", "perm", "inv_perm"):
+            np.testing.assert_array_equal(got[n], ref[n], err_msg=n)
+    else:
+        parity.check_dispatch_valid(got["idx"], got["counts"], got["offsets"], got["perm"],
+                                    got["inv_perm"], cfg.n_experts)
+    np.testing.assert_allclose(got["w"], ref["w"], rtol=1e-5, atol=1e-6)
+    rng = np.random.default_rng(seed + 1)
+    pool = np.setdiff1d(np.arange(cfg.bt), diff)
+    tokens = np.sort(rng.choice(pool, size=min(n_sample, pool.size), replace=False))
+    if cfg.bt > 1:  # always include the first and the last token (tile edges)
+        tokens = np.unique(np.concatenate([tokens, [pool[0], pool[-1]]]))
+    say(f"  oracle y on {len(tokens)} tokens")
+    yref = parity.oracle_tokens(cfg, tokens, ref["idx"], ref["w"], seed=seed, x=ref["x"])
+    err = parity.normwise_err(yg[tokens], yref)
+    say(f"  normwise err {err:.3e} (tol {parity.tol_of(cfg)})")
+    assert err <= parity.tol_of(cfg)
+    return cfg, got
+
+
+def test_k3_decode_all_tokens():
+    cfg, got = _run_k3("k3_decode_bf16", n_sample=64)
+    say("  experts touched", int((got["counts"] > 0).sum()))
+
+
+def test_k3_prefill_zipf_batch_cutoffs():
+    cfg, got = _run_k3("k3_prefill_bf16", n_sample=10)
+    # the batch cutoffs balance the Zipf-skewed load: every expert near bt*k/E
+    mean = cfg.bt * cfg.top_k / cfg.n_experts
+    say(f"  load max/mean {got['counts'].max() / mean:.3f} min/mean {got['counts'].min() / mean:.3f}")
+    assert got["counts"].max() < 1.5 * mean and got["counts"].min() > 0.5 * mean
+
+
+def test_k3_prefill_fp8_weights():
+    _run_k3("k3_prefill_fp8", n_sample=10)

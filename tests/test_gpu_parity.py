@@ -141,3 +141,113 @@ def test_forward_small_all_tokens(cfg_name, cutoff, routing):
     err = parity.normwise_err(parity.y_to_f64(y)[keep], ref["y"][keep])
     say(f"  normwise err {err:.3e} (tol {parity.tol_of(cfg)}), near ties {len(diff)}")
     assert err <= parity.tol_of(cfg)
+
+
+# ---- edge cases ----------------------------------------------------------------------------
+
+def _small_forward_check(cfg, cutoff, seed=0, alpha=None, routing="normal"):
+    layer, x = parity.device_layer(cfg, seed=seed, cutoff=cutoff, alpha=alpha,
+                                   routing=routing)
+    y, r = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(cfg, synth.host_layer(cfg, seed, routing),
+                         cutoff=oracle.BATCH if cutoff == "batch" else oracle.GIVEN,
+                         alpha=alpha)
+    diff, bad = parity.routing_mismatches(parity.to_np(r["idx"]), ref["idx"], ref["z32"],
+                                          ref["zeta"])
+    assert not bad
+    keep = np.setdiff1d(np.arange(cfg.bt), diff)
+    err = parity.normwise_err(parity.y_to_f64(y)[keep], ref["y"][keep])
+    say(f"  {cfg.name} bt={cfg.bt} {cutoff}: err {err:.2e}, near ties {len(diff)}")
+    assert err <= parity.tol_of(cfg)
+    return r, ref
+
+
+@pytest.mark.parametrize("bt", [1, 2, 63, 100, 129, 1000])
+@pytest.mark.parametrize("cutoff", ["batch", "given"])
+def test_forward_ragged_batches(bt, cutoff):
+    cfg = synth.CONFIGS["mid_bf16"].with_(bt=bt)
+    say("ragged", bt, cutoff)
+    r, ref = _small_forward_check(cfg, cutoff)
+    if bt == 1 and cutoff == "batch":
+        # m = 1: every cutoff equals the token's own logit, all r = 0, so the
+        # k lowest expert ids are chosen
+        assert (parity.to_np(r["idx"]) == np.arange(cfg.top_k)).all()
+
+
+def test_forward_given_nonzero_cutoffs():
+    cfg = synth.CONFIGS["mid_bf16"].with_(bt=512)
+    alpha = np.random.default_rng(3).normal(size=cfg.n_experts).astype(np.float32)
+    say("given cutoffs")
+    r, ref = _small_forward_check(cfg, "given", alpha=alpha)
+    np.testing.assert_array_equal(parity.to_np(r["cutoff"]), alpha)
+
+
+@pytest.mark.parametrize("n_shared,shared_inter", [(0, 0), (1, 256), (3, 128)])
+def test_forward_shared_expert_counts(n_shared, shared_inter):
+    cfg = synth.CONFIGS["mid_bf16"].with_(bt=300, n_shared=n_shared, shared_inter=shared_inter)
+    say("shared", n_shared, shared_inter)
+    _small_forward_check(cfg, "batch")
+
+
+def test_forward_k_equals_E_and_single_expert():
+    for cfg in (synth.CONFIGS["mid_bf16"].with_(bt=200, n_experts=8, top_k=8),
+                synth.CONFIGS["mid_bf16"].with_(bt=200, n_experts=1, top_k=1)):
+        say("k=E", cfg.n_experts)
+        _small_forward_check(cfg, "batch")
+
+
+def test_forward_bt_zero_is_a_no_op():
+    cfg = synth.CONFIGS["mid_bf16"]
+    layer, x = parity.device_layer(cfg, seed=0)
+    y = layer.forward(x[:0])
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.d)
+
+
+def test_forward_deterministic_and_stream_independent():
+    cfg = synth.CONFIGS["mid_bf16"]
+    layer, x = parity.device_layer(cfg, seed=0, cutoff="batch")
+    y1 = layer.forward(x).clone()
+    side = torch.cuda.Stream()
+    y2 = layer.forward(x, shared_stream=side).clone()
+    y3 = layer.forward(x, shared_stream=side).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y2, y3)
+
+
+def test_forward_output_bounded_for_large_inputs():
+    """SiTU-GLU caps the expert activations: x scaled x100 still gives finite
+    outputs matching the oracle."""
+    cfg = synth.CONFIGS["tiny_fp32"]
+    layer, x = parity.device_layer(cfg, seed=0, cutoff="batch")
+    y = layer.forward(x * 100.0)
+    torch.cuda.synchronize()
+    lay = synth.host_layer(cfg, 0)
+    lay["x"] = (lay["x"] * np.float32(100.0)).astype(np.float32)
+    ref = oracle.forward(cfg, lay, cutoff=oracle.BATCH)
+    assert torch.isfinite(y).all()
+    err = parity.normwise_err(parity.y_to_f64(y), ref["y"])
+    assert err <= parity.tol_of(cfg)
+
+
+def test_error_codes():
+    import sparse_moe_layer_quantile_amd as moe
+    cfg = synth.CONFIGS["mid_bf16"]
+    layer, x = parity.device_layer(cfg, seed=0)
+    y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
+    ws = layer.workspace(cfg.bt)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = moe.moe_forward(layer.cfg, layer.w, x.data_ptr(), cfg.bt, y.data_ptr(), None, None,
+                         ws.data_ptr(), 1024, stream)
+    assert st == -3
+    st = moe.moe_forward(layer.cfg, moe.MoeWeights(), x.data_ptr(), cfg.bt, y.data_ptr(), None,
+                         None, ws.data_ptr(), ws.numel(), stream)
+    assert st == -1
+    bad = parity.abi_config(cfg.with_(latent=500))
+    st = moe.moe_forward(bad, layer.w, x.data_ptr(), cfg.bt, y.data_ptr(), None, None,
+                         ws.data_ptr(), ws.numel(), stream)
+    assert st == -2
+    st = moe.moe_forward(layer.cfg, layer.w, x.data_ptr(), cfg.bt, y.data_ptr(), None, None,
+                         ws.data_ptr() + 8, ws.numel() - 8, stream)
+    assert st == -3
