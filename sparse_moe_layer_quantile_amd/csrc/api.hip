@@ -422,8 +422,9 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   int32_t *tile_offsets = at<int32_t>(ws, p.tile_offsets);
   {
     PhaseScope ph(PH_DISPATCH, s);
-    MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, bm, at<uint64_t>(ws, p.masks), counts, offsets,
-                                tile_offsets, perm, inv_perm, s));
+    MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, grouped_tile_rows(p.path, fp8),
+                                at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
+                                inv_perm, s));
   }
 
   // ---- x_lat = x W_down_proj^T ---------------------------------------------------

@@ -47,6 +47,7 @@ struct GemmArgs {
   const int32_t *row_perm;
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;
+  int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
 };
 
 struct Tile {

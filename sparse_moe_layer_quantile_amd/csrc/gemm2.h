@@ -1,0 +1,414 @@
+// gemm2.h -- bf16 MFMA GEMM engine with direct-to-LDS loads.
+//
+// Same problem description as gemm.h (GemmArgs: dense / grouped / gathered /
+// dual gate-up / K-segmented), for bf16 operands.  Tile TM x TN x BK with
+// TM = WM * SUBM * 32 A rows, TN = WN * FRN * 32 B rows and BK = 32 or 64;
+// 4 waves in a WM x WN layout, each wave SUBM x FRN blocks of
+// v_mfma_f32_32x32x16_bf16; OCC workgroups per CU.
+//
+//  * Global -> LDS with global_load_lds_dwordx4 (gfx950): no staging
+//    registers; each wave instruction fills 1 KB = RPI tile rows of 2 BK
+//    bytes (CPR 16 B chunks each).  Rows are XOR-swizzled on chunks,
+//    slot = chunk ^ ((row / (16 / CPR)) % CPR), which puts the 16 rows an
+//    MFMA operand read touches per 16 lanes on 16 distinct 16 B bank groups.
+//    The DMA writes lane l at slot l % CPR, so lane l fetches the global
+//    chunk that belongs there.
+//  * STAGES-deep ring of LDS stages: the loads of tile kt + STAGES - 1 are in
+//    flight while tile kt is multiplied; every thread issues the same number
+//    of loads per tile, so "tile kt landed" is s_waitcnt vmcnt(L (STAGES-2)).
+//  * Work items are spread over the 8 XCDs in contiguous ranges (workgroup i
+//    runs on XCD i % 8), so the N tiles that share an A tile (one expert's
+//    gathered tokens, one token block) run on one XCD and share its L2.
+//  * A partial M tile skips the MFMAs of its empty 32-row sub-blocks.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "gemm.h"
+
+namespace moe {
+namespace g2 {
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14; expcnt 6:4 and
+  // lgkmcnt 11:8 left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void barrier() {
+  // s_barrier without the memory fence of __syncthreads (which would wait for
+  // every outstanding load, in-flight prefetches included); the asm memory
+  // clobber keeps LDS accesses on their side of it.
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(g),
+                                   (__attribute__((address_space(3))) void *)(lds_wave_base),
+                                   16, 0, 0);
+}
+
+// Tile coordinates.  The tile list (M tiles x N tiles) is cut into 8
+// contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so all N
+// tiles of an M tile -- which share its A rows -- stay in one L2.  Inside a
+// range, tiles go in groups of group_m M tiles with M fastest: the concurrent
+// workgroups of an XCD then cover a group_m x (32 / group_m) block of tiles
+// and each A and B slice is fetched into L2 once for several of them.
+template <int TM, int TN_OUT>
+__device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
+  const int64_t nt = a.n_tiles_n;
+  int64_t mtiles;
+  if (a.offsets == nullptr) mtiles = (a.M + TM - 1) / TM;
+  else mtiles = a.tile_offsets[a.n_experts];
+  const int64_t total = mtiles * nt;
+  Tile t;
+  const int64_t per = (total + 7) / 8;
+  const int64_t b = blockIdx.x;
+  const int64_t idx = b >> 3;
+  const int64_t lin = (b & 7) * per + idx;
+  if (idx >= per || lin >= total) {
+    t.valid = false;
+    return t;
+  }
+  const int64_t group_m = a.group_m > 0 ? a.group_m : 1;
+  const int64_t gsz = group_m * nt;
+  const int64_t g = lin / gsz, r = lin - g * gsz;
+  const int64_t first_m = g * group_m;
+  const int64_t gm = min(group_m, mtiles - first_m);
+  const int64_t mt = first_m + r % gm;
+  t.n0 = (r / gm) * TN_OUT;
+  if (a.offsets == nullptr) {
+    t.e = 0;
+    t.m0 = mt * TM;
+    t.m_end = min(a.M, t.m0 + TM);
+    t.valid = true;
+    return t;
+  }
+  int lo = 0, hi = a.n_experts;  // tile_offsets[lo] <= mt < tile_offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_offsets[mid] <= mt) lo = mid;
+    else hi = mid;
+  }
+  t.e = lo;
+  t.m0 = a.offsets[lo] + (mt - a.tile_offsets[lo]) * TM;
+  t.m_end = min((int64_t)a.offsets[lo + 1], t.m0 + TM);
+  t.valid = true;
+  return t;
+}
+
+template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
+          bool GATHER, bool MSEG, typename OutT>
+__global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
+  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
+  constexpr int RB = BK * 2;          // bytes per tile row
+  constexpr int CPR = RB / 16;        // 16 B chunks per row
+  constexpr int RPI = 1024 / RB;      // rows per DMA wave instruction
+  constexpr int TM = WM * SUBM * 32, TN = WN * FRN * 32;
+  constexpr int TN_OUT = DUAL ? TN / 2 : TN;
+  constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int A_LD = TM / (4 * RPI), B_LD = TN / (4 * RPI);  // DMA instructions per wave
+  constexpr int L = A_LD + B_LD;
+  static_assert(TM % (4 * RPI) == 0 && TN % (4 * RPI) == 0, "tile rows per DMA round");
+  static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const Tile tile = map_tile_xcd<TM, TN_OUT>(args);
+  if (!tile.valid) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (WN == 4) ? 0 : wave / WN, wn = (WN == 4) ? wave : wave % WN;
+  const int rsub = lane / CPR, slot = lane % CPR;
+
+  // ---- per-lane source rows -------------------------------------------------
+  // A: instruction i of this wave fills tile rows (wave + 4 i) * RPI + rsub.
+  int32_t a_row[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = (wave + 4 * i) * RPI + rsub;
+    int64_t m = tile.m0 + r;
+    if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+    if constexpr (GATHER) m = args.gather[m] / args.gather_div;
+    a_row[i] = (int32_t)m;
+  }
+  // B: tile rows below TN/2 are gate rows and the rest up rows for a dual
+  // problem; with 4 waves that split falls exactly at instruction B_LD / 2.
+  int32_t b_row[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int r = (wave + 4 * i) * RPI + rsub;
+    int64_t n = tile.n0 + ((DUAL && i >= B_LD / 2) ? r - TN / 2 : r);
+    if (n >= args.N) n = tile.n0;
+    b_row[i] = (int32_t)n;
+  }
+  const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
+  const uint16_t *bu = static_cast<const uint16_t *>(args.b_up);
+  if (args.offsets != nullptr) {
+    b0 += (int64_t)tile.e * args.b_estride;
+    if (DUAL) bu += (int64_t)tile.e * args.b_estride;
+  }
+  // chunk this lane fetches so that the DMA slot order realises the swizzle;
+  // the rows of one instruction start at a multiple of RPI, so the swizzle
+  // key of row (wave + 4 i) * RPI + rsub does not depend on i
+  const int fetch_chunk = slot ^ ((((wave * RPI) + rsub) / (16 / CPR)) % CPR);
+
+  // ---- K segments -------------------------------------------------------------
+  int ktiles = (int)(args.seg[0].k / BK);
+  if constexpr (MSEG) {
+#pragma unroll
+    for (int s = 1; s < 5; ++s)
+      if (s < args.nseg) ktiles += (int)(args.seg[s].k / BK);
+  }
+
+  // Prefetch cursor over (segment, K tile); segment fields are reloaded from
+  // the kernel arguments (scalar loads) only when it crosses a boundary.
+  int cur_seg = 0, cur_k = 0, cur_nk = (int)(args.seg[0].k / BK);
+  const uint16_t *cur_a = static_cast<const uint16_t *>(args.seg[0].a);
+  const uint16_t *cur_b = b0;
+  int64_t cur_lda = args.seg[0].lda, cur_ldb = args.seg[0].ldb;
+
+  auto issue = [&](int kt) {
+    if (MSEG && cur_k == cur_nk) {
+      ++cur_seg;
+      const GemmSeg *sg = &args.seg[cur_seg];
+      cur_a = static_cast<const uint16_t *>(sg->a);
+      cur_b = static_cast<const uint16_t *>(sg->b);
+      cur_lda = sg->lda;
+      cur_ldb = sg->ldb;
+      cur_nk = (int)(sg->k / BK);
+      cur_k = 0;
+    }
+    const int64_t k0 = (int64_t)cur_k * BK + fetch_chunk * 8;
+    char *st = smem + (kt % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      dma16(cur_a + (int64_t)a_row[i] * cur_lda + k0, st + (wave + 4 * i) * 1024);
+    static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const uint16_t *Bm = (DUAL && i >= B_LD / 2) ? bu : cur_b;  // dual: one segment
+      dma16(Bm + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + 4 * i) * 1024);
+    }
+    ++cur_k;
+  };
+
+  // valid 32-row sub-blocks of this wave (partial tiles skip the rest)
+  const int rows_valid = (int)(tile.m_end - tile.m0);
+  int sub_valid = (rows_valid - wm * SUBM * 32 + 31) / 32;
+  sub_valid = sub_valid < 0 ? 0 : (sub_valid > SUBM ? SUBM : sub_valid);
+  sub_valid = __builtin_amdgcn_readfirstlane(sub_valid);
+
+  f32x16 acc[SUBM][FRN];
+#pragma unroll
+  for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+    for (int j = 0; j < FRN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Single-segment problems: source pointer of each DMA instruction (K offset
+  // excluded), computed once.
+  const uint16_t *a_src[MSEG ? 1 : A_LD];
+  const uint16_t *b_src[MSEG ? 1 : B_LD];
+  if constexpr (!MSEG) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      a_src[i] = cur_a + (int64_t)a_row[i] * cur_lda + fetch_chunk * 8;
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i)
+      b_src[i] = ((DUAL && i >= B_LD / 2) ? bu : cur_b) + (int64_t)b_row[i] * cur_ldb + fetch_chunk * 8;
+  }
+  // DMA instruction d (A rows first, then B rows) of K tile kt into stage st.
+  auto dma_one = [&](auto d_tag, int kt, int st) {
+    constexpr int d = decltype(d_tag)::value;
+    char *dst = smem + st * STAGE_BYTES;
+    if constexpr (d < A_LD) dma16(a_src[d] + kt * BK, dst + (wave + 4 * d) * 1024);
+    else dma16(b_src[d - A_LD] + kt * BK, dst + A_BYTES + (wave + 4 * (d - A_LD)) * 1024);
+  };
+
+  // Operand fragment f of k step ks (f < FRN: B fragment f, else A fragment f - FRN).
+  auto read_frag = [&](const char *st, int ks, auto f_tag, bf16x8 *af, bf16x8 *bfr) {
+    constexpr int f = decltype(f_tag)::value;
+    const int chunk = ks * 2 + (lane >> 5);
+    int r;
+    const char *base;
+    if constexpr (f < FRN) {
+      constexpr int j = f;
+      if (DUAL) r = (j < FRN / 2) ? ((wn * (FRN / 2) + j) * 32 + (lane & 31))
+                                  : (TN / 2 + (wn * (FRN / 2) + j - FRN / 2) * 32 + (lane & 31));
+      else r = (wn * FRN + j) * 32 + (lane & 31);
+      base = st + A_BYTES;
+    } else {
+      r = (wm * SUBM + (f - FRN)) * 32 + (lane & 31);
+      base = st;
+    }
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ ((r / (16 / CPR)) % CPR)) << 4));
+    if constexpr (f < FRN) bfr[f] = v;
+    else af[f - FRN] = v;
+  };
+
+  // K loop for NS active sub-blocks.  Single-segment problems run one
+  // straight-line schedule per stage: MFMAs one at a time, with the fragment
+  // reads of the next k step and the DMA instructions of the tile STAGES - 1
+  // ahead placed between them, so the in-order issue hides them behind the
+  // MFMA pipe.  The prefetch is unconditional (past the end it re-reads the
+  // last tile into a stage nobody reads again), so every thread has exactly
+  // L loads per tile in flight and the wait count is a constant.
+  auto mainloop = [&](auto ns_tag) {
+    constexpr int NS = decltype(ns_tag)::value;
+    constexpr int NA = NS > 0 ? NS : 1;
+    constexpr int KS = BK / 16;   // k steps per stage
+    constexpr int NF = NS + FRN;  // fragment reads per k step
+    constexpr int Q = NS * FRN;   // MFMAs per k step
+    if constexpr (!MSEG) {
+#pragma unroll
+      for (int p = 0; p < STAGES - 1; ++p) {
+        const int kp = p < ktiles ? p : ktiles - 1;
+        static_for<L>([&](auto d) { dma_one(d, kp, p); });
+      }
+      for (int kt = 0; kt < ktiles; ++kt) {
+        wait_vmcnt<L * (STAGES - 2)>();
+        barrier();
+        const char *st = smem + (kt % STAGES) * STAGE_BYTES;
+        const int kd = kt + STAGES - 1;
+        const int kdc = kd < ktiles ? kd : ktiles - 1;
+        const int dst = kd % STAGES;
+        if constexpr (NS == 0) {
+          static_for<L>([&](auto d) { dma_one(d, kdc, dst); });
+        } else {
+          bf16x8 fa[2][NA], fb[2][FRN];
+          static_for<NF>([&](auto f) { read_frag(st, 0, f, fa[0], fb[0]); });
+          static_for<KS>([&](auto s_tag) {
+            constexpr int S = decltype(s_tag)::value;
+            static_for<Q>([&](auto q_tag) {
+              constexpr int q = decltype(q_tag)::value;
+              constexpr int i = q / FRN, j = q % FRN;
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S & 1][i], fb[S & 1][j],
+                                                                  acc[i][j], 0, 0, 0);
+              if constexpr (S + 1 < KS) {
+                static_for<NF>([&](auto f_tag) {
+                  constexpr int f = decltype(f_tag)::value;
+                  if constexpr (f >= q * NF / Q && f < (q + 1) * NF / Q)
+                    read_frag(st, S + 1, f_tag, fa[(S + 1) & 1], fb[(S + 1) & 1]);
+                });
+              }
+              constexpr int g = S * Q + q;
+              static_for<L>([&](auto d_tag) {
+                constexpr int d = decltype(d_tag)::value;
+                if constexpr (d >= g * L / (KS * Q) && d < (g + 1) * L / (KS * Q))
+                  dma_one(d_tag, kdc, dst);
+              });
+              __builtin_amdgcn_sched_barrier(0);
+            });
+          });
+        }
+      }
+      wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
+    } else {
+#pragma unroll
+      for (int p = 0; p < STAGES - 1; ++p)
+        if (p < ktiles) issue(p);
+      for (int kt = 0; kt < ktiles; ++kt) {
+        // tile kt landed: at most (STAGES - 2) later tiles may still be in flight
+        if (kt + STAGES - 2 < ktiles) wait_vmcnt<L * (STAGES - 2)>();
+        else wait_vmcnt<0>();
+        barrier();
+        const char *st = smem + (kt % STAGES) * STAGE_BYTES;
+        // a segment switch waits on scalar loads (lgkmcnt), which would also
+        // wait for LDS reads in flight: issue first, then read fragments
+        if (kt + STAGES - 1 < ktiles) issue(kt + STAGES - 1);
+        if constexpr (NS > 0) {
+          bf16x8 fa[NA], fb[FRN];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            static_for<NF>([&](auto f) { read_frag(st, ks, f, fa, fb); });
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+#pragma unroll
+              for (int j = 0; j < FRN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  // one specialised copy of the K loop per number of active sub-blocks
+  static_assert(SUBM <= 5, "mainloop dispatch covers up to 5 sub-blocks");
+  switch (sub_valid) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (SUBM >= 2) mainloop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (SUBM >= 3) mainloop(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (SUBM >= 4) mainloop(std::integral_constant<int, 4>{}); break;
+    default: if constexpr (SUBM >= 5) mainloop(std::integral_constant<int, 5>{}); break;
+  }
+
+  // ---- epilogue: lane holds column (lane & 31), rows 8(r/4) + 4(lane/32) + r%4 ----
+#pragma unroll
+  for (int i = 0; i < SUBM; ++i) {
+    if (i >= sub_valid) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row =
+          tile.m0 + (wm * SUBM + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= tile.m_end) continue;
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < FRN / 2; ++j) {
+          const int64_t col = tile.n0 + (wn * (FRN / 2) + j) * 32 + (lane & 31);
+          if (col < args.N)
+            epilogue<EPI, OutT>(args, row, col, acc[i][j][r], acc[i][j + FRN / 2][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FRN; ++j) {
+          const int64_t col = tile.n0 + (wn * FRN + j) * 32 + (lane & 31);
+          if (col < args.N) epilogue<EPI, OutT>(args, row, col, acc[i][j][r], 0.0f);
+        }
+      }
+    }
+  }
+  if constexpr (EPI == EPI_ROUTER) {
+    if (args.out_t != nullptr) {
+#pragma unroll
+      for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+        for (int j = 0; j < FRN; ++j) {
+          const int64_t col = tile.n0 + (wn * FRN + j) * 32 + (lane & 31);
+          if (col >= args.N) continue;
+          const float bias = args.bias ? args.bias[col] : 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t row0 = tile.m0 + (wm * SUBM + i) * 32 + 8 * q + 4 * (lane >> 5);
+            float *dst = args.out_t + col * args.M + row0;
+            if (row0 + 3 < tile.m_end && (args.M & 3) == 0) {
+              *reinterpret_cast<float4 *>(dst) =
+                  make_float4(acc[i][j][q * 4 + 0] + bias, acc[i][j][q * 4 + 1] + bias,
+                              acc[i][j][q * 4 + 2] + bias, acc[i][j][q * 4 + 3] + bias);
+            } else {
+              for (int u = 0; u < 4; ++u)
+                if (row0 + u < tile.m_end) dst[u] = acc[i][j][q * 4 + u] + bias;
+            }
+          }
+        }
+    }
+  }
+}
+
+}  // namespace g2
+}  // namespace moe
