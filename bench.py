@@ -15,6 +15,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -60,6 +61,33 @@ def phase_work(cfg, touched: int) -> dict:
                    bt * (L + S * Is) * ab + d * (L + S * Is) * wb + sc(d, L) + S * sc(d, Is)
                    + bt * d * ab),
     }
+
+
+KERNEL_SOURCES = ("sparse_moe_layer_quantile_amd/csrc/gemm.h",
+                  "sparse_moe_layer_quantile_amd/csrc/gemm2.h",
+                  "sparse_moe_layer_quantile_amd/csrc/gemm.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when it is missing or the GEMM sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("gemm_source_hash") != kernel_source_hash():
+        return None
+    return k["bytes_per_launch"]
 
 
 def roofline_of(name, flops, nbytes, ms):
@@ -166,6 +194,9 @@ def main(argv=None):
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true", help="shared experts on the main stream")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -181,6 +212,13 @@ def main(argv=None):
 
     cfg = synth.CONFIGS[args.config]
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     layer, x = parity.device_layer(cfg, seed=args.seed)
     y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
     side = None if args.one_stream else torch.cuda.Stream()
@@ -212,6 +250,7 @@ def main(argv=None):
     work = phase_work(cfg, touched)
     dom = max(phases, key=lambda n: phases[n][0])
     roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0])
+    roof["traffic"] = measured_traffic(cfg.name, dom)
     layer_flops = cfg.flops()
     line = {
         "metric": METRIC,

@@ -64,6 +64,11 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    # One HIP runtime per process: torch ships its own libamdhip64, and every
+    # HIP library loaded later binds to whichever copy was loaded first.  Load
+    # it through torch before this library, so torch's device memory, streams
+    # and the library's launches all go through the same runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     CP = ctypes.POINTER
     lib.moe_workspace_bytes.argtypes = [CP(MoeConfig), ctypes.c_int64]

@@ -89,12 +89,10 @@ hipError_t launch_combine_norm(const void *o, bool bf16, const int32_t *inv_perm
   const dim3 grid((unsigned)((bt + 3) / 4)), block(256);
   const size_t lds = sizeof(float) * 4 * (size_t)L;
   if (bf16)
-    hipLaunchKernelGGL(combine_norm_kernel<true>, grid, block, lds, s, o, inv_perm, bt, (int)k,
+    return launch_kernel(combine_norm_kernel<true>, grid, block, lds, s, o, inv_perm, bt, (int)k,
+                         (int)L, gamma, eps, n);
+  return launch_kernel(combine_norm_kernel<false>, grid, block, lds, s, o, inv_perm, bt, (int)k,
                        (int)L, gamma, eps, n);
-  else
-    hipLaunchKernelGGL(combine_norm_kernel<false>, grid, block, lds, s, o, inv_perm, bt, (int)k,
-                       (int)L, gamma, eps, n);
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -12,6 +12,19 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 namespace moe {
 
+// Launch returning that launch's own status (hipGetLastError would also
+// report errors left behind by earlier runtime calls of the process).
+template <typename T>
+struct launch_arg {
+  using type = T;
+};
+template <typename... KArgs>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, typename launch_arg<KArgs>::type... args) {
+  void *argv[] = {static_cast<void *>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, stream);
+}
+
 // ---- bf16 storage ------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);

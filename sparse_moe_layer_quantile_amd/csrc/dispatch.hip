@@ -136,18 +136,16 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_
   if (err != hipSuccess) return err;
   const int nb = (int)((bt + 63) / 64);
   if (nb > 0) {
-    hipLaunchKernelGGL(dispatch_mask_kernel, dim3(nb), dim3(256), sizeof(uint64_t) * E, s, idx,
-                       bt, (int)k, E, nb, masks, counts);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = launch_kernel(dispatch_mask_kernel, dim3(nb), dim3(256), sizeof(uint64_t) * E, s, idx,
+                        bt, (int)k, E, nb, masks, counts);
+    if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, tile_bm,
-                     offsets, tile_offsets);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (nb > 0) {
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, masks, nb, idx,
-                       (int)k, offsets, perm, inv_perm);
-    err = hipGetLastError();
-  }
+  err = launch_kernel(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, tile_bm, offsets,
+                      tile_offsets);
+  if (err != hipSuccess) return err;
+  if (nb > 0)
+    err = launch_kernel(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, masks, nb, idx, (int)k,
+                        offsets, perm, inv_perm);
   return err;
 }
 

@@ -19,9 +19,8 @@ static hipError_t launch_mfma(GemmArgs a, int64_t m_tiles, hipStream_t s) {
   a.n_tiles_n = (int32_t)((a.N + bn_out - 1) / bn_out);
   const int64_t blocks = m_tiles * a.n_tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_mfma_kernel<EPI, DUAL, FP8, GATHER, OutT>), dim3((unsigned)blocks),
-                     dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(gemm_mfma_kernel<EPI, DUAL, FP8, GATHER, OutT>, dim3((unsigned)blocks),
+                       dim3(256), 0, s, a);
 }
 
 template <int EPI, bool DUAL, bool GATHER>
@@ -30,9 +29,8 @@ static hipError_t launch_f32(GemmArgs a, int64_t m_tiles, hipStream_t s) {
   a.n_tiles_n = (int32_t)((a.N + bn_out - 1) / bn_out);
   const int64_t blocks = m_tiles * a.n_tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_f32_kernel<EPI, DUAL, GATHER>), dim3((unsigned)blocks), dim3(256), 0,
-                     s, a);
-  return hipGetLastError();
+  return launch_kernel(gemm_f32_kernel<EPI, DUAL, GATHER>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       a);
 }
 
 static int env_int(const char *name, int dflt) {
@@ -83,8 +81,7 @@ static hipError_t launch_dma_v(GemmArgs a, hipStream_t s) {
   int64_t blocks = m_tiles * a.n_tiles_n;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), sh.lds(), s, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3((unsigned)blocks), dim3(256), sh.lds(), s, a);
 }
 
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
@@ -105,7 +102,7 @@ static hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
 // Tile shape of the bf16 engine per kind (a tuning override is read from
 // MOE_GEMM_DENSE / MOE_GEMM_GROUPED).
 int dma_variant(GemmKind kind) {
-  const int dense = env_int("MOE_GEMM_DENSE", 4);
+  const int dense = env_int("MOE_GEMM_DENSE", 1);
   const int grouped = env_int("MOE_GEMM_GROUPED", 0);
   const int v = (kind == GK_EXPERT_SITU || kind == GK_EXPERT_DOWN) ? grouped : dense;
   return (v >= 0 && v < kNumDma) ? v : 0;

@@ -72,9 +72,8 @@ __global__ void __launch_bounds__(256) quantile_kernel(const float *__restrict__
 hipError_t launch_quantile(const float *zT, int64_t bt, int64_t n_experts, int64_t m,
                            float *alpha, hipStream_t s) {
   if (n_experts <= 0 || bt <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quantile_kernel, dim3((unsigned)n_experts), dim3(256), 0, s, zT, bt, m,
-                     alpha);
-  return hipGetLastError();
+  return launch_kernel(quantile_kernel, dim3((unsigned)n_experts), dim3(256), 0, s, zT, bt, m,
+                       alpha);
 }
 
 // ---- top-k: one wavefront per token -------------------------------------------
@@ -144,10 +143,9 @@ hipError_t launch_topk(const float *z, const float *alpha, int64_t bt, int64_t n
   const dim3 grid((unsigned)((bt + 3) / 4)), block(256);
   const int E = (int)n_experts, K = (int)k;
   switch ((E + 63) / 64) {
-#define MOE_TOPK_CASE(n)                                                                  \
-  case n:                                                                                 \
-    hipLaunchKernelGGL(topk_kernel<n>, grid, block, 0, s, z, alpha, bt, E, K, idx, w); \
-    break;
+#define MOE_TOPK_CASE(n) \
+  case n:                \
+    return launch_kernel(topk_kernel<n>, grid, block, 0, s, z, alpha, bt, E, K, idx, w);
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
     MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
     MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
@@ -156,7 +154,6 @@ hipError_t launch_topk(const float *z, const float *alpha, int64_t bt, int64_t n
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // ---- small fills ----------------------------------------------------------------
@@ -171,15 +168,13 @@ __global__ void zero_i32_kernel(int32_t *dst, int64_t n) {
 
 hipError_t launch_copy_or_zero_f32(float *dst, const float *src, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_or_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     s, dst, src, n);
-  return hipGetLastError();
+  return launch_kernel(copy_or_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       dst, src, n);
 }
 hipError_t launch_zero_i32(int32_t *dst, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst,
-                     n);
-  return hipGetLastError();
+  return launch_kernel(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst,
+                       n);
 }
 
 }  // namespace moe

@@ -222,6 +222,7 @@ def lib_dev():
         path = os.path.join(HERE, "libsynth_dev.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (torch's HIP runtime first: one runtime per process)
         lib = ctypes.CDLL(path)
         lib.synth_fill_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                           ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,

@@ -26,7 +26,7 @@ __global__ void __launch_bounds__(256) synth_fill_kernel(void *out, int64_t n, u
 
 // Device twin of synth_fill_host.  `out` is a device pointer with room for n
 // elements of dtype.  Enqueued on `stream`; returns 0, -1 on a bad argument,
-// -4 if the launch failed.
+// -1000 - (hipError_t) if the launch failed.
 SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
                                 uint32_t tensor_id, int64_t offset, int kind, float scale,
                                 int32_t range, hipStream_t stream) {
@@ -37,22 +37,17 @@ SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
   if (kind == SYNTH_DYADIC && range < 0) return -1;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  dim3 grid((unsigned)blocks), block(256);
+  void (*kern)(void *, int64_t, uint64_t, uint32_t, int64_t, int, float, int32_t);
   switch (dtype) {
-    case SYNTH_F32:
-      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_F32>, grid, block, 0, stream, out, n, seed,
-                         tensor_id, offset, kind, scale, range);
-      break;
-    case SYNTH_BF16:
-      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_BF16>, grid, block, 0, stream, out, n, seed,
-                         tensor_id, offset, kind, scale, range);
-      break;
-    case SYNTH_FP8E4M3:
-      hipLaunchKernelGGL(synth_fill_kernel<SYNTH_FP8E4M3>, grid, block, 0, stream, out, n,
-                         seed, tensor_id, offset, kind, scale, range);
-      break;
-    default:
-      return -1;
+    case SYNTH_F32: kern = synth_fill_kernel<SYNTH_F32>; break;
+    case SYNTH_BF16: kern = synth_fill_kernel<SYNTH_BF16>; break;
+    case SYNTH_FP8E4M3: kern = synth_fill_kernel<SYNTH_FP8E4M3>; break;
+    default: return -1;
   }
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  // hipLaunchKernel reports this launch's own status (hipGetLastError would
+  // also report errors left behind by earlier runtime calls of the process)
+  void *args[] = {&out, &n, &seed, &tensor_id, &offset, &kind, &scale, &range};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3((unsigned)blocks),
+                                       dim3(256), args, 0, stream);
+  return e == hipSuccess ? 0 : -1000 - (int)e;
 }

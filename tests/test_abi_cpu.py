@@ -1,0 +1,117 @@
+"""The C-ABI library on the host: exported symbols, struct layouts, validation.
+
+No compute is launched: these run without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import synth
+from tests import parity
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("sparse_moe_layer_quantile_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
+            "moe_status_str"} <= set(names)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(moe.EXPORTED) == set(names)
+
+
+def test_struct_layouts_match_header():
+    """sizeof / offsetof of every ABI struct, from gcc on the header, equal the
+    ctypes mirrors used by the binding."""
+    structs = {"moe_config": moe.MoeConfig, "moe_weights": moe.MoeWeights,
+               "moe_route_out": moe.MoeRouteOut, "moe_dispatch_out": moe.MoeDispatchOut}
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
+    for s, cls in structs.items():
+        src.append(f'printf("{s} %zu\\n", sizeof({s}));')
+        for f, _ in cls._fields_:
+            src.append(f'printf("{s}.{f} %zu\\n", offsetof({s}, {f}));')
+    src.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.split() for line in out.strip().splitlines())
+    for s, cls in structs.items():
+        assert int(got[s]) == ctypes.sizeof(cls), s
+        for f, _ in cls._fields_:
+            assert int(got[f"{s}.{f}"]) == getattr(cls, f).offset, f"{s}.{f}"
+
+
+def test_workspace_sizes():
+    for name, cfg in synth.CONFIGS.items():
+        c = parity.abi_config(cfg)
+        n = moe.workspace_bytes(c, cfg.bt)
+        assert n > 0, name
+        assert moe.workspace_bytes(c, cfg.bt * 2) > n
+    k3 = parity.abi_config(synth.CONFIGS["k3_prefill_bf16"])
+    assert 3.5e9 < moe.workspace_bytes(k3, 16384) < 4.5e9
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(latent=500), -2),                 # not a multiple of 64
+    (dict(n_experts=2000), -2),             # more than 1024 experts
+    (dict(top_k=0), -1),
+    (dict(top_k=65, n_experts=128), -2),    # k above 64
+    (dict(d=-1), -1),
+    (dict(beta=0.0), -1),
+    (dict(latent=4160), -2),                # latent row over the LDS staging limit
+])
+def test_invalid_configs_rejected_on_host(change, code):
+    cfg = synth.CONFIGS["mid_bf16"].with_(**change)
+    c = parity.abi_config(cfg)
+    assert moe.workspace_bytes(c, 64) == 0
+    out = moe.MoeRouteOut(1, 1, 0, 0)
+    assert moe.moe_route(c, moe.MoeWeights(w_router=1), 1, 64, out, 256, 1 << 30, 0) == code
+
+
+def test_dtype_combinations():
+    base = synth.CONFIGS["mid_bf16"]
+    ok = parity.abi_config(base)
+    assert moe.workspace_bytes(ok, 64) > 0
+    bad = moe.make_config(2048, 512, 64, 8, 512, 2, 1024, act="f32", weight="bf16")
+    assert moe.workspace_bytes(bad, 64) == 0
+    bad = moe.make_config(2048, 512, 64, 8, 512, 2, 1024, act="bf16", weight="f32")
+    assert moe.workspace_bytes(bad, 64) == 0
+    fp8_odd = moe.make_config(2048, 576, 64, 8, 512, 2, 1024, act="bf16", weight="fp8")
+    assert moe.workspace_bytes(fp8_odd, 64) == 0  # fp8 needs multiples of 128
+
+
+def test_argument_errors_before_any_launch():
+    c = parity.abi_config(synth.CONFIGS["mid_bf16"])
+    need = moe.workspace_bytes(c, 64)
+    w = moe.MoeWeights(w_router=1)
+    out = moe.MoeRouteOut(1, 1, 0, 0)
+    # missing weights, outputs, workspace
+    assert moe.moe_route(c, moe.MoeWeights(), 1, 64, out, 256, need, 0) == -1
+    assert moe.moe_route(c, w, 1, 64, moe.MoeRouteOut(0, 1, 0, 0), 256, need, 0) == -1
+    assert moe.moe_route(c, w, 1, 64, out, 0, need, 0) == -3
+    assert moe.moe_route(c, w, 1, 64, out, 256, need - 1, 0) == -3
+    assert moe.moe_route(c, w, 1, 64, out, 257, need, 0) == -3       # misaligned
+    assert moe.moe_route(c, w, 1, -1, out, 256, need, 0) == -1
+    d = moe.MoeDispatchOut(1, 1, 1, 0)
+    assert moe.moe_dispatch(c, 1, 64, d, 256, need, 0) == -1
+    assert moe.moe_forward(c, w, 1, 64, 1, None, None, 256, need, 0) == -1  # no expert weights
+    assert moe.status_str(-3).startswith("workspace")
+    assert moe.status_str(7) == "unknown status"
