@@ -41,6 +41,7 @@ static int env_int(const char *name, int dflt) {
 // ---- direct-to-LDS bf16 engine ----------------------------------------------------
 struct DmaShape {
   int wm, wn, subm, frn, bk, stages, occ;
+  constexpr int threads() const { return 64 * wm * wn; }
   constexpr int tm() const { return wm * subm * 32; }
   constexpr int tn() const { return wn * frn * 32; }
   constexpr size_t lds() const { return (size_t)stages * (tm() + tn()) * bk * 2; }
@@ -54,6 +55,10 @@ constexpr DmaShape kDma[] = {
     {1, 4, 4, 2, 32, 3, 2},  // 5: 128 x 256, BK 32, 3 stages (72 KB), 2 per CU
     {2, 2, 2, 2, 64, 2, 2},  // 6: 128 x 128, BK 64, 2 stages (64 KB), 2 per CU
     {2, 2, 5, 2, 32, 4, 1},  // 7: 320 x 128, BK 32, 4 stages (112 KB)
+    {2, 4, 5, 2, 64, 2, 1},  // 8: 320 x 256, 8 waves, BK 64, 2 stages (144 KB)
+    {2, 4, 3, 2, 64, 2, 1},  // 9: 192 x 256, 8 waves, BK 64, 2 stages (112 KB)
+    {2, 4, 4, 2, 64, 2, 1},  // 10: 256 x 256, 8 waves, BK 64, 2 stages (128 KB)
+    {2, 4, 4, 2, 32, 4, 1},  // 11: 256 x 256, 8 waves, BK 32, 4 stages (128 KB)
 };
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 
@@ -72,7 +77,7 @@ static hipError_t launch_dma_v(GemmArgs a, hipStream_t s) {
   const int tn_out = DUAL ? sh.tn() / 2 : sh.tn();
   a.n_tiles_n = (int32_t)((a.N + tn_out - 1) / tn_out);
   const int gm_dense = env_int("MOE_GROUP_M_DENSE", 4);
-  const int gm_grouped = env_int("MOE_GROUP_M_GROUPED", 2);
+  const int gm_grouped = env_int("MOE_GROUP_M_GROUPED", 1);
   a.group_m = a.offsets == nullptr ? gm_dense : gm_grouped;
   if (a.group_m < 1) a.group_m = 1;
   int64_t m_tiles;
@@ -81,7 +86,7 @@ static hipError_t launch_dma_v(GemmArgs a, hipStream_t s) {
   int64_t blocks = m_tiles * a.n_tiles_n;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  return launch_kernel(kern, dim3((unsigned)blocks), dim3(256), sh.lds(), s, a);
+  return launch_kernel(kern, dim3((unsigned)blocks), dim3(sh.threads()), sh.lds(), s, a);
 }
 
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
@@ -95,6 +100,10 @@ static hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
     case 5: return launch_dma_v<5, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
     case 6: return launch_dma_v<6, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
     case 7: return launch_dma_v<7, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 8: return launch_dma_v<8, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 9: return launch_dma_v<9, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 10: return launch_dma_v<10, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 11: return launch_dma_v<11, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -102,8 +111,8 @@ static hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
 // Tile shape of the bf16 engine per kind (a tuning override is read from
 // MOE_GEMM_DENSE / MOE_GEMM_GROUPED).
 int dma_variant(GemmKind kind) {
-  const int dense = env_int("MOE_GEMM_DENSE", 1);
-  const int grouped = env_int("MOE_GEMM_GROUPED", 0);
+  const int dense = env_int("MOE_GEMM_DENSE", 10);
+  const int grouped = env_int("MOE_GEMM_GROUPED", 8);
   const int v = (kind == GK_EXPERT_SITU || kind == GK_EXPERT_DOWN) ? grouped : dense;
   return (v >= 0 && v < kNumDma) ? v : 0;
 }

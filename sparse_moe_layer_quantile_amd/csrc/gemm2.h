@@ -4,7 +4,7 @@
 // dual gate-up / K-segmented), for bf16 operands.  Tile TM x TN x BK with
 // TM = WM * SUBM * 32 A rows, TN = WN * FRN * 32 B rows and BK = 32 or 64;
 // 4 waves in a WM x WN layout, each wave SUBM x FRN blocks of
-// v_mfma_f32_32x32x16_bf16; OCC workgroups per CU.
+// v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC workgroups per CU.
 //
 //  * Global -> LDS with global_load_lds_dwordx4 (gfx950): no staging
 //    registers; each wave instruction fills 1 KB = RPI tile rows of 2 BK
@@ -112,7 +112,7 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
 
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
           bool GATHER, bool MSEG, typename OutT>
-__global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
+__global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
   constexpr int RB = BK * 2;          // bytes per tile row
   constexpr int CPR = RB / 16;        // 16 B chunks per row
@@ -121,9 +121,12 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
   constexpr int TN_OUT = DUAL ? TN / 2 : TN;
   constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  constexpr int A_LD = TM / (4 * RPI), B_LD = TN / (4 * RPI);  // DMA instructions per wave
+  constexpr int NW = WM * WN;  // waves per workgroup
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int A_LD = TM / (NW * RPI), B_LD = TN / (NW * RPI);  // DMA instructions per wave
   constexpr int L = A_LD + B_LD;
-  static_assert(TM % (4 * RPI) == 0 && TN % (4 * RPI) == 0, "tile rows per DMA round");
+  static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per DMA round");
+  static_assert(!DUAL || (TN / 2) % (NW * RPI) == 0, "gate/up split on a DMA round");
   static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -132,26 +135,26 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (WN == 4) ? 0 : wave / WN, wn = (WN == 4) ? wave : wave % WN;
+  const int wm = wave / WN, wn = wave % WN;
   const int rsub = lane / CPR, slot = lane % CPR;
 
   // ---- per-lane source rows -------------------------------------------------
-  // A: instruction i of this wave fills tile rows (wave + 4 i) * RPI + rsub.
+  // A: instruction i of this wave fills tile rows (wave + NW i) * RPI + rsub.
   int32_t a_row[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = (wave + 4 * i) * RPI + rsub;
+    const int r = (wave + NW * i) * RPI + rsub;
     int64_t m = tile.m0 + r;
     if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
     if constexpr (GATHER) m = args.gather[m] / args.gather_div;
     a_row[i] = (int32_t)m;
   }
   // B: tile rows below TN/2 are gate rows and the rest up rows for a dual
-  // problem; with 4 waves that split falls exactly at instruction B_LD / 2.
+  // problem; that split falls exactly at instruction B_LD / 2.
   int32_t b_row[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int r = (wave + 4 * i) * RPI + rsub;
+    const int r = (wave + NW * i) * RPI + rsub;
     int64_t n = tile.n0 + ((DUAL && i >= B_LD / 2) ? r - TN / 2 : r);
     if (n >= args.N) n = tile.n0;
     b_row[i] = (int32_t)n;
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
   }
   // chunk this lane fetches so that the DMA slot order realises the swizzle;
   // the rows of one instruction start at a multiple of RPI, so the swizzle
-  // key of row (wave + 4 i) * RPI + rsub does not depend on i
+  // key of row (wave + NW i) * RPI + rsub does not depend on i
   const int fetch_chunk = slot ^ ((((wave * RPI) + rsub) / (16 / CPR)) % CPR);
 
   // ---- K segments -------------------------------------------------------------
@@ -197,12 +200,12 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
     char *st = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
-      dma16(cur_a + (int64_t)a_row[i] * cur_lda + k0, st + (wave + 4 * i) * 1024);
+      dma16(cur_a + (int64_t)a_row[i] * cur_lda + k0, st + (wave + NW * i) * 1024);
     static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const uint16_t *Bm = (DUAL && i >= B_LD / 2) ? bu : cur_b;  // dual: one segment
-      dma16(Bm + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + 4 * i) * 1024);
+      dma16(Bm + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + NW * i) * 1024);
     }
     ++cur_k;
   };
@@ -237,8 +240,8 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
   auto dma_one = [&](auto d_tag, int kt, int st) {
     constexpr int d = decltype(d_tag)::value;
     char *dst = smem + st * STAGE_BYTES;
-    if constexpr (d < A_LD) dma16(a_src[d] + kt * BK, dst + (wave + 4 * d) * 1024);
-    else dma16(b_src[d - A_LD] + kt * BK, dst + A_BYTES + (wave + 4 * (d - A_LD)) * 1024);
+    if constexpr (d < A_LD) dma16(a_src[d] + kt * BK, dst + (wave + NW * d) * 1024);
+    else dma16(b_src[d - A_LD] + kt * BK, dst + A_BYTES + (wave + NW * (d - A_LD)) * 1024);
   };
 
   // Operand fragment f of k step ks (f < FRN: B fragment f, else A fragment f - FRN).
@@ -300,19 +303,28 @@ __global__ void __launch_bounds__(256, OCC) gemm_dma_kernel(GemmArgs args) {
               constexpr int i = q / FRN, j = q % FRN;
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S & 1][i], fb[S & 1][j],
                                                                   acc[i][j], 0, 0, 0);
+              // next step's fragments from the first MFMAs on (one per MFMA when
+              // they fit), so they have landed when the step starts
               if constexpr (S + 1 < KS) {
                 static_for<NF>([&](auto f_tag) {
                   constexpr int f = decltype(f_tag)::value;
-                  if constexpr (f >= q * NF / Q && f < (q + 1) * NF / Q)
+                  constexpr bool mine = NF <= Q ? (f == q) : (f >= q * NF / Q && f < (q + 1) * NF / Q);
+                  if constexpr (mine)
                     read_frag(st, S + 1, f_tag, fa[(S + 1) & 1], fb[(S + 1) & 1]);
                 });
               }
-              constexpr int g = S * Q + q;
-              static_for<L>([&](auto d_tag) {
-                constexpr int d = decltype(d_tag)::value;
-                if constexpr (d >= g * L / (KS * Q) && d < (g + 1) * L / (KS * Q))
-                  dma_one(d_tag, kdc, dst);
-              });
+              // DMAs of the tile STAGES - 1 ahead: with two stages that tile is
+              // needed at the next barrier, so they all go out in the first k
+              // step; deeper rings spread them over the whole stage
+              constexpr int DS = STAGES == 2 ? 1 : KS;  // k steps that carry DMAs
+              if constexpr (S < DS) {
+                constexpr int g = S * Q + q;
+                static_for<L>([&](auto d_tag) {
+                  constexpr int d = decltype(d_tag)::value;
+                  if constexpr (d >= g * L / (DS * Q) && d < (g + 1) * L / (DS * Q))
+                    dma_one(d_tag, kdc, dst);
+                });
+              }
               __builtin_amdgcn_sched_barrier(0);
             });
           });
