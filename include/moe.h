@@ -81,7 +81,9 @@ typedef struct moe_config {
   int32_t cutoff_mode;  /* moe_cutoff_mode */
 } moe_config;
 /* Shape limits: bf16/fp8 paths need d, latent, expert_inter, shared_inter
- * multiples of 64 (of 128 with fp8 weights); else MOE_ERR_UNSUPPORTED. */
+ * multiples of 64 (of 128 with fp8 weights); bt * top_k below 2^31; with bf16
+ * activations the latent activations bt * latent * 2 bytes stay below 4 GiB
+ * (bt < 599186 at latent 3584).  Else MOE_ERR_UNSUPPORTED. */
 
 typedef struct moe_weights {
   const void *w_router;      /* [E][d] router_dtype */

@@ -7,8 +7,9 @@
 //   shared_stream: shared gate/up + SiTU -> hs                    (step g, part 1)
 //   stream:        router logits -> cutoffs -> top-k -> dispatch  (step c)
 //                  x_lat = x W_down_proj^T                        (step d)
-//                  grouped gate/up + SiTU -> h (gathered rows)    (step e)
-//                  grouped down, x routing weight -> o            (step e)
+//                  grouped gate/up + SiTU, x routing weight -> h  (step e; the
+//                    weight is applied before W_d, which is linear)
+//                  grouped down -> o                              (step e)
 //                  combine + latent RMSNorm -> n                  (step f)
 //                  join(shared_stream)
 //                  y = [n | hs] [W_up_proj | W_ds,0 | W_ds,1]^T   (steps f, g; the final sum)
@@ -43,8 +44,8 @@ struct Plan {
   bool fp8 = false;
   int64_t act_bytes = 2;
   // byte offsets into the workspace
-  size_t z, zT, alpha, idx, w, counts, offsets, tile_offsets, perm, inv_perm, masks, xlat, h, o,
-      n, hs, total;
+  size_t z, zT, alpha, idx, w, w_sorted, counts, offsets, tile_offsets, perm, inv_perm, masks,
+      xlat, h, o, n, hs, total;
 };
 
 moe_status check_config(const moe_config *c) {
@@ -85,6 +86,8 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->fp8 = c->weight_dtype == MOE_FP8E4M3_B128;
   p->act_bytes = elem_size(c->act_dtype);
   const int64_t E = c->n_experts, k = c->top_k, P = bt * k, L = c->latent;
+  // the bf16 engine addresses gathered x_lat rows with 32-bit byte offsets
+  if (p->path == PATH_BF16 && bt * L * 2 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   const int64_t nb = (bt + 63) / 64;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -97,6 +100,7 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->alpha = take(4 * E);
   p->idx = take(4 * P);
   p->w = take(4 * P);
+  p->w_sorted = take(4 * P);
   p->counts = take(4 * E);
   p->offsets = take(4 * (E + 1));
   p->tile_offsets = take(4 * (E + 1));
@@ -354,9 +358,10 @@ MOE_API moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, 
   if (bt > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MOE_TRY_HIP(launch_dispatch(topk_idx, bt, cfg->top_k, cfg->n_experts, gemm_bm(p.path),
-                              at<uint64_t>(ws, p.masks), out->counts, out->offsets,
-                              at<int32_t>(ws, p.tile_offsets), out->perm, out->inv_perm, s));
+  MOE_TRY_HIP(launch_dispatch(topk_idx, nullptr, bt, cfg->top_k, cfg->n_experts,
+                              gemm_bm(p.path), at<uint64_t>(ws, p.masks), out->counts,
+                              out->offsets, at<int32_t>(ws, p.tile_offsets), out->perm,
+                              out->inv_perm, nullptr, s));
   return MOE_OK;
 }
 
@@ -420,11 +425,12 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   int32_t *perm = disp ? disp->perm : at<int32_t>(ws, p.perm);
   int32_t *inv_perm = disp ? disp->inv_perm : at<int32_t>(ws, p.inv_perm);
   int32_t *tile_offsets = at<int32_t>(ws, p.tile_offsets);
+  float *w_sorted = at<float>(ws, p.w_sorted);
   {
     PhaseScope ph(PH_DISPATCH, s);
-    MOE_TRY_HIP(launch_dispatch(idx, bt, k, E, grouped_tile_rows(p.path, fp8),
+    MOE_TRY_HIP(launch_dispatch(idx, wts, bt, k, E, grouped_tile_rows(p.path, fp8),
                                 at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
-                                inv_perm, s));
+                                inv_perm, w_sorted, s));
   }
 
   // ---- x_lat = x W_down_proj^T ---------------------------------------------------
@@ -460,6 +466,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.s_estride = fp8 ? (I / 128) * (L / 128) : 0;
     a.gather = perm;
     a.gather_div = (int32_t)k;
+    a.row_scale = w_sorted;  // h rows carry the routing weight: W_d (w h) = w (W_d h)
     a.out = h;
     a.ldo = I;
     PhaseScope ph(PH_EXPERT_GATEUP, s);
@@ -476,8 +483,6 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.n_experts = (int32_t)E;
     a.b_estride = L * I;
     a.s_estride = fp8 ? (L / 128) * (I / 128) : 0;
-    a.row_w = wts;
-    a.row_perm = perm;
     a.out = o;
     a.ldo = L;
     PhaseScope ph(PH_EXPERT_DOWN, s);

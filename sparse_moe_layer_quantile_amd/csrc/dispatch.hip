@@ -13,7 +13,8 @@
 //   2. one workgroup scans counts -> offsets, and ceil(counts / tile_bm) ->
 //      the first M-tile of each expert for the grouped GEMMs;
 //   3. one workgroup per expert walks its masks in token order: a prefix
-//      over the blocks' popcounts places every pair at its stable position.
+//      over the blocks' popcounts places every pair at its stable position
+//      (and, for the forward pass, copies the pair's routing weight there).
 #include "common.h"
 #include "kernels.h"
 
@@ -86,8 +87,8 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int32_t 
 
 __global__ void __launch_bounds__(256) dispatch_scatter_kernel(
     const uint64_t *__restrict__ masks, int nb, const int32_t *__restrict__ idx, int k,
-    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-    int32_t *__restrict__ inv_perm) {
+    const int32_t *__restrict__ offsets, const float *__restrict__ w,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm, float *__restrict__ w_sorted) {
   __shared__ int32_t wsum[4];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,6 +121,7 @@ __global__ void __launch_bounds__(256) dispatch_scatter_kernel(
       const int32_t p = (int32_t)(t * k + j);
       perm[pos] = p;
       inv_perm[p] = pos;
+      if (w_sorted) w_sorted[pos] = w[p];
       ++pos;
     }
     run += total;
@@ -127,10 +129,10 @@ __global__ void __launch_bounds__(256) dispatch_scatter_kernel(
   }
 }
 
-hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
-                           int tile_bm, uint64_t *masks, int32_t *counts, int32_t *offsets,
-                           int32_t *tile_offsets, int32_t *perm, int32_t *inv_perm,
-                           hipStream_t s) {
+hipError_t launch_dispatch(const int32_t *idx, const float *w, int64_t bt, int64_t k,
+                           int64_t n_experts, int tile_bm, uint64_t *masks, int32_t *counts,
+                           int32_t *offsets, int32_t *tile_offsets, int32_t *perm,
+                           int32_t *inv_perm, float *w_sorted, hipStream_t s) {
   const int E = (int)n_experts;
   hipError_t err = launch_zero_i32(counts, E, s);
   if (err != hipSuccess) return err;
@@ -145,7 +147,7 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_
   if (err != hipSuccess) return err;
   if (nb > 0)
     err = launch_kernel(dispatch_scatter_kernel, dim3(E), dim3(256), 0, s, masks, nb, idx, (int)k,
-                        offsets, perm, inv_perm);
+                        offsets, w_sorted ? w : nullptr, perm, inv_perm, w_sorted);
   return err;
 }
 

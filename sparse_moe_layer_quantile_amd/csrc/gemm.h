@@ -15,7 +15,7 @@
 
 namespace moe {
 
-enum Epi { EPI_STORE = 0, EPI_ROUTER = 1, EPI_SITU = 2, EPI_ROWSCALE = 3 };
+enum Epi { EPI_STORE = 0, EPI_ROUTER = 1, EPI_SITU = 2 };
 
 struct GemmSeg {
   const void *a;
@@ -43,8 +43,7 @@ struct GemmArgs {
   int64_t ldo;
   float *out_t;              // router: transposed copy [N][M] (may be NULL)
   const float *bias;         // router: [N] (may be NULL)
-  const float *row_w;        // rowscale: weight of pair row_perm[p]
-  const int32_t *row_perm;
+  const float *row_scale;    // SiTU: factor of output row m (NULL = 1)
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
@@ -104,10 +103,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, int64_t row, int64_t
     const float z = v + (a.bias ? a.bias[col] : 0.0f);
     static_cast<float *>(a.out)[row * a.ldo + col] = z;
   } else if constexpr (EPI == EPI_SITU) {
+    const float f = a.row_scale ? a.row_scale[row] : 1.0f;
     store_out<OutT>(a.out, row * a.ldo + col,
-                    situ(v, vu, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
-  } else if constexpr (EPI == EPI_ROWSCALE) {
-    store_out<OutT>(a.out, row * a.ldo + col, v * a.row_w[a.row_perm[row]]);
+                    f * situ(v, vu, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
   } else {
     store_out<OutT>(a.out, row * a.ldo + col, v);
   }

@@ -67,18 +67,19 @@ static hipError_t launch_dma_v(GemmArgs a, hipStream_t s) {
   constexpr DmaShape sh = kDma[V];
   auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, EPI,
                                   DUAL, GATHER, MSEG, OutT>;
+  constexpr size_t lds = sh.lds() + g2::epilogue_lds_bytes<EPI, sh.tm()>();
+  static_assert(lds <= 160 * 1024, "LDS of a gfx950 workgroup");
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds());
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tn_out = DUAL ? sh.tn() / 2 : sh.tn();
   a.n_tiles_n = (int32_t)((a.N + tn_out - 1) / tn_out);
-  const int gm_dense = env_int("MOE_GROUP_M_DENSE", 4);
-  const int gm_grouped = env_int("MOE_GROUP_M_GROUPED", 1);
-  a.group_m = a.offsets == nullptr ? gm_dense : gm_grouped;
+  // dense rasterisation groups (grouped problems group by expert)
+  a.group_m = env_int("MOE_GROUP_M_DENSE", 4);
   if (a.group_m < 1) a.group_m = 1;
   int64_t m_tiles;
   if (a.offsets == nullptr) m_tiles = (a.M + sh.tm() - 1) / sh.tm();
@@ -86,7 +87,7 @@ static hipError_t launch_dma_v(GemmArgs a, hipStream_t s) {
   int64_t blocks = m_tiles * a.n_tiles_n;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  return launch_kernel(kern, dim3((unsigned)blocks), dim3(sh.threads()), sh.lds(), s, a);
+  return launch_kernel(kern, dim3((unsigned)blocks), dim3(sh.threads()), lds, s, a);
 }
 
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
@@ -135,7 +136,7 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int
         return launch_dma<EPI_STORE, false, false, uint16_t>(v, a, s);
       case GK_DENSE_SITU: return launch_dma<EPI_SITU, true, false, uint16_t>(v, a, s);
       case GK_EXPERT_SITU: return launch_dma<EPI_SITU, true, true, uint16_t>(v, a, s);
-      case GK_EXPERT_DOWN: return launch_dma<EPI_ROWSCALE, false, false, uint16_t>(v, a, s);
+      case GK_EXPERT_DOWN: return launch_dma<EPI_STORE, false, false, uint16_t>(v, a, s);
     }
     return hipErrorInvalidValue;
   }
@@ -145,7 +146,7 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int
       case GK_DENSE: return launch_f32<EPI_STORE, false, false>(a, m_tiles, s);
       case GK_DENSE_SITU: return launch_f32<EPI_SITU, true, false>(a, m_tiles, s);
       case GK_EXPERT_SITU: return launch_f32<EPI_SITU, true, true>(a, m_tiles, s);
-      case GK_EXPERT_DOWN: return launch_f32<EPI_ROWSCALE, false, false>(a, m_tiles, s);
+      case GK_EXPERT_DOWN: return launch_f32<EPI_STORE, false, false>(a, m_tiles, s);
     }
     return hipErrorInvalidValue;
   }
@@ -158,7 +159,7 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int
       case GK_EXPERT_SITU:
         return launch_mfma<EPI_SITU, true, false, true, uint16_t>(a, m_tiles, s);
       case GK_EXPERT_DOWN:
-        return launch_mfma<EPI_ROWSCALE, false, false, false, uint16_t>(a, m_tiles, s);
+        return launch_mfma<EPI_STORE, false, false, false, uint16_t>(a, m_tiles, s);
     }
   } else {
     switch (kind) {
@@ -169,7 +170,7 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int
       case GK_EXPERT_SITU:
         return launch_mfma<EPI_SITU, true, true, true, uint16_t>(a, m_tiles, s);
       case GK_EXPERT_DOWN:
-        return launch_mfma<EPI_ROWSCALE, false, true, false, uint16_t>(a, m_tiles, s);
+        return launch_mfma<EPI_STORE, false, true, false, uint16_t>(a, m_tiles, s);
     }
   }
   return hipErrorInvalidValue;

@@ -3,7 +3,7 @@
 // Same problem description as gemm.h (GemmArgs: dense / grouped / gathered /
 // dual gate-up / K-segmented), for bf16 operands.  Tile TM x TN x BK with
 // TM = WM * SUBM * 32 A rows, TN = WN * FRN * 32 B rows and BK = 32 or 64;
-// 4 waves in a WM x WN layout, each wave SUBM x FRN blocks of
+// WM x WN waves, each wave SUBM x FRN blocks of
 // v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC workgroups per CU.
 //
 //  * Global -> LDS with global_load_lds_dwordx4 (gfx950): no staging
@@ -19,7 +19,12 @@
 //  * Work items are spread over the 8 XCDs in contiguous ranges (workgroup i
 //    runs on XCD i % 8), so the N tiles that share an A tile (one expert's
 //    gathered tokens, one token block) run on one XCD and share its L2.
-//  * A partial M tile skips the MFMAs of its empty 32-row sub-blocks.
+//  * Sub-block i of wave row wm holds tile rows (i WM + wm) 32 ..+32, so a
+//    partial M tile (an expert's last rows) is shared by all wave rows and
+//    skips the MFMAs of its empty sub-blocks.
+//  * Single-segment problems address every DMA from a uniform base with a
+//    32-bit per-lane offset, which keeps the address registers at one VGPR
+//    per load instruction.
 #pragma once
 
 #include <type_traits>
@@ -61,18 +66,25 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
                                    16, 0, 0);
 }
 
+// One dword per lane: lane l's 4 bytes land at lds_wave_base + 4 l.
+__device__ __forceinline__ void dma4(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(g),
+                                   (__attribute__((address_space(3))) void *)(lds_wave_base),
+                                   4, 0, 0);
+}
+
 // Tile coordinates.  The tile list (M tiles x N tiles) is cut into 8
 // contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so all N
 // tiles of an M tile -- which share its A rows -- stay in one L2.  Inside a
-// range, tiles go in groups of group_m M tiles with M fastest: the concurrent
-// workgroups of an XCD then cover a group_m x (32 / group_m) block of tiles
-// and each A and B slice is fetched into L2 once for several of them.
+// range, tiles go in groups with M fastest, so the concurrent workgroups of an
+// XCD share A and B slices in its L2: dense problems use groups of group_m M
+// tiles; grouped problems use one group per expert, so the M tiles of an
+// expert, which read the same expert matrix, run side by side.
 template <int TM, int TN_OUT>
 __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
   const int64_t nt = a.n_tiles_n;
-  int64_t mtiles;
-  if (a.offsets == nullptr) mtiles = (a.M + TM - 1) / TM;
-  else mtiles = a.tile_offsets[a.n_experts];
+  const bool grouped = a.offsets != nullptr;
+  const int64_t mtiles = grouped ? (int64_t)a.tile_offsets[a.n_experts] : (a.M + TM - 1) / TM;
   const int64_t total = mtiles * nt;
   Tile t;
   const int64_t per = (total + 7) / 8;
@@ -83,31 +95,48 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
     t.valid = false;
     return t;
   }
-  const int64_t group_m = a.group_m > 0 ? a.group_m : 1;
-  const int64_t gsz = group_m * nt;
-  const int64_t g = lin / gsz, r = lin - g * gsz;
-  const int64_t first_m = g * group_m;
-  const int64_t gm = min(group_m, mtiles - first_m);
+  int64_t first_m, gm, r;
+  int e = 0;
+  if (!grouped) {
+    const int64_t group_m = a.group_m > 0 ? a.group_m : 1;
+    const int64_t gsz = group_m * nt;
+    const int64_t g = lin / gsz;
+    r = lin - g * gsz;
+    first_m = g * group_m;
+    gm = min(group_m, mtiles - first_m);
+  } else {
+    // expert e owns the linear range [tile_offsets[e] nt, tile_offsets[e+1] nt)
+    const int64_t mt_lin = lin / nt;
+    int lo = 0, hi = a.n_experts;  // tile_offsets[lo] <= mt_lin < tile_offsets[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tile_offsets[mid] <= mt_lin) lo = mid;
+      else hi = mid;
+    }
+    e = lo;
+    first_m = a.tile_offsets[lo];
+    gm = a.tile_offsets[lo + 1] - first_m;
+    r = lin - first_m * nt;
+  }
   const int64_t mt = first_m + r % gm;
   t.n0 = (r / gm) * TN_OUT;
-  if (a.offsets == nullptr) {
-    t.e = 0;
+  t.e = e;
+  if (!grouped) {
     t.m0 = mt * TM;
     t.m_end = min(a.M, t.m0 + TM);
-    t.valid = true;
-    return t;
+  } else {
+    t.m0 = a.offsets[e] + (mt - first_m) * TM;
+    t.m_end = min((int64_t)a.offsets[e + 1], t.m0 + TM);
   }
-  int lo = 0, hi = a.n_experts;  // tile_offsets[lo] <= mt < tile_offsets[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_offsets[mid] <= mt) lo = mid;
-    else hi = mid;
-  }
-  t.e = lo;
-  t.m0 = a.offsets[lo] + (mt - a.tile_offsets[lo]) * TM;
-  t.m_end = min((int64_t)a.offsets[lo + 1], t.m0 + TM);
   t.valid = true;
   return t;
+}
+
+// Extra LDS of a kernel instance past its stage ring: the per-row factors of a
+// SiTU epilogue.
+template <int EPI, int TM>
+constexpr int epilogue_lds_bytes() {
+  return EPI == EPI_SITU ? TM * 4 : 0;
 }
 
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
@@ -128,6 +157,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per DMA round");
   static_assert(!DUAL || (TN / 2) % (NW * RPI) == 0, "gate/up split on a DMA round");
   static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
+  static_assert(!GATHER || !MSEG, "gathered A has one K segment");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const Tile tile = map_tile_xcd<TM, TN_OUT>(args);
@@ -137,6 +167,18 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int rsub = lane / CPR, slot = lane % CPR;
+
+  // ---- per-row factors of the SiTU epilogue, into LDS past the ring --------
+  // (older than every operand load, so the first tile's wait covers them)
+  float *rs_lds = reinterpret_cast<float *>(smem + STAGES * STAGE_BYTES);
+  const bool use_rs = EPI == EPI_SITU && args.row_scale != nullptr;
+  if constexpr (EPI == EPI_SITU) {
+    if (use_rs && wave < TM / 64) {
+      int64_t m = tile.m0 + wave * 64 + lane;
+      if (m >= tile.m_end) m = tile.m0;  // loaded, never used
+      dma4(args.row_scale + m, rs_lds + wave * 64);
+    }
+  }
 
   // ---- per-lane source rows -------------------------------------------------
   // A: instruction i of this wave fills tile rows (wave + NW i) * RPI + rsub.
@@ -210,10 +252,13 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     ++cur_k;
   };
 
-  // valid 32-row sub-blocks of this wave (partial tiles skip the rest)
+  // valid 32-row sub-blocks of this wave: sub-block i of wave row wm covers
+  // tile rows (i WM + wm) 32 ..+32, so a partial tile spreads over both wave
+  // rows; the MFMAs of empty sub-blocks are skipped
   const int rows_valid = (int)(tile.m_end - tile.m0);
-  int sub_valid = (rows_valid - wm * SUBM * 32 + 31) / 32;
-  sub_valid = sub_valid < 0 ? 0 : (sub_valid > SUBM ? SUBM : sub_valid);
+  const int sb_left = (rows_valid + 31) / 32 - wm;
+  int sub_valid = sb_left <= 0 ? 0 : (sb_left + WM - 1) / WM;
+  sub_valid = sub_valid > SUBM ? SUBM : sub_valid;
   sub_valid = __builtin_amdgcn_readfirstlane(sub_valid);
 
   f32x16 acc[SUBM][FRN];
@@ -224,24 +269,45 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Single-segment problems: source pointer of each DMA instruction (K offset
-  // excluded), computed once.
-  const uint16_t *a_src[MSEG ? 1 : A_LD];
-  const uint16_t *b_src[MSEG ? 1 : B_LD];
+  // Single-segment problems: every DMA source is a uniform base plus a 32-bit
+  // per-lane byte offset (global_load_lds with an SGPR base).  Contiguous A
+  // and B are addressed from the tile's first row, so the offsets stay below
+  // TM (TN) rows; gathered A is addressed from the matrix start, which holds
+  // as long as the gathered matrix is under 4 GiB.
+  const char *a_base = nullptr, *b_base = nullptr, *bu_base = nullptr;
+  uint32_t a_off[MSEG ? 1 : A_LD];
+  uint32_t b_off[MSEG ? 1 : B_LD];
   if constexpr (!MSEG) {
+    const int64_t a_first = GATHER ? 0 : tile.m0;
+    a_base = reinterpret_cast<const char *>(cur_a + a_first * cur_lda);
+    b_base = reinterpret_cast<const char *>(cur_b + tile.n0 * cur_ldb);
+    if constexpr (DUAL) bu_base = reinterpret_cast<const char *>(bu + tile.n0 * cur_ldb);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
-      a_src[i] = cur_a + (int64_t)a_row[i] * cur_lda + fetch_chunk * 8;
+      a_off[i] = (uint32_t)(((int64_t)a_row[i] - a_first) * cur_lda * 2 + fetch_chunk * 16);
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
-      b_src[i] = ((DUAL && i >= B_LD / 2) ? bu : cur_b) + (int64_t)b_row[i] * cur_ldb + fetch_chunk * 8;
+      b_off[i] = (uint32_t)(((int64_t)b_row[i] - tile.n0) * cur_ldb * 2 + fetch_chunk * 16);
   }
   // DMA instruction d (A rows first, then B rows) of K tile kt into stage st.
   auto dma_one = [&](auto d_tag, int kt, int st) {
     constexpr int d = decltype(d_tag)::value;
     char *dst = smem + st * STAGE_BYTES;
-    if constexpr (d < A_LD) dma16(a_src[d] + kt * BK, dst + (wave + NW * d) * 1024);
-    else dma16(b_src[d - A_LD] + kt * BK, dst + A_BYTES + (wave + NW * (d - A_LD)) * 1024);
+    const int64_t kb = (int64_t)kt * RB;
+    // the empty asm re-issues the 32-bit offset inside the loop body, so the
+    // instruction selector sees uniform base + zext(offset) there (SGPR-base
+    // form) instead of a 64-bit address hoisted out of the loop
+    if constexpr (d < A_LD) {
+      uint32_t off = a_off[d];
+      asm volatile("" : "+v"(off));
+      dma16(a_base + kb + off, dst + (wave + NW * d) * 1024);
+    } else {
+      constexpr int i = d - A_LD;
+      const char *base = (DUAL && i >= B_LD / 2) ? bu_base : b_base;
+      uint32_t off = b_off[i];
+      asm volatile("" : "+v"(off));
+      dma16(base + kb + off, dst + A_BYTES + (wave + NW * i) * 1024);
+    }
   };
 
   // Operand fragment f of k step ks (f < FRN: B fragment f, else A fragment f - FRN).
@@ -257,14 +323,13 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       else r = (wn * FRN + j) * 32 + (lane & 31);
       base = st + A_BYTES;
     } else {
-      r = (wm * SUBM + (f - FRN)) * 32 + (lane & 31);
+      r = ((f - FRN) * WM + wm) * 32 + (lane & 31);
       base = st;
     }
     const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ ((r / (16 / CPR)) % CPR)) << 4));
     if constexpr (f < FRN) bfr[f] = v;
     else af[f - FRN] = v;
   };
-
   // K loop for NS active sub-blocks.  Single-segment problems run one
   // straight-line schedule per stage: MFMAs one at a time, with the fragment
   // reads of the next k step and the DMA instructions of the tile STAGES - 1
@@ -370,28 +435,52 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     default: if constexpr (SUBM >= 5) mainloop(std::integral_constant<int, 5>{}); break;
   }
 
-  // ---- epilogue: lane holds column (lane & 31), rows 8(r/4) + 4(lane/32) + r%4 ----
+
+  // ---- epilogue: lane holds column (lane & 31), rows 8(r/4) + 4(lane/32) + r%4
+  // of each 32 x 32 block.  Row quantities are formed once per row, column
+  // ones once per block column; the SiTU row factors come from LDS.
+  if constexpr (EPI == EPI_SITU) {
+    if (use_rs) {
+      wait_vmcnt<0>();
+      barrier();
+    }
+  }
+  constexpr int JN = DUAL ? FRN / 2 : FRN;  // output block columns of this wave
+  int64_t col[JN];
+  bool col_ok[JN];
+  float bias[JN];
+#pragma unroll
+  for (int j = 0; j < JN; ++j) {
+    col[j] = tile.n0 + (wn * JN + j) * 32 + (lane & 31);
+    col_ok[j] = col[j] < args.N;
+    bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
+  }
+  OutT *out = static_cast<OutT *>(args.out);
 #pragma unroll
   for (int i = 0; i < SUBM; ++i) {
     if (i >= sub_valid) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row =
-          tile.m0 + (wm * SUBM + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int rr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int64_t row = tile.m0 + rr;
       if (row >= tile.m_end) continue;
-      if constexpr (DUAL) {
+      OutT *orow = out + row * args.ldo;
+      if constexpr (EPI == EPI_SITU) {
+        const float f = use_rs ? rs_lds[rr] : 1.0f;
 #pragma unroll
-        for (int j = 0; j < FRN / 2; ++j) {
-          const int64_t col = tile.n0 + (wn * (FRN / 2) + j) * 32 + (lane & 31);
-          if (col < args.N)
-            epilogue<EPI, OutT>(args, row, col, acc[i][j][r], acc[i][j + FRN / 2][r]);
-        }
+        for (int j = 0; j < JN; ++j)
+          if (col_ok[j])
+            store_out<OutT>(orow, col[j],
+                            f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
+                                     args.inv_beta, args.beta_u, args.inv_beta_u));
+      } else if constexpr (EPI == EPI_ROUTER) {
+#pragma unroll
+        for (int j = 0; j < JN; ++j)
+          if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
       } else {
 #pragma unroll
-        for (int j = 0; j < FRN; ++j) {
-          const int64_t col = tile.n0 + (wn * FRN + j) * 32 + (lane & 31);
-          if (col < args.N) epilogue<EPI, OutT>(args, row, col, acc[i][j][r], 0.0f);
-        }
+        for (int j = 0; j < JN; ++j)
+          if (col_ok[j]) store_out<OutT>(orow, col[j], acc[i][j][r]);
       }
     }
   }
@@ -401,20 +490,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       for (int i = 0; i < SUBM; ++i)
 #pragma unroll
         for (int j = 0; j < FRN; ++j) {
-          const int64_t col = tile.n0 + (wn * FRN + j) * 32 + (lane & 31);
-          if (col >= args.N) continue;
-          const float bias = args.bias ? args.bias[col] : 0.0f;
+          const int64_t c = col[j];
+          if (!col_ok[j]) continue;
+          const float b = bias[j];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int64_t row0 = tile.m0 + (wm * SUBM + i) * 32 + 8 * q + 4 * (lane >> 5);
-            float *dst = args.out_t + col * args.M + row0;
+            const int64_t row0 = tile.m0 + (i * WM + wm) * 32 + 8 * q + 4 * (lane >> 5);
+            float *dst = args.out_t + c * args.M + row0;
             if (row0 + 3 < tile.m_end && (args.M & 3) == 0) {
               *reinterpret_cast<float4 *>(dst) =
-                  make_float4(acc[i][j][q * 4 + 0] + bias, acc[i][j][q * 4 + 1] + bias,
-                              acc[i][j][q * 4 + 2] + bias, acc[i][j][q * 4 + 3] + bias);
+                  make_float4(acc[i][j][q * 4 + 0] + b, acc[i][j][q * 4 + 1] + b,
+                              acc[i][j][q * 4 + 2] + b, acc[i][j][q * 4 + 3] + b);
             } else {
               for (int u = 0; u < 4; ++u)
-                if (row0 + u < tile.m_end) dst[u] = acc[i][j][q * 4 + u] + bias;
+                if (row0 + u < tile.m_end) dst[u] = acc[i][j][q * 4 + u] + b;
             }
           }
         }

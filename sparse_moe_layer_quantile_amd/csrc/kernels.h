@@ -16,7 +16,7 @@ enum GemmKind {
   GK_DENSE = 1,        // C = A B^T (K may be split over segments)
   GK_DENSE_SITU = 2,   // h = SiTU(A Bg^T, A Bu^T)
   GK_EXPERT_SITU = 3,  // grouped + gathered A, SiTU epilogue
-  GK_EXPERT_DOWN = 4,  // grouped, epilogue scales row p by its routing weight
+  GK_EXPERT_DOWN = 4,  // grouped, plain store (h rows already carry the routing weight)
 };
 
 int gemm_bm(int path);
@@ -40,10 +40,11 @@ hipError_t launch_zero_i32(int32_t *dst, int64_t n, hipStream_t s);
 
 // ---- dispatch -------------------------------------------------------------------
 // masks: [E][ceil(bt/64)] u64 scratch; counts must be zeroed first.
-hipError_t launch_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
-                           int tile_bm, uint64_t *masks, int32_t *counts, int32_t *offsets,
-                           int32_t *tile_offsets, int32_t *perm, int32_t *inv_perm,
-                           hipStream_t s);
+// w / w_sorted may be NULL; otherwise w_sorted[pos] = w[perm[pos]].
+hipError_t launch_dispatch(const int32_t *idx, const float *w, int64_t bt, int64_t k,
+                           int64_t n_experts, int tile_bm, uint64_t *masks, int32_t *counts,
+                           int32_t *offsets, int32_t *tile_offsets, int32_t *perm,
+                           int32_t *inv_perm, float *w_sorted, hipStream_t s);
 
 // ---- combine + latent RMSNorm ---------------------------------------------------
 // o [P][L] (act) rows already scaled by their routing weight; n [bt][L] (act).
