@@ -15,6 +15,7 @@
 //                  y = [n | hs] [W_up_proj | W_ds,0 | W_ds,1]^T   (steps f, g; the final sum)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -27,6 +28,7 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kSplitMaxRows = 256;  // batches up to this size may split K
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -45,7 +47,8 @@ struct Plan {
   int64_t act_bytes = 2;
   // byte offsets into the workspace
   size_t z, zT, alpha, idx, w, w_sorted, counts, offsets, tile_offsets, perm, inv_perm, masks,
-      xlat, h, o, n, hs, total;
+      xlat, h, o, n, hs, split, split_sh, total;
+  int64_t split_cap = 0;  // floats in each split-K region (0: split K off)
 };
 
 moe_status check_config(const moe_config *c) {
@@ -112,6 +115,14 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->o = take(p->act_bytes * P * L);
   p->n = take(p->act_bytes * bt * L);
   p->hs = take(p->act_bytes * bt * c->n_shared * c->shared_inter);
+  // split-K partial sums of the dense bf16 GEMMs of short batches (up to 16
+  // splits of the widest output), one region per stream
+  if (p->path == PATH_BF16 && !p->fp8 && bt > 0 && bt <= kSplitMaxRows) {
+    const int64_t cols = std::max({E, L, c->d, 2 * c->n_shared * c->shared_inter});
+    p->split_cap = 16 * bt * cols;
+  }
+  p->split = take(4 * p->split_cap);
+  p->split_sh = take(4 * p->split_cap);
   p->total = off + kAlign;
   return MOE_OK;
 }
@@ -219,6 +230,8 @@ moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, c
   a.ldo = E;
   a.out_t = batch ? zT : nullptr;
   a.bias = w->router_bias;
+  a.partial = at<float>(ws, p.split);
+  a.partial_cap = p.split_cap;
   const int bm = gemm_bm(p.path);
   {
     PhaseScope ph(PH_ROUTER, s);
@@ -405,6 +418,8 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.seg[0] = GemmSeg{x, d, w->sh_gate, d, w->s_sh_gate, d};
     a.b_up = w->sh_up;
     a.bscale_up = w->s_sh_up;
+    a.partial = at<float>(ws, p.split_sh);
+    a.partial_cap = p.split_cap;
     a.out = hs;
     a.ldo = S * Is;
     PhaseScope ph(PH_SHARED, ss);
@@ -428,7 +443,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   float *w_sorted = at<float>(ws, p.w_sorted);
   {
     PhaseScope ph(PH_DISPATCH, s);
-    MOE_TRY_HIP(launch_dispatch(idx, wts, bt, k, E, grouped_tile_rows(p.path, fp8),
+    MOE_TRY_HIP(launch_dispatch(idx, wts, bt, k, E, grouped_tile_rows(p.path, fp8, P, E),
                                 at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
                                 inv_perm, w_sorted, s));
   }
@@ -441,6 +456,8 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.N = L;
     a.nseg = 1;
     a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, w->s_down_proj, d};
+    a.partial = at<float>(ws, p.split);
+    a.partial_cap = p.split_cap;
     a.out = xlat;
     a.ldo = L;
     PhaseScope ph(PH_DOWN_PROJ, s);
@@ -519,6 +536,8 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
       g.bscale = fp8 ? w->s_sh_down + j * (d / 128) * (Is / 128) : nullptr;
       g.k = Is;
     }
+    a.partial = at<float>(ws, p.split);
+    a.partial_cap = p.split_cap;
     a.out = y;
     a.ldo = d;
     PhaseScope ph(PH_OUTPUT, s);

@@ -47,6 +47,14 @@ struct GemmArgs {
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
+  // split K (dense bf16 problems with few tiles): K tile range blockIdx.y of
+  // ksplit; raw fp32 sums go to partial[split][M][ldp] (a dual problem's up
+  // sums at column N + c) and a second kernel reduces them and applies the
+  // epilogue.  partial == NULL (or partial_cap too small) disables it.
+  float *partial;
+  int64_t partial_cap;       // floats available at partial
+  int64_t ldp;
+  int32_t ksplit;
 };
 
 struct Tile {

@@ -14,8 +14,10 @@
 //    The DMA writes lane l at slot l % CPR, so lane l fetches the global
 //    chunk that belongs there.
 //  * STAGES-deep ring of LDS stages: the loads of tile kt + STAGES - 1 are in
-//    flight while tile kt is multiplied; every thread issues the same number
-//    of loads per tile, so "tile kt landed" is s_waitcnt vmcnt(L (STAGES-2)).
+//    flight while tile kt is multiplied.  The 1 KB instructions of a stage
+//    are dealt round-robin to the waves; each wave issues the same number of
+//    them for every tile (LW), so "tile kt landed" is, per wave,
+//    s_waitcnt vmcnt(LW (STAGES-2)) followed by a barrier.
 //  * Work items are spread over the 8 XCDs in contiguous ranges (workgroup i
 //    runs on XCD i % 8), so the N tiles that share an A tile (one expert's
 //    gathered tokens, one token block) run on one XCD and share its L2.
@@ -31,6 +33,10 @@
 #include <utility>
 
 #include "gemm.h"
+
+// kernel-local lambdas are always inlined (an outlined one puts its captures
+// on the stack)
+#define G2_INL __attribute__((always_inline))
 
 namespace moe {
 namespace g2 {
@@ -136,7 +142,7 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
 // SiTU epilogue.
 template <int EPI, int TM>
 constexpr int epilogue_lds_bytes() {
-  return EPI == EPI_SITU ? TM * 4 : 0;
+  return EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0;
 }
 
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
@@ -152,10 +158,19 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  constexpr int A_LD = TM / (NW * RPI), B_LD = TN / (NW * RPI);  // DMA instructions per wave
-  constexpr int L = A_LD + B_LD;
-  static_assert(TM % (NW * RPI) == 0 && TN % (NW * RPI) == 0, "tile rows per DMA round");
-  static_assert(!DUAL || (TN / 2) % (NW * RPI) == 0, "gate/up split on a DMA round");
+  // A stage is TA + TB wave instructions of 1 KB each (A rows, then B rows,
+  // in LDS order).  Instruction g is issued by wave g % NW as its (g / NW)-th,
+  // so a wave issues LMAX or LMAX - 1 of them per stage.
+  constexpr int TA = TM / RPI, TB = TN / RPI, TT = TA + TB;
+  constexpr int LMAX = (TT + NW - 1) / NW;
+  constexpr bool EVEN = TT % NW == 0;
+  static_assert(TM % RPI == 0 && TN % RPI == 0 && (TM / RPI) % 4 == 0, "whole DMA rows");
+  static_assert(!DUAL || (TN / 2) % RPI == 0, "gate/up split on a DMA instruction");
+  // multi-segment problems keep whole A and B rounds per wave
+  constexpr int A_LD = TA / NW, B_LD = TB / NW;
+  static_assert(!MSEG || (TA % NW == 0 && TB % NW == 0), "segmented: whole DMA rounds");
+  static_assert(!MSEG || !DUAL, "segmented problems are single");
+  constexpr int L = LMAX;
   static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
   static_assert(!GATHER || !MSEG, "gathered A has one K segment");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -173,33 +188,37 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   float *rs_lds = reinterpret_cast<float *>(smem + STAGES * STAGE_BYTES);
   const bool use_rs = EPI == EPI_SITU && args.row_scale != nullptr;
   if constexpr (EPI == EPI_SITU) {
-    if (use_rs && wave < TM / 64) {
-      int64_t m = tile.m0 + wave * 64 + lane;
-      if (m >= tile.m_end) m = tile.m0;  // loaded, never used
-      dma4(args.row_scale + m, rs_lds + wave * 64);
+    if (use_rs) {
+      for (int q = wave; q < (TM + 63) / 64; q += NW) {
+        int64_t m = tile.m0 + q * 64 + lane;
+        if (m >= tile.m_end) m = tile.m0;  // loaded, never used
+        dma4(args.row_scale + m, rs_lds + q * 64);
+      }
     }
   }
 
-  // ---- per-lane source rows -------------------------------------------------
+  // the last instruction slot of this wave carries an instruction
+  const bool has_last = EVEN || wave + NW * (LMAX - 1) < TT;
+
+  // ---- per-lane source rows (segmented problems) ----------------------------
   // A: instruction i of this wave fills tile rows (wave + NW i) * RPI + rsub.
-  int32_t a_row[A_LD];
+  int32_t a_row[MSEG ? A_LD : 1];
+  int32_t b_row[MSEG ? B_LD : 1];
+  if constexpr (MSEG) {
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = (wave + NW * i) * RPI + rsub;
-    int64_t m = tile.m0 + r;
-    if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
-    if constexpr (GATHER) m = args.gather[m] / args.gather_div;
-    a_row[i] = (int32_t)m;
-  }
-  // B: tile rows below TN/2 are gate rows and the rest up rows for a dual
-  // problem; that split falls exactly at instruction B_LD / 2.
-  int32_t b_row[B_LD];
+    for (int i = 0; i < A_LD; ++i) {
+      const int r = (wave + NW * i) * RPI + rsub;
+      int64_t m = tile.m0 + r;
+      if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+      a_row[i] = (int32_t)m;
+    }
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int r = (wave + NW * i) * RPI + rsub;
-    int64_t n = tile.n0 + ((DUAL && i >= B_LD / 2) ? r - TN / 2 : r);
-    if (n >= args.N) n = tile.n0;
-    b_row[i] = (int32_t)n;
+    for (int i = 0; i < B_LD; ++i) {
+      const int r = (wave + NW * i) * RPI + rsub;
+      int64_t n = tile.n0 + r;
+      if (n >= args.N) n = tile.n0;
+      b_row[i] = (int32_t)n;
+    }
   }
   const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
   const uint16_t *bu = static_cast<const uint16_t *>(args.b_up);
@@ -208,8 +227,9 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     if (DUAL) bu += (int64_t)tile.e * args.b_estride;
   }
   // chunk this lane fetches so that the DMA slot order realises the swizzle;
-  // the rows of one instruction start at a multiple of RPI, so the swizzle
-  // key of row (wave + NW i) * RPI + rsub does not depend on i
+  // instruction g fills rows g RPI + rsub of its region (A, or B from TA on,
+  // TA a multiple of 4), whose swizzle key (4 g + rsub / (16 / CPR)) % CPR
+  // depends on g only through g % 2 = wave % 2 (NW is even)
   const int fetch_chunk = slot ^ ((((wave * RPI) + rsub) / (16 / CPR)) % CPR);
 
   // ---- K segments -------------------------------------------------------------
@@ -220,14 +240,35 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       if (s < args.nseg) ktiles += (int)(args.seg[s].k / BK);
   }
 
+  // split K: this workgroup's range of K tiles (the host makes none empty)
+  int k_begin = 0;
+  if (args.ksplit > 1) {
+    const int kper = (ktiles + args.ksplit - 1) / args.ksplit;
+    k_begin = (int)blockIdx.y * kper;
+    ktiles = min(ktiles - k_begin, kper);
+  }
+
   // Prefetch cursor over (segment, K tile); segment fields are reloaded from
   // the kernel arguments (scalar loads) only when it crosses a boundary.
   int cur_seg = 0, cur_k = 0, cur_nk = (int)(args.seg[0].k / BK);
   const uint16_t *cur_a = static_cast<const uint16_t *>(args.seg[0].a);
   const uint16_t *cur_b = b0;
   int64_t cur_lda = args.seg[0].lda, cur_ldb = args.seg[0].ldb;
+  if constexpr (MSEG) {
+    int skip = k_begin;
+    while (skip >= cur_nk) {
+      skip -= cur_nk;
+      const GemmSeg *sg = &args.seg[++cur_seg];
+      cur_a = static_cast<const uint16_t *>(sg->a);
+      cur_b = static_cast<const uint16_t *>(sg->b);
+      cur_lda = sg->lda;
+      cur_ldb = sg->ldb;
+      cur_nk = (int)(sg->k / BK);
+    }
+    cur_k = skip;
+  }
 
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt) G2_INL {
     if (MSEG && cur_k == cur_nk) {
       ++cur_seg;
       const GemmSeg *sg = &args.seg[cur_seg];
@@ -245,10 +286,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       dma16(cur_a + (int64_t)a_row[i] * cur_lda + k0, st + (wave + NW * i) * 1024);
     static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const uint16_t *Bm = (DUAL && i >= B_LD / 2) ? bu : cur_b;  // dual: one segment
-      dma16(Bm + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + NW * i) * 1024);
-    }
+    for (int i = 0; i < B_LD; ++i)
+      dma16(cur_b + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + NW * i) * 1024);
     ++cur_k;
   };
 
@@ -275,43 +314,68 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // TM (TN) rows; gathered A is addressed from the matrix start, which holds
   // as long as the gathered matrix is under 4 GiB.
   const char *a_base = nullptr, *b_base = nullptr, *bu_base = nullptr;
-  uint32_t a_off[MSEG ? 1 : A_LD];
-  uint32_t b_off[MSEG ? 1 : B_LD];
+  uint32_t off[MSEG ? 1 : LMAX];
+  // uniform source base of each instruction slot (an integer: a select
+  // between captured pointers would be lowered through the stack)
+  uint64_t dbase[MSEG ? 1 : LMAX];
   if constexpr (!MSEG) {
     const int64_t a_first = GATHER ? 0 : tile.m0;
-    a_base = reinterpret_cast<const char *>(cur_a + a_first * cur_lda);
-    b_base = reinterpret_cast<const char *>(cur_b + tile.n0 * cur_ldb);
-    if constexpr (DUAL) bu_base = reinterpret_cast<const char *>(bu + tile.n0 * cur_ldb);
+    const int64_t kb0 = (int64_t)k_begin * BK;
+    a_base = reinterpret_cast<const char *>(cur_a + a_first * cur_lda + kb0);
+    b_base = reinterpret_cast<const char *>(cur_b + tile.n0 * cur_ldb + kb0);
+    if constexpr (DUAL) bu_base = reinterpret_cast<const char *>(bu + tile.n0 * cur_ldb + kb0);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      a_off[i] = (uint32_t)(((int64_t)a_row[i] - a_first) * cur_lda * 2 + fetch_chunk * 16);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      b_off[i] = (uint32_t)(((int64_t)b_row[i] - tile.n0) * cur_ldb * 2 + fetch_chunk * 16);
+    for (int d = 0; d < LMAX; ++d) {
+      const int g = wave + NW * d;
+      uint32_t o = 0;
+      uint64_t bsel = reinterpret_cast<uint64_t>(a_base);
+      if (g >= TA)
+        bsel = reinterpret_cast<uint64_t>((DUAL && g - TA >= TB / 2) ? bu_base : b_base);
+      dbase[d] = bsel;
+      if (g < TA) {
+        int64_t m = tile.m0 + g * RPI + rsub;
+        if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+        if constexpr (GATHER) m = args.gather[m] / args.gather_div;
+        o = (uint32_t)((m - a_first) * cur_lda * 2 + fetch_chunk * 16);
+      } else if (g < TT) {
+        // B rows from TN/2 on are the up rows of a dual problem
+        const int rb = (g - TA) * RPI + rsub;
+        int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
+        if (n >= args.N) n = tile.n0;
+        o = (uint32_t)((n - tile.n0) * cur_ldb * 2 + fetch_chunk * 16);
+      }
+      off[d] = o;
+    }
   }
-  // DMA instruction d (A rows first, then B rows) of K tile kt into stage st.
-  auto dma_one = [&](auto d_tag, int kt, int st) {
+  // DMA instruction slot d of this wave (instruction g = wave + NW d) of K
+  // tile kt into stage st.
+  auto dma_one = [&](auto d_tag, int kt, int st) G2_INL {
     constexpr int d = decltype(d_tag)::value;
-    char *dst = smem + st * STAGE_BYTES;
-    const int64_t kb = (int64_t)kt * RB;
+    if constexpr (!EVEN && d == LMAX - 1) {
+      if (!has_last) return;
+    }
+    const int g = wave + NW * d;
+    const char *base = reinterpret_cast<const char *>(dbase[d]);
     // the empty asm re-issues the 32-bit offset inside the loop body, so the
     // instruction selector sees uniform base + zext(offset) there (SGPR-base
     // form) instead of a 64-bit address hoisted out of the loop
-    if constexpr (d < A_LD) {
-      uint32_t off = a_off[d];
-      asm volatile("" : "+v"(off));
-      dma16(a_base + kb + off, dst + (wave + NW * d) * 1024);
+    uint32_t o = off[d];
+    asm volatile("" : "+v"(o));
+    dma16(base + (int64_t)kt * RB + o, smem + st * STAGE_BYTES + g * 1024);
+  };
+  // "tile kt landed": this wave's loads of later tiles may still be in flight
+  auto wait_tile = [&]() G2_INL {
+    if constexpr (EVEN) {
+      wait_vmcnt<LMAX * (STAGES - 2)>();
     } else {
-      constexpr int i = d - A_LD;
-      const char *base = (DUAL && i >= B_LD / 2) ? bu_base : b_base;
-      uint32_t off = b_off[i];
-      asm volatile("" : "+v"(off));
-      dma16(base + kb + off, dst + A_BYTES + (wave + NW * i) * 1024);
+      if (has_last) wait_vmcnt<LMAX * (STAGES - 2)>();
+      else wait_vmcnt<(LMAX - 1) * (STAGES - 2)>();
     }
   };
 
   // Operand fragment f of k step ks (f < FRN: B fragment f, else A fragment f - FRN).
-  auto read_frag = [&](const char *st, int ks, auto f_tag, bf16x8 *af, bf16x8 *bfr) {
+  auto read_frag = [&](const char *st, int ks, auto f_tag, bf16x8 *af,
+                       bf16x8 *bfr) G2_INL {
     constexpr int f = decltype(f_tag)::value;
     const int chunk = ks * 2 + (lane >> 5);
     int r;
@@ -335,9 +399,9 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // reads of the next k step and the DMA instructions of the tile STAGES - 1
   // ahead placed between them, so the in-order issue hides them behind the
   // MFMA pipe.  The prefetch is unconditional (past the end it re-reads the
-  // last tile into a stage nobody reads again), so every thread has exactly
-  // L loads per tile in flight and the wait count is a constant.
-  auto mainloop = [&](auto ns_tag) {
+  // last tile into a stage nobody reads again), so every wave has a fixed
+  // number of loads per tile in flight and the wait count is a constant.
+  auto mainloop = [&](auto ns_tag) G2_INL {
     constexpr int NS = decltype(ns_tag)::value;
     constexpr int NA = NS > 0 ? NS : 1;
     constexpr int KS = BK / 16;   // k steps per stage
@@ -347,23 +411,23 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
 #pragma unroll
       for (int p = 0; p < STAGES - 1; ++p) {
         const int kp = p < ktiles ? p : ktiles - 1;
-        static_for<L>([&](auto d) { dma_one(d, kp, p); });
+        static_for<L>([&](auto d) G2_INL { dma_one(d, kp, p); });
       }
       for (int kt = 0; kt < ktiles; ++kt) {
-        wait_vmcnt<L * (STAGES - 2)>();
+        wait_tile();
         barrier();
         const char *st = smem + (kt % STAGES) * STAGE_BYTES;
         const int kd = kt + STAGES - 1;
         const int kdc = kd < ktiles ? kd : ktiles - 1;
         const int dst = kd % STAGES;
         if constexpr (NS == 0) {
-          static_for<L>([&](auto d) { dma_one(d, kdc, dst); });
+          static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst); });
         } else {
           bf16x8 fa[2][NA], fb[2][FRN];
-          static_for<NF>([&](auto f) { read_frag(st, 0, f, fa[0], fb[0]); });
-          static_for<KS>([&](auto s_tag) {
+          static_for<NF>([&](auto f) G2_INL { read_frag(st, 0, f, fa[0], fb[0]); });
+          static_for<KS>([&](auto s_tag) G2_INL {
             constexpr int S = decltype(s_tag)::value;
-            static_for<Q>([&](auto q_tag) {
+            static_for<Q>([&](auto q_tag) G2_INL {
               constexpr int q = decltype(q_tag)::value;
               constexpr int i = q / FRN, j = q % FRN;
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[S & 1][i], fb[S & 1][j],
@@ -371,7 +435,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
               // next step's fragments from the first MFMAs on (one per MFMA when
               // they fit), so they have landed when the step starts
               if constexpr (S + 1 < KS) {
-                static_for<NF>([&](auto f_tag) {
+                static_for<NF>([&](auto f_tag) G2_INL {
                   constexpr int f = decltype(f_tag)::value;
                   constexpr bool mine = NF <= Q ? (f == q) : (f >= q * NF / Q && f < (q + 1) * NF / Q);
                   if constexpr (mine)
@@ -384,7 +448,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
               constexpr int DS = STAGES == 2 ? 1 : KS;  // k steps that carry DMAs
               if constexpr (S < DS) {
                 constexpr int g = S * Q + q;
-                static_for<L>([&](auto d_tag) {
+                static_for<L>([&](auto d_tag) G2_INL {
                   constexpr int d = decltype(d_tag)::value;
                   if constexpr (d >= g * L / (DS * Q) && d < (g + 1) * L / (DS * Q))
                     dma_one(d_tag, kdc, dst);
@@ -413,7 +477,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           bf16x8 fa[NA], fb[FRN];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            static_for<NF>([&](auto f) { read_frag(st, ks, f, fa, fb); });
+            static_for<NF>([&](auto f) G2_INL { read_frag(st, ks, f, fa, fb); });
 #pragma unroll
             for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -439,6 +503,28 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // ---- epilogue: lane holds column (lane & 31), rows 8(r/4) + 4(lane/32) + r%4
   // of each 32 x 32 block.  Row quantities are formed once per row, column
   // ones once per block column; the SiTU row factors come from LDS.
+  if (args.ksplit > 1) {
+    // split K: raw sums of this K range; the reduction applies the epilogue
+    float *part = args.partial + (int64_t)blockIdx.y * args.M * args.ldp;
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i) {
+      if (i >= sub_valid) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row =
+            tile.m0 + (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= tile.m_end) continue;
+#pragma unroll
+        for (int j = 0; j < FRN; ++j) {
+          constexpr int JH = DUAL ? FRN / 2 : FRN;
+          const int jo = j % JH;
+          const int64_t col = tile.n0 + (wn * JH + jo) * 32 + (lane & 31);
+          if (col < args.N) part[row * args.ldp + col + (j >= JH ? args.N : 0)] = acc[i][j][r];
+        }
+      }
+    }
+    return;
+  }
   if constexpr (EPI == EPI_SITU) {
     if (use_rs) {
       wait_vmcnt<0>();
@@ -507,6 +593,47 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
             }
           }
         }
+    }
+  }
+}
+
+// Split-K reduction: out[m][c] = epilogue(sum over splits, in split order),
+// four output columns per thread.
+template <int EPI, bool DUAL, typename OutT>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a) {
+  const int64_t nq = (a.N + 3) / 4;
+  const int64_t total = a.M * nq;
+  const int64_t plane = a.M * a.ldp;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int64_t row = idx / nq;
+    const int64_t c0 = (idx - row * nq) * 4;
+    float g[4] = {0.0f, 0.0f, 0.0f, 0.0f}, u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < a.ksplit; ++sp) {
+      const float *p = a.partial + sp * plane + row * a.ldp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (c0 + q < a.N) {
+          g[q] += p[c0 + q];
+          if (DUAL) u[q] += p[a.N + c0 + q];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = c0 + q;
+      if (col >= a.N) continue;
+      if constexpr (EPI == EPI_ROUTER) {
+        const float z = g[q] + (a.bias ? a.bias[col] : 0.0f);
+        static_cast<float *>(a.out)[row * a.ldo + col] = z;
+        if (a.out_t) a.out_t[col * a.M + row] = z;
+      } else if constexpr (EPI == EPI_SITU) {
+        const float f = a.row_scale ? a.row_scale[row] : 1.0f;
+        store_out<OutT>(a.out, row * a.ldo + col,
+                        f * situ(g[q], u[q], a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
+      } else {
+        store_out<OutT>(a.out, row * a.ldo + col, g[q]);
+      }
     }
   }
 }

@@ -22,7 +22,9 @@ enum GemmKind {
 int gemm_bm(int path);
 // Rows per M tile of the grouped expert GEMMs (the dispatch lays out the
 // per-expert tile list with it).
-int grouped_tile_rows(int path, bool fp8);
+// M-tile rows of the grouped GEMMs for rows (token, expert) pairs over
+// n_experts experts (the dispatch lays its tile table out in these units).
+int grouped_tile_rows(int path, bool fp8, int64_t rows, int64_t n_experts);
 int gemm_bn_out(int path, bool dual);
 hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int64_t m_tiles,
                        hipStream_t s);
