@@ -81,7 +81,8 @@ typedef struct moe_config {
   int32_t cutoff_mode;  /* moe_cutoff_mode */
 } moe_config;
 /* Shape limits: bf16/fp8 paths need d, latent, expert_inter, shared_inter
- * multiples of 64 (of 128 with fp8 weights); bt * top_k below 2^31; with bf16
+ * multiples of 64 (of 128 with fp8 weights); latent at most 4096 (2048 with
+ * fp32 activations); bt * top_k below 2^31; with bf16
  * activations the latent activations bt * latent * 2 bytes stay below 4 GiB
  * (bt < 599186 at latent 3584).  Else MOE_ERR_UNSUPPORTED. */
 
@@ -93,7 +94,7 @@ typedef struct moe_weights {
   const void *w_gate;        /* [E][I][L] */
   const void *w_up;          /* [E][I][L] */
   const void *w_down;        /* [E][L][I] */
-  const float *latent_gamma; /* [L] RMSNorm gain */
+  const float *latent_gamma; /* [L] RMSNorm gain, 16-byte aligned */
   const void *w_up_proj;     /* [d][L] */
   const void *sh_gate;       /* [S][I_s][d] */
   const void *sh_up;         /* [S][I_s][d] */

@@ -76,7 +76,8 @@ moe_status check_config(const moe_config *c) {
   if (c->d % 64 || c->latent % q || c->expert_inter % q || (c->n_shared && c->shared_inter % q))
     return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
-  if (c->latent > 4096) return MOE_ERR_UNSUPPORTED;  // combine stages a latent row per wave in LDS
+  // the combine holds a latent row per wavefront in registers (8 chunks of 16 B a lane)
+  if (c->latent > (c->act_dtype == MOE_F32 ? 2048 : 4096)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -146,6 +147,7 @@ bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts)
       !w->w_up_proj)
     return false;
   if (c->n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return false;
+  if (reinterpret_cast<uintptr_t>(w->latent_gamma) % 16) return false;  // read as float4
   if (c->weight_dtype == MOE_FP8E4M3_B128) {
     if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
     if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;

@@ -8,91 +8,136 @@
 // per-token step f ("RMSNorm + W↑").
 //
 // One wavefront per token: y_lat = sum_j o[inv_perm[t*k + j]] with j
-// ascending (the rows of o already carry their routing weight), staged in LDS
-// as fp32, then n = y_lat / sqrt(mean(y_lat^2) + eps) * gamma.
+// ascending (the rows of o already carry their routing weight), held in
+// registers as fp32 (NCH 16-byte chunks per lane), then
+// n = y_lat / sqrt(mean(y_lat^2) + eps) * gamma.  The k rows of a token are
+// read eight at a time, so each lane has up to 8 NCH loads in flight; the
+// pass is bound by reading o once.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <bool BF16>
+template <bool BF16, int NCH>
 __global__ void __launch_bounds__(256) combine_norm_kernel(const void *__restrict__ o_,
                                                            const int32_t *__restrict__ inv_perm,
                                                            int64_t bt, int k, int L,
                                                            const float *__restrict__ gamma,
                                                            float eps, void *__restrict__ n_) {
-  extern __shared__ float ys_all[];  // [4][L]
+  constexpr int V = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= bt) return;
-  float *ys = ys_all + wave * L;
-  constexpr int V = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int nch = L / V;
   const int32_t *ip = inv_perm + t * k;
-  float ss = 0.0f;
-  for (int c = lane; c < nch; c += 64) {
-    float acc[V];
+  float acc[NCH][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t pos = ip[j];
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[c][i] = 0.0f;
+
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int64_t pos[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pos[u] = j0 + u < k ? (int64_t)ip[j0 + u] : -1;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch >= nch) continue;
       if constexpr (BF16) {
-        const uint4 v = reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(o_) + pos * L)[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint4 v[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += bf16_to_f32((uint16_t)(w[q] & 0xFFFFu));
-          acc[2 * q + 1] += bf16_to_f32((uint16_t)(w[q] >> 16));
+        for (int u = 0; u < 8; ++u)
+          if (pos[u] >= 0)
+            v[u] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(o_) +
+                                                    pos[u] * L)[ch];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (pos[u] < 0) continue;
+          const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[c][2 * q] += bf16_to_f32((uint16_t)(w[q] & 0xFFFFu));
+            acc[c][2 * q + 1] += bf16_to_f32((uint16_t)(w[q] >> 16));
+          }
         }
       } else {
-        const float4 v =
-            reinterpret_cast<const float4 *>(static_cast<const float *>(o_) + pos * L)[c];
-        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (pos[u] >= 0)
+            v[u] = reinterpret_cast<const float4 *>(static_cast<const float *>(o_) + pos[u] * L)[ch];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (pos[u] < 0) continue;
+          acc[c][0] += v[u].x;
+          acc[c][1] += v[u].y;
+          acc[c][2] += v[u].z;
+          acc[c][3] += v[u].w;
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      ys[c * V + i] = acc[i];
-      ss += acc[i] * acc[i];
-    }
   }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss += acc[c][i] * acc[c][i];  // unused chunks hold 0
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   const float inv = 1.0f / sqrtf(ss / (float)L + eps);
-  for (int c = lane; c < nch; c += 64) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch >= nch) continue;
+    const float4 *g4 = reinterpret_cast<const float4 *>(gamma) + ch * (V / 4);
     if constexpr (BF16) {
+      const float4 ga = g4[0], gb = g4[1];
+      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
       uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int l = c * V + 2 * q;
-        w[q] = pack_bf16x2(ys[l] * inv * gamma[l], ys[l + 1] * inv * gamma[l + 1]);
-      }
-      reinterpret_cast<uint4 *>(static_cast<uint16_t *>(n_) + t * L)[c] =
+      for (int q = 0; q < 4; ++q)
+        w[q] = pack_bf16x2(acc[c][2 * q] * inv * g[2 * q], acc[c][2 * q + 1] * inv * g[2 * q + 1]);
+      reinterpret_cast<uint4 *>(static_cast<uint16_t *>(n_) + t * L)[ch] =
           make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      float4 v;
-      const int l = c * V;
-      v.x = ys[l] * inv * gamma[l];
-      v.y = ys[l + 1] * inv * gamma[l + 1];
-      v.z = ys[l + 2] * inv * gamma[l + 2];
-      v.w = ys[l + 3] * inv * gamma[l + 3];
-      reinterpret_cast<float4 *>(static_cast<float *>(n_) + t * L)[c] = v;
+      const float4 g = g4[0];
+      reinterpret_cast<float4 *>(static_cast<float *>(n_) + t * L)[ch] =
+          make_float4(acc[c][0] * inv * g.x, acc[c][1] * inv * g.y, acc[c][2] * inv * g.z,
+                      acc[c][3] * inv * g.w);
     }
   }
+}
+
+template <bool BF16>
+static hipError_t launch_cn(const void *o, const int32_t *inv_perm, int64_t bt, int64_t k,
+                            int64_t L, const float *gamma, float eps, void *n, hipStream_t s) {
+  constexpr int V = BF16 ? 8 : 4;
+  const int64_t per_lane = (L / V + 63) / 64;
+  const dim3 grid((unsigned)((bt + 3) / 4)), block(256);
+  if (per_lane <= 1)
+    return launch_kernel(combine_norm_kernel<BF16, 1>, grid, block, 0, s, o, inv_perm, bt, (int)k,
+                         (int)L, gamma, eps, n);
+  if (per_lane <= 2)
+    return launch_kernel(combine_norm_kernel<BF16, 2>, grid, block, 0, s, o, inv_perm, bt, (int)k,
+                         (int)L, gamma, eps, n);
+  if (per_lane <= 4)
+    return launch_kernel(combine_norm_kernel<BF16, 4>, grid, block, 0, s, o, inv_perm, bt, (int)k,
+                         (int)L, gamma, eps, n);
+  if (per_lane <= 8)
+    return launch_kernel(combine_norm_kernel<BF16, 8>, grid, block, 0, s, o, inv_perm, bt, (int)k,
+                         (int)L, gamma, eps, n);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine_norm(const void *o, bool bf16, const int32_t *inv_perm, int64_t bt,
                                int64_t k, int64_t L, const float *gamma, float eps, void *n,
                                hipStream_t s) {
   if (bt <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((bt + 3) / 4)), block(256);
-  const size_t lds = sizeof(float) * 4 * (size_t)L;
-  if (bf16)
-    return launch_kernel(combine_norm_kernel<true>, grid, block, lds, s, o, inv_perm, bt, (int)k,
-                         (int)L, gamma, eps, n);
-  return launch_kernel(combine_norm_kernel<false>, grid, block, lds, s, o, inv_perm, bt, (int)k,
-                       (int)L, gamma, eps, n);
+  // rows are read as 16-byte chunks: L a multiple of 8 (bf16) or 4 (fp32), at most
+  // 8 chunks per lane
+  if (bf16) return launch_cn<true>(o, inv_perm, bt, k, L, gamma, eps, n, s);
+  return launch_cn<false>(o, inv_perm, bt, k, L, gamma, eps, n, s);
 }
 
 }  // namespace moe

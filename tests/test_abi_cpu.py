@@ -96,6 +96,13 @@ def test_dtype_combinations():
     assert moe.workspace_bytes(bad, 64) == 0
     fp8_odd = moe.make_config(2048, 576, 64, 8, 512, 2, 1024, act="bf16", weight="fp8")
     assert moe.workspace_bytes(fp8_odd, 64) == 0  # fp8 needs multiples of 128
+    # the combine keeps a latent row per wavefront in registers
+    assert moe.workspace_bytes(moe.make_config(2048, 4096, 64, 8, 512, 2, 1024), 64) > 0
+    assert moe.workspace_bytes(moe.make_config(2048, 4160, 64, 8, 512, 2, 1024), 64) == 0
+    assert moe.workspace_bytes(moe.make_config(256, 2048, 16, 2, 64, 1, 128, act="f32",
+                                               weight="f32"), 64) > 0
+    assert moe.workspace_bytes(moe.make_config(256, 2112, 16, 2, 64, 1, 128, act="f32",
+                                               weight="f32"), 64) == 0
 
 
 def test_argument_errors_before_any_launch():
