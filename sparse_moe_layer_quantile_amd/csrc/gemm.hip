@@ -117,8 +117,7 @@ static hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   hipError_t e = launch_kernel(kern, dim3((unsigned)blocks, (unsigned)a.ksplit),
                                dim3(sh.threads()), lds, s, a);
   if (e != hipSuccess || a.ksplit <= 1) return e;
-  const int64_t quads = a.M * ((a.N + 3) / 4);
-  const unsigned rblocks = (unsigned)std::min<int64_t>((quads + 255) / 256, 4096);
+  const unsigned rblocks = (unsigned)std::min<int64_t>((a.M * a.N + 255) / 256, 8192);
   return launch_kernel(g2::splitk_reduce_kernel<EPI, DUAL, OutT>, dim3(rblocks), dim3(256), 0, s,
                        a);
 }

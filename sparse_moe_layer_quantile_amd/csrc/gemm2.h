@@ -598,42 +598,44 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
 }
 
 // Split-K reduction: out[m][c] = epilogue(sum over splits, in split order),
-// four output columns per thread.
+// one output element per thread; eight partial sums are loaded ahead of
+// their (ordered) additions so each thread keeps several loads in flight.
 template <int EPI, bool DUAL, typename OutT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a) {
-  const int64_t nq = (a.N + 3) / 4;
-  const int64_t total = a.M * nq;
+  const int64_t total = a.M * a.N;
   const int64_t plane = a.M * a.ldp;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
-    const int64_t row = idx / nq;
-    const int64_t c0 = (idx - row * nq) * 4;
-    float g[4] = {0.0f, 0.0f, 0.0f, 0.0f}, u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp = 0; sp < a.ksplit; ++sp) {
-      const float *p = a.partial + sp * plane + row * a.ldp;
+    const int64_t row = idx / a.N;
+    const int64_t col = idx - row * a.N;
+    const float *p = a.partial + row * a.ldp + col;
+    float g = 0.0f, u = 0.0f;
+    for (int s0 = 0; s0 < a.ksplit; s0 += 8) {
+      float vg[8], vu[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (c0 + q < a.N) {
-          g[q] += p[c0 + q];
-          if (DUAL) u[q] += p[a.N + c0 + q];
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = s0 + q < a.ksplit;
+        vg[q] = ok ? p[(s0 + q) * plane] : 0.0f;
+        vu[q] = (DUAL && ok) ? p[(s0 + q) * plane + a.N] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (s0 + q < a.ksplit) {
+          g += vg[q];
+          if (DUAL) u += vu[q];
         }
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t col = c0 + q;
-      if (col >= a.N) continue;
-      if constexpr (EPI == EPI_ROUTER) {
-        const float z = g[q] + (a.bias ? a.bias[col] : 0.0f);
-        static_cast<float *>(a.out)[row * a.ldo + col] = z;
-        if (a.out_t) a.out_t[col * a.M + row] = z;
-      } else if constexpr (EPI == EPI_SITU) {
-        const float f = a.row_scale ? a.row_scale[row] : 1.0f;
-        store_out<OutT>(a.out, row * a.ldo + col,
-                        f * situ(g[q], u[q], a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
-      } else {
-        store_out<OutT>(a.out, row * a.ldo + col, g[q]);
-      }
+    if constexpr (EPI == EPI_ROUTER) {
+      const float z = g + (a.bias ? a.bias[col] : 0.0f);
+      static_cast<float *>(a.out)[row * a.ldo + col] = z;
+      if (a.out_t) a.out_t[col * a.M + row] = z;
+    } else if constexpr (EPI == EPI_SITU) {
+      const float f = a.row_scale ? a.row_scale[row] : 1.0f;
+      store_out<OutT>(a.out, row * a.ldo + col,
+                      f * situ(g, u, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
+    } else {
+      store_out<OutT>(a.out, row * a.ldo + col, g);
     }
   }
 }
