@@ -82,7 +82,8 @@ typedef struct moe_config {
 } moe_config;
 /* Shape limits: bf16/fp8 paths need d, latent, expert_inter, shared_inter
  * multiples of 64 (of 128 with fp8 weights); latent at most 4096 (2048 with
- * fp32 activations); bt * top_k below 2^31; with bf16
+ * fp32 activations); with fp8 weights d, latent, expert_inter and
+ * shared_inter at most 16384; bt * top_k below 2^31; with bf16
  * activations the latent activations bt * latent * 2 bytes stay below 4 GiB
  * (bt < 599186 at latent 3584).  Else MOE_ERR_UNSUPPORTED. */
 

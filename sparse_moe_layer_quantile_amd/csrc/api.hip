@@ -76,6 +76,10 @@ moe_status check_config(const moe_config *c) {
   if (c->d % 64 || c->latent % q || c->expert_inter % q || (c->n_shared && c->shared_inter % q))
     return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
+  // fp8 GEMMs stage the block scales of up to 128 K blocks in LDS
+  if (c->weight_dtype == MOE_FP8E4M3_B128 &&
+      std::max({c->d, c->latent, c->expert_inter, c->shared_inter}) > 16384)
+    return MOE_ERR_UNSUPPORTED;
   // the combine holds a latent row per wavefront in registers (8 chunks of 16 B a lane)
   if (c->latent > (c->act_dtype == MOE_F32 ? 2048 : 4096)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -118,7 +122,7 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->hs = take(p->act_bytes * bt * c->n_shared * c->shared_inter);
   // split-K partial sums of the dense bf16 GEMMs of short batches (up to 16
   // splits of the widest output), one region per stream
-  if (p->path == PATH_BF16 && !p->fp8 && bt > 0 && bt <= kSplitMaxRows) {
+  if (p->path == PATH_BF16 && bt > 0 && bt <= kSplitMaxRows) {
     const int64_t cols = std::max({E, L, c->d, 2 * c->n_shared * c->shared_inter});
     p->split_cap = 16 * bt * cols;
   }

@@ -49,6 +49,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+}
+
 __device__ __forceinline__ void barrier() {
   // s_barrier without the memory fence of __syncthreads (which would wait for
   // every outstanding load, in-flight prefetches included); the asm memory
@@ -70,6 +75,18 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(g),
                                    (__attribute__((address_space(3))) void *)(lds_wave_base),
                                    16, 0, 0);
+}
+
+// Eight fp8 e4m3 codes (lo: codes 0-3, hi: codes 4-7, byte order) times a
+// block scale, rounded to bf16: the B operand of one bf16 MFMA.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float s) {
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  bf16x8 r;
+  r[0] = (__bf16)(a.x * s); r[1] = (__bf16)(a.y * s); r[2] = (__bf16)(b.x * s); r[3] = (__bf16)(b.y * s);
+  r[4] = (__bf16)(c.x * s); r[5] = (__bf16)(c.y * s); r[6] = (__bf16)(d.x * s); r[7] = (__bf16)(d.y * s);
+  return r;
 }
 
 // One dword per lane: lane l's 4 bytes land at lds_wave_base + 4 l.
@@ -138,34 +155,44 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
   return t;
 }
 
+// fp8 B operands: block scales of up to this many 128-wide K blocks (K <= 16384)
+constexpr int kMaxKBlocks = 128;
+
 // Extra LDS of a kernel instance past its stage ring: the per-row factors of a
-// SiTU epilogue.
-template <int EPI, int TM>
-constexpr int epilogue_lds_bytes() {
-  return EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0;
+// SiTU epilogue, and the block scales of an fp8 B tile ([TN/128][kMaxKBlocks]).
+template <int EPI, int TM, int TN, bool B8>
+constexpr int extra_lds_bytes() {
+  return (EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0) + (B8 ? TN / 128 * kMaxKBlocks * 4 : 0);
 }
 
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
-          bool GATHER, bool MSEG, typename OutT>
+          bool GATHER, bool MSEG, bool B8, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
-  constexpr int RB = BK * 2;          // bytes per tile row
-  constexpr int CPR = RB / 16;        // 16 B chunks per row
-  constexpr int RPI = 1024 / RB;      // rows per DMA wave instruction
+  constexpr int RB = BK * 2;          // bytes per A tile row
+  constexpr int CPR = RB / 16;        // 16 B chunks per A row
+  constexpr int RPI = 1024 / RB;      // A rows per DMA wave instruction
+  // B is bf16, or fp8 e4m3 with 128 x 128 block scales (B8)
+  constexpr int ESZ_B = B8 ? 1 : 2;   // bytes per B element
+  constexpr int RB_B = BK * ESZ_B;    // bytes per B tile row
+  constexpr int CPR_B = RB_B / 16;
+  constexpr int RPI_B = 1024 / RB_B;
   constexpr int TM = WM * SUBM * 32, TN = WN * FRN * 32;
   constexpr int TN_OUT = DUAL ? TN / 2 : TN;
-  constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB;
+  constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB_B;
+  static_assert(!B8 || (BK == 64 && TN_OUT % 128 == 0),
+                "fp8 B: K tile 64, whole 128-row scale blocks");
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   // A stage is TA + TB wave instructions of 1 KB each (A rows, then B rows,
   // in LDS order).  Instruction g is issued by wave g % NW as its (g / NW)-th,
   // so a wave issues LMAX or LMAX - 1 of them per stage.
-  constexpr int TA = TM / RPI, TB = TN / RPI, TT = TA + TB;
+  constexpr int TA = TM / RPI, TB = TN / RPI_B, TT = TA + TB;
   constexpr int LMAX = (TT + NW - 1) / NW;
   constexpr bool EVEN = TT % NW == 0;
-  static_assert(TM % RPI == 0 && TN % RPI == 0 && (TM / RPI) % 4 == 0, "whole DMA rows");
-  static_assert(!DUAL || (TN / 2) % RPI == 0, "gate/up split on a DMA instruction");
+  static_assert(TM % RPI == 0 && TN % RPI_B == 0 && (TM / RPI) % 4 == 0, "whole DMA rows");
+  static_assert(!DUAL || (TN / 2) % RPI_B == 0, "gate/up split on a DMA instruction");
   // multi-segment problems keep whole A and B rounds per wave
   constexpr int A_LD = TA / NW, B_LD = TB / NW;
   static_assert(!MSEG || (TA % NW == 0 && TB % NW == 0), "segmented: whole DMA rounds");
@@ -197,6 +224,46 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
   }
 
+  // ---- fp8 B: block scales of this tile's B rows over the whole K range ------
+  // sc_lds[b][kb], b = 128-row block of the tile (dual: gate blocks, then up
+  // blocks), kb = 128-wide K block; loaded like the row factors
+  constexpr int NBL = TN / 128;
+  float *sc_lds = rs_lds + (EPI == EPI_SITU ? (TM + 63) / 64 * 64 : 0);
+  int kblocks = B8 ? (int)(args.seg[0].k / 128) : 0;
+  if constexpr (B8 && MSEG) {
+    // segments one after another along K: [NBL][sum of the segments' K blocks]
+    // (plain loads into LDS, made visible by the first barrier)
+#pragma unroll
+    for (int sgi = 1; sgi < 5; ++sgi)
+      if (sgi < args.nseg) kblocks += (int)(args.seg[sgi].k / 128);
+    int kb0 = 0;
+    for (int sgi = 0; sgi < args.nseg; ++sgi) {
+      const int kbs = (int)(args.seg[sgi].k / 128);
+      const float *bs = args.seg[sgi].bscale;
+      for (int i = tid; i < NBL * kbs; i += 64 * NW) {
+        const int b = i / kbs, kbl = i - b * kbs;
+        int64_t nb = tile.n0 / 128 + b;
+        if (nb >= (args.N + 127) / 128) nb = (args.N + 127) / 128 - 1;  // never stored
+        sc_lds[b * kblocks + kb0 + kbl] = bs[nb * kbs + kbl];
+      }
+      kb0 += kbs;
+    }
+    wait_lgkm0();
+  } else if constexpr (B8) {
+    const int64_t nblocks = (args.N + 127) / 128;
+    for (int q = wave; q * 64 < NBL * kblocks; q += NW) {
+      const int i0 = q * 64 + lane;
+      const int idx = i0 < NBL * kblocks ? i0 : 0;  // past the table: loaded, never used
+      const int b = idx / kblocks, kb = idx - b * kblocks;
+      const bool up = DUAL && b >= NBL / 2;
+      int64_t nb = tile.n0 / 128 + (DUAL ? b % (NBL / 2) : b);
+      if (nb >= nblocks) nb = nblocks - 1;  // rows past N: never stored
+      const float *sp = (up ? args.bscale_up : args.seg[0].bscale) +
+                        (int64_t)tile.e * args.s_estride + nb * kblocks + kb;
+      dma4(sp, sc_lds + q * 64);
+    }
+  }
+
   // the last instruction slot of this wave carries an instruction
   const bool has_last = EVEN || wave + NW * (LMAX - 1) < TT;
 
@@ -214,12 +281,14 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const int r = (wave + NW * i) * RPI + rsub;
+      const int r = (wave + NW * i) * RPI_B + lane / CPR_B;
       int64_t n = tile.n0 + r;
       if (n >= args.N) n = tile.n0;
       b_row[i] = (int32_t)n;
     }
   }
+  // B chunk of a segmented problem's lanes (same argument as for A)
+  const int fetch_chunk_b = (lane % CPR_B) ^ ((((wave * RPI_B) + lane / CPR_B) / (16 / CPR_B)) % CPR_B);
   const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
   const uint16_t *bu = static_cast<const uint16_t *>(args.b_up);
   if (args.offsets != nullptr) {
@@ -252,7 +321,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // the kernel arguments (scalar loads) only when it crosses a boundary.
   int cur_seg = 0, cur_k = 0, cur_nk = (int)(args.seg[0].k / BK);
   const uint16_t *cur_a = static_cast<const uint16_t *>(args.seg[0].a);
-  const uint16_t *cur_b = b0;
+  const char *cur_b = reinterpret_cast<const char *>(b0);
   int64_t cur_lda = args.seg[0].lda, cur_ldb = args.seg[0].ldb;
   if constexpr (MSEG) {
     int skip = k_begin;
@@ -260,7 +329,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       skip -= cur_nk;
       const GemmSeg *sg = &args.seg[++cur_seg];
       cur_a = static_cast<const uint16_t *>(sg->a);
-      cur_b = static_cast<const uint16_t *>(sg->b);
+      cur_b = static_cast<const char *>(sg->b);
       cur_lda = sg->lda;
       cur_ldb = sg->ldb;
       cur_nk = (int)(sg->k / BK);
@@ -273,7 +342,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       ++cur_seg;
       const GemmSeg *sg = &args.seg[cur_seg];
       cur_a = static_cast<const uint16_t *>(sg->a);
-      cur_b = static_cast<const uint16_t *>(sg->b);
+      cur_b = static_cast<const char *>(sg->b);
       cur_lda = sg->lda;
       cur_ldb = sg->ldb;
       cur_nk = (int)(sg->k / BK);
@@ -287,7 +356,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
-      dma16(cur_b + (int64_t)b_row[i] * cur_ldb + k0, st + A_BYTES + (wave + NW * i) * 1024);
+      dma16(cur_b + ((int64_t)b_row[i] * cur_ldb + (int64_t)cur_k * BK) * ESZ_B + fetch_chunk_b * 16,
+            st + A_BYTES + (wave + NW * i) * 1024);
     ++cur_k;
   };
 
@@ -322,8 +392,14 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     const int64_t a_first = GATHER ? 0 : tile.m0;
     const int64_t kb0 = (int64_t)k_begin * BK;
     a_base = reinterpret_cast<const char *>(cur_a + a_first * cur_lda + kb0);
-    b_base = reinterpret_cast<const char *>(cur_b + tile.n0 * cur_ldb + kb0);
-    if constexpr (DUAL) bu_base = reinterpret_cast<const char *>(bu + tile.n0 * cur_ldb + kb0);
+    const char *bsrc = static_cast<const char *>(args.seg[0].b);
+    const char *busrc = static_cast<const char *>(args.b_up);
+    if (args.offsets != nullptr) {
+      bsrc += (int64_t)tile.e * args.b_estride * ESZ_B;
+      if (DUAL) busrc += (int64_t)tile.e * args.b_estride * ESZ_B;
+    }
+    b_base = bsrc + (tile.n0 * cur_ldb + kb0) * ESZ_B;
+    if constexpr (DUAL) bu_base = busrc + (tile.n0 * cur_ldb + kb0) * ESZ_B;
 #pragma unroll
     for (int d = 0; d < LMAX; ++d) {
       const int g = wave + NW * d;
@@ -332,17 +408,22 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       if (g >= TA)
         bsel = reinterpret_cast<uint64_t>((DUAL && g - TA >= TB / 2) ? bu_base : b_base);
       dbase[d] = bsel;
+      // lane l of an instruction fills 16 B slot l % CPR of tile row l / CPR
+      // and fetches the chunk that the swizzle puts there
       if (g < TA) {
-        int64_t m = tile.m0 + g * RPI + rsub;
+        const int r = g * RPI + lane / CPR;
+        const int ch = (lane % CPR) ^ ((r / (16 / CPR)) % CPR);
+        int64_t m = tile.m0 + r;
         if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
         if constexpr (GATHER) m = args.gather[m] / args.gather_div;
-        o = (uint32_t)((m - a_first) * cur_lda * 2 + fetch_chunk * 16);
+        o = (uint32_t)((m - a_first) * cur_lda * 2 + ch * 16);
       } else if (g < TT) {
         // B rows from TN/2 on are the up rows of a dual problem
-        const int rb = (g - TA) * RPI + rsub;
+        const int rb = (g - TA) * RPI_B + lane / CPR_B;
+        const int ch = (lane % CPR_B) ^ ((rb / (16 / CPR_B)) % CPR_B);
         int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
         if (n >= args.N) n = tile.n0;
-        o = (uint32_t)((n - tile.n0) * cur_ldb * 2 + fetch_chunk * 16);
+        o = (uint32_t)((n - tile.n0) * cur_ldb * ESZ_B + ch * 16);
       }
       off[d] = o;
     }
@@ -361,7 +442,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     // form) instead of a 64-bit address hoisted out of the loop
     uint32_t o = off[d];
     asm volatile("" : "+v"(o));
-    dma16(base + (int64_t)kt * RB + o, smem + st * STAGE_BYTES + g * 1024);
+    const int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
+    dma16(base + kb + o, smem + st * STAGE_BYTES + g * 1024);
   };
   // "tile kt landed": this wave's loads of later tiles may still be in flight
   auto wait_tile = [&]() G2_INL {
@@ -377,7 +459,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   auto read_frag = [&](const char *st, int ks, auto f_tag, bf16x8 *af,
                        bf16x8 *bfr) G2_INL {
     constexpr int f = decltype(f_tag)::value;
-    const int chunk = ks * 2 + (lane >> 5);
+    // k order of a step: lane half h takes k 8h..8h+8 of the step's 16; with
+    // fp8 B, steps 2p and 2p+1 take the two halves of chunk 2p + h instead
+    // (one 16-byte B read per lane per two steps; A follows the same order)
+    const int chunk = B8 ? 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1) : ks * 2 + (lane >> 5);
     int r;
     const char *base;
     if constexpr (f < FRN) {
@@ -393,6 +478,28 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ ((r / (16 / CPR)) % CPR)) << 4));
     if constexpr (f < FRN) bfr[f] = v;
     else af[f - FRN] = v;
+  };
+  // fp8 B: tile row of B fragment j for this lane (dual: gate fragments, then up)
+  auto b_row_of = [&](auto j_tag) G2_INL {
+    constexpr int j = decltype(j_tag)::value;
+    if constexpr (DUAL)
+      return j < FRN / 2 ? (wn * (FRN / 2) + j) * 32 + (lane & 31)
+                         : TN / 2 + (wn * (FRN / 2) + j - FRN / 2) * 32 + (lane & 31);
+    else
+      return (wn * FRN + j) * 32 + (lane & 31);
+  };
+  // fp8 B: the 16 codes of fragment j for the k-step pair p (chunk 2p + h)
+  auto read_b8 = [&](const char *st, int p, auto j_tag, uint4 *raw) G2_INL {
+    constexpr int j = decltype(j_tag)::value;
+    const int r = b_row_of(j_tag);
+    const int chunk = 2 * p + (lane >> 5);
+    raw[j] = *reinterpret_cast<const uint4 *>(st + A_BYTES + r * RB_B +
+                                              ((chunk ^ ((r / (16 / CPR_B)) % CPR_B)) << 4));
+  };
+  // fp8 B: block scale of fragment j for K tile kt (uniform per wave)
+  auto scale_b8 = [&](int kt, auto j_tag) G2_INL {
+    const int rb = b_row_of(j_tag) - (lane & 31);
+    return sc_lds[(rb / 128) * kblocks + ((k_begin + kt) * BK) / 128];
   };
   // K loop for NS active sub-blocks.  Single-segment problems run one
   // straight-line schedule per stage: MFMAs one at a time, with the fragment
@@ -424,7 +531,22 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst); });
         } else {
           bf16x8 fa[2][NA], fb[2][FRN];
-          static_for<NF>([&](auto f) G2_INL { read_frag(st, 0, f, fa[0], fb[0]); });
+          uint4 braw[B8 ? FRN : 1];
+          float bsc[B8 ? FRN : 1];
+          if constexpr (B8) {
+            static_for<FRN>([&](auto j) G2_INL {
+              bsc[j] = scale_b8(kt, j);
+              read_b8(st, 0, j, braw);
+            });
+            static_for<NF>([&](auto f) G2_INL {
+              if constexpr (f >= FRN) read_frag(st, 0, f, fa[0], fb[0]);
+            });
+            static_for<FRN>([&](auto j) G2_INL {
+              fb[0][j] = e4m3x8_to_bf16(braw[j].x, braw[j].y, bsc[j]);
+            });
+          } else {
+            static_for<NF>([&](auto f) G2_INL { read_frag(st, 0, f, fa[0], fb[0]); });
+          }
           static_for<KS>([&](auto s_tag) G2_INL {
             constexpr int S = decltype(s_tag)::value;
             static_for<Q>([&](auto q_tag) G2_INL {
@@ -438,9 +560,26 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                 static_for<NF>([&](auto f_tag) G2_INL {
                   constexpr int f = decltype(f_tag)::value;
                   constexpr bool mine = NF <= Q ? (f == q) : (f >= q * NF / Q && f < (q + 1) * NF / Q);
-                  if constexpr (mine)
-                    read_frag(st, S + 1, f_tag, fa[(S + 1) & 1], fb[(S + 1) & 1]);
+                  if constexpr (mine) {
+                    if constexpr (B8 && f < FRN) {
+                      // fp8 B: an even step reads the pair's codes, an odd step
+                      // converts the upper half read one step earlier
+                      if constexpr ((S + 1) % 2 == 0) read_b8(st, (S + 1) / 2, f_tag, braw);
+                      else fb[(S + 1) & 1][f] = e4m3x8_to_bf16(braw[f].z, braw[f].w, bsc[f]);
+                    } else {
+                      read_frag(st, S + 1, f_tag, fa[(S + 1) & 1], fb[(S + 1) & 1]);
+                    }
+                  }
                 });
+                if constexpr (B8 && (S + 1) % 2 == 0) {
+                  // lower half of the codes read above, late in the step
+                  static_for<FRN>([&](auto j_tag) G2_INL {
+                    constexpr int j = decltype(j_tag)::value;
+                    constexpr int at = Q - FRN + j > j ? Q - FRN + j : j;
+                    if constexpr (q == at)
+                      fb[(S + 1) & 1][j] = e4m3x8_to_bf16(braw[j].x, braw[j].y, bsc[j]);
+                  });
+                }
               }
               // DMAs of the tile STAGES - 1 ahead: with two stages that tile is
               // needed at the next barrier, so they all go out in the first k
@@ -475,15 +614,31 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         if (kt + STAGES - 1 < ktiles) issue(kt + STAGES - 1);
         if constexpr (NS > 0) {
           bf16x8 fa[NA], fb[FRN];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            static_for<NF>([&](auto f) G2_INL { read_frag(st, ks, f, fa, fb); });
+          uint4 braw[B8 ? FRN : 1];
+          float bsc[B8 ? FRN : 1];
+          if constexpr (B8) static_for<FRN>([&](auto j) G2_INL { bsc[j] = scale_b8(kt, j); });
+          static_for<KS>([&](auto ks_tag) G2_INL {
+            constexpr int ks = decltype(ks_tag)::value;
+            static_for<NF>([&](auto f) G2_INL {
+              if constexpr (f >= FRN || !B8) read_frag(st, ks, f, fa, fb);
+            });
+            if constexpr (B8) {
+              // fp8 B: an even step reads the codes of the step pair
+              static_for<FRN>([&](auto j) G2_INL {
+                if constexpr (ks % 2 == 0) {
+                  read_b8(st, ks / 2, j, braw);
+                  fb[j] = e4m3x8_to_bf16(braw[j].x, braw[j].y, bsc[j]);
+                } else {
+                  fb[j] = e4m3x8_to_bf16(braw[j].z, braw[j].w, bsc[j]);
+                }
+              });
+            }
 #pragma unroll
             for (int i = 0; i < NS; ++i)
 #pragma unroll
               for (int j = 0; j < FRN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-          }
+          });
         }
       }
     }

@@ -1,0 +1,173 @@
+// gemm_launch.h -- tile shapes of the direct-to-LDS engine and its host-side
+// launch templates (instantiated in the gemm_dma_*.hip units, dispatched from
+// gemm.hip).
+#pragma once
+
+#include <algorithm>
+#include <cstdlib>
+
+#include "gemm.h"
+#include "gemm2.h"
+#include "kernels.h"
+
+namespace moe {
+
+inline int env_int(const char *name, int dflt) {
+  const char *v = std::getenv(name);
+  return v ? std::atoi(v) : dflt;
+}
+
+// ---- direct-to-LDS bf16 engine ----------------------------------------------------
+struct DmaShape {
+  int wm, wn, subm, frn, bk, stages, occ;
+  constexpr int threads() const { return 64 * wm * wn; }
+  constexpr int tm() const { return wm * subm * 32; }
+  constexpr int tn() const { return wn * frn * 32; }
+  // stage ring: bf16 A rows, and B rows of bf16 (b8 = false) or fp8 codes
+  constexpr size_t lds(bool b8 = false) const {
+    return (size_t)stages * (tm() * bk * 2 + tn() * bk * (b8 ? 1 : 2));
+  }
+  // every wave issues whole rounds of A and of B DMA instructions (1 KB each)
+  constexpr bool whole_rounds(bool b8 = false) const {
+    return (tm() / (512 / bk)) % (wm * wn) == 0 &&
+           (tn() / ((b8 ? 1024 : 512) / bk)) % (wm * wn) == 0;
+  }
+};
+constexpr DmaShape kDma[] = {
+    {1, 4, 5, 2, 64, 3, 1},  // 0: 160 x 256, BK 64, 3 stages (156 KB)
+    {2, 2, 4, 4, 64, 2, 1},  // 1: 256 x 256, BK 64, 2 stages (128 KB)
+    {1, 4, 4, 2, 64, 3, 1},  // 2: 128 x 256, BK 64, 3 stages (144 KB)
+    {2, 2, 4, 2, 32, 3, 2},  // 3: 256 x 128, BK 32, 3 stages (72 KB), 2 per CU
+    {2, 2, 4, 4, 32, 4, 1},  // 4: 256 x 256, BK 32, 4 stages (128 KB)
+    {1, 4, 4, 2, 32, 3, 2},  // 5: 128 x 256, BK 32, 3 stages (72 KB), 2 per CU
+    {2, 2, 2, 2, 64, 2, 2},  // 6: 128 x 128, BK 64, 2 stages (64 KB), 2 per CU
+    {2, 2, 5, 2, 32, 4, 1},  // 7: 320 x 128, BK 32, 4 stages (112 KB)
+    {2, 4, 5, 2, 64, 2, 1},  // 8: 320 x 256, 8 waves, BK 64, 2 stages (144 KB)
+    {2, 4, 3, 2, 64, 2, 1},  // 9: 192 x 256, 8 waves, BK 64, 2 stages (112 KB)
+    {2, 4, 4, 2, 64, 2, 1},  // 10: 256 x 256, 8 waves, BK 64, 2 stages (128 KB)
+    {2, 4, 4, 2, 32, 4, 1},  // 11: 256 x 256, 8 waves, BK 32, 4 stages (128 KB)
+    {2, 4, 5, 2, 32, 4, 1},  // 12: 320 x 256, 8 waves, BK 32, 4 stages (144 KB)
+    {2, 4, 5, 2, 32, 3, 1},  // 13: 320 x 256, 8 waves, BK 32, 3 stages (108 KB)
+    // small-M shapes for weight streaming (a few rows per expert)
+    {1, 4, 1, 2, 64, 4, 1},  // 14: 32 x 256, BK 64, 4 stages (144 KB)
+    {1, 4, 2, 2, 64, 3, 1},  // 15: 64 x 256, BK 64, 3 stages (120 KB)
+    {1, 4, 1, 2, 64, 2, 2},  // 16: 32 x 256, BK 64, 2 stages (72 KB), 2 per CU
+};
+constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
+
+template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, bool B8, typename OutT>
+hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
+  constexpr DmaShape sh = kDma[V];
+  auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, EPI,
+                                  DUAL, GATHER, MSEG, B8, OutT>;
+  constexpr size_t lds = sh.lds(B8) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), B8>();
+  static_assert(lds <= 160 * 1024, "LDS of a gfx950 workgroup");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tn_out = DUAL ? sh.tn() / 2 : sh.tn();
+  a.n_tiles_n = (int32_t)((a.N + tn_out - 1) / tn_out);
+  // dense rasterisation groups (grouped problems group by expert)
+  a.group_m = env_int("MOE_GROUP_M_DENSE", 4);
+  if (a.group_m < 1) a.group_m = 1;
+  int64_t m_tiles;
+  if (a.offsets == nullptr) m_tiles = (a.M + sh.tm() - 1) / sh.tm();
+  else m_tiles = (a.M + sh.tm() - 1) / sh.tm() + a.n_experts;  // upper bound
+  int64_t blocks = m_tiles * a.n_tiles_n;
+  // split K when a dense problem has too few tiles to spread its weight
+  // stream over the chip (short batches): about 256 workgroups, two or more
+  // K tiles each, within the partial-sum buffer
+  a.ksplit = 1;
+  if (a.offsets == nullptr && a.partial != nullptr && blocks > 0 && blocks < 128) {
+    int64_t ktiles = 0;
+    for (int i = 0; i < a.nseg; ++i) ktiles += a.seg[i].k / sh.bk;
+    const int64_t ldp = DUAL ? 2 * a.N : a.N;
+    int64_t ks = std::min((256 + blocks - 1) / blocks, ktiles / 2);
+    ks = std::min(ks, a.partial_cap / (a.M * ldp));
+    if (ks > 1) {
+      const int64_t kper = (ktiles + ks - 1) / ks;
+      a.ksplit = (int32_t)((ktiles + kper - 1) / kper);  // every split gets K tiles
+      a.ldp = ldp;
+    }
+  }
+  blocks = (blocks + 7) / 8 * 8;
+  if (blocks <= 0) return hipSuccess;
+  hipError_t e = launch_kernel(kern, dim3((unsigned)blocks, (unsigned)a.ksplit),
+                               dim3(sh.threads()), lds, s, a);
+  if (e != hipSuccess || a.ksplit <= 1) return e;
+  const unsigned rblocks = (unsigned)std::min<int64_t>((a.M * a.N + 255) / 256, 8192);
+  return launch_kernel(g2::splitk_reduce_kernel<EPI, DUAL, OutT>, dim3(rblocks), dim3(256), 0, s,
+                       a);
+}
+
+template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, typename OutT>
+hipError_t launch_dma_v(const GemmArgs &a, hipStream_t s) {
+  // K-segmented problems need whole DMA rounds per wave: else the 256 x 256 shape
+  if constexpr (MSEG && !kDma[V].whole_rounds())
+    return launch_dma_impl<10, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
+  else
+    return launch_dma_impl<V, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
+}
+
+// fp8 e4m3 B with block scales: the three default shapes (dense, grouped,
+// small-M); other requests take the dense one
+template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
+hipError_t launch_dma_b8(int v, const GemmArgs &a, hipStream_t s) {
+  static_assert(!MSEG || kDma[10].whole_rounds(true), "segmented fp8 shape");
+  if constexpr (MSEG) return launch_dma_impl<10, EPI, DUAL, GATHER, true, true, OutT>(a, s);
+  switch (v) {
+    case 8: return launch_dma_impl<8, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case 9: return launch_dma_impl<9, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case 14: return launch_dma_impl<14, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    default: return launch_dma_impl<10, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+  }
+}
+
+template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
+hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
+  switch (v) {
+    case 0: return launch_dma_v<0, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 1: return launch_dma_v<1, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 2: return launch_dma_v<2, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 3: return launch_dma_v<3, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 4: return launch_dma_v<4, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 5: return launch_dma_v<5, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 6: return launch_dma_v<6, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 7: return launch_dma_v<7, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 8: return launch_dma_v<8, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 9: return launch_dma_v<9, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 10: return launch_dma_v<10, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 11: return launch_dma_v<11, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 12: return launch_dma_v<12, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 13: return launch_dma_v<13, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 14: return launch_dma_v<14, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 15: return launch_dma_v<15, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+    case 16: return launch_dma_v<16, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// launch_dma instantiations, one per problem kind (gemm_dma_*.hip)
+#define MOE_DMA_KINDS(X)                                  \
+  X(EPI_ROUTER, false, false, float, false)               \
+  X(EPI_STORE, false, false, uint16_t, true)              \
+  X(EPI_STORE, false, false, uint16_t, false)             \
+  X(EPI_SITU, true, false, uint16_t, false)               \
+  X(EPI_SITU, true, true, uint16_t, false)
+#define MOE_DMA_EXTERN(E, D, G, T, M) \
+  extern template hipError_t launch_dma<E, D, G, T, M>(int, const GemmArgs &, hipStream_t);
+MOE_DMA_KINDS(MOE_DMA_EXTERN)
+#define MOE_B8_KINDS(X)                      \
+  X(EPI_STORE, false, false, uint16_t, false) \
+  X(EPI_STORE, false, false, uint16_t, true)  \
+  X(EPI_SITU, true, false, uint16_t, false)   \
+  X(EPI_SITU, true, true, uint16_t, false)
+#define MOE_B8_EXTERN(E, D, G, T, M) \
+  extern template hipError_t launch_dma_b8<E, D, G, T, M>(int, const GemmArgs &, hipStream_t);
+MOE_B8_KINDS(MOE_B8_EXTERN)
+
+}  // namespace moe

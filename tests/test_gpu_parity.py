@@ -143,6 +143,27 @@ def test_forward_small_all_tokens(cfg_name, cutoff, routing):
     assert err <= parity.tol_of(cfg)
 
 
+@pytest.mark.parametrize("bt,cutoff", [(4096, "batch"), (64, "given"), (100, "batch")])
+def test_forward_fp8_weights_mid(bt, cutoff):
+    """fp8 e4m3 weights with 128 x 128 block scales at the mid shapes: the
+    prefill-sized batch runs the 320-row grouped tiles, the short ones the
+    32-row tiles and split-K dense GEMMs."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="fp8", bt=bt)
+    say("forward fp8", bt, cutoff)
+    layer, x = parity.device_layer(cfg, seed=0, cutoff=cutoff)
+    y, r = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(cfg, synth.host_layer(cfg, 0),
+                         cutoff=oracle.BATCH if cutoff == "batch" else oracle.GIVEN)
+    diff, bad = parity.routing_mismatches(parity.to_np(r["idx"]), ref["idx"], ref["z32"],
+                                          ref["zeta"])
+    assert not bad
+    keep = np.setdiff1d(np.arange(cfg.bt), diff)
+    err = parity.normwise_err(parity.y_to_f64(y)[keep], ref["y"][keep])
+    say(f"  normwise err {err:.3e} (tol {parity.tol_of(cfg)}), near ties {len(diff)}")
+    assert err <= parity.tol_of(cfg)
+
+
 # ---- edge cases ----------------------------------------------------------------------------
 
 def _small_forward_check(cfg, cutoff, seed=0, alpha=None, routing="normal"):
