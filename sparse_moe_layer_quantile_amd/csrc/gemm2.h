@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   constexpr int TA = TM / RPI, TB = TN / RPI_B, TT = TA + TB;
   constexpr int LMAX = (TT + NW - 1) / NW;
   constexpr bool EVEN = TT % NW == 0;
-  static_assert(TM % RPI == 0 && TN % RPI_B == 0 && (TM / RPI) % 4 == 0, "whole DMA rows");
+  static_assert(TM % RPI == 0 && TN % RPI_B == 0, "whole DMA rows");
   static_assert(!DUAL || (TN / 2) % RPI_B == 0, "gate/up split on a DMA instruction");
   // multi-segment problems keep whole A and B rounds per wave
   constexpr int A_LD = TA / NW, B_LD = TB / NW;
@@ -295,10 +295,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     b0 += (int64_t)tile.e * args.b_estride;
     if (DUAL) bu += (int64_t)tile.e * args.b_estride;
   }
-  // chunk this lane fetches so that the DMA slot order realises the swizzle;
-  // instruction g fills rows g RPI + rsub of its region (A, or B from TA on,
-  // TA a multiple of 4), whose swizzle key (4 g + rsub / (16 / CPR)) % CPR
-  // depends on g only through g % 2 = wave % 2 (NW is even)
+  // chunk a lane of a segmented problem fetches so that the DMA slot order
+  // realises the swizzle: instruction i of the wave fills region rows
+  // (wave + NW i) RPI + rsub, whose swizzle key (4 (wave + NW i) + rsub /
+  // (16 / CPR)) % CPR does not depend on i (CPR divides 4 NW)
   const int fetch_chunk = slot ^ ((((wave * RPI) + rsub) / (16 / CPR)) % CPR);
 
   // ---- K segments -------------------------------------------------------------
