@@ -141,9 +141,10 @@ moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int64_t 
                         moe_dispatch_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Whole layer: y[bt][d] (act_dtype).  route / disp may be NULL; when given
- * they receive the routing and dispatch of this call.  The shared experts
- * run on shared_stream (NULL: on `stream`) and are joined into `stream`
- * before the output projection. */
+ * they receive the routing and dispatch of this call.  The latent down
+ * projection and the shared experts' gate/up do not depend on routing: they
+ * run on shared_stream (NULL: on `stream`), joined into `stream` before the
+ * routed experts and before the output projection respectively. */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
                        void *y, moe_route_out *route, moe_dispatch_out *disp, void *ws,
                        size_t ws_bytes, void *stream, void *shared_stream);

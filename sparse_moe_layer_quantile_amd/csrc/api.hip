@@ -4,9 +4,10 @@
 // Launch order of moe_forward (tech.news18a.com "KimiK3的StableLatentMoE架构解析",
 // figure 2: two parallel paths from the flattened x; mkdocs.reaper.mx "Vue
 // d'ensemble de l'architecture", per-token steps c-g):
-//   shared_stream: shared gate/up + SiTU -> hs                    (step g, part 1)
+//   shared_stream: x_lat = x W_down_proj^T                        (step d)
+//                  shared gate/up + SiTU -> hs                    (step g, part 1)
 //   stream:        router logits -> cutoffs -> top-k -> dispatch  (step c)
-//                  x_lat = x W_down_proj^T                        (step d)
+//                  join(x_lat)
 //                  grouped gate/up + SiTU, x routing weight -> h  (step e; the
 //                    weight is applied before W_d, which is linear)
 //                  grouped down -> o                              (step e)
@@ -407,16 +408,36 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   const bool fp8 = p.fp8;
   const int64_t dense_mt = (bt + bm - 1) / bm;
 
-  // ---- shared experts: gate/up + SiTU on the second stream -----------------------
-  hipEvent_t ev_x = nullptr, ev_sh = nullptr;
-  const bool two_streams = S > 0 && ss != s;
+  // ---- second stream: x_lat = x W_down_proj^T, then the shared experts' gate/up -----
+  // Neither depends on routing: W_down_proj runs beside the (small, latency-bound)
+  // routing kernels, and the shared gate/up beside the routed experts.
+  hipEvent_t ev_x = nullptr, ev_lat = nullptr, ev_sh = nullptr;
+  const bool two_streams = ss != s;
+  hipStream_t side = two_streams ? ss : s;
+  if (two_streams) {
+    if (ev_get(&ev_x) != hipSuccess || ev_get(&ev_lat) != hipSuccess ||
+        ev_get(&ev_sh) != hipSuccess)
+      return MOE_ERR_HIP;
+    MOE_TRY_HIP(hipEventRecord(ev_x, s));
+    MOE_TRY_HIP(hipStreamWaitEvent(ss, ev_x, 0));
+  }
+  void *xlat = at<void>(ws, p.xlat);
+  {
+    GemmArgs a = base_args(cfg);
+    a.M = bt;
+    a.N = L;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, w->s_down_proj, d};
+    a.partial = at<float>(ws, p.split_sh);
+    a.partial_cap = p.split_cap;
+    a.out = xlat;
+    a.ldo = L;
+    PhaseScope ph(PH_DOWN_PROJ, side);
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, side));
+  }
+  if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_lat, ss));
   void *hs = at<void>(ws, p.hs);
   if (S > 0) {
-    if (two_streams) {
-      if (ev_get(&ev_x) != hipSuccess || ev_get(&ev_sh) != hipSuccess) return MOE_ERR_HIP;
-      MOE_TRY_HIP(hipEventRecord(ev_x, s));
-      MOE_TRY_HIP(hipStreamWaitEvent(ss, ev_x, 0));
-    }
     GemmArgs a = base_args(cfg);
     a.M = bt;
     a.N = S * Is;
@@ -428,10 +449,10 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.partial_cap = p.split_cap;
     a.out = hs;
     a.ldo = S * Is;
-    PhaseScope ph(PH_SHARED, ss);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, fp8, dense_mt, ss));
-    if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_sh, ss));
+    PhaseScope ph(PH_SHARED, side);
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, fp8, dense_mt, side));
   }
+  if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_sh, ss));
 
   // ---- routing -----------------------------------------------------------------
   float *z = (route && route->logits) ? route->logits : at<float>(ws, p.z);
@@ -453,22 +474,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
                                 at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
                                 inv_perm, w_sorted, s));
   }
-
-  // ---- x_lat = x W_down_proj^T ---------------------------------------------------
-  void *xlat = at<void>(ws, p.xlat);
-  {
-    GemmArgs a = base_args(cfg);
-    a.M = bt;
-    a.N = L;
-    a.nseg = 1;
-    a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, w->s_down_proj, d};
-    a.partial = at<float>(ws, p.split);
-    a.partial_cap = p.split_cap;
-    a.out = xlat;
-    a.ldo = L;
-    PhaseScope ph(PH_DOWN_PROJ, s);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
-  }
+  if (two_streams) MOE_TRY_HIP(hipStreamWaitEvent(s, ev_lat, 0));  // x_lat ready
 
   // ---- routed experts ---------------------------------------------------------------
   const int64_t grouped_mt = (P + bm - 1) / bm + E;
@@ -524,6 +530,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   if (two_streams) {
     MOE_TRY_HIP(hipStreamWaitEvent(s, ev_sh, 0));
     ev_put(ev_x);
+    ev_put(ev_lat);
     ev_put(ev_sh);
   }
   {
