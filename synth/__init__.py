@@ -100,6 +100,12 @@ CONFIGS: Dict[str, Config] = {
     "k3_prefill_fp8": Config("k3_prefill_fp8", bt=8192, d=7168, latent=3584, n_experts=896,
                              top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
                              weight="fp8", router="bf16", cutoff="batch"),
+    # one GPU's share of K3 prefill under 8-way expert parallelism: its own 16384 tokens
+    # through the replicated dense parts, and 262144 pairs over its 112 experts
+    # (about 2341 rows per expert), so the grouped GEMMs run at the sharded shape
+    "k3_ep8_share_bf16": Config("k3_ep8_share_bf16", bt=16384, d=7168, latent=3584,
+                                n_experts=112, top_k=16, expert_inter=3072, n_shared=2,
+                                shared_inter=3072, cutoff="batch"),
 }
 
 

@@ -80,3 +80,11 @@ def test_k3_prefill_zipf_batch_cutoffs():
 
 def test_k3_prefill_fp8_weights():
     _run_k3("k3_prefill_fp8", n_sample=10)
+
+
+def test_k3_expert_parallel_share():
+    """One GPU's share of 8-way expert parallelism: 112 experts with about 2341
+    rows each, so every expert spans several M tiles of the grouped GEMMs."""
+    cfg, got = _run_k3("k3_ep8_share_bf16", n_sample=10)
+    say(f"  rows per expert: min {got['counts'].min()} max {got['counts'].max()}")
+    assert got["counts"].min() > 320  # several M tiles per expert
