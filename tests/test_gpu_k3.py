@@ -1,8 +1,9 @@
 """GPU parity at the full K3 layer shapes (d=7168, L=3584, 896 experts, top 16,
 I=3072, 2 shared experts of 3072), in the launch configuration the benchmark
-times (two streams).  Routing is checked on every token against the full-batch
-oracle; the layer output on every token (decode) or on a seeded sample of
-tokens the oracle computes one by one (prefill)."""
+times (one stream), and the prefill case on two streams as well.  Routing is
+checked on every token against the full-batch oracle; the layer output on every
+token (decode) or on a seeded sample of tokens the oracle computes one by one
+(prefill)."""
 import numpy as np
 import pytest
 
@@ -25,11 +26,11 @@ def _need_gpu():
     torch.cuda.empty_cache()
 
 
-def _run_k3(cfg_name, n_sample, seed=0):
+def _run_k3(cfg_name, n_sample, seed=0, two_streams=False):
     cfg = synth.CONFIGS[cfg_name]
-    say("k3 parity", cfg.name, "bt", cfg.bt, "sample", n_sample)
+    say("k3 parity", cfg.name, "bt", cfg.bt, "sample", n_sample, "two streams", two_streams)
     layer, x = parity.device_layer(cfg, seed=seed)
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if two_streams else None
     y, r = layer.forward(x, shared_stream=side, return_routing=True)
     torch.cuda.synchronize()
     yg = parity.y_to_f64(y)
@@ -70,8 +71,9 @@ def test_k3_decode_all_tokens():
     say("  experts touched", int((got["counts"] > 0).sum()))
 
 
-def test_k3_prefill_zipf_batch_cutoffs():
-    cfg, got = _run_k3("k3_prefill_bf16", n_sample=10)
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_k3_prefill_zipf_batch_cutoffs(two_streams):
+    cfg, got = _run_k3("k3_prefill_bf16", n_sample=10, two_streams=two_streams)
     # the batch cutoffs balance the Zipf-skewed load: every expert near bt*k/E
     mean = cfg.bt * cfg.top_k / cfg.n_experts
     say(f"  load max/mean {got['counts'].max() / mean:.3f} min/mean {got['counts'].min() / mean:.3f}")
