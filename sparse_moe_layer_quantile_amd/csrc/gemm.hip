@@ -41,11 +41,13 @@ static hipError_t launch_f32(GemmArgs a, int64_t m_tiles, hipStream_t s) {
 // ones 256 x 256 tiles.
 int dma_variant(GemmKind kind, int64_t rows, int64_t n_experts) {
   if (kind == GK_EXPERT_SITU || kind == GK_EXPERT_DOWN) {
-    const int dflt = rows <= 8 * n_experts ? 14 : rows <= 200 * n_experts ? 9 : 8;
+    const int dflt = rows <= 8 * n_experts       ? kVSmallM
+                     : rows <= 200 * n_experts ? kVGroupedShort
+                                               : kVGrouped;
     const int v = env_int("MOE_GEMM_GROUPED", dflt);
     return (v >= 0 && v < kNumDma) ? v : dflt;
   }
-  const int dflt = rows <= 64 ? 14 : 10;
+  const int dflt = rows <= 64 ? kVSmallM : kVDense;
   const int v = env_int("MOE_GEMM_DENSE", dflt);
   return (v >= 0 && v < kNumDma) ? v : dflt;
 }
@@ -53,7 +55,8 @@ int dma_variant(GemmKind kind, int64_t rows, int64_t n_experts) {
 int grouped_tile_rows(int path, bool fp8, int64_t rows, int64_t n_experts) {
   if (path == PATH_F32) return sf::BM;
   const int v = dma_variant(GK_EXPERT_SITU, rows, n_experts);
-  if (fp8 && v != 8 && v != 9 && v != 14) return kDma[10].tm();  // the fp8 engine's shapes
+  // the fp8 engine's shapes (launch_dma_b8)
+  if (fp8 && v != kVGrouped && v != kVGroupedShort && v != kVSmallM) return kDma[kVDense].tm();
   return kDma[v].tm();
 }
 

@@ -34,25 +34,16 @@ struct DmaShape {
   }
 };
 constexpr DmaShape kDma[] = {
-    {1, 4, 5, 2, 64, 3, 1},  // 0: 160 x 256, BK 64, 3 stages (156 KB)
-    {2, 2, 4, 4, 64, 2, 1},  // 1: 256 x 256, BK 64, 2 stages (128 KB)
-    {1, 4, 4, 2, 64, 3, 1},  // 2: 128 x 256, BK 64, 3 stages (144 KB)
-    {2, 2, 4, 2, 32, 3, 2},  // 3: 256 x 128, BK 32, 3 stages (72 KB), 2 per CU
-    {2, 2, 4, 4, 32, 4, 1},  // 4: 256 x 256, BK 32, 4 stages (128 KB)
-    {1, 4, 4, 2, 32, 3, 2},  // 5: 128 x 256, BK 32, 3 stages (72 KB), 2 per CU
-    {2, 2, 2, 2, 64, 2, 2},  // 6: 128 x 128, BK 64, 2 stages (64 KB), 2 per CU
-    {2, 2, 5, 2, 32, 4, 1},  // 7: 320 x 128, BK 32, 4 stages (112 KB)
-    {2, 4, 5, 2, 64, 2, 1},  // 8: 320 x 256, 8 waves, BK 64, 2 stages (144 KB)
-    {2, 4, 3, 2, 64, 2, 1},  // 9: 192 x 256, 8 waves, BK 64, 2 stages (112 KB)
-    {2, 4, 4, 2, 64, 2, 1},  // 10: 256 x 256, 8 waves, BK 64, 2 stages (128 KB)
-    {2, 4, 4, 2, 32, 4, 1},  // 11: 256 x 256, 8 waves, BK 32, 4 stages (128 KB)
-    {2, 4, 5, 2, 32, 4, 1},  // 12: 320 x 256, 8 waves, BK 32, 4 stages (144 KB)
-    {2, 4, 5, 2, 32, 3, 1},  // 13: 320 x 256, 8 waves, BK 32, 3 stages (108 KB)
-    // small-M shapes for weight streaming (a few rows per expert)
-    {1, 4, 1, 2, 64, 4, 1},  // 14: 32 x 256, BK 64, 4 stages (144 KB)
-    {1, 4, 2, 2, 64, 3, 1},  // 15: 64 x 256, BK 64, 3 stages (120 KB)
-    {1, 4, 1, 2, 64, 2, 2},  // 16: 32 x 256, BK 64, 2 stages (72 KB), 2 per CU
+    {2, 4, 5, 2, 64, 2, 1},  // 0: 320 x 256, 8 waves, BK 64, 2 stages (144 KB)
+    {2, 4, 3, 2, 64, 2, 1},  // 1: 192 x 256, 8 waves, BK 64, 2 stages (112 KB)
+    {2, 4, 4, 2, 64, 2, 1},  // 2: 256 x 256, 8 waves, BK 64, 2 stages (128 KB)
+    {1, 4, 1, 2, 64, 4, 1},  // 3: 32 x 256, 4 waves, BK 64, 4 stages (144 KB)
+    // measured alternatives (slower on the K3 shapes), kept for tuning
+    {2, 4, 5, 2, 32, 4, 1},  // 4: 320 x 256, 8 waves, BK 32, 4 stages (144 KB)
+    {1, 4, 5, 2, 64, 3, 1},  // 5: 160 x 256, 4 waves, BK 64, 3 stages (156 KB)
 };
+// the shapes the engine picks by default (gemm.hip, dma_variant)
+constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 
 template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, bool B8, typename OutT>
@@ -108,22 +99,23 @@ template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, typename OutT>
 hipError_t launch_dma_v(const GemmArgs &a, hipStream_t s) {
   // K-segmented problems need whole DMA rounds per wave: else the 256 x 256 shape
   if constexpr (MSEG && !kDma[V].whole_rounds())
-    return launch_dma_impl<10, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
+    return launch_dma_impl<kVDense, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
   else
     return launch_dma_impl<V, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
 }
 
-// fp8 e4m3 B with block scales: the three default shapes (dense, grouped,
-// small-M); other requests take the dense one
+// fp8 e4m3 B with block scales: the default shapes; other requests take the
+// dense one
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
 hipError_t launch_dma_b8(int v, const GemmArgs &a, hipStream_t s) {
-  static_assert(!MSEG || kDma[10].whole_rounds(true), "segmented fp8 shape");
-  if constexpr (MSEG) return launch_dma_impl<10, EPI, DUAL, GATHER, true, true, OutT>(a, s);
+  static_assert(!MSEG || kDma[kVDense].whole_rounds(true), "segmented fp8 shape");
+  if constexpr (MSEG) return launch_dma_impl<kVDense, EPI, DUAL, GATHER, true, true, OutT>(a, s);
   switch (v) {
-    case 8: return launch_dma_impl<8, EPI, DUAL, GATHER, false, true, OutT>(a, s);
-    case 9: return launch_dma_impl<9, EPI, DUAL, GATHER, false, true, OutT>(a, s);
-    case 14: return launch_dma_impl<14, EPI, DUAL, GATHER, false, true, OutT>(a, s);
-    default: return launch_dma_impl<10, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case kVGroupedShort:
+      return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case kVSmallM: return launch_dma_impl<kVSmallM, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    default: return launch_dma_impl<kVDense, EPI, DUAL, GATHER, false, true, OutT>(a, s);
   }
 }
 
@@ -136,17 +128,6 @@ hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
     case 3: return launch_dma_v<3, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
     case 4: return launch_dma_v<4, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
     case 5: return launch_dma_v<5, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 6: return launch_dma_v<6, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 7: return launch_dma_v<7, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 8: return launch_dma_v<8, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 9: return launch_dma_v<9, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 10: return launch_dma_v<10, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 11: return launch_dma_v<11, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 12: return launch_dma_v<12, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 13: return launch_dma_v<13, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 14: return launch_dma_v<14, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 15: return launch_dma_v<15, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
-    case 16: return launch_dma_v<16, EPI, DUAL, GATHER, MSEG, OutT>(a, s);
   }
   return hipErrorInvalidValue;
 }
