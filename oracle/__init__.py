@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 GIVEN, BATCH = 0, 1
 
 _NP_DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): FP8}
@@ -57,6 +57,8 @@ def lib():
         sig = {
             "orc_bf16_to_double": ([ctypes.c_uint16], D),
             "orc_e4m3_to_double": ([ctypes.c_uint8], D),
+            "orc_e2m1_to_double": ([ctypes.c_uint8], D),
+            "orc_e8m0_to_double": ([ctypes.c_uint8], D),
             "orc_decode": ([P, I64, I64, I64], D),
             "orc_matvec": ([P, I64, P, P], None),
             "orc_sigmoid": ([D], D),
@@ -99,17 +101,24 @@ def shape_of(cfg) -> OrcShape:
 
 
 class Mat:
-    """Keeps the arrays behind an OrcMat alive."""
+    """Keeps the arrays behind an OrcMat alive.  A uint8 `scale` (E8M0 codes)
+    marks `data` as MXFP4: bytes [.., rows, cols / 2] of two codes each."""
 
     def __init__(self, data: np.ndarray, scale: np.ndarray | None = None, n_mats=None,
                  rows=None, cols=None):
         self.data = np.ascontiguousarray(data)
-        self.scale = None if scale is None else np.ascontiguousarray(scale, np.float32)
-        dt = _NP_DT[self.data.dtype]
+        mx = scale is not None and np.asarray(scale).dtype == np.uint8
+        if scale is None:
+            self.scale = None
+        else:
+            self.scale = np.ascontiguousarray(scale, np.uint8 if mx else np.float32)
+        dt = MXFP4 if mx else _NP_DT[self.data.dtype]
         if data.ndim == 3:
             n_mats, rows, cols = data.shape
         elif data.ndim == 2:
             n_mats, rows, cols = 1, data.shape[0], data.shape[1]
+        if mx:
+            cols *= 2
         self.c = OrcMat(self.data.ctypes.data, dt,
                         None if self.scale is None else self.scale.ctypes.data,
                         n_mats, rows, cols)
@@ -165,6 +174,14 @@ def bf16_to_double(bits):
 
 def e4m3_to_double(code):
     return lib().orc_e4m3_to_double(int(code))
+
+
+def e2m1_to_double(code):
+    return lib().orc_e2m1_to_double(int(code))
+
+
+def e8m0_to_double(code):
+    return lib().orc_e8m0_to_double(int(code))
 
 
 def matvec(mat: Mat, vec, index=0):
@@ -278,7 +295,7 @@ def decode(arr: np.ndarray, scale=None) -> np.ndarray:
     for i in range(rows):
         for c in range(m.c.cols):
             out[i, c] = lib().orc_decode(m.ref, i // m.c.rows, i % m.c.rows, c)
-    return out.reshape(a.shape)
+    return out.reshape(a.shape[:-1] + (m.c.cols,))
 
 
 def forward(cfg, layer: dict, cutoff: int = BATCH, alpha=None):

@@ -15,13 +15,14 @@
 
 namespace {
 
-const int32_t ORC_F64 = 3;  // internal: fully decoded fp64 copy
+const int32_t ORC_F64 = 64;  // internal: fully decoded fp64 copy
 
 int64_t elem_bytes(int32_t dt) {
   switch (dt) {
     case ORC_F32: return 4;
     case ORC_BF16: return 2;
     case ORC_FP8E4M3: return 1;
+    case ORC_MXFP4: return 1;  // (half a byte per element)
     case ORC_F64: return 8;
   }
   return 0;
@@ -31,6 +32,7 @@ bool valid_mat(const orc_mat *m) {
   if (!m || !m->data || m->rows <= 0 || m->cols <= 0 || m->n_mats <= 0) return false;
   if (elem_bytes(m->dtype) == 0) return false;
   if (m->dtype == ORC_FP8E4M3 && (!m->scale || m->rows % 128 || m->cols % 128)) return false;
+  if (m->dtype == ORC_MXFP4 && (!m->scale || m->cols % 32)) return false;
   return true;
 }
 
@@ -52,9 +54,20 @@ void decode_row(const orc_mat *m, int64_t mat, int64_t r, double *buf) {
     case ORC_FP8E4M3: {
       const uint8_t *p = static_cast<const uint8_t *>(m->data) + base;
       const int64_t bc = cols / 128;
-      const float *srow = m->scale + (mat * (m->rows / 128) + r / 128) * bc;
+      const float *srow = static_cast<const float *>(m->scale) + (mat * (m->rows / 128) + r / 128) * bc;
       for (int64_t c = 0; c < cols; ++c)
         buf[c] = orc_e4m3_to_double(p[c]) * (double)srow[c / 128];
+      break;
+    }
+    case ORC_MXFP4: {
+      // element c: nibble (c odd ? high : low) of byte c/2 of the row, times
+      // the E8M0 scale of its 32-element block
+      const uint8_t *p = static_cast<const uint8_t *>(m->data) + base / 2;
+      const uint8_t *srow = static_cast<const uint8_t *>(m->scale) + (mat * m->rows + r) * (cols / 32);
+      for (int64_t c = 0; c < cols; ++c) {
+        const uint8_t code = (c & 1) ? (uint8_t)(p[c / 2] >> 4) : (uint8_t)(p[c / 2] & 0xF);
+        buf[c] = orc_e2m1_to_double(code) * orc_e8m0_to_double(srow[c / 32]);
+      }
       break;
     }
     case ORC_F64: {
@@ -109,6 +122,22 @@ double orc_e4m3_to_double(uint8_t code) {
   else if (ex == 0) v = std::ldexp((double)man, -9);
   else v = std::ldexp(1.0 + man / 8.0, ex - 7);
   return sign ? -v : v;
+}
+
+// OCP MX FP4 E2M1: exponent field 0 is subnormal (m * 2^-1), else
+// (1 + m/2) * 2^(e - 1); the largest magnitude is 6.
+double orc_e2m1_to_double(uint8_t code) {
+  const int sign = (code >> 3) & 1;
+  const int ex = (code >> 1) & 0x3;
+  const int man = code & 0x1;
+  const double v = ex == 0 ? 0.5 * man : std::ldexp(1.0 + man / 2.0, ex - 1);
+  return sign ? -v : v;
+}
+
+// OCP MX E8M0 scale: an unsigned biased exponent, 2^(code - 127); 0xFF is NaN.
+double orc_e8m0_to_double(uint8_t code) {
+  if (code == 0xFF) return std::nan("");
+  return std::ldexp(1.0, (int)code - 127);
 }
 
 double orc_decode(const orc_mat *m, int64_t mat, int64_t r, int64_t c) {

@@ -28,7 +28,8 @@
  *
  * Every dot product is accumulated in fp64 in index order.  Inputs are
  * decoded exactly: fp32 and bf16 widen, an fp8 e4m3fn code times its fp32
- * 128x128 block scale is exact in fp64.
+ * 128x128 block scale is exact in fp64, and so is an MXFP4 E2M1 code times
+ * its power-of-two E8M0 block scale.
  *
  * Parity pins (tests/test_oracle_pins.py): closed forms, invariants and
  * brute force as listed there.  The layer output as a whole is pinned only
@@ -44,15 +45,22 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8E4M3 = 2, ORC_MXFP4 = 3 };
 enum { ORC_CUTOFF_GIVEN = 0, ORC_CUTOFF_BATCH = 1 };
 
-/* n_mats matrices of rows x cols, row-major, raw storage.  For ORC_FP8E4M3,
- * scale holds [n_mats][rows/128][cols/128] fp32 block scales. */
+/* n_mats matrices of rows x cols, row-major, raw storage.
+ *   ORC_FP8E4M3: one byte per element; scale -> float [n_mats][rows/128][cols/128],
+ *                one factor per 128 x 128 block.
+ *   ORC_MXFP4:   OCP MX FP4 -- two E2M1 codes per byte, element 2i of a row in
+ *                the low nibble of byte i, 2i+1 in the high nibble (a row is
+ *                cols/2 bytes); scale -> uint8 E8M0 codes [n_mats][rows][cols/32],
+ *                one per 32 consecutive elements of a row.
+ * (OCP Microscaling Formats (MX) Specification v1.0: element type FP4 E2M1,
+ * scale type E8M0, block size 32.) */
 typedef struct {
   const void *data;
   int32_t dtype;
-  const float *scale;
+  const void *scale;
   int64_t n_mats, rows, cols;
 } orc_mat;
 
@@ -77,6 +85,11 @@ typedef struct {
 double orc_decode(const orc_mat *m, int64_t mat, int64_t r, int64_t c);
 double orc_bf16_to_double(uint16_t bits);
 double orc_e4m3_to_double(uint8_t code);
+/* OCP MX element FP4 E2M1 (low 4 bits of code): sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; no infinities or NaN.  E8M0 scale: 2^(code - 127),
+ * code 255 is NaN. */
+double orc_e2m1_to_double(uint8_t code);
+double orc_e8m0_to_double(uint8_t code);
 
 /* out[r] = sum_c M[mat][r][c] in[c], fp64, c ascending. */
 void orc_matvec(const orc_mat *m, int64_t mat, const double *in, double *out);

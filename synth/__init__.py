@@ -1,7 +1,8 @@
 """Seeded synthetic workloads for the Stable LatentMoE layer.
 
 This module generates inputs only: token activations, layer weights, fp8 block
-scales, Zipf logit offsets and routing-index fixtures.  It holds none of the
+scales, MXFP4 expert weights with their E8M0 block scales, Zipf logit offsets
+and routing-index fixtures.  It holds none of the
 layer's arithmetic.  The host generator (``libsynth_host.so``, gcc) and the
 device generator (``libsynth_dev.so``, hipcc) expand the same counter-based
 Philox-4x32-10 definition in ``synth_rng.h`` and produce identical bits, so the
@@ -25,16 +26,24 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4, E8M0 = 0, 1, 2, 3, 4
 NORMAL, DYADIC = 0, 1
 NORMAL_INT_STD = 107022.329313
 NORMAL_INT_MAX = 524280
 FP8_MAX = 448.0
 FP8_BLOCK = 128
+MX_BLOCK = 32        # MXFP4: elements per E8M0 scale
+MX_CODE_SIGMA = 2.0  # MXFP4: standard deviation of the draws rounded to E2M1 codes
+# standard deviation of the E2M1 value of a N(0, MX_CODE_SIGMA^2) draw (rounded
+# to the grid, saturating at 6), and the rms of 2^u, u uniform in {-1, 0, 1}
+MX_CODE_STD = 1.9885
+MX_SCALE_RMS = math.sqrt((0.25 + 1.0 + 4.0) / 3.0)
 
-DTYPE_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8}
-NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
-ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1}
+# weight="mxfp4": the routed experts in MXFP4, every other weight bf16
+DTYPE_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
+NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8, MXFP4: np.uint8}
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, MXFP4: 1}  # per storage unit (MXFP4: 2 elements)
+MX_NAMES = ("w_gate", "w_up", "w_down")
 
 # Tensor ids: distinct Philox counter words per tensor.
 TID = {
@@ -114,16 +123,21 @@ CONFIGS: Dict[str, Config] = {
 @dataclasses.dataclass(frozen=True)
 class Spec:
     name: str
-    shape: tuple          # storage shape, row-major, weights [out][in]
+    shape: tuple          # storage shape, row-major, weights [out][in] (MXFP4: [out][in/2])
     dtype: int
     fan_in: int           # sets sigma = 1/sqrt(fan_in) for weights
-    mat_rows: int         # rows / cols of one matrix (block scales tile these)
+    mat_rows: int         # rows / cols (elements) of one matrix (block scales tile these)
     mat_cols: int
     n_mats: int
 
     @property
     def numel(self) -> int:
+        """Storage units (elements; bytes of two elements for MXFP4)."""
         return int(np.prod(self.shape))
+
+    @property
+    def mat_units(self) -> int:
+        return self.mat_rows * self.mat_cols // (2 if self.dtype == MXFP4 else 1)
 
     @property
     def nbytes(self) -> int:
@@ -131,20 +145,33 @@ class Spec:
 
     @property
     def n_scale_blocks(self) -> int:
+        if self.dtype == MXFP4:
+            return self.n_mats * self.mat_rows * (self.mat_cols // MX_BLOCK)
         return self.n_mats * (self.mat_rows // FP8_BLOCK) * (self.mat_cols // FP8_BLOCK)
+
+    @property
+    def scale_shape(self) -> tuple:
+        if self.dtype == MXFP4:
+            return (self.n_mats, self.mat_rows, self.mat_cols // MX_BLOCK)
+        return (self.n_mats, self.mat_rows // FP8_BLOCK, self.mat_cols // FP8_BLOCK)
 
 
 def specs(cfg: Config) -> Dict[str, Spec]:
     d, L, E, I, S, Is = (cfg.d, cfg.latent, cfg.n_experts, cfg.expert_inter, cfg.n_shared,
                          cfg.shared_inter)
     a, w, r = DTYPE_NAMES[cfg.act], DTYPE_NAMES[cfg.weight], DTYPE_NAMES[cfg.router]
+    # MXFP4 applies to the routed experts; the dense weights stay bf16
+    xw = w
+    if w == MXFP4:
+        w = BF16
+    h = 2 if xw == MXFP4 else 1  # elements per storage unit of the experts
     return {
         "x": Spec("x", (cfg.bt, d), a, 1, cfg.bt, d, 1),
         "w_router": Spec("w_router", (E, d), r, d, E, d, 1),
         "w_down_proj": Spec("w_down_proj", (L, d), w, d, L, d, 1),
-        "w_gate": Spec("w_gate", (E, I, L), w, L, I, L, E),
-        "w_up": Spec("w_up", (E, I, L), w, L, I, L, E),
-        "w_down": Spec("w_down", (E, L, I), w, I, L, I, E),
+        "w_gate": Spec("w_gate", (E, I, L // h), xw, L, I, L, E),
+        "w_up": Spec("w_up", (E, I, L // h), xw, L, I, L, E),
+        "w_down": Spec("w_down", (E, L, I // h), xw, I, L, I, E),
         "w_up_proj": Spec("w_up_proj", (d, L), w, L, d, L, 1),
         "sh_gate": Spec("sh_gate", (S, Is, d), w, d, Is, d, S),
         "sh_up": Spec("sh_up", (S, Is, d), w, d, Is, d, S),
@@ -173,8 +200,18 @@ def draw_params(cfg: Config, name: str, routing: str = "normal"):
         return DYADIC, 2.0 ** -dyadic_router_shift(cfg.d), 8
     if sp.dtype == FP8:
         return NORMAL, FP8_MAX / NORMAL_INT_MAX, 0
+    if sp.dtype == MXFP4:
+        return NORMAL, float(np.float32(MX_CODE_SIGMA / NORMAL_INT_STD)), 0
     sigma = 1.0 if (name == "x" or sp.fan_in == 0) else 1.0 / math.sqrt(sp.fan_in)
     return NORMAL, float(np.float32(sigma / NORMAL_INT_STD)), 0
+
+
+def mx_centre(cfg: Config, name: str) -> int:
+    """Centre E8M0 code of the MXFP4 block scales of `name`: decoded weights
+    then have standard deviation ~ 1/sqrt(fan_in) (within a factor sqrt 2)."""
+    sp = specs(cfg)[name]
+    sigma = 1.0 / math.sqrt(max(sp.fan_in, 1))
+    return 127 + int(round(math.log2(sigma / (MX_CODE_STD * MX_SCALE_RMS))))
 
 
 def scale_base(cfg: Config, name: str) -> float:
@@ -210,6 +247,8 @@ def lib_host():
         lib.synth_bf16_host.restype = ctypes.c_uint16
         lib.synth_e4m3_host.argtypes = [ctypes.c_float]
         lib.synth_e4m3_host.restype = ctypes.c_uint8
+        lib.synth_e2m1_host.argtypes = [ctypes.c_float]
+        lib.synth_e2m1_host.restype = ctypes.c_uint8
         lib.synth_block_scales_host.argtypes = [ctypes.c_void_p, ctypes.c_int64,
                                                 ctypes.c_uint64, ctypes.c_uint32,
                                                 ctypes.c_double]
@@ -243,7 +282,7 @@ def lib_dev():
 
 def host_fill(dtype: int, n: int, seed: int, tid: int, offset: int, kind: int, scale: float,
               rng: int) -> np.ndarray:
-    out = np.empty(n, dtype=NP_STORAGE[dtype])
+    out = np.empty(n, dtype=np.uint8 if dtype == E8M0 else NP_STORAGE[dtype])
     rc = lib_host().synth_fill_host(out.ctypes.data, dtype, n, seed, tid, offset, kind,
                                     scale, rng)
     if rc != 0:
@@ -253,8 +292,9 @@ def host_fill(dtype: int, n: int, seed: int, tid: int, offset: int, kind: int, s
 
 def host_tensor(cfg: Config, name: str, seed: int = 0, routing: str = "normal",
                 start: int = 0, count: Optional[int] = None) -> np.ndarray:
-    """Raw storage (float32 / uint16 bf16 bits / uint8 e4m3 codes) of elements
-    start..start+count of tensor `name`, flat."""
+    """Raw storage (float32 / uint16 bf16 bits / uint8 e4m3 codes / uint8 bytes
+    of two MXFP4 codes) of storage units start..start+count of tensor `name`,
+    flat."""
     sp = specs(cfg)[name]
     if count is None:
         count = sp.numel - start
@@ -266,9 +306,9 @@ def host_matrix(cfg: Config, name: str, index: int = 0, seed: int = 0,
                 routing: str = "normal") -> np.ndarray:
     """Matrix `index` (an expert, a shared expert) of tensor `name`, 2-D raw storage."""
     sp = specs(cfg)[name]
-    n = sp.mat_rows * sp.mat_cols
+    n = sp.mat_units
     return host_tensor(cfg, name, seed, routing, index * n, n).reshape(sp.mat_rows,
-                                                                      sp.mat_cols)
+                                                                      n // sp.mat_rows)
 
 
 def host_rows(cfg: Config, name: str, rows, seed: int = 0, routing: str = "normal"):
@@ -281,8 +321,12 @@ def host_rows(cfg: Config, name: str, rows, seed: int = 0, routing: str = "norma
 
 
 def host_scales(cfg: Config, name: str, seed: int = 0) -> Optional[np.ndarray]:
-    """fp32 block scales [n_mats][rows/128][cols/128] of an fp8 tensor, else None."""
+    """fp32 block scales [n_mats][rows/128][cols/128] of an fp8 tensor, uint8
+    E8M0 codes [n_mats][rows][cols/32] of an MXFP4 tensor, else None."""
     sp = specs(cfg)[name]
+    if sp.dtype == MXFP4:
+        return host_fill(E8M0, sp.n_scale_blocks, seed, SCALE_TID_BASE + TID[name], 0, NORMAL,
+                         0.0, mx_centre(cfg, name)).reshape(sp.scale_shape)
     if sp.dtype != FP8:
         return None
     out = np.empty(sp.n_scale_blocks, dtype=np.float32)
@@ -340,20 +384,29 @@ def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cu
     """Every tensor of the layer generated directly in device memory (torch
     tensors of the raw storage dtype).  Same bits as host_layer()."""
     import torch
-    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8}
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP4: torch.uint8}
     stream = torch.cuda.current_stream().cuda_stream
+
+    def fill(t, dtype, n, tid, kind, scale, rng, what):
+        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()), dtype, n, seed, tid, 0,
+                                         kind, scale, rng, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"synth_fill_device failed ({rc}) for {what}")
+
     out = {}
     for name, sp in specs(cfg).items():
         if names is not None and name not in names:
             continue
         t = torch.empty(sp.shape, dtype=tdt[sp.dtype], device=device)
         kind, scale, rng = draw_params(cfg, name, routing)
-        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()), sp.dtype, sp.numel,
-                                         seed, TID[name], 0, kind, scale, rng,
-                                         ctypes.c_void_p(stream))
-        if rc != 0:
-            raise RuntimeError(f"synth_fill_device failed ({rc}) for {name}")
+        fill(t, sp.dtype, sp.numel, TID[name], kind, scale, rng, name)
         out[name] = t
+        if sp.dtype == MXFP4:
+            sc = torch.empty(sp.scale_shape, dtype=torch.uint8, device=device)
+            fill(sc, E8M0, sp.n_scale_blocks, SCALE_TID_BASE + TID[name], NORMAL, 0.0,
+                 mx_centre(cfg, name), "scale:" + name)
+            out["scale:" + name] = sc
+            continue
         sc = host_scales(cfg, name, seed)
         if sc is not None:
             out["scale:" + name] = torch.from_numpy(sc).to(device)

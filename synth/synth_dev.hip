@@ -17,15 +17,15 @@ __global__ void __launch_bounds__(256) synth_fill_kernel(void *out, int64_t n, u
                                                          int kind, float scale, int32_t range) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    float v = synth_value(seed, tensor_id, (uint64_t)(offset + i), kind, scale, range);
-    if (DT == SYNTH_F32) ((float *)out)[i] = v;
-    else if (DT == SYNTH_BF16) ((uint16_t *)out)[i] = synth_f32_to_bf16(v);
-    else ((uint8_t *)out)[i] = synth_f32_to_e4m3(v);
+    const uint32_t v = synth_unit(DT, seed, tensor_id, (uint64_t)(offset + i), kind, scale, range);
+    if (DT == SYNTH_F32) ((uint32_t *)out)[i] = v;
+    else if (DT == SYNTH_BF16) ((uint16_t *)out)[i] = (uint16_t)v;
+    else ((uint8_t *)out)[i] = (uint8_t)v;
   }
 }
 
 // Device twin of synth_fill_host.  `out` is a device pointer with room for n
-// elements of dtype.  Enqueued on `stream`; returns 0, -1 on a bad argument,
+// storage units of dtype.  Enqueued on `stream`; returns 0, -1 on a bad argument,
 // -1000 - (hipError_t) if the launch failed.
 SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
                                 uint32_t tensor_id, int64_t offset, int kind, float scale,
@@ -35,6 +35,7 @@ SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
   if (!out) return -1;
   if (kind != SYNTH_NORMAL && kind != SYNTH_DYADIC) return -1;
   if (kind == SYNTH_DYADIC && range < 0) return -1;
+  if (dtype == SYNTH_E8M0 && (range < 1 || range > 253)) return -1;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   void (*kern)(void *, int64_t, uint64_t, uint32_t, int64_t, int, float, int32_t);
@@ -42,6 +43,8 @@ SYNTH_API int synth_fill_device(void *out, int dtype, int64_t n, uint64_t seed,
     case SYNTH_F32: kern = synth_fill_kernel<SYNTH_F32>; break;
     case SYNTH_BF16: kern = synth_fill_kernel<SYNTH_BF16>; break;
     case SYNTH_FP8E4M3: kern = synth_fill_kernel<SYNTH_FP8E4M3>; break;
+    case SYNTH_MXFP4: kern = synth_fill_kernel<SYNTH_MXFP4>; break;
+    case SYNTH_E8M0: kern = synth_fill_kernel<SYNTH_E8M0>; break;
     default: return -1;
   }
   // hipLaunchKernel reports this launch's own status (hipGetLastError would

@@ -14,22 +14,24 @@
 
 #define SYNTH_API __attribute__((visibility("default")))
 
-/* Fill out[0..n) with elements offset..offset+n of tensor (seed, tensor_id),
- * encoded as dtype.  kind/scale/range as in synth_value().  Returns 0, or -1
- * on a bad argument. */
+/* Fill out[0..n) with storage units offset..offset+n of tensor (seed,
+ * tensor_id), encoded as dtype (a unit is one element; one byte of two
+ * elements for SYNTH_MXFP4).  kind/scale/range as in synth_unit().  Returns
+ * 0, or -1 on a bad argument. */
 SYNTH_API int synth_fill_host(void *out, int dtype, int64_t n, uint64_t seed,
                               uint32_t tensor_id, int64_t offset, int kind, float scale,
                               int32_t range) {
   if (!out || n < 0 || offset < 0) return -1;
-  if (dtype < SYNTH_F32 || dtype > SYNTH_FP8E4M3) return -1;
+  if (dtype < SYNTH_F32 || dtype > SYNTH_E8M0) return -1;
   if (kind != SYNTH_NORMAL && kind != SYNTH_DYADIC) return -1;
   if (kind == SYNTH_DYADIC && range < 0) return -1;
+  if (dtype == SYNTH_E8M0 && (range < 1 || range > 253)) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
-    float v = synth_value(seed, tensor_id, (uint64_t)(offset + i), kind, scale, range);
-    if (dtype == SYNTH_F32) ((float *)out)[i] = v;
-    else if (dtype == SYNTH_BF16) ((uint16_t *)out)[i] = synth_f32_to_bf16(v);
-    else ((uint8_t *)out)[i] = synth_f32_to_e4m3(v);
+    uint32_t v = synth_unit(dtype, seed, tensor_id, (uint64_t)(offset + i), kind, scale, range);
+    if (dtype == SYNTH_F32) ((uint32_t *)out)[i] = v;
+    else if (dtype == SYNTH_BF16) ((uint16_t *)out)[i] = (uint16_t)v;
+    else ((uint8_t *)out)[i] = (uint8_t)v;
   }
   return 0;
 }
@@ -45,6 +47,7 @@ SYNTH_API int32_t synth_normal_int_host(uint64_t seed, uint32_t tensor_id, uint6
 
 SYNTH_API uint16_t synth_bf16_host(float f) { return synth_f32_to_bf16(f); }
 SYNTH_API uint8_t synth_e4m3_host(float f) { return synth_f32_to_e4m3(f); }
+SYNTH_API uint8_t synth_e2m1_host(float f) { return synth_f32_to_e2m1(f); }
 
 /* Per-block fp32 scales for an fp8 matrix: out[b] = base * (0.75 + 0.5 u_b),
  * u_b uniform in [0,1).  A block scale multiplies every code of its block. */

@@ -5,7 +5,8 @@
  * (synth_host.c, built by gcc) and the device generator (synth_dev.hip,
  * built by hipcc) have in common.  It holds no arithmetic of the MoE layer:
  * only a random-number generator and the encodings of its draws into the
- * storage formats the layer reads (fp32, bf16, fp8 e4m3fn).  Everything is
+ * storage formats the layer reads (fp32, bf16, fp8 e4m3fn, OCP MX FP4 E2M1
+ * with E8M0 block scales).  Everything is
  * integer arithmetic or a single IEEE fp32 multiply, so the host and the
  * device produce bit-identical tensors.
  *
@@ -35,7 +36,10 @@
 #define SYNTH_FN static inline
 #endif
 
-enum { SYNTH_F32 = 0, SYNTH_BF16 = 1, SYNTH_FP8E4M3 = 2 };
+/* SYNTH_MXFP4 fills bytes of two E2M1 codes each: byte i holds tensor
+ * elements 2i (low nibble) and 2i + 1 (high nibble).  SYNTH_E8M0 fills block
+ * scale codes centre + u, u uniform in {-1, 0, 1}. */
+enum { SYNTH_F32 = 0, SYNTH_BF16 = 1, SYNTH_FP8E4M3 = 2, SYNTH_MXFP4 = 3, SYNTH_E8M0 = 4 };
 enum { SYNTH_NORMAL = 0, SYNTH_DYADIC = 1 };
 
 /* sqrt(8 * 4 * (65536^2 - 1) / 12): std of v = 2*sum(8 uniform u16) - 8*65535 */
@@ -142,12 +146,66 @@ SYNTH_FN uint8_t synth_f32_to_e4m3(float f) {
   return (uint8_t)(sign | code);
 }
 
+/* fp32 -> OCP MX FP4 E2M1 code (sign bit 3, exponent bits 2:1 with bias 1,
+ * mantissa bit 0; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or
+ * NaN), round to nearest even, saturating to +-6 (finite inputs). */
+SYNTH_FN uint8_t synth_f32_to_e2m1(float f) {
+  uint32_t u = synth_f32_bits(f);
+  uint32_t sign = (u >> 28) & 0x8u;
+  u &= 0x7FFFFFFFu;
+  if (u == 0u) return (uint8_t)sign;
+  int32_t ex = (int32_t)(u >> 23) - 127;
+  uint32_t code;
+  if (ex > 2) {
+    code = 0x7u; /* 8 and above */
+  } else if (ex < 0) {
+    /* below 1: value = q * 2^-1, q in [0, 2]; q == 2 is code 2 (1.0) */
+    uint32_t m = (u & 0x7FFFFFu) | 0x800000u; /* value = m * 2^(ex-23) */
+    int32_t shift = 22 - ex;                   /* q = m * 2^(ex-22) */
+    if (shift > 25) {
+      code = 0u;
+    } else {
+      uint32_t half = 1u << (shift - 1);
+      code = (m + half - 1u + ((m >> shift) & 1u)) >> shift;
+    }
+  } else {
+    uint32_t m23 = u & 0x7FFFFFu;
+    uint32_t mant = (m23 + 0x1FFFFFu + ((m23 >> 22) & 1u)) >> 22;
+    int32_t eb = ex + 1;
+    if (mant == 2u) { mant = 0u; eb += 1; }
+    code = eb > 3 ? 0x7u : (((uint32_t)eb << 1) | mant);
+  }
+  return (uint8_t)(sign | code);
+}
+
+/* E8M0 block-scale code of draw `index`: centre + u, u uniform in {-1, 0, 1}. */
+SYNTH_FN uint8_t synth_e8m0(uint64_t seed, uint32_t tensor_id, uint64_t index, int32_t centre) {
+  return (uint8_t)(centre + synth_dyadic_int(seed, tensor_id, index, 1));
+}
+
 /* The value of element `index` of a tensor as an fp32 number. */
 SYNTH_FN float synth_value(uint64_t seed, uint32_t tensor_id, uint64_t index, int kind,
                            float scale, int32_t range) {
   if (kind == SYNTH_DYADIC)
     return (float)synth_dyadic_int(seed, tensor_id, index, range) * scale;
   return (float)synth_normal_int(seed, tensor_id, index) * scale;
+}
+
+/* Storage unit i (of a fill starting at unit `offset`) of a tensor of the
+ * given dtype, as raw bits in the low bytes of the result.  kind/scale/range
+ * as in synth_value(); for SYNTH_E8M0, range is the centre code. */
+SYNTH_FN uint32_t synth_unit(int dtype, uint64_t seed, uint32_t tensor_id, uint64_t unit,
+                             int kind, float scale, int32_t range) {
+  if (dtype == SYNTH_E8M0) return synth_e8m0(seed, tensor_id, unit, range);
+  if (dtype == SYNTH_MXFP4) {
+    uint32_t lo = synth_f32_to_e2m1(synth_value(seed, tensor_id, 2 * unit, kind, scale, range));
+    uint32_t hi = synth_f32_to_e2m1(synth_value(seed, tensor_id, 2 * unit + 1, kind, scale, range));
+    return lo | (hi << 4);
+  }
+  float v = synth_value(seed, tensor_id, unit, kind, scale, range);
+  if (dtype == SYNTH_F32) return synth_f32_bits(v);
+  if (dtype == SYNTH_BF16) return synth_f32_to_bf16(v);
+  return synth_f32_to_e4m3(v);
 }
 
 #endif /* SYNTH_RNG_H */

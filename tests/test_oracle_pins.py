@@ -106,6 +106,81 @@ def test_fp8_block_scale_applied_per_block():
         assert oracle.lib().orc_decode(m.ref, 0, r, c) == s
 
 
+def _golden(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        out.append((int(code, 16), float(val)))
+    return out
+
+
+def test_e2m1_decode_matches_ocp_table():
+    table = _golden("e2m1_codes.txt")
+    assert len(table) == 16
+    for code, val in table:
+        got = oracle.e2m1_to_double(code)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(code)
+
+
+def test_e8m0_decode_matches_ocp_table():
+    for code, val in _golden("e8m0_codes.txt"):
+        got = oracle.e8m0_to_double(code)
+        if math.isnan(val):
+            assert math.isnan(got)
+        else:
+            assert got == val, hex(code)
+    # every other code is a power of two, doubling per code
+    for c in range(1, 255):
+        assert oracle.e8m0_to_double(c) == 2 * oracle.e8m0_to_double(c - 1)
+
+
+def _mx_table_decode(codes, e8):
+    """Independent MXFP4 decode for the pins: the golden E2M1 table and the
+    E8M0 doubling rule, element 2i in the low nibble of byte i."""
+    table = np.array([v for _, v in _golden("e2m1_codes.txt")])
+    nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (-1,))
+    sc = np.ldexp(1.0, e8.astype(np.int64) - 127)
+    return table[nib] * np.repeat(sc, 32, axis=-1)
+
+
+def test_mxfp4_nibble_order_and_block_scale():
+    """Element 2i is the low nibble of byte i, 2i+1 the high one; each element
+    takes the E8M0 scale of its own row and 32-wide column block."""
+    rows, cols = 3, 96
+    codes = np.full((rows, cols // 2), 0x72, np.uint8)  # low nibble 1.0, high nibble 6.0
+    e8 = np.array([[120, 127, 130], [1, 200, 126], [127, 127, 128]], np.uint8)
+    m = oracle.Mat(codes, e8)
+    assert m.c.cols == cols and m.c.dtype == oracle.MXFP4
+    for r in range(rows):
+        for c in (0, 1, 30, 31, 32, 33, 63, 64, 95):
+            s = 2.0 ** (int(e8[r, c // 32]) - 127)
+            assert oracle.lib().orc_decode(m.ref, 0, r, c) == (6.0 if c % 2 else 1.0) * s
+
+
+def test_mxfp4_expert_equals_expert_on_decoded_values():
+    """An expert with MXFP4 matrices gives exactly the expert on the same values
+    written out in fp64-exact fp32 (decoded here from the spec tables)."""
+    rng = np.random.default_rng(21)
+    E, L, I = 2, 64, 96
+    def mx(rows, cols):
+        codes = rng.integers(0, 256, size=(E, rows, cols // 2), dtype=np.uint8)
+        e8 = rng.integers(118, 124, size=(E, rows, cols // 32), dtype=np.uint8)
+        return codes, e8
+    (gc, ge), (uc, ue), (dc, de) = mx(I, L), mx(I, L), mx(L, I)
+    x = rng.normal(size=L)
+    s = Shape(latent=L, expert_inter=I)
+    for e in range(E):
+        a = oracle.expert(s, oracle.Mat(gc, ge), oracle.Mat(uc, ue), oracle.Mat(dc, de), x,
+                          index=e)
+        dec = [f32(_mx_table_decode(c[e], sc[e])) for c, sc in ((gc, ge), (uc, ue), (dc, de))]
+        assert all((d.astype(np.float64) == _mx_table_decode(c[e], sc[e])).all()
+                   for d, (c, sc) in zip(dec, ((gc, ge), (uc, ue), (dc, de))))
+        b = oracle.expert(s, *(oracle.Mat(d) for d in dec), x)
+        np.testing.assert_array_equal(a, b)
+
+
 # ---- scalar functions -----------------------------------------------------------------
 
 def test_sigmoid_closed_forms():

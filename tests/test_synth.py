@@ -50,6 +50,52 @@ def test_e4m3_encoding_roundtrip_and_rounding():
     assert enc(460.0) == 0x7E
 
 
+def test_e2m1_encoding_roundtrip_and_rounding():
+    enc = synth.lib_host().synth_e2m1_host
+    vals = [oracle.e2m1_to_double(c) for c in range(16)]
+    for code in range(16):
+        if code == 8:
+            continue  # -0 encodes as 8 too, checked below
+        assert enc(vals[code]) == code, hex(code)
+    assert enc(-0.0) == 8
+    assert enc(100.0) == 7 and enc(-100.0) == 15 and enc(7.0) == 7  # saturating
+    # ties go to the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0,
+    # 2.5 -> 2.0, 3.5 -> 4.0, 5.0 -> 4.0
+    for v, c in ((0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)):
+        assert enc(v) == c and enc(-v) == (c | 8 if c else 8), v
+    # nearest grid point (brute force) for random values
+    rng = np.random.default_rng(3)
+    grid = np.array(vals[:8])
+    for x in np.float32(rng.normal(0, 3, 4000)):
+        d = np.abs(grid - min(abs(float(x)), 6.0))
+        assert enc(float(x)) & 7 == int(np.argmin(d)), x
+
+
+def test_mxfp4_layer_packing_and_scales():
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", n_experts=2, latent=256,
+                                          expert_inter=128)
+    sp = synth.specs(cfg)
+    assert sp["w_gate"].shape == (2, 128, 128) and sp["w_down"].shape == (2, 256, 64)
+    assert sp["w_down_proj"].dtype == synth.BF16 and sp["sh_up"].dtype == synth.BF16
+    codes = synth.host_matrix(cfg, "w_gate", 1)
+    # byte i of the matrix holds draws 2i and 2i + 1 of the tensor, encoded
+    kind, scale, _ = synth.draw_params(cfg, "w_gate")
+    enc = synth.lib_host().synth_e2m1_host
+    off = sp["w_gate"].mat_rows * sp["w_gate"].mat_cols  # first element of expert 1
+    for i in (0, 1, 77, codes.size - 1):
+        lo = synth.lib_host().synth_normal_int_host(0, synth.TID["w_gate"], off + 2 * i)
+        hi = synth.lib_host().synth_normal_int_host(0, synth.TID["w_gate"], off + 2 * i + 1)
+        want = enc(float(np.float32(lo) * np.float32(scale))) | (
+            enc(float(np.float32(hi) * np.float32(scale))) << 4)
+        assert codes.ravel()[i] == want
+    sc = synth.host_scales(cfg, "w_gate")
+    assert sc.dtype == np.uint8 and sc.shape == (2, 128, 8)
+    c = synth.mx_centre(cfg, "w_gate")
+    assert set(np.unique(sc)) == {c - 1, c, c + 1}
+    deq = oracle.decode(codes, sc[1])
+    assert abs(deq.std() * math.sqrt(cfg.latent) - 1.0) < 0.45
+
+
 def test_normal_draw_statistics():
     cfg = synth.CONFIGS["tiny_fp32"]
     x = synth.host_tensor(cfg, "x")
