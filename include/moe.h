@@ -54,7 +54,15 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_FP8E4M3_B128 = 2 /* OCP e4m3fn codes + fp32 scale per 128x128 block */
+  MOE_FP8E4M3_B128 = 2, /* OCP e4m3fn codes + fp32 scale per 128x128 block */
+  /* Routed experts in OCP MX FP4 (OCP Microscaling Formats (MX) Specification
+   * v1.0: E2M1 elements, E8M0 scale, block 32): each [out][in] matrix stored
+   * as [out][in/2] bytes, element 2i of a row in the low nibble of byte i and
+   * 2i+1 in the high nibble, plus uint8 E8M0 codes [out][in/32], one per 32
+   * consecutive elements of a row.  Every other weight is bf16.  The codes
+   * are widened to bf16 (code value * 2^(scale - 127), exact for scale codes
+   * 2..252) and multiplied on the bf16 MFMA. */
+  MOE_MXFP4 = 3
 } moe_dtype;
 
 /* Quantile Balancing cutoff (tech.news18a.com page, third technique): BATCH
@@ -76,14 +84,16 @@ typedef struct moe_config {
   float rms_eps;        /* latent RMSNorm epsilon (1e-6) */
   int32_t act_dtype;    /* x and y: MOE_F32 or MOE_BF16 */
   int32_t weight_dtype; /* W_down_proj, experts, W_up_proj, shared: MOE_F32 (with f32
-                           act), MOE_BF16 or MOE_FP8E4M3_B128 (with bf16 act) */
+                           act), MOE_BF16 or MOE_FP8E4M3_B128 (with bf16 act); or
+                           MOE_MXFP4 (bf16 act): MXFP4 experts, the rest bf16 */
   int32_t router_dtype; /* W_r: equal to act_dtype */
   int32_t cutoff_mode;  /* moe_cutoff_mode */
 } moe_config;
 /* Shape limits: bf16/fp8 paths need d, latent, expert_inter, shared_inter
  * multiples of 64 (of 128 with fp8 weights); latent at most 4096 (2048 with
  * fp32 activations); with fp8 weights d, latent, expert_inter and
- * shared_inter at most 16384; bt * top_k below 2^31; with bf16
+ * shared_inter at most 16384; with MXFP4 experts latent and expert_inter
+ * multiples of 128 and expert_inter at most 4096; bt * top_k below 2^31; with bf16
  * activations the latent activations bt * latent * 2 bytes stay below 4 GiB
  * (bt < 599186 at latent 3584).  Else MOE_ERR_UNSUPPORTED. */
 
@@ -104,6 +114,9 @@ typedef struct moe_weights {
    * block of each [out][in] matrix, laid out [matrices][out/128][in/128]. */
   const float *s_down_proj, *s_gate, *s_up, *s_down, *s_up_proj, *s_sh_gate, *s_sh_up,
       *s_sh_down;
+  /* MOE_MXFP4 only (else NULL): E8M0 codes of the routed experts' matrices,
+   * [E][I][L/32] (gate, up) and [E][L][I/32] (down), 4-byte aligned. */
+  const uint8_t *e8_gate, *e8_up, *e8_down;
 } moe_weights;
 
 /* Router results.  The router "computes scores and indices" (tech.news18a.com

@@ -19,9 +19,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8E4M3_B128 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4 = 0, 1, 2, 3
 CUTOFF_GIVEN, CUTOFF_BATCH = 0, 1
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128, "mxfp4": MOE_MXFP4}
 CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH}
 
 _P = ctypes.c_void_p
@@ -40,7 +40,7 @@ class MoeConfig(ctypes.Structure):
 WEIGHT_FIELDS = ("w_router", "router_bias", "cutoff", "w_down_proj", "w_gate", "w_up",
                  "w_down", "latent_gamma", "w_up_proj", "sh_gate", "sh_up", "sh_down",
                  "s_down_proj", "s_gate", "s_up", "s_down", "s_up_proj", "s_sh_gate",
-                 "s_sh_up", "s_sh_down")
+                 "s_sh_up", "s_sh_down", "e8_gate", "e8_up", "e8_down")
 
 
 class MoeWeights(ctypes.Structure):

@@ -38,6 +38,7 @@ int64_t elem_size(int32_t dt) {
     case MOE_F32: return 4;
     case MOE_BF16: return 2;
     case MOE_FP8E4M3_B128: return 1;
+    case MOE_MXFP4: return 2;  // the dense weights of an MXFP4 layer are bf16
   }
   return 0;
 }
@@ -45,6 +46,8 @@ int64_t elem_size(int32_t dt) {
 struct Plan {
   int path = PATH_BF16;
   bool fp8 = false;
+  int dense_wf = WF_BF16;   // weight format of the dense GEMMs
+  int expert_wf = WF_BF16;  // and of the routed experts' GEMMs
   int64_t act_bytes = 2;
   // byte offsets into the workspace
   size_t z, zT, alpha, idx, w, w_sorted, counts, offsets, tile_offsets, perm, inv_perm, masks,
@@ -76,6 +79,11 @@ moe_status check_config(const moe_config *c) {
   const int64_t q = c->weight_dtype == MOE_FP8E4M3_B128 ? 128 : 64;
   if (c->d % 64 || c->latent % q || c->expert_inter % q || (c->n_shared && c->shared_inter % q))
     return MOE_ERR_UNSUPPORTED;
+  // MXFP4 experts: K ranges (latent, expert_inter) of whole 128-element groups
+  // (a dword of E8M0 codes), with the codes of a B row (K/32 <= 128) in LDS
+  if (c->weight_dtype == MOE_MXFP4 &&
+      (c->latent % 128 || c->expert_inter % 128 || c->expert_inter > 4096))
+    return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
   // fp8 GEMMs stage the block scales of up to 128 K blocks in LDS
   if (c->weight_dtype == MOE_FP8E4M3_B128 &&
@@ -93,6 +101,8 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   if (bt * c->top_k > INT32_MAX || bt > INT32_MAX / 64) return MOE_ERR_UNSUPPORTED;
   p->path = c->act_dtype == MOE_F32 ? PATH_F32 : PATH_BF16;
   p->fp8 = c->weight_dtype == MOE_FP8E4M3_B128;
+  p->dense_wf = p->fp8 ? WF_FP8 : WF_BF16;
+  p->expert_wf = c->weight_dtype == MOE_MXFP4 ? WF_MX4 : p->dense_wf;
   p->act_bytes = elem_size(c->act_dtype);
   const int64_t E = c->n_experts, k = c->top_k, P = bt * k, L = c->latent;
   // the bf16 engine addresses gathered x_lat rows with 32-bit byte offsets
@@ -156,6 +166,11 @@ bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts)
   if (c->weight_dtype == MOE_FP8E4M3_B128) {
     if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
     if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;
+  }
+  if (c->weight_dtype == MOE_MXFP4) {
+    // E8M0 codes are copied a dword at a time
+    for (const uint8_t *e8 : {w->e8_gate, w->e8_up, w->e8_down})
+      if (!e8 || reinterpret_cast<uintptr_t>(e8) % 4) return false;
   }
   return true;
 }
@@ -242,7 +257,7 @@ moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, c
   const int bm = gemm_bm(p.path);
   {
     PhaseScope ph(PH_ROUTER, s);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_ROUTER, false, (bt + bm - 1) / bm, s));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_ROUTER, WF_BF16, (bt + bm - 1) / bm, s));
   }
   const float *alpha;
   {
@@ -406,6 +421,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   const int64_t I = cfg->expert_inter, S = cfg->n_shared, Is = cfg->shared_inter;
   const int bm = gemm_bm(p.path);
   const bool fp8 = p.fp8;
+  const int dwf = p.dense_wf, ewf = p.expert_wf;
   const int64_t dense_mt = (bt + bm - 1) / bm;
 
   // ---- second stream: x_lat = x W_down_proj^T, then the shared experts' gate/up -----
@@ -433,7 +449,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.out = xlat;
     a.ldo = L;
     PhaseScope ph(PH_DOWN_PROJ, side);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, side));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, dwf, dense_mt, side));
   }
   if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_lat, ss));
   void *hs = at<void>(ws, p.hs);
@@ -450,7 +466,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.out = hs;
     a.ldo = S * Is;
     PhaseScope ph(PH_SHARED, side);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, fp8, dense_mt, side));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, dwf, dense_mt, side));
   }
   if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_sh, ss));
 
@@ -470,7 +486,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   float *w_sorted = at<float>(ws, p.w_sorted);
   {
     PhaseScope ph(PH_DISPATCH, s);
-    MOE_TRY_HIP(launch_dispatch(idx, wts, bt, k, E, grouped_tile_rows(p.path, fp8, P, E),
+    MOE_TRY_HIP(launch_dispatch(idx, wts, bt, k, E, grouped_tile_rows(p.path, ewf, P, E),
                                 at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
                                 inv_perm, w_sorted, s));
   }
@@ -492,14 +508,16 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.tile_offsets = tile_offsets;
     a.n_experts = (int32_t)E;
     a.b_estride = I * L;
-    a.s_estride = fp8 ? (I / 128) * (L / 128) : 0;
+    a.s_estride = fp8 ? (I / 128) * (L / 128) : ewf == WF_MX4 ? I * (L / 32) : 0;
+    a.e8 = w->e8_gate;
+    a.e8_up = w->e8_up;
     a.gather = perm;
     a.gather_div = (int32_t)k;
     a.row_scale = w_sorted;  // h rows carry the routing weight: W_d (w h) = w (W_d h)
     a.out = h;
     a.ldo = I;
     PhaseScope ph(PH_EXPERT_GATEUP, s);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, fp8, grouped_mt, s));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, ewf, grouped_mt, s));
   }
   {
     GemmArgs a = base_args(cfg);
@@ -511,11 +529,12 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.tile_offsets = tile_offsets;
     a.n_experts = (int32_t)E;
     a.b_estride = L * I;
-    a.s_estride = fp8 ? (L / 128) * (I / 128) : 0;
+    a.s_estride = fp8 ? (L / 128) * (I / 128) : ewf == WF_MX4 ? L * (I / 32) : 0;
+    a.e8 = w->e8_down;
     a.out = o;
     a.ldo = L;
     PhaseScope ph(PH_EXPERT_DOWN, s);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_DOWN, fp8, grouped_mt, s));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_DOWN, ewf, grouped_mt, s));
   }
 
   // ---- combine + latent RMSNorm -------------------------------------------------------
@@ -554,7 +573,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.out = y;
     a.ldo = d;
     PhaseScope ph(PH_OUTPUT, s);
-    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, fp8, dense_mt, s));
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, dwf, dense_mt, s));
   }
   return MOE_OK;
 }

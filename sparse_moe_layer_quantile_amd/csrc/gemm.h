@@ -8,7 +8,7 @@
 //   dual       B = (gate, up) pair, the epilogue applies SiTU-GLU
 //   segmented  K split over up to three (A, B) pairs: [n | hs] x [W_up | W_ds,j]
 // and two inner engines: bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16, B in
-// bf16 or fp8 e4m3 with 128x128 block scales) and fp32 SIMT.
+// bf16, fp8 e4m3 with 128x128 block scales, or MXFP4) and fp32 SIMT.
 #pragma once
 
 #include "common.h"
@@ -37,6 +37,9 @@ struct GemmArgs {
   int32_t n_experts;
   int64_t b_estride;         // elements between consecutive experts' B matrices
   int64_t s_estride;         // block scales between consecutive experts
+  // MXFP4 B: E8M0 codes [rows][k/32] of seg[0].b and of b_up (expert 0; 4-byte
+  // aligned); consecutive experts s_estride codes apart
+  const uint8_t *e8, *e8_up;
   const int32_t *gather;     // A row of position p = gather[p] / gather_div
   int32_t gather_div;
   void *out;

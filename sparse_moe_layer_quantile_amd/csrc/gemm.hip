@@ -1,12 +1,17 @@
 // gemm.hip -- dispatch of the layer's contractions to the GEMM engines (see
-// gemm.h): tile shape per kind, the direct-to-LDS engine (gemm_dma_*.hip), the
-// register-staged fp8 kernel for the K-segmented output projection, fp32 SIMT.
+// gemm.h): tile shape per kind, the direct-to-LDS engine (gemm_dma_*.hip; bf16,
+// fp8 and MXFP4 weights), the register-staged fp8 kernel for K ranges past the
+// engine's scale table, fp32 SIMT.
 #include <algorithm>
 #include <cstdlib>
 
 #include "gemm_launch.h"
 
 namespace moe {
+
+static_assert((int)WF_BF16 == g2::BF_BF16 && (int)WF_FP8 == g2::BF_FP8 &&
+                  (int)WF_MX4 == g2::BF_MX4,
+              "weight format codes");
 
 int gemm_bm(int path) { return path == PATH_F32 ? sf::BM : mf::BM; }
 int gemm_bn_out(int path, bool dual) {
@@ -45,24 +50,37 @@ int dma_variant(GemmKind kind, int64_t rows, int64_t n_experts) {
                      : rows <= 200 * n_experts ? kVGroupedShort
                                                : kVGrouped;
     const int v = env_int("MOE_GEMM_GROUPED", dflt);
-    return (v >= 0 && v < kNumDma) ? v : dflt;
+    return (v >= 0 && v < kNumDmaBf16) ? v : dflt;
   }
   const int dflt = rows <= 64 ? kVSmallM : kVDense;
   const int v = env_int("MOE_GEMM_DENSE", dflt);
-  return (v >= 0 && v < kNumDma) ? v : dflt;
+  return (v >= 0 && v < kNumDmaBf16) ? v : dflt;
 }
 
-int grouped_tile_rows(int path, bool fp8, int64_t rows, int64_t n_experts) {
+int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts) {
   if (path == PATH_F32) return sf::BM;
   const int v = dma_variant(GK_EXPERT_SITU, rows, n_experts);
+  // the MXFP4 engine's shapes (launch_dma_b4)
+  if (wf == WF_MX4) return kDma[mx4_variant(v)].tm();
   // the fp8 engine's shapes (launch_dma_b8)
-  if (fp8 && v != kVGrouped && v != kVGroupedShort && v != kVSmallM) return kDma[kVDense].tm();
+  if (wf == WF_FP8 && v != kVGrouped && v != kVGroupedShort && v != kVSmallM)
+    return kDma[kVDense].tm();
   return kDma[v].tm();
 }
 
 // The contractions of the layer, by kind.
-hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int64_t m_tiles,
+hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64_t m_tiles,
                        hipStream_t s) {
+  if (path == PATH_BF16 && wf == WF_MX4) {
+    // MXFP4 weights: the routed experts only
+    const int v = dma_variant(kind, a.M, a.n_experts);
+    switch (kind) {
+      case GK_EXPERT_SITU: return launch_dma_b4<EPI_SITU, true, true, uint16_t>(v, a, s);
+      case GK_EXPERT_DOWN: return launch_dma_b4<EPI_STORE, false, false, uint16_t>(v, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const bool fp8 = wf == WF_FP8;
   if (path == PATH_BF16 && !fp8) {
     const int v = dma_variant(kind, a.M, a.n_experts);
     switch (kind) {

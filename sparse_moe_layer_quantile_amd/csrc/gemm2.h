@@ -1,7 +1,11 @@
 // gemm2.h -- bf16 MFMA GEMM engine with direct-to-LDS loads.
 //
 // Same problem description as gemm.h (GemmArgs: dense / grouped / gathered /
-// dual gate-up / K-segmented), for bf16 operands.  Tile TM x TN x BK with
+// dual gate-up / K-segmented), for bf16 A operands and B in one of three
+// formats (BFmt): bf16; fp8 e4m3 with 128 x 128 block scales; OCP MX FP4
+// (E2M1 codes, two per byte, with an E8M0 scale per 32 K elements of a row).
+// Quantised B tiles travel to LDS as stored and are widened to bf16 in
+// registers, times their scale, just before the MFMA.  Tile TM x TN x BK with
 // TM = WM * SUBM * 32 A rows, TN = WN * FRN * 32 B rows and BK = 32 or 64;
 // WM x WN waves, each wave SUBM x FRN blocks of
 // v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC workgroups per CU.
@@ -89,6 +93,28 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float
   return r;
 }
 
+// Eight E2M1 codes (element 2i in the low nibble of byte i) times an E8M0
+// block scale, as bf16: the B operand of one bf16 MFMA.  The gfx950
+// conversion of byte b puts its low nibble's value in bits 15:0 and its high
+// nibble's in bits 31:16, times the scale; with power-of-two scales that keep
+// the products in bf16's normal range every result is exact.  The four packed
+// words are moved as 32-bit values (no per-element extraction).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w, float s) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  u32x4 v;
+  v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t word_of(const uint4 &v) {
+  static_assert(W >= 0 && W < 4, "four words");
+  return W == 0 ? v.x : W == 1 ? v.y : W == 2 ? v.z : v.w;
+}
+
 // One dword per lane: lane l's 4 bytes land at lds_wave_base + 4 l.
 __device__ __forceinline__ void dma4(const void *g, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(g),
@@ -155,26 +181,36 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
   return t;
 }
 
+// Storage format of the B operand.
+enum BFmt { BF_BF16 = 0, BF_FP8 = 1, BF_MX4 = 2 };
+
 // fp8 B operands: block scales of up to this many 128-wide K blocks (K <= 16384)
 constexpr int kMaxKBlocks = 128;
+// MXFP4 B operands: E8M0 codes of up to this many 32-wide K blocks per row (K <= 4096)
+constexpr int kMaxK32 = 128;
 
 // Extra LDS of a kernel instance past its stage ring: the per-row factors of a
-// SiTU epilogue, and the block scales of an fp8 B tile ([TN/128][kMaxKBlocks]).
-template <int EPI, int TM, int TN, bool B8>
+// SiTU epilogue, and the block scales of the B tile over the whole K range
+// (fp8: [TN/128][kMaxKBlocks] floats; MXFP4: [TN][kMaxK32] E8M0 codes).
+template <int EPI, int TM, int TN, int BF>
 constexpr int extra_lds_bytes() {
-  return (EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0) + (B8 ? TN / 128 * kMaxKBlocks * 4 : 0);
+  return (EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0) +
+         (BF == BF_FP8 ? TN / 128 * kMaxKBlocks * 4 : BF == BF_MX4 ? TN * kMaxK32 : 0);
 }
 
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
-          bool GATHER, bool MSEG, bool B8, typename OutT>
+          bool GATHER, bool MSEG, int BF, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
   constexpr int RB = BK * 2;          // bytes per A tile row
   constexpr int CPR = RB / 16;        // 16 B chunks per A row
   constexpr int RPI = 1024 / RB;      // A rows per DMA wave instruction
-  // B is bf16, or fp8 e4m3 with 128 x 128 block scales (B8)
-  constexpr int ESZ_B = B8 ? 1 : 2;   // bytes per B element
-  constexpr int RB_B = BK * ESZ_B;    // bytes per B tile row
+  // B is bf16, fp8 e4m3 with 128 x 128 block scales (B8), or MXFP4 (MX4)
+  constexpr bool B8 = BF == BF_FP8, MX4 = BF == BF_MX4;
+  constexpr int ESZ_B = B8 ? 1 : 2;   // bytes per B element (bf16, fp8)
+  // B bytes of n elements: n * BNUM / BDEN
+  constexpr int BNUM = MX4 ? 1 : ESZ_B, BDEN = MX4 ? 2 : 1;
+  constexpr int RB_B = BK * BNUM / BDEN;  // bytes per B tile row
   constexpr int CPR_B = RB_B / 16;
   constexpr int RPI_B = 1024 / RB_B;
   constexpr int TM = WM * SUBM * 32, TN = WN * FRN * 32;
@@ -182,6 +218,9 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB_B;
   static_assert(!B8 || (BK == 64 && TN_OUT % 128 == 0),
                 "fp8 B: K tile 64, whole 128-row scale blocks");
+  // MXFP4 B: a lane's 16-byte read of a B row holds 32 codes, one E8M0 block
+  static_assert(!MX4 || (BK == 64 && !MSEG && TN % 64 == 0),
+                "MXFP4 B: K tile 64, single segment");
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -264,6 +303,28 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
   }
 
+  // ---- MXFP4 B: E8M0 codes of this tile's B rows over the whole K range -------
+  // mx_lds[r][kb], r = B tile row (dual: gate rows, then up rows), kb = 32-wide
+  // K block; K/32 codes a row, copied a dword per lane (rows are contiguous in
+  // the tensor, K/32 is a multiple of 4)
+  uint8_t *mx_lds = reinterpret_cast<uint8_t *>(sc_lds);
+  const int kb32 = MX4 ? (int)(args.seg[0].k / 32) : 0;
+  if constexpr (MX4) {
+    const int wpr = kb32 / 4;  // dwords a row
+    const int total = TN * wpr;
+    const uint8_t *e8g = args.e8 + (int64_t)tile.e * args.s_estride;
+    const uint8_t *e8u = DUAL ? args.e8_up + (int64_t)tile.e * args.s_estride : e8g;
+    for (int q = wave; q * 64 < total; q += NW) {
+      const int i0 = q * 64 + lane;
+      const int i = i0 < total ? i0 : 0;  // past the table: loaded, never used
+      const int rr = i / wpr, w4 = i - rr * wpr;
+      const bool up = DUAL && rr >= TN / 2;
+      int64_t n = tile.n0 + (up ? rr - TN / 2 : rr);
+      if (n >= args.N) n = tile.n0;  // rows past N: never stored
+      dma4((up ? e8u : e8g) + n * kb32 + 4 * w4, mx_lds + q * 256);
+    }
+  }
+
   // the last instruction slot of this wave carries an instruction
   const bool has_last = EVEN || wave + NW * (LMAX - 1) < TT;
 
@@ -289,12 +350,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   }
   // B chunk of a segmented problem's lanes (same argument as for A)
   const int fetch_chunk_b = (lane % CPR_B) ^ ((((wave * RPI_B) + lane / CPR_B) / (16 / CPR_B)) % CPR_B);
+  // (segmented problems are dense: no expert offset)
   const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
-  const uint16_t *bu = static_cast<const uint16_t *>(args.b_up);
-  if (args.offsets != nullptr) {
-    b0 += (int64_t)tile.e * args.b_estride;
-    if (DUAL) bu += (int64_t)tile.e * args.b_estride;
-  }
   // chunk a lane of a segmented problem fetches so that the DMA slot order
   // realises the swizzle: instruction i of the wave fills region rows
   // (wave + NW i) RPI + rsub, whose swizzle key (4 (wave + NW i) + rsub /
@@ -356,7 +413,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
-      dma16(cur_b + ((int64_t)b_row[i] * cur_ldb + (int64_t)cur_k * BK) * ESZ_B + fetch_chunk_b * 16,
+      dma16(cur_b + ((int64_t)b_row[i] * cur_ldb + (int64_t)cur_k * BK) * BNUM / BDEN + fetch_chunk_b * 16,
             st + A_BYTES + (wave + NW * i) * 1024);
     ++cur_k;
   };
@@ -395,11 +452,11 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     const char *bsrc = static_cast<const char *>(args.seg[0].b);
     const char *busrc = static_cast<const char *>(args.b_up);
     if (args.offsets != nullptr) {
-      bsrc += (int64_t)tile.e * args.b_estride * ESZ_B;
-      if (DUAL) busrc += (int64_t)tile.e * args.b_estride * ESZ_B;
+      bsrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
+      if (DUAL) busrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
     }
-    b_base = bsrc + (tile.n0 * cur_ldb + kb0) * ESZ_B;
-    if constexpr (DUAL) bu_base = busrc + (tile.n0 * cur_ldb + kb0) * ESZ_B;
+    b_base = bsrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
+    if constexpr (DUAL) bu_base = busrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
 #pragma unroll
     for (int d = 0; d < LMAX; ++d) {
       const int g = wave + NW * d;
@@ -423,7 +480,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         const int ch = (lane % CPR_B) ^ ((rb / (16 / CPR_B)) % CPR_B);
         int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
         if (n >= args.N) n = tile.n0;
-        o = (uint32_t)((n - tile.n0) * cur_ldb * ESZ_B + ch * 16);
+        o = (uint32_t)((n - tile.n0) * cur_ldb * BNUM / BDEN + ch * 16);
       }
       off[d] = o;
     }
@@ -461,8 +518,13 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     constexpr int f = decltype(f_tag)::value;
     // k order of a step: lane half h takes k 8h..8h+8 of the step's 16; with
     // fp8 B, steps 2p and 2p+1 take the two halves of chunk 2p + h instead
-    // (one 16-byte B read per lane per two steps; A follows the same order)
-    const int chunk = B8 ? 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1) : ks * 2 + (lane >> 5);
+    // (one 16-byte B read per lane per two steps); with MXFP4 B, the four
+    // steps of a 64-wide K tile take the four quarters of K range 32h..32h+32
+    // (one 16-byte read, one E8M0 block per lane per tile).  A follows the
+    // same order.
+    const int chunk = B8 ? 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1)
+                      : MX4 ? 4 * (lane >> 5) + ks
+                            : ks * 2 + (lane >> 5);
     int r;
     const char *base;
     if constexpr (f < FRN) {
@@ -488,7 +550,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     else
       return (wn * FRN + j) * 32 + (lane & 31);
   };
-  // fp8 B: the 16 codes of fragment j for the k-step pair p (chunk 2p + h)
+  // quantised B: 16 bytes of fragment j's row at chunk 2p + h -- fp8: the codes
+  // of k-step pair p; MXFP4 (p = 0): the 32 codes of the whole K tile
   auto read_b8 = [&](const char *st, int p, auto j_tag, uint4 *raw) G2_INL {
     constexpr int j = decltype(j_tag)::value;
     const int r = b_row_of(j_tag);
@@ -500,6 +563,13 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   auto scale_b8 = [&](int kt, auto j_tag) G2_INL {
     const int rb = b_row_of(j_tag) - (lane & 31);
     return sc_lds[(rb / 128) * kblocks + ((k_begin + kt) * BK) / 128];
+  };
+  // MXFP4 B: E8M0 scale of this lane's row and K block (32 h of K tile kt) for
+  // fragment j, as an fp32 power of two (codes 1..254)
+  auto scale_b4 = [&](int kt, auto j_tag) G2_INL {
+    const int r = b_row_of(j_tag);
+    const uint32_t e = mx_lds[r * kb32 + (k_begin + kt) * 2 + (lane >> 5)];
+    return __uint_as_float(e << 23);
   };
   // K loop for NS active sub-blocks.  Single-segment problems run one
   // straight-line schedule per stage: MFMAs one at a time, with the fragment
@@ -531,9 +601,21 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst); });
         } else {
           bf16x8 fa[2][NA], fb[2][FRN];
-          uint4 braw[B8 ? FRN : 1];
-          float bsc[B8 ? FRN : 1];
-          if constexpr (B8) {
+          uint4 braw[B8 || MX4 ? FRN : 1];
+          float bsc[B8 || MX4 ? FRN : 1];
+          if constexpr (MX4) {
+            // the codes of all four k steps of the tile, one read per fragment
+            static_for<FRN>([&](auto j) G2_INL {
+              bsc[j] = scale_b4(kt, j);
+              read_b8(st, 0, j, braw);
+            });
+            static_for<NF>([&](auto f) G2_INL {
+              if constexpr (f >= FRN) read_frag(st, 0, f, fa[0], fb[0]);
+            });
+            static_for<FRN>([&](auto j) G2_INL {
+              fb[0][j] = e2m1x8_to_bf16(braw[j].x, bsc[j]);
+            });
+          } else if constexpr (B8) {
             static_for<FRN>([&](auto j) G2_INL {
               bsc[j] = scale_b8(kt, j);
               read_b8(st, 0, j, braw);
@@ -561,7 +643,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                   constexpr int f = decltype(f_tag)::value;
                   constexpr bool mine = NF <= Q ? (f == q) : (f >= q * NF / Q && f < (q + 1) * NF / Q);
                   if constexpr (mine) {
-                    if constexpr (B8 && f < FRN) {
+                    if constexpr (MX4 && f < FRN) {
+                      // MXFP4 B: widen the next step's codes (already in registers)
+                      fb[(S + 1) & 1][f] = e2m1x8_to_bf16(word_of<S + 1>(braw[f]), bsc[f]);
+                    } else if constexpr (B8 && f < FRN) {
                       // fp8 B: an even step reads the pair's codes, an odd step
                       // converts the upper half read one step earlier
                       if constexpr ((S + 1) % 2 == 0) read_b8(st, (S + 1) / 2, f_tag, braw);

@@ -23,14 +23,18 @@ struct DmaShape {
   constexpr int threads() const { return 64 * wm * wn; }
   constexpr int tm() const { return wm * subm * 32; }
   constexpr int tn() const { return wn * frn * 32; }
-  // stage ring: bf16 A rows, and B rows of bf16 (b8 = false) or fp8 codes
-  constexpr size_t lds(bool b8 = false) const {
-    return (size_t)stages * (tm() * bk * 2 + tn() * bk * (b8 ? 1 : 2));
+  // bytes of a B tile row in format bf (g2::BFmt): bf16, fp8 codes, MXFP4 bytes
+  static constexpr int b_row_bytes(int bk, int bf) {
+    return bf == g2::BF_FP8 ? bk : bf == g2::BF_MX4 ? bk / 2 : bk * 2;
+  }
+  // stage ring: bf16 A rows and B rows
+  constexpr size_t lds(int bf = g2::BF_BF16) const {
+    return (size_t)stages * (tm() * bk * 2 + tn() * b_row_bytes(bk, bf));
   }
   // every wave issues whole rounds of A and of B DMA instructions (1 KB each)
-  constexpr bool whole_rounds(bool b8 = false) const {
+  constexpr bool whole_rounds(int bf = g2::BF_BF16) const {
     return (tm() / (512 / bk)) % (wm * wn) == 0 &&
-           (tn() / ((b8 ? 1024 : 512) / bk)) % (wm * wn) == 0;
+           (tn() / (1024 / b_row_bytes(bk, bf))) % (wm * wn) == 0;
   }
 };
 constexpr DmaShape kDma[] = {
@@ -41,17 +45,21 @@ constexpr DmaShape kDma[] = {
     // measured alternatives (slower on the K3 shapes), kept for tuning
     {2, 4, 5, 2, 32, 4, 1},  // 4: 320 x 256, 8 waves, BK 32, 4 stages (144 KB)
     {1, 4, 5, 2, 64, 3, 1},  // 5: 160 x 256, 4 waves, BK 64, 3 stages (156 KB)
+    // MXFP4 B (a quarter of the bf16 B bytes a stage): a deeper ring keeps as
+    // many weight bytes in flight when a few rows stream the weights
+    {1, 4, 1, 2, 64, 8, 1},  // 6: 32 x 256, 4 waves, BK 64, 8 stages (96 KB + 32 KB scales)
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
-constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3;
+constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
+constexpr int kNumDmaBf16 = 6;  // shapes 0..5 fit bf16 B
 
-template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, bool B8, typename OutT>
+template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
 hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   constexpr DmaShape sh = kDma[V];
   auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, EPI,
-                                  DUAL, GATHER, MSEG, B8, OutT>;
-  constexpr size_t lds = sh.lds(B8) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), B8>();
+                                  DUAL, GATHER, MSEG, BF, OutT>;
+  constexpr size_t lds = sh.lds(BF) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), BF>();
   static_assert(lds <= 160 * 1024, "LDS of a gfx950 workgroup");
   static bool attr_set = false;
   if (!attr_set) {
@@ -99,23 +107,40 @@ template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, typename OutT>
 hipError_t launch_dma_v(const GemmArgs &a, hipStream_t s) {
   // K-segmented problems need whole DMA rounds per wave: else the 256 x 256 shape
   if constexpr (MSEG && !kDma[V].whole_rounds())
-    return launch_dma_impl<kVDense, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
+    return launch_dma_impl<kVDense, EPI, DUAL, GATHER, MSEG, g2::BF_BF16, OutT>(a, s);
   else
-    return launch_dma_impl<V, EPI, DUAL, GATHER, MSEG, false, OutT>(a, s);
+    return launch_dma_impl<V, EPI, DUAL, GATHER, MSEG, g2::BF_BF16, OutT>(a, s);
 }
 
 // fp8 e4m3 B with block scales: the default shapes; other requests take the
 // dense one
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
 hipError_t launch_dma_b8(int v, const GemmArgs &a, hipStream_t s) {
-  static_assert(!MSEG || kDma[kVDense].whole_rounds(true), "segmented fp8 shape");
-  if constexpr (MSEG) return launch_dma_impl<kVDense, EPI, DUAL, GATHER, true, true, OutT>(a, s);
+  constexpr int F = g2::BF_FP8;
+  static_assert(!MSEG || kDma[kVDense].whole_rounds(F), "segmented fp8 shape");
+  if constexpr (MSEG) return launch_dma_impl<kVDense, EPI, DUAL, GATHER, true, F, OutT>(a, s);
   switch (v) {
-    case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+    case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVGroupedShort:
-      return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, true, OutT>(a, s);
-    case kVSmallM: return launch_dma_impl<kVSmallM, EPI, DUAL, GATHER, false, true, OutT>(a, s);
-    default: return launch_dma_impl<kVDense, EPI, DUAL, GATHER, false, true, OutT>(a, s);
+      return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVSmallM: return launch_dma_impl<kVSmallM, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    default: return launch_dma_impl<kVDense, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+  }
+}
+
+// MXFP4 B (routed experts): the shape for a requested variant (the grouped
+// ones, and a deeper-ring small-M shape); other requests take the short
+// grouped shape
+constexpr int mx4_variant(int v) {
+  return v == kVGrouped ? kVGrouped : v == kVSmallM ? kVSmallMX4 : kVGroupedShort;
+}
+template <int EPI, bool DUAL, bool GATHER, typename OutT>
+hipError_t launch_dma_b4(int v, const GemmArgs &a, hipStream_t s) {
+  constexpr int F = g2::BF_MX4;
+  switch (mx4_variant(v)) {
+    case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVSmallMX4: return launch_dma_impl<kVSmallMX4, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    default: return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, F, OutT>(a, s);
   }
 }
 
@@ -150,5 +175,11 @@ MOE_DMA_KINDS(MOE_DMA_EXTERN)
 #define MOE_B8_EXTERN(E, D, G, T, M) \
   extern template hipError_t launch_dma_b8<E, D, G, T, M>(int, const GemmArgs &, hipStream_t);
 MOE_B8_KINDS(MOE_B8_EXTERN)
+#define MOE_B4_KINDS(X)                     \
+  X(EPI_STORE, false, false, uint16_t)      \
+  X(EPI_SITU, true, true, uint16_t)
+#define MOE_B4_EXTERN(E, D, G, T) \
+  extern template hipError_t launch_dma_b4<E, D, G, T>(int, const GemmArgs &, hipStream_t);
+MOE_B4_KINDS(MOE_B4_EXTERN)
 
 }  // namespace moe

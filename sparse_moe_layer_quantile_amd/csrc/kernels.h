@@ -20,13 +20,15 @@ enum GemmKind {
 };
 
 int gemm_bm(int path);
-// Rows per M tile of the grouped expert GEMMs (the dispatch lays out the
-// per-expert tile list with it).
+// Storage format of a GEMM's weights (B operand): bf16 (fp32 on the fp32
+// path), fp8 e4m3 with 128 x 128 block scales, MXFP4 with E8M0 scales per 32.
+enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2 };
 // M-tile rows of the grouped GEMMs for rows (token, expert) pairs over
-// n_experts experts (the dispatch lays its tile table out in these units).
-int grouped_tile_rows(int path, bool fp8, int64_t rows, int64_t n_experts);
+// n_experts experts with weights in format wf (the dispatch lays its tile
+// table out in these units).
+int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts);
 int gemm_bn_out(int path, bool dual);
-hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, bool fp8, int64_t m_tiles,
+hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64_t m_tiles,
                        hipStream_t s);
 
 // ---- routing ------------------------------------------------------------------

@@ -109,6 +109,15 @@ CONFIGS: Dict[str, Config] = {
     "k3_prefill_fp8": Config("k3_prefill_fp8", bt=8192, d=7168, latent=3584, n_experts=896,
                              top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
                              weight="fp8", router="bf16", cutoff="batch"),
+    # the routed experts in MXFP4 (E2M1 codes, E8M0 scale per 32 inputs), as the
+    # released checkpoint stores them; every other weight bf16
+    "k3_decode_mxfp4": Config("k3_decode_mxfp4", bt=64, d=7168, latent=3584, n_experts=896,
+                              top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
+                              weight="mxfp4", cutoff="given"),
+    "k3_prefill_mxfp4": Config("k3_prefill_mxfp4", bt=16384, d=7168, latent=3584,
+                               n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                               shared_inter=3072, weight="mxfp4", bias="zipf1.1",
+                               cutoff="batch"),
     # one GPU's share of K3 prefill under 8-way expert parallelism: its own 16384 tokens
     # through the replicated dense parts, and 262144 pairs over its 112 experts
     # (about 2341 rows per expert), so the grouped GEMMs run at the sharded shape

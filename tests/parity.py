@@ -7,7 +7,9 @@ Comparison rules:
     sigmoid(z - alpha) within TIE_BAND, and such tokens are logged.
   * floating-point outputs: normwise max relative error
     max|y - y_ref| / max|y_ref| within TOL[dtype] (bf16 2e-2, fp8-weight 6e-2,
-    fp32 1e-4), on the tokens whose routing matches.
+    fp32 1e-4), on the tokens whose routing matches.  MXFP4 experts take the
+    bf16 bound: their weights widen to bf16 exactly, so the arithmetic and its
+    roundings are those of the bf16 path.
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ ABI_NAME = {"w_router": "w_router", "router_bias": "router_bias", "w_down_proj":
 SCALE_ABI = {"w_down_proj": "s_down_proj", "w_gate": "s_gate", "w_up": "s_up",
              "w_down": "s_down", "w_up_proj": "s_up_proj", "sh_gate": "s_sh_gate",
              "sh_up": "s_sh_up", "sh_down": "s_sh_down"}
+MX_ABI = {"w_gate": "e8_gate", "w_up": "e8_up", "w_down": "e8_down"}
 
 
 def tol_of(cfg) -> float:
@@ -55,7 +58,8 @@ def device_layer(cfg, seed=0, routing="normal", cutoff=None, alpha=None, names=N
         if k == "x" or v is None:
             continue
         if k.startswith("scale:"):
-            t[SCALE_ABI[k[6:]]] = v
+            mx = cfg.weight == "mxfp4" and k[6:] in MX_ABI
+            t[(MX_ABI if mx else SCALE_ABI)[k[6:]]] = v
         else:
             t[ABI_NAME[k]] = v
     if alpha is not None:

@@ -84,6 +84,16 @@ def test_k3_prefill_fp8_weights():
     _run_k3("k3_prefill_fp8", n_sample=10)
 
 
+def test_k3_decode_mxfp4_experts():
+    """K3 decode with the routed experts in MXFP4 (the weight format of the
+    released checkpoint), every token checked."""
+    _run_k3("k3_decode_mxfp4", n_sample=64)
+
+
+def test_k3_prefill_mxfp4_experts():
+    _run_k3("k3_prefill_mxfp4", n_sample=10)
+
+
 def test_k3_expert_parallel_share():
     """One GPU's share of 8-way expert parallelism: 112 experts with about 2341
     rows each, so every expert spans several M tiles of the grouped GEMMs."""

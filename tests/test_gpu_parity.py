@@ -164,6 +164,32 @@ def test_forward_fp8_weights_mid(bt, cutoff):
     assert err <= parity.tol_of(cfg)
 
 
+@pytest.mark.parametrize("bt,cutoff,shape", [(4096, "batch", None), (64, "given", None),
+                                             (100, "batch", None), (300, "batch", (640, 384))])
+def test_forward_mxfp4_experts_mid(bt, cutoff, shape):
+    """MXFP4 routed experts (E2M1 codes, E8M0 scales per 32) at the mid shapes:
+    the prefill-sized batch runs the 320-row grouped tiles, the 64-token one
+    the 32-row tiles with the deep ring, the others the 192-row tiles; the
+    last case has a partial N tile in the down GEMM (latent 640) and K ranges
+    of 20 and 12 scale blocks."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", bt=bt)
+    if shape is not None:
+        cfg = cfg.with_(latent=shape[0], expert_inter=shape[1])
+    say("forward mxfp4", bt, cutoff, cfg.latent, cfg.expert_inter)
+    layer, x = parity.device_layer(cfg, seed=0, cutoff=cutoff)
+    y, r = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(cfg, synth.host_layer(cfg, 0),
+                         cutoff=oracle.BATCH if cutoff == "batch" else oracle.GIVEN)
+    diff, bad = parity.routing_mismatches(parity.to_np(r["idx"]), ref["idx"], ref["z32"],
+                                          ref["zeta"])
+    assert not bad
+    keep = np.setdiff1d(np.arange(cfg.bt), diff)
+    err = parity.normwise_err(parity.y_to_f64(y)[keep], ref["y"][keep])
+    say(f"  normwise err {err:.3e} (tol {parity.tol_of(cfg)}), near ties {len(diff)}")
+    assert err <= parity.tol_of(cfg)
+
+
 # ---- edge cases ----------------------------------------------------------------------------
 
 def _small_forward_check(cfg, cutoff, seed=0, alpha=None, routing="normal"):
