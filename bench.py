@@ -36,14 +36,20 @@ def phase_work(cfg, touched: int) -> dict:
     """Algorithmic FLOPs and HBM bytes of each phase of one forward.
 
     Bytes count each operand once: weights actually needed (every touched
-    expert once), activations in, results out."""
+    expert once), activations in, results out.  MXFP4 experts count half a
+    byte per weight plus one E8M0 byte per 32 weights; the dense weights of
+    such a layer are bf16."""
     bt, d, L, E, k = cfg.bt, cfg.d, cfg.latent, cfg.n_experts, cfg.top_k
     I, S, Is = cfg.expert_inter, cfg.n_shared, cfg.shared_inter
     P = bt * k
     ab = 4 if cfg.act == "f32" else 2
-    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2}[cfg.weight]
     rb = {"f32": 4, "bf16": 2}[cfg.router]
     sc = (lambda r, c: (r // 128) * (c // 128) * 4) if cfg.weight == "fp8" else (lambda r, c: 0)
+    if cfg.weight == "mxfp4":
+        xw = lambda r, c: r * c // 2 + r * (c // 32)  # an expert matrix, codes + scales
+    else:
+        xw = lambda r, c: r * c * wb + sc(r, c)
     batch = cfg.cutoff == "batch"
     return {
         "shared_gateup": (2 * bt * d * 2 * S * Is,
@@ -53,9 +59,8 @@ def phase_work(cfg, touched: int) -> dict:
         "topk": (0, bt * E * 4 + P * 8),
         "dispatch": (0, P * 4 + P * 8),
         "down_proj": (2 * bt * d * L, bt * d * ab + L * d * wb + sc(L, d) + bt * L * ab),
-        "expert_gateup": (2 * P * 2 * L * I,
-                          touched * 2 * (I * L * wb + sc(I, L)) + bt * L * ab + P * I * ab),
-        "expert_down": (2 * P * L * I, touched * (L * I * wb + sc(L, I)) + P * I * ab + P * L * ab),
+        "expert_gateup": (2 * P * 2 * L * I, touched * 2 * xw(I, L) + bt * L * ab + P * I * ab),
+        "expert_down": (2 * P * L * I, touched * xw(L, I) + P * I * ab + P * L * ab),
         "combine_norm": (0, P * L * ab + bt * L * ab),
         "output": (2 * bt * (L + S * Is) * d,
                    bt * (L + S * Is) * ab + d * (L + S * Is) * wb + sc(d, L) + S * sc(d, Is)
@@ -281,8 +286,9 @@ def main(argv=None):
         "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": layer_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                   "experts_touched": touched,
-                  "weight_gb": sum(sp.nbytes for n, sp in synth.specs(cfg).items() if n != "x")
-                  / 1e9},
+                  "weight_gb": sum(sp.nbytes + (sp.n_scale_blocks * (1 if sp.dtype == synth.MXFP4 else 4)
+                                                if sp.dtype in (synth.FP8, synth.MXFP4) else 0)
+                                   for n, sp in synth.specs(cfg).items() if n != "x") / 1e9},
         "phases_ms": {n: round(v[0], 4) for n, v in phases.items()},
         "kernel_sources": kernel_source_hash(),
         "cpu_baseline": None,

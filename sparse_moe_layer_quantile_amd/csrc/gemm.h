@@ -48,8 +48,9 @@ struct GemmArgs {
   const float *bias;         // router: [N] (may be NULL)
   const float *row_scale;    // SiTU: factor of output row m (NULL = 1)
   float beta, inv_beta, beta_u, inv_beta_u;
-  int32_t n_tiles_n;
+  int32_t n_tiles_n;         // N tiles (direct-to-LDS engine: groups of nper N tiles)
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
+  int32_t nper;              // direct-to-LDS short tiles: N tiles a workgroup runs in turn
   // split K (dense bf16 problems with few tiles): K tile range blockIdx.y of
   // ksplit; raw fp32 sums go to partial[split][M][ldp] (a dual problem's up
   // sums at column N + c) and a second kernel reduces them and applies the

@@ -61,7 +61,7 @@ int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts) {
   if (path == PATH_F32) return sf::BM;
   const int v = dma_variant(GK_EXPERT_SITU, rows, n_experts);
   // the MXFP4 engine's shapes (launch_dma_b4)
-  if (wf == WF_MX4) return kDma[mx4_variant(v)].tm();
+  if (wf == WF_MX4) return kDma[mx4_shape(v, rows, n_experts)].tm();
   // the fp8 engine's shapes (launch_dma_b8)
   if (wf == WF_FP8 && v != kVGrouped && v != kVGroupedShort && v != kVSmallM)
     return kDma[kVDense].tm();
@@ -73,7 +73,7 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64
                        hipStream_t s) {
   if (path == PATH_BF16 && wf == WF_MX4) {
     // MXFP4 weights: the routed experts only
-    const int v = dma_variant(kind, a.M, a.n_experts);
+    const int v = mx4_shape(dma_variant(kind, a.M, a.n_experts), a.M, a.n_experts);
     switch (kind) {
       case GK_EXPERT_SITU: return launch_dma_b4<EPI_SITU, true, true, uint16_t>(v, a, s);
       case GK_EXPERT_DOWN: return launch_dma_b4<EPI_STORE, false, false, uint16_t>(v, a, s);

@@ -6,14 +6,15 @@
 // (E2M1 codes, two per byte, with an E8M0 scale per 32 K elements of a row).
 // Quantised B tiles travel to LDS as stored and are widened to bf16 in
 // registers, times their scale, just before the MFMA.  Tile TM x TN x BK with
-// TM = WM * SUBM * 32 A rows, TN = WN * FRN * 32 B rows and BK = 32 or 64;
+// TM = WM * SUBM * 32 A rows (or MA < 32 rows, see below), TN = WN * FRN * 32
+// B rows and BK = 32 or 64;
 // WM x WN waves, each wave SUBM x FRN blocks of
 // v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC workgroups per CU.
 //
 //  * Global -> LDS with global_load_lds_dwordx4 (gfx950): no staging
 //    registers; each wave instruction fills 1 KB = RPI tile rows of 2 BK
 //    bytes (CPR 16 B chunks each).  Rows are XOR-swizzled on chunks,
-//    slot = chunk ^ ((row / (16 / CPR)) % CPR), which puts the 16 rows an
+//    slot = chunk ^ swz(row, CPR) (swz below), which puts the 16 rows an
 //    MFMA operand read touches per 16 lanes on 16 distinct 16 B bank groups.
 //    The DMA writes lane l at slot l % CPR, so lane l fetches the global
 //    chunk that belongs there.
@@ -31,6 +32,11 @@
 //  * Single-segment problems address every DMA from a uniform base with a
 //    32-bit per-lane offset, which keeps the address registers at one VGPR
 //    per load instruction.
+//  * Short tiles (MA > 0, one wave row of one sub-block): a tile holds MA < 32
+//    rows and stages only those in LDS; the MFMA's 32 rows read them modulo
+//    MA, and the rows past MA, never stored, are discarded.  When a few rows
+//    stream a large weight matrix (decode), the LDS then goes to a deeper
+//    ring of B tiles, i.e. more weight bytes in flight.
 #pragma once
 
 #include <type_traits>
@@ -44,6 +50,14 @@
 
 namespace moe {
 namespace g2 {
+
+// Swizzle key of tile row `row` with cpr 16-byte chunks a row: rows shorter
+// than 256 bytes share a 256-byte bank line 16 / cpr at a time, and each
+// group of them takes its own XOR key; rows of 256 bytes or more start on
+// bank group 0 and take key row % 16.
+__device__ __forceinline__ constexpr int swz(int row, int cpr) {
+  return cpr >= 16 ? row % 16 : (row / (16 / cpr)) % cpr;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -122,6 +136,36 @@ __device__ __forceinline__ void dma4(const void *g, void *lds_wave_base) {
                                    4, 0, 0);
 }
 
+// The same direct-to-LDS loads written out in assembly (uniform base in
+// SGPRs plus a 32-bit lane offset; a per-lane 64-bit address).  They return
+// nothing to registers, and the compiler's wait-count pass does not see them:
+// with the builtin it must assume that an LDS read may hit the bytes of any
+// load still in flight, and where it cannot prove otherwise (the quantised-B
+// operand reads) it drains every load (vmcnt(0)) before the read, which
+// undoes the ring.  The kernels order these loads themselves: wait_vmcnt
+// before a stage is read and before the workgroup ends, and a barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void *lds) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+}
+__device__ __forceinline__ void dma16_asm(const char *sbase, uint32_t voff, void *lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_sb_asm(const char *sbase, uint32_t voff, void *lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_asm(const void *g, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+
 // Tile coordinates.  The tile list (M tiles x N tiles) is cut into 8
 // contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so all N
 // tiles of an M tile -- which share its A rows -- stay in one L2.  Inside a
@@ -168,7 +212,7 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
     r = lin - first_m * nt;
   }
   const int64_t mt = first_m + r % gm;
-  t.n0 = (r / gm) * TN_OUT;
+  t.n0 = (r / gm) * TN_OUT * (a.nper > 1 ? a.nper : 1);
   t.e = e;
   if (!grouped) {
     t.m0 = mt * TM;
@@ -191,17 +235,19 @@ constexpr int kMaxK32 = 128;
 
 // Extra LDS of a kernel instance past its stage ring: the per-row factors of a
 // SiTU epilogue, and the block scales of the B tile over the whole K range
-// (fp8: [TN/128][kMaxKBlocks] floats; MXFP4: [TN][kMaxK32] E8M0 codes).
-template <int EPI, int TM, int TN, int BF>
+// (fp8: [TN/128][kMaxKBlocks] floats; MXFP4 with K tiles of 64: [TN][kMaxK32]
+// E8M0 codes -- wider K tiles carry their codes in the stage instead).
+template <int EPI, int TM, int TN, int BF, int BK>
 constexpr int extra_lds_bytes() {
   return (EPI == EPI_SITU ? (TM + 63) / 64 * 64 * 4 : 0) +
-         (BF == BF_FP8 ? TN / 128 * kMaxKBlocks * 4 : BF == BF_MX4 ? TN * kMaxK32 : 0);
+         (BF == BF_FP8 ? TN / 128 * kMaxKBlocks * 4
+                       : (BF == BF_MX4 && BK < 128) ? TN * kMaxK32 : 0);
 }
 
-template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int EPI, bool DUAL,
-          bool GATHER, bool MSEG, int BF, typename OutT>
+template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int MA, int EPI,
+          bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
-  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
+  static_assert(BK == 32 || BK == 64 || BK == 128 || BK == 256, "K tile of 32 to 256");
   constexpr int RB = BK * 2;          // bytes per A tile row
   constexpr int CPR = RB / 16;        // 16 B chunks per A row
   constexpr int RPI = 1024 / RB;      // A rows per DMA wave instruction
@@ -213,25 +259,39 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   constexpr int RB_B = BK * BNUM / BDEN;  // bytes per B tile row
   constexpr int CPR_B = RB_B / 16;
   constexpr int RPI_B = 1024 / RB_B;
-  constexpr int TM = WM * SUBM * 32, TN = WN * FRN * 32;
+  constexpr int TM = MA > 0 ? MA : WM * SUBM * 32, TN = WN * FRN * 32;
+  static_assert(MA == 0 || (WM == 1 && SUBM == 1 && 32 % MA == 0 && MA % RPI == 0 && !MSEG),
+                "short tiles: one 32-row MFMA block over MA staged rows");
   constexpr int TN_OUT = DUAL ? TN / 2 : TN;
   constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB_B;
   static_assert(!B8 || (BK == 64 && TN_OUT % 128 == 0),
                 "fp8 B: K tile 64, whole 128-row scale blocks");
   // MXFP4 B: a lane's 16-byte read of a B row holds 32 codes, one E8M0 block
-  static_assert(!MX4 || (BK == 64 && !MSEG && TN % 64 == 0),
-                "MXFP4 B: K tile 64, single segment");
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static_assert(!MX4 || (BK >= 64 && !MSEG && TN % 64 == 0),
+                "MXFP4 B: K tile of 64 or more, single segment");
   constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  // MXFP4 with K tiles of 128 or more: the E8M0 codes of a tile's B rows
+  // (SPR bytes a row) travel with the tile, after its B rows, copied a dword a
+  // lane: LS instructions of 256 bytes a wave a tile, besides the operand
+  // ones.  K tiles of 64 (2 bytes a row) take a whole-K table loaded up front.
+  constexpr bool MXS = MX4 && BK >= 128;
+  constexpr int SPR = MXS ? BK / 32 : 0;
+  constexpr int S_BYTES = TN * SPR;
+  constexpr int LS = S_BYTES / 256 / NW;
+  static_assert(S_BYTES == LS * NW * 256, "whole scale instructions for every wave");
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
   // A stage is TA + TB wave instructions of 1 KB each (A rows, then B rows,
   // in LDS order).  Instruction g is issued by wave g % NW as its (g / NW)-th,
-  // so a wave issues LMAX or LMAX - 1 of them per stage.
+  // so a wave issues LMAX or LMAX - 1 of them per stage (plus LS scale ones).
   constexpr int TA = TM / RPI, TB = TN / RPI_B, TT = TA + TB;
   constexpr int LMAX = (TT + NW - 1) / NW;
   constexpr bool EVEN = TT % NW == 0;
   static_assert(TM % RPI == 0 && TN % RPI_B == 0, "whole DMA rows");
   static_assert(!DUAL || (TN / 2) % RPI_B == 0, "gate/up split on a DMA instruction");
+  static_assert(!DUAL || !MXS || (TN / 2) % (256 / SPR) == 0,
+                "gate/up split on a scale instruction");
+  static_assert(LMAX + LS < 64 / (STAGES > 2 ? STAGES - 2 : 1), "vmcnt range");
   // multi-segment problems keep whole A and B rounds per wave
   constexpr int A_LD = TA / NW, B_LD = TB / NW;
   static_assert(!MSEG || (TA % NW == 0 && TB % NW == 0), "segmented: whole DMA rounds");
@@ -258,7 +318,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       for (int q = wave; q < (TM + 63) / 64; q += NW) {
         int64_t m = tile.m0 + q * 64 + lane;
         if (m >= tile.m_end) m = tile.m0;  // loaded, never used
-        dma4(args.row_scale + m, rs_lds + q * 64);
+        if constexpr (BF == BF_BF16) dma4(args.row_scale + m, rs_lds + q * 64);
+        else dma4_asm(args.row_scale + m, rs_lds + q * 64);
       }
     }
   }
@@ -299,7 +360,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       if (nb >= nblocks) nb = nblocks - 1;  // rows past N: never stored
       const float *sp = (up ? args.bscale_up : args.seg[0].bscale) +
                         (int64_t)tile.e * args.s_estride + nb * kblocks + kb;
-      dma4(sp, sc_lds + q * 64);
+      dma4_asm(sp, sc_lds + q * 64);
     }
   }
 
@@ -307,9 +368,14 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // mx_lds[r][kb], r = B tile row (dual: gate rows, then up rows), kb = 32-wide
   // K block; K/32 codes a row, copied a dword per lane (rows are contiguous in
   // the tensor, K/32 is a multiple of 4)
+  // Persistent N tiles (short tiles with bf16 or in-stage-scaled MXFP4 B): a
+  // workgroup runs nper consecutive N tiles of its M tile, one ring over all
+  // of their K tiles, storing each N tile's outputs inside the loop
+  constexpr bool PN = MA > 0 && !B8 && !MSEG && EPI != EPI_ROUTER && (!MX4 || MXS);
+  const int nper = PN ? max((int)args.nper, 1) : 1;
   uint8_t *mx_lds = reinterpret_cast<uint8_t *>(sc_lds);
   const int kb32 = MX4 ? (int)(args.seg[0].k / 32) : 0;
-  if constexpr (MX4) {
+  if constexpr (MX4 && !MXS) {
     const int wpr = kb32 / 4;  // dwords a row
     const int total = TN * wpr;
     const uint8_t *e8g = args.e8 + (int64_t)tile.e * args.s_estride;
@@ -321,7 +387,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       const bool up = DUAL && rr >= TN / 2;
       int64_t n = tile.n0 + (up ? rr - TN / 2 : rr);
       if (n >= args.N) n = tile.n0;  // rows past N: never stored
-      dma4((up ? e8u : e8g) + n * kb32 + 4 * w4, mx_lds + q * 256);
+      dma4_asm((up ? e8u : e8g) + n * kb32 + 4 * w4, mx_lds + q * 256);
     }
   }
 
@@ -349,14 +415,15 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
   }
   // B chunk of a segmented problem's lanes (same argument as for A)
-  const int fetch_chunk_b = (lane % CPR_B) ^ ((((wave * RPI_B) + lane / CPR_B) / (16 / CPR_B)) % CPR_B);
+  const int fetch_chunk_b = (lane % CPR_B) ^ swz(wave * RPI_B + lane / CPR_B, CPR_B);
   // (segmented problems are dense: no expert offset)
   const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
   // chunk a lane of a segmented problem fetches so that the DMA slot order
   // realises the swizzle: instruction i of the wave fills region rows
   // (wave + NW i) RPI + rsub, whose swizzle key (4 (wave + NW i) + rsub /
   // (16 / CPR)) % CPR does not depend on i (CPR divides 4 NW)
-  const int fetch_chunk = slot ^ ((((wave * RPI) + rsub) / (16 / CPR)) % CPR);
+  static_assert(!MSEG || CPR <= 16, "segmented problems: K tile up to 64");
+  const int fetch_chunk = slot ^ swz(wave * RPI + rsub, CPR);
 
   // ---- K segments -------------------------------------------------------------
   int ktiles = (int)(args.seg[0].k / BK);
@@ -469,7 +536,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       // and fetches the chunk that the swizzle puts there
       if (g < TA) {
         const int r = g * RPI + lane / CPR;
-        const int ch = (lane % CPR) ^ ((r / (16 / CPR)) % CPR);
+        const int ch = (lane % CPR) ^ swz(r, CPR);
         int64_t m = tile.m0 + r;
         if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
         if constexpr (GATHER) m = args.gather[m] / args.gather_div;
@@ -477,7 +544,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       } else if (g < TT) {
         // B rows from TN/2 on are the up rows of a dual problem
         const int rb = (g - TA) * RPI_B + lane / CPR_B;
-        const int ch = (lane % CPR_B) ^ ((rb / (16 / CPR_B)) % CPR_B);
+        const int ch = (lane % CPR_B) ^ swz(rb, CPR_B);
         int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
         if (n >= args.N) n = tile.n0;
         o = (uint32_t)((n - tile.n0) * cur_ldb * BNUM / BDEN + ch * 16);
@@ -485,30 +552,70 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       off[d] = o;
     }
   }
+  // MXFP4 scale instructions of this wave: instruction gs = wave + NW q fills
+  // bytes 256 gs.. of the stage's code area; lane l copies dword w of the
+  // codes of tile row rr (the B row numbering: dual up rows from TN/2), from
+  // a uniform base (gate or up codes of this expert, from this split's first
+  // K block) plus a 32-bit lane offset
+  uint32_t soff[MXS ? LS : 1];
+  uint64_t sbase[MXS ? LS : 1];
+  if constexpr (MXS) {
+#pragma unroll
+    for (int q = 0; q < LS; ++q) {
+      const int gs = wave + NW * q;
+      const int i = gs * 64 + lane;
+      const int rr = i / (SPR / 4), w = i % (SPR / 4);
+      const bool up = DUAL && gs * 64 / (SPR / 4) >= TN / 2;
+      int64_t n = tile.n0 + (up ? rr - TN / 2 : rr);
+      if (n >= args.N) n = tile.n0;
+      soff[q] = (uint32_t)(n * kb32 + 4 * w);
+      sbase[q] = reinterpret_cast<uint64_t>((up ? args.e8_up : args.e8) +
+                                            (int64_t)tile.e * args.s_estride +
+                                            (int64_t)k_begin * BK / 32);
+    }
+  }
+  // B bytes from one N tile to the next (persistent N tiles)
+  const int64_t nstep_b = PN ? (int64_t)TN_OUT * cur_ldb * BNUM / BDEN : 0;
   // DMA instruction slot d of this wave (instruction g = wave + NW d) of K
-  // tile kt into stage st.
-  auto dma_one = [&](auto d_tag, int kt, int st) G2_INL {
+  // tile kt of N tile jn (persistent N tiles; else 0) into stage st.
+  auto dma_one = [&](auto d_tag, int kt, int st, int jn) G2_INL {
     constexpr int d = decltype(d_tag)::value;
     if constexpr (!EVEN && d == LMAX - 1) {
       if (!has_last) return;
     }
     const int g = wave + NW * d;
     const char *base = reinterpret_cast<const char *>(dbase[d]);
-    // the empty asm re-issues the 32-bit offset inside the loop body, so the
-    // instruction selector sees uniform base + zext(offset) there (SGPR-base
-    // form) instead of a 64-bit address hoisted out of the loop
+    // (builtin form: the empty asm re-issues the 32-bit offset inside the loop
+    // body, so the instruction selector sees uniform base + zext(offset) there
+    // (SGPR-base form) instead of a 64-bit address hoisted out of the loop)
     uint32_t o = off[d];
-    asm volatile("" : "+v"(o));
-    const int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
-    dma16(base + kb + o, smem + st * STAGE_BYTES + g * 1024);
+    int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
+    if constexpr (PN) kb += g < TA ? 0 : jn * nstep_b;
+    if constexpr (BF != BF_BF16) {
+      dma16_asm(base + kb, o, smem + st * STAGE_BYTES + g * 1024);
+    } else {
+      asm volatile("" : "+v"(o));
+      dma16(base + kb + o, smem + st * STAGE_BYTES + g * 1024);
+    }
+  };
+  // the MXFP4 scale instructions of K tile kt of N tile jn into stage st
+  auto dma_scales = [&](int kt, int st, int jn) G2_INL {
+    if constexpr (MXS) {
+#pragma unroll
+      for (int q = 0; q < LS; ++q)
+        dma4_sb_asm(reinterpret_cast<const char *>(sbase[q]) + (int64_t)kt * SPR +
+                        (PN ? (int64_t)jn * TN_OUT * kb32 : 0),
+                    soff[q],
+                    smem + st * STAGE_BYTES + A_BYTES + B_BYTES + (wave + NW * q) * 256);
+    }
   };
   // "tile kt landed": this wave's loads of later tiles may still be in flight
   auto wait_tile = [&]() G2_INL {
     if constexpr (EVEN) {
-      wait_vmcnt<LMAX * (STAGES - 2)>();
+      wait_vmcnt<(LMAX + LS) * (STAGES - 2)>();
     } else {
-      if (has_last) wait_vmcnt<LMAX * (STAGES - 2)>();
-      else wait_vmcnt<(LMAX - 1) * (STAGES - 2)>();
+      if (has_last) wait_vmcnt<(LMAX + LS) * (STAGES - 2)>();
+      else wait_vmcnt<(LMAX - 1 + LS) * (STAGES - 2)>();
     }
   };
 
@@ -518,12 +625,12 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     constexpr int f = decltype(f_tag)::value;
     // k order of a step: lane half h takes k 8h..8h+8 of the step's 16; with
     // fp8 B, steps 2p and 2p+1 take the two halves of chunk 2p + h instead
-    // (one 16-byte B read per lane per two steps); with MXFP4 B, the four
-    // steps of a 64-wide K tile take the four quarters of K range 32h..32h+32
-    // (one 16-byte read, one E8M0 block per lane per tile).  A follows the
-    // same order.
+    // (one 16-byte B read per lane per two steps); with MXFP4 B, steps 4g ..
+    // 4g+3 take the four quarters of K range 64g + 32h ..+32 (B chunk 2g + h:
+    // one 16-byte read and one E8M0 block per lane per four steps).  A follows
+    // the same order.
     const int chunk = B8 ? 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1)
-                      : MX4 ? 4 * (lane >> 5) + ks
+                      : MX4 ? 8 * (ks >> 2) + 4 * (lane >> 5) + (ks & 3)
                             : ks * 2 + (lane >> 5);
     int r;
     const char *base;
@@ -534,10 +641,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       else r = (wn * FRN + j) * 32 + (lane & 31);
       base = st + A_BYTES;
     } else {
-      r = ((f - FRN) * WM + wm) * 32 + (lane & 31);
+      r = MA > 0 ? (lane & 31) % MA : ((f - FRN) * WM + wm) * 32 + (lane & 31);
       base = st;
     }
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ ((r / (16 / CPR)) % CPR)) << 4));
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ swz(r, CPR)) << 4));
     if constexpr (f < FRN) bfr[f] = v;
     else af[f - FRN] = v;
   };
@@ -551,26 +658,105 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       return (wn * FRN + j) * 32 + (lane & 31);
   };
   // quantised B: 16 bytes of fragment j's row at chunk 2p + h -- fp8: the codes
-  // of k-step pair p; MXFP4 (p = 0): the 32 codes of the whole K tile
+  // of k-step pair p; MXFP4: the 32 codes of k-step group p (steps 4p..4p+3)
   auto read_b8 = [&](const char *st, int p, auto j_tag, uint4 *raw) G2_INL {
     constexpr int j = decltype(j_tag)::value;
     const int r = b_row_of(j_tag);
     const int chunk = 2 * p + (lane >> 5);
-    raw[j] = *reinterpret_cast<const uint4 *>(st + A_BYTES + r * RB_B +
-                                              ((chunk ^ ((r / (16 / CPR_B)) % CPR_B)) << 4));
+    // (read with the operand type of the bf16 reads: the compiler then keeps
+    // its LDS accesses independent of the DMA writes in flight, as for those)
+    raw[j] = __builtin_bit_cast(uint4, *reinterpret_cast<const bf16x8 *>(
+                                           st + A_BYTES + r * RB_B + ((chunk ^ swz(r, CPR_B)) << 4)));
   };
   // fp8 B: block scale of fragment j for K tile kt (uniform per wave)
   auto scale_b8 = [&](int kt, auto j_tag) G2_INL {
     const int rb = b_row_of(j_tag) - (lane & 31);
     return sc_lds[(rb / 128) * kblocks + ((k_begin + kt) * BK) / 128];
   };
-  // MXFP4 B: E8M0 scale of this lane's row and K block (32 h of K tile kt) for
-  // fragment j, as an fp32 power of two (codes 1..254)
-  auto scale_b4 = [&](int kt, auto j_tag) G2_INL {
+  // MXFP4 B: E8M0 scale of this lane's row and K block (chunk 2g + h of K tile
+  // kt, in stage st) for fragment j, as an fp32 power of two (codes 1..254)
+  auto scale_b4 = [&](const char *st, int kt, int g, auto j_tag) G2_INL {
     const int r = b_row_of(j_tag);
-    const uint32_t e = mx_lds[r * kb32 + (k_begin + kt) * 2 + (lane >> 5)];
+    uint32_t e;
+    if constexpr (MXS)
+      e = *reinterpret_cast<const uint8_t *>(st + A_BYTES + B_BYTES + r * SPR + 2 * g +
+                                             (lane >> 5));
+    else
+      e = mx_lds[r * kb32 + (k_begin + kt) * (BK / 32) + 2 * g + (lane >> 5)];
     return __uint_as_float(e << 23);
   };
+  // ---- stores of the output tile at columns n0.. (the epilogue; with
+  // persistent N tiles also called inside the K loop): lane holds column
+  // (lane & 31), rows 8(r/4) + 4(lane/32) + r%4 of each 32 x 32 block.  Row
+  // quantities are formed once per row, column ones once per block column;
+  // the SiTU row factors come from LDS.
+  constexpr int JN = DUAL ? FRN / 2 : FRN;  // output block columns of this wave
+  auto store_tile = [&](int64_t n0) G2_INL {
+    int64_t col[JN];
+    bool col_ok[JN];
+    float bias[JN];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+      col[j] = n0 + (wn * JN + j) * 32 + (lane & 31);
+      col_ok[j] = col[j] < args.N;
+      bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
+    }
+    OutT *out = static_cast<OutT *>(args.out);
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i) {
+      if (i >= sub_valid) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = tile.m0 + rr;
+        if (row >= tile.m_end) continue;
+        OutT *orow = out + row * args.ldo;
+        if constexpr (EPI == EPI_SITU) {
+          const float f = use_rs ? rs_lds[rr] : 1.0f;
+#pragma unroll
+          for (int j = 0; j < JN; ++j)
+            if (col_ok[j])
+              store_out<OutT>(orow, col[j],
+                              f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
+                                       args.inv_beta, args.beta_u, args.inv_beta_u));
+        } else if constexpr (EPI == EPI_ROUTER) {
+#pragma unroll
+          for (int j = 0; j < JN; ++j)
+            if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < JN; ++j)
+            if (col_ok[j]) store_out<OutT>(orow, col[j], acc[i][j][r]);
+        }
+      }
+    }
+    if constexpr (EPI == EPI_ROUTER) {
+      if (args.out_t != nullptr) {
+#pragma unroll
+        for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+          for (int j = 0; j < FRN; ++j) {
+            const int64_t c = col[j];
+            if (!col_ok[j]) continue;
+            const float b = bias[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t row0 = tile.m0 + (i * WM + wm) * 32 + 8 * q + 4 * (lane >> 5);
+              float *dst = args.out_t + c * args.M + row0;
+              if (row0 + 3 < tile.m_end && (args.M & 3) == 0) {
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(acc[i][j][q * 4 + 0] + b, acc[i][j][q * 4 + 1] + b,
+                                acc[i][j][q * 4 + 2] + b, acc[i][j][q * 4 + 3] + b);
+              } else {
+                for (int u = 0; u < 4; ++u)
+                  if (row0 + u < tile.m_end) dst[u] = acc[i][j][q * 4 + u] + b;
+              }
+            }
+          }
+      }
+    }
+  };
+
   // K loop for NS active sub-blocks.  Single-segment problems run one
   // straight-line schedule per stage: MFMAs one at a time, with the fragment
   // reads of the next k step and the DMA instructions of the tile STAGES - 1
@@ -585,28 +771,40 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     constexpr int NF = NS + FRN;  // fragment reads per k step
     constexpr int Q = NS * FRN;   // MFMAs per k step
     if constexpr (!MSEG) {
+      // tile t of the T = nper ktiles of this workgroup: N tile t / ktiles,
+      // K tile t % ktiles
+      const int T = nper * ktiles;
 #pragma unroll
       for (int p = 0; p < STAGES - 1; ++p) {
-        const int kp = p < ktiles ? p : ktiles - 1;
-        static_for<L>([&](auto d) G2_INL { dma_one(d, kp, p); });
+        const int tp = p < T ? p : T - 1;
+        const int jp = PN ? tp / ktiles : 0;
+        static_for<L>([&](auto d) G2_INL { dma_one(d, tp - jp * ktiles, p, jp); });
+        dma_scales(tp - jp * ktiles, p, jp);
       }
-      for (int kt = 0; kt < ktiles; ++kt) {
+      int kt = 0, jn = 0;  // K tile and N tile of t
+      for (int t = 0; t < T; ++t) {
         wait_tile();
         barrier();
-        const char *st = smem + (kt % STAGES) * STAGE_BYTES;
-        const int kd = kt + STAGES - 1;
-        const int kdc = kd < ktiles ? kd : ktiles - 1;
+        const char *st = smem + (t % STAGES) * STAGE_BYTES;
+        const int kd = t + STAGES - 1;
+        const int kdt = kd < T ? kd : T - 1;
+        const int dj = PN ? kdt / ktiles : 0;
+        const int kdc = kdt - dj * ktiles;
         const int dst = kd % STAGES;
         if constexpr (NS == 0) {
-          static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst); });
+          static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst, dj); });
+          dma_scales(kdc, dst, dj);
         } else {
           bf16x8 fa[2][NA], fb[2][FRN];
           uint4 braw[B8 || MX4 ? FRN : 1];
           float bsc[B8 || MX4 ? FRN : 1];
+          // MXFP4: codes and scale of the next group of four k steps
+          uint4 braw2[MX4 && KS > 4 ? FRN : 1];
+          float bsc2[MX4 && KS > 4 ? FRN : 1];
           if constexpr (MX4) {
-            // the codes of all four k steps of the tile, one read per fragment
+            // the codes of the first four k steps, one read per fragment
             static_for<FRN>([&](auto j) G2_INL {
-              bsc[j] = scale_b4(kt, j);
+              bsc[j] = scale_b4(st, kt, 0, j);
               read_b8(st, 0, j, braw);
             });
             static_for<NF>([&](auto f) G2_INL {
@@ -644,8 +842,23 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                   constexpr bool mine = NF <= Q ? (f == q) : (f >= q * NF / Q && f < (q + 1) * NF / Q);
                   if constexpr (mine) {
                     if constexpr (MX4 && f < FRN) {
-                      // MXFP4 B: widen the next step's codes (already in registers)
-                      fb[(S + 1) & 1][f] = e2m1x8_to_bf16(word_of<S + 1>(braw[f]), bsc[f]);
+                      // MXFP4 B: widen the next step's codes (in registers: the
+                      // group's read two steps ahead of its first step)
+                      constexpr int G = (S + 1) / 4, W = (S + 1) % 4;
+                      if constexpr (G % 2 == 0)
+                        fb[(S + 1) & 1][f] = e2m1x8_to_bf16(word_of<W>(braw[f]), bsc[f]);
+                      else
+                        fb[(S + 1) & 1][f] = e2m1x8_to_bf16(word_of<W>(braw2[f]), bsc2[f]);
+                      if constexpr ((S + 2) % 4 == 0 && S + 2 < KS) {
+                        constexpr int G2 = (S + 2) / 4;
+                        if constexpr (G2 % 2 == 0) {
+                          read_b8(st, G2, f_tag, braw);
+                          bsc[f] = scale_b4(st, kt, G2, f_tag);
+                        } else {
+                          read_b8(st, G2, f_tag, braw2);
+                          bsc2[f] = scale_b4(st, kt, G2, f_tag);
+                        }
+                      }
                     } else if constexpr (B8 && f < FRN) {
                       // fp8 B: an even step reads the pair's codes, an odd step
                       // converts the upper half read one step earlier
@@ -675,12 +888,32 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                 static_for<L>([&](auto d_tag) G2_INL {
                   constexpr int d = decltype(d_tag)::value;
                   if constexpr (d >= g * L / (DS * Q) && d < (g + 1) * L / (DS * Q))
-                    dma_one(d_tag, kdc, dst);
+                    dma_one(d_tag, kdc, dst, dj);
                 });
+                if constexpr (g == 0) dma_scales(kdc, dst, dj);
               }
               __builtin_amdgcn_sched_barrier(0);
             });
           });
+        }
+        if constexpr (PN) {
+          // the last K tile of N tile jn: store it, start the next one afresh
+          // (the row factors in LDS landed before the first tile: older loads)
+          if (kt == ktiles - 1) {
+            store_tile(tile.n0 + (int64_t)jn * TN_OUT);
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+              for (int j = 0; j < FRN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            kt = 0;
+            ++jn;
+          } else {
+            ++kt;
+          }
+        } else {
+          ++kt;
         }
       }
       wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
@@ -738,6 +971,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     case 4: if constexpr (SUBM >= 4) mainloop(std::integral_constant<int, 4>{}); break;
     default: if constexpr (SUBM >= 5) mainloop(std::integral_constant<int, 5>{}); break;
   }
+  if constexpr (PN) return;  // stored inside the K loop
 
 
   // ---- epilogue: lane holds column (lane & 31), rows 8(r/4) + 4(lane/32) + r%4
@@ -771,70 +1005,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       barrier();
     }
   }
-  constexpr int JN = DUAL ? FRN / 2 : FRN;  // output block columns of this wave
-  int64_t col[JN];
-  bool col_ok[JN];
-  float bias[JN];
-#pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    col[j] = tile.n0 + (wn * JN + j) * 32 + (lane & 31);
-    col_ok[j] = col[j] < args.N;
-    bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
-  }
-  OutT *out = static_cast<OutT *>(args.out);
-#pragma unroll
-  for (int i = 0; i < SUBM; ++i) {
-    if (i >= sub_valid) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int64_t row = tile.m0 + rr;
-      if (row >= tile.m_end) continue;
-      OutT *orow = out + row * args.ldo;
-      if constexpr (EPI == EPI_SITU) {
-        const float f = use_rs ? rs_lds[rr] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-          if (col_ok[j])
-            store_out<OutT>(orow, col[j],
-                            f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
-                                     args.inv_beta, args.beta_u, args.inv_beta_u));
-      } else if constexpr (EPI == EPI_ROUTER) {
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-          if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-          if (col_ok[j]) store_out<OutT>(orow, col[j], acc[i][j][r]);
-      }
-    }
-  }
-  if constexpr (EPI == EPI_ROUTER) {
-    if (args.out_t != nullptr) {
-#pragma unroll
-      for (int i = 0; i < SUBM; ++i)
-#pragma unroll
-        for (int j = 0; j < FRN; ++j) {
-          const int64_t c = col[j];
-          if (!col_ok[j]) continue;
-          const float b = bias[j];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t row0 = tile.m0 + (i * WM + wm) * 32 + 8 * q + 4 * (lane >> 5);
-            float *dst = args.out_t + c * args.M + row0;
-            if (row0 + 3 < tile.m_end && (args.M & 3) == 0) {
-              *reinterpret_cast<float4 *>(dst) =
-                  make_float4(acc[i][j][q * 4 + 0] + b, acc[i][j][q * 4 + 1] + b,
-                              acc[i][j][q * 4 + 2] + b, acc[i][j][q * 4 + 3] + b);
-            } else {
-              for (int u = 0; u < 4; ++u)
-                if (row0 + u < tile.m_end) dst[u] = acc[i][j][q * 4 + u] + b;
-            }
-          }
-        }
-    }
-  }
+  store_tile(tile.n0);
 }
 
 // Split-K reduction: out[m][c] = epilogue(sum over splits, in split order),

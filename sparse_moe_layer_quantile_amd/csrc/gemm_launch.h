@@ -20,16 +20,19 @@ inline int env_int(const char *name, int dflt) {
 // ---- direct-to-LDS bf16 engine ----------------------------------------------------
 struct DmaShape {
   int wm, wn, subm, frn, bk, stages, occ;
+  int ma = 0;  // rows of a short tile (0: wm * subm * 32)
   constexpr int threads() const { return 64 * wm * wn; }
-  constexpr int tm() const { return wm * subm * 32; }
+  constexpr int tm() const { return ma > 0 ? ma : wm * subm * 32; }
   constexpr int tn() const { return wn * frn * 32; }
   // bytes of a B tile row in format bf (g2::BFmt): bf16, fp8 codes, MXFP4 bytes
   static constexpr int b_row_bytes(int bk, int bf) {
     return bf == g2::BF_FP8 ? bk : bf == g2::BF_MX4 ? bk / 2 : bk * 2;
   }
-  // stage ring: bf16 A rows and B rows
+  // stage ring: bf16 A rows and B rows (MXFP4 with K tiles of 128 or more:
+  // and the B rows' E8M0 codes)
   constexpr size_t lds(int bf = g2::BF_BF16) const {
-    return (size_t)stages * (tm() * bk * 2 + tn() * b_row_bytes(bk, bf));
+    return (size_t)stages * (tm() * bk * 2 + tn() * b_row_bytes(bk, bf) +
+                             (bf == g2::BF_MX4 && bk >= 128 ? tn() * (bk / 32) : 0));
   }
   // every wave issues whole rounds of A and of B DMA instructions (1 KB each)
   constexpr bool whole_rounds(int bf = g2::BF_BF16) const {
@@ -48,18 +51,25 @@ constexpr DmaShape kDma[] = {
     // MXFP4 B (a quarter of the bf16 B bytes a stage): a deeper ring keeps as
     // many weight bytes in flight when a few rows stream the weights
     {1, 4, 1, 2, 64, 8, 1},  // 6: 32 x 256, 4 waves, BK 64, 8 stages (96 KB + 32 KB scales)
+    // 7: 8 x 256 short tile (decode), BK 128: 64 bytes of each weight row and
+    //    its 4 scale codes a stage, 8 stages (152 KB)
+    {1, 4, 1, 2, 128, 8, 1, 8},
+    // 8: the same with BK 256: a whole 128-byte line of each weight row and its
+    //    8 scale codes a stage, 4 stages (152 KB); for K a multiple of 256
+    {1, 4, 1, 2, 256, 4, 1, 8},
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
-constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6;
+constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6,
+              kVTinyMX4 = 7, kVTinyMX4W = 8;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 constexpr int kNumDmaBf16 = 6;  // shapes 0..5 fit bf16 B
 
 template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
 hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   constexpr DmaShape sh = kDma[V];
-  auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, EPI,
-                                  DUAL, GATHER, MSEG, BF, OutT>;
-  constexpr size_t lds = sh.lds(BF) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), BF>();
+  auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, sh.ma,
+                                  EPI, DUAL, GATHER, MSEG, BF, OutT>;
+  constexpr size_t lds = sh.lds(BF) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), BF, sh.bk>();
   static_assert(lds <= 160 * 1024, "LDS of a gfx950 workgroup");
   static bool attr_set = false;
   if (!attr_set) {
@@ -70,6 +80,19 @@ hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   }
   const int tn_out = DUAL ? sh.tn() / 2 : sh.tn();
   a.n_tiles_n = (int32_t)((a.N + tn_out - 1) / tn_out);
+  // short tiles of a grouped problem run nper consecutive N tiles in one
+  // workgroup (the kernel's persistent-N form: bf16 or MXFP4 B with in-stage
+  // scales), nper dividing the N tiles of whole tiles only
+  a.nper = 1;
+  if constexpr (sh.ma > 0 && BF != g2::BF_FP8 && EPI != EPI_ROUTER &&
+                (BF != g2::BF_MX4 || sh.bk >= 128)) {
+    if (a.offsets != nullptr && a.N % tn_out == 0) {
+      int nper = std::max(1, env_int("MOE_GEMM_NPER", 8));
+      while (nper > 1 && a.n_tiles_n % nper) --nper;
+      a.nper = nper;
+      a.n_tiles_n /= nper;
+    }
+  }
   // dense rasterisation groups (grouped problems group by expert)
   a.group_m = env_int("MOE_GROUP_M_DENSE", 4);
   if (a.group_m < 1) a.group_m = 1;
@@ -128,18 +151,30 @@ hipError_t launch_dma_b8(int v, const GemmArgs &a, hipStream_t s) {
   }
 }
 
-// MXFP4 B (routed experts): the shape for a requested variant (the grouped
-// ones, and a deeper-ring small-M shape); other requests take the short
-// grouped shape
-constexpr int mx4_variant(int v) {
-  return v == kVGrouped ? kVGrouped : v == kVSmallM ? kVSmallMX4 : kVGroupedShort;
+// MXFP4 B (routed experts): the shape for the variant v the bf16 engine would
+// take for `rows` pairs over n_experts: the grouped shapes as they are; for
+// few rows a deeper-ring 32-row shape, and the 8-row short tile when experts
+// hold about two rows each (decode); MOE_GEMM_MX4 overrides
+inline int mx4_shape(int v, int64_t rows, int64_t n_experts) {
+  const int dflt = v == kVGrouped        ? kVGrouped
+                   : v != kVSmallM       ? kVGroupedShort
+                   : rows <= 2 * n_experts ? kVTinyMX4
+                                           : kVSmallMX4;
+  const int o = env_int("MOE_GEMM_MX4", -1);
+  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallMX4 || o == kVTinyMX4) ? o : dflt;
 }
+// (the 8-row short tile takes its 256-wide K tiles where K allows; both forms
+// have 8-row tiles, so the dispatch's tile table is the same)
 template <int EPI, bool DUAL, bool GATHER, typename OutT>
-hipError_t launch_dma_b4(int v, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_dma_b4(int shape, const GemmArgs &a, hipStream_t s) {
   constexpr int F = g2::BF_MX4;
-  switch (mx4_variant(v)) {
+  if (shape == kVTinyMX4 && a.seg[0].k % 256 == 0 && env_int("MOE_GEMM_MX4_BK128", 0) == 0)
+    shape = kVTinyMX4W;
+  switch (shape) {
     case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVSmallMX4: return launch_dma_impl<kVSmallMX4, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVTinyMX4: return launch_dma_impl<kVTinyMX4, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVTinyMX4W: return launch_dma_impl<kVTinyMX4W, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     default: return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, F, OutT>(a, s);
   }
 }

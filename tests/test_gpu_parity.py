@@ -165,17 +165,36 @@ def test_forward_fp8_weights_mid(bt, cutoff):
 
 
 @pytest.mark.parametrize("bt,cutoff,shape", [(4096, "batch", None), (64, "given", None),
-                                             (100, "batch", None), (300, "batch", (640, 384))])
+                                             (100, "batch", None), (300, "batch", (640, 384)),
+                                             (16, "given", None), (8, "batch", (640, 384))])
 def test_forward_mxfp4_experts_mid(bt, cutoff, shape):
     """MXFP4 routed experts (E2M1 codes, E8M0 scales per 32) at the mid shapes:
     the prefill-sized batch runs the 320-row grouped tiles, the 64-token one
-    the 32-row tiles with the deep ring, the others the 192-row tiles; the
-    last case has a partial N tile in the down GEMM (latent 640) and K ranges
-    of 20 and 12 scale blocks."""
+    the 32-row tiles with the deep ring, 16 and 8 tokens (two rows an expert)
+    the 8-row short tiles, the others the 192-row tiles; the (640, 384) cases
+    have a partial N tile in the down GEMM and K ranges of 20 and 12 scale
+    blocks."""
     cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", bt=bt)
     if shape is not None:
         cfg = cfg.with_(latent=shape[0], expert_inter=shape[1])
     say("forward mxfp4", bt, cutoff, cfg.latent, cfg.expert_inter)
+    _mxfp4_check(cfg, cutoff)
+
+
+@pytest.mark.parametrize("shape_id", ["0", "1", "6", "7", "7-bk128"])
+def test_forward_mxfp4_every_tile_shape(shape_id, monkeypatch):
+    """Each MXFP4 tile shape (forced) on one batch of about 25 rows an expert:
+    several M tiles an expert for the short shapes, a partial one for the long;
+    the 8-row tile with its 256-wide K tiles and with 128-wide ones."""
+    monkeypatch.setenv("MOE_GEMM_MX4", shape_id.split("-")[0])
+    if shape_id.endswith("bk128"):
+        monkeypatch.setenv("MOE_GEMM_MX4_BK128", "1")
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", bt=200)
+    say("forward mxfp4 forced shape", shape_id)
+    _mxfp4_check(cfg, "batch")
+
+
+def _mxfp4_check(cfg, cutoff):
     layer, x = parity.device_layer(cfg, seed=0, cutoff=cutoff)
     y, r = layer.forward(x, return_routing=True)
     torch.cuda.synchronize()
