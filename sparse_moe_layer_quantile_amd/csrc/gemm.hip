@@ -50,11 +50,11 @@ int dma_variant(GemmKind kind, int64_t rows, int64_t n_experts) {
                      : rows <= 200 * n_experts ? kVGroupedShort
                                                : kVGrouped;
     const int v = env_int("MOE_GEMM_GROUPED", dflt);
-    return (v >= 0 && v < kNumDmaBf16) ? v : dflt;
+    return bf16_shape(v) ? v : dflt;
   }
   const int dflt = rows <= 64 ? kVSmallM : kVDense;
   const int v = env_int("MOE_GEMM_DENSE", dflt);
-  return (v >= 0 && v < kNumDmaBf16) ? v : dflt;
+  return bf16_shape(v) ? v : dflt;
 }
 
 int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts) {
@@ -63,8 +63,7 @@ int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts) {
   // the MXFP4 engine's shapes (launch_dma_b4)
   if (wf == WF_MX4) return kDma[mx4_shape(v, rows, n_experts)].tm();
   // the fp8 engine's shapes (launch_dma_b8)
-  if (wf == WF_FP8 && v != kVGrouped && v != kVGroupedShort && v != kVSmallM)
-    return kDma[kVDense].tm();
+  if (wf == WF_FP8) return kDma[fp8_shape(v, true)].tm();
   return kDma[v].tm();
 }
 
@@ -110,7 +109,8 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64
   int64_t kblocks = 0;
   for (int i = 0; i < a.nseg; ++i) kblocks += a.seg[i].k / 128;
   if (kblocks <= g2::kMaxKBlocks) {
-    const int v = dma_variant(kind, a.M, a.n_experts);
+    const bool grouped = kind == GK_EXPERT_SITU || kind == GK_EXPERT_DOWN;
+    const int v = fp8_shape(dma_variant(kind, a.M, a.n_experts), grouped);
     switch (kind) {
       case GK_ROUTER: return hipErrorInvalidValue;  // the router stays bf16
       case GK_DENSE:

@@ -57,12 +57,17 @@ constexpr DmaShape kDma[] = {
     // 8: the same with BK 256: a whole 128-byte line of each weight row and its
     //    8 scale codes a stage, 4 stages (152 KB); for K a multiple of 256
     {1, 4, 1, 2, 256, 4, 1, 8},
+    // quantised B (fp8, MXFP4): B stages a half or a quarter of bf16's leave
+    // room for a third stage of the grouped tiles
+    {2, 4, 4, 2, 64, 3, 1},  // 9: 256 x 256, BK 64, 3 stages
+    {2, 4, 3, 2, 64, 3, 1},  // 10: 192 x 256, BK 64, 3 stages
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
 constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6,
-              kVTinyMX4 = 7, kVTinyMX4W = 8;
+              kVTinyMX4 = 7, kVTinyMX4W = 8, kVQ256 = 9, kVQ192 = 10;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
-constexpr int kNumDmaBf16 = 6;  // shapes 0..5 fit bf16 B
+// shapes a bf16 B operand can take (6..8 are MXFP4-only)
+constexpr bool bf16_shape(int v) { return v >= 0 && v < 6; }
 
 template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
 hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
@@ -135,18 +140,31 @@ hipError_t launch_dma_v(const GemmArgs &a, hipStream_t s) {
     return launch_dma_impl<V, EPI, DUAL, GATHER, MSEG, g2::BF_BF16, OutT>(a, s);
 }
 
-// fp8 e4m3 B with block scales: the default shapes; other requests take the
-// dense one
+// fp8 e4m3 B with block scales: the shape for the variant v the bf16 engine
+// would take (the 192-row grouped tiles with a third stage, which the half-size
+// B stage leaves room for; the other grouped and small-M ones as they are, the
+// dense one otherwise); MOE_GEMM_FP8 overrides the grouped shape
+inline int fp8_shape(int v, bool grouped) {
+  const int dflt = v == kVGroupedShort                          ? kVQ192
+                   : (v == kVGrouped || v == kVSmallM) ? v
+                                                                : kVDense;
+  const int o = grouped ? env_int("MOE_GEMM_FP8", -1) : -1;
+  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallM || o == kVQ256 || o == kVQ192)
+             ? o
+             : dflt;
+}
 template <int EPI, bool DUAL, bool GATHER, typename OutT, bool MSEG = false>
-hipError_t launch_dma_b8(int v, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_dma_b8(int shape, const GemmArgs &a, hipStream_t s) {
   constexpr int F = g2::BF_FP8;
   static_assert(!MSEG || kDma[kVDense].whole_rounds(F), "segmented fp8 shape");
   if constexpr (MSEG) return launch_dma_impl<kVDense, EPI, DUAL, GATHER, true, F, OutT>(a, s);
-  switch (v) {
+  switch (shape) {
     case kVGrouped: return launch_dma_impl<kVGrouped, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVGroupedShort:
       return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVSmallM: return launch_dma_impl<kVSmallM, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVQ256: return launch_dma_impl<kVQ256, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVQ192: return launch_dma_impl<kVQ192, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     default: return launch_dma_impl<kVDense, EPI, DUAL, GATHER, false, F, OutT>(a, s);
   }
 }
@@ -161,7 +179,10 @@ inline int mx4_shape(int v, int64_t rows, int64_t n_experts) {
                    : rows <= 2 * n_experts ? kVTinyMX4
                                            : kVSmallMX4;
   const int o = env_int("MOE_GEMM_MX4", -1);
-  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallMX4 || o == kVTinyMX4) ? o : dflt;
+  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallMX4 || o == kVTinyMX4 ||
+          o == kVQ256 || o == kVQ192)
+             ? o
+             : dflt;
 }
 // (the 8-row short tile takes its 256-wide K tiles where K allows; both forms
 // have 8-row tiles, so the dispatch's tile table is the same)
@@ -175,6 +196,8 @@ hipError_t launch_dma_b4(int shape, const GemmArgs &a, hipStream_t s) {
     case kVSmallMX4: return launch_dma_impl<kVSmallMX4, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVTinyMX4: return launch_dma_impl<kVTinyMX4, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVTinyMX4W: return launch_dma_impl<kVTinyMX4W, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVQ256: return launch_dma_impl<kVQ256, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVQ192: return launch_dma_impl<kVQ192, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     default: return launch_dma_impl<kVGroupedShort, EPI, DUAL, GATHER, false, F, OutT>(a, s);
   }
 }
