@@ -73,6 +73,8 @@ def lib():
             "orc_shared": ([P, P, P, P], ctypes.c_int),
             "orc_output": ([P, P, P, P, P], ctypes.c_int),
             "orc_forward": ([P, P, P, I64, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+            "orc_rmsnorm": ([P, I64, P, D, P], None),
+            "orc_dense_ffn": ([P, P, P, P, P, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -279,6 +281,34 @@ def output(cfg, w: Weights, n, x_t) -> np.ndarray:
     y = np.empty(cfg.d, np.float64)
     if lib().orc_output(ctypes.byref(shape_of(cfg)), w.ref, _ptr(n), _ptr(x_t), _ptr(y)):
         raise ValueError("orc_output rejected its arguments")
+    return y
+
+
+def rmsnorm(x, gamma=None, eps=1e-6) -> np.ndarray:
+    x = _c(x, np.float64)
+    gamma = _c(gamma, np.float32)
+    out = np.empty(x.size, np.float64)
+    lib().orc_rmsnorm(_ptr(x), x.size, _ptr(gamma), float(eps), _ptr(out))
+    return out
+
+
+class FfnShape:
+    """Oracle shape of the dense FFN: width d, intermediate width inter."""
+
+    def __init__(self, d, inter, beta=4.0, beta_u=25.0, rms_eps=1e-6):
+        self.d, self.expert_inter, self.latent = d, inter, d
+        self.beta, self.beta_u, self.rms_eps = beta, beta_u, rms_eps
+
+
+def dense_ffn(shape, gate: Mat, up: Mat, down: Mat, x, r=None, gamma=None) -> np.ndarray:
+    """y = r + W_d (phi(W_g n) psi(W_u n)), n = RMSNorm(x) gamma, for one row (fp64)."""
+    x = _c(x, np.float64)
+    r = _c(r, np.float64)
+    gamma = _c(gamma, np.float32)
+    y = np.empty(shape.d, np.float64)
+    if lib().orc_dense_ffn(ctypes.byref(shape_of(shape)), gate.ref, up.ref, down.ref,
+                           _ptr(gamma), _ptr(x), _ptr(r), _ptr(y)):
+        raise ValueError("orc_dense_ffn rejected its arguments")
     return y
 
 

@@ -278,6 +278,34 @@ int orc_expert(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
   return 0;
 }
 
+// RMSNorm of one row: out = x / sqrt(mean(x^2) + eps) * gamma (gamma NULL = 1).
+void orc_rmsnorm(const double *x, int64_t n, const float *gamma, double eps, double *out) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
+  const double inv = 1.0 / std::sqrt(ss / (double)n + eps);
+  for (int64_t i = 0; i < n; ++i) out[i] = x[i] * inv * (gamma ? (double)gamma[i] : 1.0);
+}
+
+// Dense FFN of one row: the SiTU-GLU of the experts at width d and
+// intermediate width I, on the RMS-normalised row, added to r.
+int orc_dense_ffn(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
+                  const orc_mat *w_down, const float *gamma, const double *x, const double *r,
+                  double *y) {
+  if (!s || !w_gate || !w_up || !w_down || !x || !y || s->d <= 0 || s->expert_inter <= 0)
+    return -1;
+  if (w_gate->rows != s->expert_inter || w_gate->cols != s->d || w_up->rows != s->expert_inter ||
+      w_up->cols != s->d || w_down->rows != s->d || w_down->cols != s->expert_inter)
+    return -1;
+  const int64_t d = s->d;
+  std::vector<double> n((size_t)d), o((size_t)d);
+  orc_rmsnorm(x, d, gamma, s->rms_eps, n.data());
+  orc_shape e = *s;
+  e.latent = d;  // the expert GLU reads its input at width "latent"
+  if (orc_expert(&e, w_gate, w_up, w_down, 0, n.data(), o.data())) return -1;
+  for (int64_t i = 0; i < d; ++i) y[i] = (r ? r[i] : 0.0) + o[i];
+  return 0;
+}
+
 int orc_combine_norm(const orc_shape *s, const double *o, const double *w,
                      const float *gamma, double *y_lat, double *n) {
   if (!s || !o || !w || !y_lat || !n) return -1;

@@ -136,6 +136,22 @@ int orc_output(const orc_shape *s, const orc_weights *w, const double *n,
  * alpha_given: GIVEN-mode cutoffs (NULL: 0).  z32 [bt][E], zeta [E] (BATCH),
  * idx [bt][k], wts [bt][k], counts [E], offsets [E+1], perm/inv_perm [bt*k],
  * y [bt][d] fp64. */
+/* ---- Dense layer-1 FFN (a second workload of the same building blocks) ----
+ * mkdocs.reaper.mx "Vue d'ensemble de l'architecture": section "Le décompte des
+ * couches" (layer 1 is dense: a full-width SiTU-GLU FFN of intermediate width
+ * 33 792, no routing) and section "Ce que fait une couche" (each sublayer is
+ * preceded by an RMSNorm, and its output is summed into the block
+ * representation).  For one token row x[d]:
+ *   n = x / sqrt(mean(x^2) + eps) * gamma
+ *   y = r + W_d (phi(W_g n) * psi(W_u n))
+ * with s->d the width, s->expert_inter the intermediate width I and
+ * s->beta, s->beta_u, s->rms_eps; w_gate, w_up hold [1][I][d], w_down [1][d][I];
+ * gamma [d] or NULL (= 1); r [d] or NULL (= 0). */
+void orc_rmsnorm(const double *x, int64_t n, const float *gamma, double eps, double *out);
+int orc_dense_ffn(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
+                  const orc_mat *w_down, const float *gamma, const double *x, const double *r,
+                  double *y);
+
 int orc_forward(const orc_shape *s, const orc_weights *w, const orc_mat *x, int64_t bt,
                 int32_t cutoff_mode, const float *alpha_given, float *z32_out,
                 float *zeta_out, int32_t *idx_out, double *wts_out, int32_t *counts,

@@ -423,3 +423,110 @@ def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cu
     out["router_bias"] = None if b is None else torch.from_numpy(b).to(device)
     out["gamma"] = torch.from_numpy(gamma(cfg)).to(device)
     return out
+
+
+# ---- dense layer-1 FFN workloads ----------------------------------------------------------
+# mkdocs.reaper.mx "Vue d'ensemble de l'architecture": layer 1 is a dense SiTU-GLU FFN
+# of intermediate width 33 792 (section "Le décompte des couches"), pre-RMSNorm with
+# its output summed into the block representation (section "Ce que fait une couche").
+
+FFN_TID = {"x": 20, "r": 21, "w_gate": 22, "w_up": 23, "w_down": 24}
+
+
+@dataclasses.dataclass(frozen=True)
+class FfnConfig:
+    name: str
+    bt: int
+    d: int
+    inter: int
+    act: str = "bf16"
+    beta: float = 4.0
+    beta_u: float = 25.0
+    rms_eps: float = 1e-6
+
+    @property
+    def expert_inter(self) -> int:  # the oracle's name for the intermediate width
+        return self.inter
+
+    def flops(self) -> int:
+        return 2 * self.bt * 3 * self.d * self.inter
+
+    def with_(self, **kw) -> "FfnConfig":
+        return dataclasses.replace(self, **kw)
+
+
+FFN_CONFIGS: Dict[str, FfnConfig] = {
+    "ffn_tiny_fp32": FfnConfig("ffn_tiny_fp32", bt=64, d=256, inter=384, act="f32"),
+    "ffn_mid_bf16": FfnConfig("ffn_mid_bf16", bt=1024, d=2048, inter=5632),
+    "k3_dense_ffn_prefill_bf16": FfnConfig("k3_dense_ffn_prefill_bf16", bt=16384, d=7168,
+                                           inter=33792),
+    "k3_dense_ffn_decode_bf16": FfnConfig("k3_dense_ffn_decode_bf16", bt=64, d=7168,
+                                          inter=33792),
+}
+
+
+def ffn_specs(cfg: FfnConfig) -> Dict[str, Spec]:
+    a = DTYPE_NAMES[cfg.act]
+    d, I = cfg.d, cfg.inter
+    return {
+        "x": Spec("x", (cfg.bt, d), a, 1, cfg.bt, d, 1),
+        "r": Spec("r", (cfg.bt, d), a, 1, cfg.bt, d, 1),
+        "w_gate": Spec("w_gate", (I, d), a, d, I, d, 1),
+        "w_up": Spec("w_up", (I, d), a, d, I, d, 1),
+        "w_down": Spec("w_down", (d, I), a, I, d, I, 1),
+    }
+
+
+def ffn_draw_params(cfg: FfnConfig, name: str):
+    sp = ffn_specs(cfg)[name]
+    sigma = 1.0 if name in ("x", "r") else 1.0 / math.sqrt(sp.fan_in)
+    return NORMAL, float(np.float32(sigma / NORMAL_INT_STD)), 0
+
+
+def ffn_gamma(cfg: FfnConfig) -> np.ndarray:
+    """RMSNorm gain (7/6)(0.75 + 0.5 u), u uniform in [0, 1): values in [0.875, 1.46),
+    so a dropped or misplaced gain shows."""
+    out = np.empty(cfg.d, dtype=np.float32)
+    lib_host().synth_block_scales_host(out.ctypes.data, cfg.d, 0, 30, 7.0 / 6.0)
+    return out
+
+
+def ffn_host_tensor(cfg: FfnConfig, name: str, seed: int = 0, start: int = 0,
+                    count: Optional[int] = None) -> np.ndarray:
+    sp = ffn_specs(cfg)[name]
+    if count is None:
+        count = sp.numel - start
+    kind, scale, rng = ffn_draw_params(cfg, name)
+    return host_fill(sp.dtype, count, seed, FFN_TID[name], start, kind, scale, rng)
+
+
+def ffn_host_rows(cfg: FfnConfig, name: str, rows, seed: int = 0) -> np.ndarray:
+    sp = ffn_specs(cfg)[name]
+    cols = sp.shape[-1]
+    return np.stack([ffn_host_tensor(cfg, name, seed, int(r) * cols, cols) for r in rows])
+
+
+def ffn_host_layer(cfg: FfnConfig, seed: int = 0) -> dict:
+    out = {n: ffn_host_tensor(cfg, n, seed).reshape(sp.shape)
+           for n, sp in ffn_specs(cfg).items()}
+    out["gamma"] = ffn_gamma(cfg)
+    return out
+
+
+def ffn_device_layer(cfg: FfnConfig, seed: int = 0, device="cuda") -> dict:
+    """Every tensor of the FFN generated in device memory (same bits as ffn_host_layer)."""
+    import torch
+    tdt = {F32: torch.float32, BF16: torch.bfloat16}
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, sp in ffn_specs(cfg).items():
+        t = torch.empty(sp.shape, dtype=tdt[sp.dtype], device=device)
+        kind, scale, rng = ffn_draw_params(cfg, name)
+        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()), sp.dtype, sp.numel, seed,
+                                         FFN_TID[name], 0, kind, scale, rng,
+                                         ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"synth_fill_device failed ({rc}) for {name}")
+        out[name] = t
+    out["gamma"] = torch.from_numpy(ffn_gamma(cfg)).to(device)
+    return out

@@ -430,6 +430,70 @@ def test_expert_picks_matrix_by_index():
         np.testing.assert_array_equal(a, b)
 
 
+# ---- dense layer-1 FFN ---------------------------------------------------------------------
+
+def test_rmsnorm_closed_forms():
+    # a constant row c: every element becomes c / sqrt(c^2 + eps) * gamma
+    for c, eps in ((3.0, 0.0), (-0.5, 1e-6), (2.0, 0.25)):
+        x = np.full(8, c)
+        g = f32(np.arange(1, 9) / 4)
+        np.testing.assert_allclose(oracle.rmsnorm(x, g, eps),
+                                   c / math.sqrt(c * c + eps) * g.astype(np.float64),
+                                   rtol=1e-15)
+    # with eps = 0 the result has unit RMS and is exactly invariant to a power-of-two scale
+    rng = np.random.default_rng(30)
+    x = rng.normal(size=97)
+    n = oracle.rmsnorm(x, None, 0.0)
+    assert abs(np.sqrt(np.mean(n * n)) - 1.0) < 1e-14
+    np.testing.assert_array_equal(oracle.rmsnorm(4.0 * x, None, 0.0), n)
+
+
+def test_dense_ffn_structure():
+    rng = np.random.default_rng(31)
+    d, I = 24, 40
+    Wg, Wu = f32(rng.normal(size=(I, d))), f32(rng.normal(size=(I, d)))
+    Wd = f32(rng.normal(size=(d, I)))
+    x, r = rng.normal(size=d), rng.normal(size=d)
+    s = oracle.FfnShape(d, I, rms_eps=0.0)
+    M = oracle.Mat
+    y = oracle.dense_ffn(s, M(Wg), M(Wu), M(Wd), x, r)
+    # the residual enters additively, exactly: y(r) - y(0) = r
+    y0 = oracle.dense_ffn(s, M(Wg), M(Wu), M(Wd), x)
+    np.testing.assert_array_equal(y - y0, (y0 + r) - y0)
+    # gamma = 0 zeroes the FFN (phi(0) = psi(0) = 0): y = r
+    np.testing.assert_array_equal(
+        oracle.dense_ffn(s, M(Wg), M(Wu), M(Wd), x, r, gamma=np.zeros(d, np.float32)), r)
+    # pre-norm: the output does not depend on the input's scale (eps = 0)
+    np.testing.assert_array_equal(oracle.dense_ffn(s, M(Wg), M(Wu), M(Wd), 8.0 * x, r), y)
+    # it is the expert GLU on the normalised row
+    n = oracle.rmsnorm(x, None, 0.0)
+    np.testing.assert_array_equal(y0, oracle.expert(s, M(Wg), M(Wu), M(Wd), n))
+
+
+def test_dense_ffn_reduces_to_swiglu_when_caps_vanish():
+    """beta, beta_u -> inf and a plain RMSNorm: the textbook pre-norm SwiGLU block."""
+    rng = np.random.default_rng(32)
+    d, I = 16, 28
+    Wg, Wu = f32(rng.normal(size=(I, d))), f32(rng.normal(size=(I, d)))
+    Wd = f32(rng.normal(size=(d, I)))
+    x, r = rng.normal(size=d), rng.normal(size=d)
+    s = oracle.FfnShape(d, I, beta=1e8, beta_u=1e8, rms_eps=1e-6)
+    y = oracle.dense_ffn(s, oracle.Mat(Wg), oracle.Mat(Wu), oracle.Mat(Wd), x, r)
+    n = x / np.sqrt(np.mean(x * x) + 1e-6)
+    g, u = Wg.astype(np.float64) @ n, Wu.astype(np.float64) @ n
+    ref = r + Wd.astype(np.float64) @ (g / (1 + np.exp(-g)) * u)
+    np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-12)
+
+
+def test_dense_ffn_rejects_mismatched_shapes():
+    d, I = 8, 12
+    z = np.zeros
+    with pytest.raises(ValueError):
+        oracle.dense_ffn(oracle.FfnShape(d, I), oracle.Mat(z((I, d), np.float32)),
+                         oracle.Mat(z((I, d), np.float32)), oracle.Mat(z((I, d), np.float32)),
+                         np.ones(d))
+
+
 # ---- step 7: combine + latent RMSNorm ----------------------------------------------------
 
 def test_combine_is_score_weighted_sum():
