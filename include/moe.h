@@ -165,16 +165,50 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
 /* Static text for a status code. */
 const char *moe_status_str(int status);
 
+/* ---- Dense layer-1 FFN -------------------------------------------------------
+ * The first layer of K3 is dense: a full-width SiTU-GLU FFN of intermediate
+ * width 33 792, with no routing (mkdocs.reaper.mx "Vue d'ensemble de
+ * l'architecture", section "Le décompte des couches").  As every sublayer it is
+ * preceded by an RMSNorm and its output is summed into the block representation
+ * (same page, section "Ce que fait une couche").  For bt rows x[bt][d]:
+ *   n = x / sqrt(mean(x^2) + eps) * gamma
+ *   y = r + W_d (phi(W_g n) * psi(W_u n))        phi, psi as for the experts
+ * r (the representation the output is summed into) may be NULL (= 0) and may
+ * be y itself (in place).  Same conventions as above (device pointers, caller
+ * allocates, validation before enqueue, work on `stream`). */
+typedef struct moe_ffn_config {
+  int64_t d;            /* width (7168 for K3); multiple of 64, at most 8192 (4096 fp32) */
+  int64_t inter;        /* intermediate width (33 792); multiple of 64 */
+  float beta, beta_u;   /* SiTU caps (4, 25) */
+  float rms_eps;        /* 1e-6 */
+  int32_t act_dtype;    /* x, r, y and the weights: MOE_F32 or MOE_BF16 */
+} moe_ffn_config;
+
+typedef struct moe_ffn_weights {
+  const void *w_gate;   /* [inter][d] */
+  const void *w_up;     /* [inter][d] */
+  const void *w_down;   /* [d][inter] */
+  const float *gamma;   /* [d] RMSNorm gain, 16-byte aligned */
+} moe_ffn_weights;
+
+/* Device bytes of workspace moe_ffn_forward needs for bt rows; 0 for an invalid config. */
+size_t moe_ffn_workspace_bytes(const moe_ffn_config *cfg, int64_t bt);
+
+moe_status moe_ffn_forward(const moe_ffn_config *cfg, const moe_ffn_weights *w, const void *x,
+                           const void *r, int64_t bt, void *y, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* ---- Measurement support (not part of the layer) ----------------------------
- * While enabled, moe_forward records a timing hipEvent pair around each of its
- * phases on the stream that phase runs on (the shared experts on
- * shared_stream).  moe_profile_read waits for the recorded events, returns the
- * average milliseconds per call of each phase and clears the record.  Phases:
- * 0 shared gate/up, 1 router logits, 2 cutoffs, 3 top-k, 4 dispatch,
- * 5 W_down_proj, 6 expert gate/up, 7 expert down, 8 combine + RMSNorm,
- * 9 output projection.  Events are created by the library and kept for reuse
- * (no device memory).  Not thread-safe against concurrent forwards. */
-#define MOE_N_PHASES 10
+ * While enabled, moe_forward and moe_ffn_forward record a timing hipEvent pair
+ * around each of their phases on the stream that phase runs on (the shared
+ * experts on shared_stream).  moe_profile_read waits for the recorded events,
+ * returns the average milliseconds per call of each phase and clears the
+ * record.  Phases: 0 shared gate/up, 1 router logits, 2 cutoffs, 3 top-k,
+ * 4 dispatch, 5 W_down_proj, 6 expert gate/up, 7 expert down, 8 combine +
+ * RMSNorm, 9 output projection; dense FFN: 10 RMSNorm, 11 gate/up, 12 down.
+ * Events are created by the library and kept for reuse (no device memory).
+ * Not thread-safe against concurrent forwards. */
+#define MOE_N_PHASES 13
 moe_status moe_profile_enable(int on);
 moe_status moe_profile_read(double *ms_avg, int64_t *calls); /* arrays of MOE_N_PHASES */
 const char *moe_profile_phase_name(int phase);

@@ -47,6 +47,16 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in WEIGHT_FIELDS]
 
 
+class MoeFfnConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("inter", ctypes.c_int64), ("beta", ctypes.c_float),
+                ("beta_u", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32)]
+
+
+class MoeFfnWeights(ctypes.Structure):
+    _fields_ = [("w_gate", _P), ("w_up", _P), ("w_down", _P), ("gamma", _P)]
+
+
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", _P), ("topk_w", _P), ("cutoff", _P), ("logits", _P)]
 
@@ -83,6 +93,11 @@ def _load():
                                 CP(MoeRouteOut), CP(MoeDispatchOut), _P, ctypes.c_size_t, _P,
                                 _P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_ffn_workspace_bytes.argtypes = [CP(MoeFfnConfig), ctypes.c_int64]
+    lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_ffn_forward.argtypes = [CP(MoeFfnConfig), CP(MoeFfnWeights), _P, _P, ctypes.c_int64,
+                                    _P, _P, ctypes.c_size_t, _P]
+    lib.moe_ffn_forward.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_profile_enable.argtypes = [ctypes.c_int]
@@ -98,8 +113,8 @@ LIB = _load()
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_status_str", "moe_profile_enable", "moe_profile_read",
-            "moe_profile_phase_name")
-N_PHASES = 10
+            "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward")
+N_PHASES = 13
 
 
 def status_str(status: int) -> str:
@@ -250,3 +265,54 @@ class StableLatentMoE:
         if st != 0:
             raise MoeError(st, "moe_forward")
         return (y, extra) if return_routing else y
+
+
+# ---- dense layer-1 FFN -----------------------------------------------------------------
+
+def make_ffn_config(d, inter, beta=4.0, beta_u=25.0, rms_eps=1e-6, act="bf16") -> MoeFfnConfig:
+    return MoeFfnConfig(d, inter, beta, beta_u, rms_eps, DTYPES[act])
+
+
+def ffn_workspace_bytes(cfg: MoeFfnConfig, bt: int) -> int:
+    return int(LIB.moe_ffn_workspace_bytes(ctypes.byref(cfg), bt))
+
+
+def moe_ffn_forward(cfg, weights: MoeFfnWeights, x: int, r: int, bt: int, y: int, ws: int,
+                    ws_bytes: int, stream: int) -> int:
+    return LIB.moe_ffn_forward(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None),
+                               _P(r or None), bt, _P(y or None), _P(ws or None), ws_bytes,
+                               _P(stream or None))
+
+
+class DenseFFN:
+    """The dense layer-1 FFN: a config and its device-resident weights
+    (w_gate, w_up, w_down, gamma), borrowed, not copied."""
+
+    def __init__(self, cfg: MoeFfnConfig, tensors: dict):
+        self.cfg = cfg
+        self.tensors = dict(tensors)
+        self.w = MoeFfnWeights(*(_ptr(self.tensors.get(n)) for n in
+                                 ("w_gate", "w_up", "w_down", "gamma")))
+        self._ws = None
+
+    def workspace(self, bt: int):
+        import torch
+        need = ffn_workspace_bytes(self.cfg, bt)
+        if need == 0 and bt > 0:
+            raise MoeError(-2, "moe_ffn_workspace_bytes")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def forward(self, x, r=None, out=None):
+        """y = r + FFN(RMSNorm(x)); out may be r (in place)."""
+        import torch
+        bt = x.shape[0]
+        y = out if out is not None else torch.empty((bt, self.cfg.d), dtype=x.dtype,
+                                                    device=x.device)
+        ws = self.workspace(bt)
+        st = moe_ffn_forward(self.cfg, self.w, _ptr(x), _ptr(r), bt, y.data_ptr(),
+                             ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise MoeError(st, "moe_ffn_forward")
+        return y

@@ -192,11 +192,12 @@ GemmArgs base_args(const moe_config *c) {
 // ---- phase timing (measurement support) -------------------------------------------
 enum Phase {
   PH_SHARED = 0, PH_ROUTER, PH_CUTOFF, PH_TOPK, PH_DISPATCH, PH_DOWN_PROJ, PH_EXPERT_GATEUP,
-  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT
+  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT, PH_FFN_NORM, PH_FFN_GATEUP, PH_FFN_DOWN
 };
 const char *kPhaseNames[MOE_N_PHASES] = {
     "shared_gateup", "router_logits", "cutoff", "topk", "dispatch", "down_proj",
-    "expert_gateup", "expert_down", "combine_norm", "output"};
+    "expert_gateup", "expert_down", "combine_norm", "output", "ffn_norm", "ffn_gateup",
+    "ffn_down"};
 
 struct Profiler {
   bool on = false;
@@ -574,6 +575,118 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.ldo = d;
     PhaseScope ph(PH_OUTPUT, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, dwf, dense_mt, s));
+  }
+  return MOE_OK;
+}
+
+// ---- dense layer-1 FFN ------------------------------------------------------------
+// RMSNorm -> n, gate/up + SiTU -> h, down + residual -> y, all on `stream`
+// (mkdocs.reaper.mx "Vue d'ensemble de l'architecture": layer 1 is a dense
+// SiTU-GLU FFN of width 33 792; each sublayer is pre-normed and its output is
+// summed into the block representation).
+
+namespace {
+
+struct FfnPlan {
+  int path = PATH_BF16;
+  int64_t act_bytes = 2;
+  size_t n, h, split, total;
+  int64_t split_cap = 0;
+};
+
+moe_status ffn_plan(const moe_ffn_config *c, int64_t bt, FfnPlan *p) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->d <= 0 || c->inter <= 0 || bt < 0) return MOE_ERR_INVALID_ARG;
+  if (!(c->beta > 0.0f) || !(c->beta_u > 0.0f) || !(c->rms_eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  p->path = c->act_dtype == MOE_F32 ? PATH_F32 : PATH_BF16;
+  p->act_bytes = elem_size(c->act_dtype);
+  if (c->d % 64 || c->inter % 64) return MOE_ERR_UNSUPPORTED;
+  // the RMSNorm holds a row per wavefront in registers (16 chunks of 16 B a lane)
+  if (c->d > (c->act_dtype == MOE_F32 ? 4096 : 8192)) return MOE_ERR_UNSUPPORTED;
+  if (bt > INT32_MAX / 64) return MOE_ERR_UNSUPPORTED;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  p->n = take(p->act_bytes * bt * c->d);
+  p->h = take(p->act_bytes * bt * c->inter);
+  // split-K partial sums of the down projection for short batches (up to 16 splits)
+  if (p->path == PATH_BF16 && bt > 0 && bt <= kSplitMaxRows) p->split_cap = 16 * bt * c->d;
+  p->split = take(4 * p->split_cap);
+  p->total = off + kAlign;
+  return MOE_OK;
+}
+
+GemmArgs ffn_args(const moe_ffn_config *c) {
+  GemmArgs a = {};
+  a.beta = c->beta;
+  a.inv_beta = 1.0f / c->beta;
+  a.beta_u = c->beta_u;
+  a.inv_beta_u = 1.0f / c->beta_u;
+  return a;
+}
+
+}  // namespace
+
+MOE_API size_t moe_ffn_workspace_bytes(const moe_ffn_config *cfg, int64_t bt) {
+  FfnPlan p;
+  if (ffn_plan(cfg, bt, &p) != MOE_OK) return 0;
+  return p.total - kAlign;
+}
+
+MOE_API moe_status moe_ffn_forward(const moe_ffn_config *cfg, const moe_ffn_weights *w,
+                                   const void *x, const void *r, int64_t bt, void *y, void *ws,
+                                   size_t ws_bytes, void *stream) {
+  FfnPlan p;
+  moe_status st = ffn_plan(cfg, bt, &p);
+  if (st != MOE_OK) return st;
+  if (!w || !w->w_gate || !w->w_up || !w->w_down || !w->gamma) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(w->gamma) % 16) return MOE_ERR_INVALID_ARG;  // float4 reads
+  if (bt > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total - kAlign || (reinterpret_cast<uintptr_t>(ws) % kAlign))
+    return MOE_ERR_WORKSPACE;
+  if (bt == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t d = cfg->d, I = cfg->inter;
+  const int bm = gemm_bm(p.path);
+  const int64_t mt = (bt + bm - 1) / bm;
+  void *n = at<void>(ws, p.n);
+  void *h = at<void>(ws, p.h);
+  {
+    PhaseScope ph(PH_FFN_NORM, s);
+    MOE_TRY_HIP(launch_combine_norm(x, p.path == PATH_BF16, nullptr, bt, 1, d, w->gamma,
+                                    cfg->rms_eps, n, s));
+  }
+  {
+    GemmArgs a = ffn_args(cfg);
+    a.M = bt;
+    a.N = I;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{n, d, w->w_gate, d, nullptr, d};
+    a.b_up = w->w_up;
+    a.out = h;
+    a.ldo = I;
+    PhaseScope ph(PH_FFN_GATEUP, s);
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE_SITU, WF_BF16, mt, s));
+  }
+  {
+    GemmArgs a = ffn_args(cfg);
+    a.M = bt;
+    a.N = d;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{h, I, w->w_down, I, nullptr, I};
+    a.partial = at<float>(ws, p.split);
+    a.partial_cap = p.split_cap;
+    a.resid = r;
+    a.ldr = d;
+    a.out = y;
+    a.ldo = d;
+    PhaseScope ph(PH_FFN_DOWN, s);
+    MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, WF_BF16, mt, s));
   }
   return MOE_OK;
 }

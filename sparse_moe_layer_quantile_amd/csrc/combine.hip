@@ -12,7 +12,9 @@
 // registers as fp32 (NCH 16-byte chunks per lane), then
 // n = y_lat / sqrt(mean(y_lat^2) + eps) * gamma.  The k rows of a token are
 // read eight at a time, so each lane has up to 8 NCH loads in flight; the
-// pass is bound by reading o once.
+// pass is bound by reading o once.  With inv_perm NULL and k = 1 it is a plain
+// RMSNorm of row t (the dense FFN's pre-norm; mkdocs.reaper.mx "Vue d'ensemble
+// de l'architecture", section "Ce que fait une couche").
 #include "common.h"
 #include "kernels.h"
 
@@ -39,7 +41,8 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const void *__restric
   for (int j0 = 0; j0 < k; j0 += 8) {
     int64_t pos[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pos[u] = j0 + u < k ? (int64_t)ip[j0 + u] : -1;
+    for (int u = 0; u < 8; ++u)
+      pos[u] = j0 + u < k ? (inv_perm ? (int64_t)ip[j0 + u] : t) : -1;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
@@ -127,6 +130,9 @@ static hipError_t launch_cn(const void *o, const int32_t *inv_perm, int64_t bt, 
   if (per_lane <= 8)
     return launch_kernel(combine_norm_kernel<BF16, 8>, grid, block, 0, s, o, inv_perm, bt, (int)k,
                          (int)L, gamma, eps, n);
+  if (per_lane <= 16 && inv_perm == nullptr)  // plain RMSNorm rows up to 16 chunks a lane
+    return launch_kernel(combine_norm_kernel<BF16, 16>, grid, block, 0, s, o, inv_perm, bt,
+                         (int)k, (int)L, gamma, eps, n);
   return hipErrorInvalidValue;
 }
 
@@ -135,7 +141,7 @@ hipError_t launch_combine_norm(const void *o, bool bf16, const int32_t *inv_perm
                                hipStream_t s) {
   if (bt <= 0) return hipSuccess;
   // rows are read as 16-byte chunks: L a multiple of 8 (bf16) or 4 (fp32), at most
-  // 8 chunks per lane
+  // 8 chunks per lane (16 for a plain RMSNorm: inv_perm NULL, k = 1)
   if (bf16) return launch_cn<true>(o, inv_perm, bt, k, L, gamma, eps, n, s);
   return launch_cn<false>(o, inv_perm, bt, k, L, gamma, eps, n, s);
 }

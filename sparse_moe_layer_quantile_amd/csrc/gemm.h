@@ -47,6 +47,8 @@ struct GemmArgs {
   float *out_t;              // router: transposed copy [N][M] (may be NULL)
   const float *bias;         // router: [N] (may be NULL)
   const float *row_scale;    // SiTU: factor of output row m (NULL = 1)
+  const void *resid;         // store: out = acc + resid[m][ldr] (OutT; NULL = none; may be out)
+  int64_t ldr;
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;         // N tiles (direct-to-LDS engine: groups of nper N tiles)
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
@@ -106,6 +108,13 @@ __device__ __forceinline__ void store_out(void *out, int64_t i, float v) {
   else static_cast<uint16_t *>(out)[i] = f32_to_bf16(v);
 }
 
+// Element i of an OutT tensor, as fp32 (the residual of a store epilogue).
+template <typename OutT>
+__device__ __forceinline__ float load_in(const void *p, int64_t i) {
+  if constexpr (sizeof(OutT) == 4) return static_cast<const float *>(p)[i];
+  else return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+}
+
 // Epilogue of one output element (row, col).  v: accumulator (gate for
 // dual), vu: the up accumulator of a dual problem.
 template <int EPI, typename OutT>
@@ -119,6 +128,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, int64_t row, int64_t
     store_out<OutT>(a.out, row * a.ldo + col,
                     f * situ(v, vu, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
   } else {
+    if (a.resid) v += load_in<OutT>(a.resid, row * a.ldr + col);
     store_out<OutT>(a.out, row * a.ldo + col, v);
   }
 }

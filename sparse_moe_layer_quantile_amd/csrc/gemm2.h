@@ -724,9 +724,15 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           for (int j = 0; j < JN; ++j)
             if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
         } else {
+          // store, plus the residual row (read before the write: it may be the output)
+          const void *rrow = args.resid ? static_cast<const char *>(args.resid) +
+                                              row * args.ldr * (int64_t)sizeof(OutT)
+                                        : nullptr;
 #pragma unroll
           for (int j = 0; j < JN; ++j)
-            if (col_ok[j]) store_out<OutT>(orow, col[j], acc[i][j][r]);
+            if (col_ok[j])
+              store_out<OutT>(orow, col[j],
+                              acc[i][j][r] + (rrow ? load_in<OutT>(rrow, col[j]) : 0.0f));
         }
       }
     }
@@ -1046,6 +1052,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a) {
       store_out<OutT>(a.out, row * a.ldo + col,
                       f * situ(g, u, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
     } else {
+      if (a.resid) g += load_in<OutT>(a.resid, row * a.ldr + col);
       store_out<OutT>(a.out, row * a.ldo + col, g);
     }
   }

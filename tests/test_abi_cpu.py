@@ -39,7 +39,8 @@ def test_struct_layouts_match_header():
     """sizeof / offsetof of every ABI struct, from gcc on the header, equal the
     ctypes mirrors used by the binding."""
     structs = {"moe_config": moe.MoeConfig, "moe_weights": moe.MoeWeights,
-               "moe_route_out": moe.MoeRouteOut, "moe_dispatch_out": moe.MoeDispatchOut}
+               "moe_route_out": moe.MoeRouteOut, "moe_dispatch_out": moe.MoeDispatchOut,
+               "moe_ffn_config": moe.MoeFfnConfig, "moe_ffn_weights": moe.MoeFfnWeights}
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
     for s, cls in structs.items():
         src.append(f'printf("{s} %zu\\n", sizeof({s}));')
@@ -122,3 +123,21 @@ def test_argument_errors_before_any_launch():
     assert moe.moe_forward(c, w, 1, 64, 1, None, None, 256, need, 0) == -1  # no expert weights
     assert moe.status_str(-3).startswith("workspace")
     assert moe.status_str(7) == "unknown status"
+
+
+def test_ffn_workspace_and_validation():
+    """The dense FFN's host-side checks (no launch)."""
+    c = moe.make_ffn_config(7168, 33792)
+    ws = moe.ffn_workspace_bytes(c, 16384)
+    # n [bt][d] and h [bt][inter] in bf16, no split-K region above 256 rows
+    assert ws >= 2 * 16384 * (7168 + 33792) and ws < 2 * 16384 * (7168 + 33792) + 4096
+    small = moe.ffn_workspace_bytes(c, 64)
+    assert small >= 2 * 64 * (7168 + 33792) + 4 * 16 * 64 * 7168  # with the split-K region
+    assert moe.ffn_workspace_bytes(moe.make_ffn_config(7168 + 32, 33792), 8) == 0  # d % 64
+    assert moe.ffn_workspace_bytes(moe.make_ffn_config(8192 + 64, 1024), 8) == 0   # d > 8192
+    assert moe.ffn_workspace_bytes(moe.make_ffn_config(4096 + 64, 1024, act="f32"), 8) == 0
+    assert moe.ffn_workspace_bytes(moe.make_ffn_config(1024, 1000), 8) == 0        # inter % 64
+    assert moe.ffn_workspace_bytes(moe.make_ffn_config(1024, 1024), -1) == 0
+    w = moe.MoeFfnWeights(0, 0, 0, 0)
+    # NULL weights are rejected before anything touches the device
+    assert moe.moe_ffn_forward(c, w, 0, 0, 8, 0, 0, 0, 0) == -1
