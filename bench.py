@@ -116,6 +116,103 @@ def roofline_of(name, flops, nbytes, ms):
     return out
 
 
+def ffn_phase_work(cfg) -> dict:
+    """Algorithmic FLOPs and HBM bytes of each phase of the dense FFN."""
+    bt, d, I = cfg.bt, cfg.d, cfg.inter
+    ab = 4 if cfg.act == "f32" else 2
+    return {
+        "ffn_norm": (0, 2 * bt * d * ab + 4 * d),
+        "ffn_gateup": (2 * bt * d * 2 * I, bt * d * ab + 2 * I * d * ab + bt * I * ab),
+        "ffn_down": (2 * bt * I * d, bt * I * ab + d * I * ab + 2 * bt * d * ab),
+    }
+
+
+def ffn_cpu_baseline(cfg, seed: int, n_rows: int) -> dict:
+    """The fp64 CPU oracle on a bounded sample of rows of the same FFN workload."""
+    import oracle
+    import synth
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    sp = synth.ffn_specs(cfg)
+    m = {n: oracle.Mat(synth.ffn_host_tensor(cfg, n, seed).reshape(sp[n].shape))
+         for n in ("w_gate", "w_up", "w_down")}
+    rows = np.arange(min(n_rows, cfg.bt))
+    x = oracle.decode(synth.ffn_host_rows(cfg, "x", rows, seed))
+    r = oracle.decode(synth.ffn_host_rows(cfg, "r", rows, seed))
+    g = synth.ffn_gamma(cfg)
+    shape = oracle.FfnShape(cfg.d, cfg.inter, cfg.beta, cfg.beta_u, cfg.rms_eps)
+    t0 = time.perf_counter()
+    for i in range(len(rows)):
+        oracle.dense_ffn(shape, m["w_gate"], m["w_up"], m["w_down"], x[i], r[i], g)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {cfg.bt} rows through RMSNorm, gate/up, SiTU, down and "
+                      f"the residual ({dt:.1f} s); extrapolated to tokens/s"}
+
+
+def bench_ffn(args) -> int:
+    """The dense layer-1 FFN workloads: same timing protocol and JSON line."""
+    import torch
+    import synth
+    import sparse_moe_layer_quantile_amd as moe
+    cfg = synth.FFN_CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    t = synth.ffn_device_layer(cfg, args.seed)
+    layer = moe.DenseFFN(moe.make_ffn_config(cfg.d, cfg.inter, cfg.beta, cfg.beta_u,
+                                             cfg.rms_eps, act=cfg.act), t)
+    x, r = t["x"], t["r"]
+    y = torch.empty_like(x)
+    moe.profile_enable(True)
+    for _ in range(args.warmup):
+        layer.forward(x, r, out=y)
+    torch.cuda.synchronize()
+    moe.profile_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, r, out=y)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    phases = {n: v for n, v in moe.profile_read().items() if n.startswith("ffn_")}
+    moe.profile_enable(False)
+    work = ffn_phase_work(cfg)
+    dom = max(phases, key=lambda n: phases[n][0])
+    roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0])
+    roof["traffic"] = measured_traffic(cfg.name, dom)
+    line = {
+        "metric": "dense layer-1 FFN tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)",
+        "value": cfg.bt * args.steps / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "bt": cfg.bt, "d": cfg.d, "inter": cfg.inter,
+                   "parallelism": "1 GPU"},
+        "roofline": roof,
+        "layer": {"tflops": cfg.flops() / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": cfg.flops() / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)},
+        "phases_ms": {n: round(v[0], 4) for n, v in phases.items()},
+        "kernel_sources": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = ffn_cpu_baseline(cfg, args.seed, min(args.cpu_tokens, 64))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
     """The fp64 CPU oracle on a bounded sample of the same workload."""
     import oracle
@@ -217,8 +314,11 @@ def main(argv=None):
               "(run with --gpus 1).", file=sys.stderr)
         return 2
 
-    import torch
     import synth
+    if args.config in synth.FFN_CONFIGS:
+        return bench_ffn(args)
+
+    import torch
     import sparse_moe_layer_quantile_amd as moe
     from tests import parity
 
