@@ -33,7 +33,8 @@ class OrcShape(ctypes.Structure):
                 ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
                 ("expert_inter", ctypes.c_int64), ("n_shared", ctypes.c_int64),
                 ("shared_inter", ctypes.c_int64), ("beta", ctypes.c_double),
-                ("beta_u", ctypes.c_double), ("rms_eps", ctypes.c_double)]
+                ("beta_u", ctypes.c_double), ("rms_eps", ctypes.c_double),
+                ("act_mx_block", ctypes.c_int64)]
 
 
 class OrcWeights(ctypes.Structure):
@@ -74,6 +75,8 @@ def lib():
             "orc_output": ([P, P, P, P, P], ctypes.c_int),
             "orc_forward": ([P, P, P, I64, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "orc_rmsnorm": ([P, I64, P, D, P], None),
+            "orc_mx8_quantize": ([P, I64, I64, P, P], ctypes.c_int),
+            "orc_double_to_e4m3": ([D], ctypes.c_uint8),
             "orc_dense_ffn": ([P, P, P, P, P, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -97,9 +100,10 @@ def _c(a, dt=None):
 
 def shape_of(cfg) -> OrcShape:
     g = lambda n, dflt=0: getattr(cfg, n, dflt)
+    mx = 32 if getattr(cfg, "act_quant", "none") == "mxfp8" else 0
     return OrcShape(g("d"), g("latent"), g("n_experts"), g("top_k"), g("expert_inter"),
                     g("n_shared"), g("shared_inter"), float(g("beta", 4.0)),
-                    float(g("beta_u", 25.0)), float(g("rms_eps", 1e-6)))
+                    float(g("beta_u", 25.0)), float(g("rms_eps", 1e-6)), mx)
 
 
 class Mat:
@@ -282,6 +286,20 @@ def output(cfg, w: Weights, n, x_t) -> np.ndarray:
     if lib().orc_output(ctypes.byref(shape_of(cfg)), w.ref, _ptr(n), _ptr(x_t), _ptr(y)):
         raise ValueError("orc_output rejected its arguments")
     return y
+
+
+def double_to_e4m3(v) -> int:
+    return int(lib().orc_double_to_e4m3(float(v)))
+
+
+def mx8_quantize(x, block=32):
+    """(E4M3 codes uint8 [n], E8M0 scales uint8 [n / block]) of x (OCP MX FP8)."""
+    x = _c(x, np.float64).ravel()
+    codes = np.empty(x.size, np.uint8)
+    scales = np.empty(x.size // block, np.uint8)
+    if lib().orc_mx8_quantize(_ptr(x), x.size, block, _ptr(codes), _ptr(scales)):
+        raise ValueError("orc_mx8_quantize rejected its arguments")
+    return codes, scales
 
 
 def rmsnorm(x, gamma=None, eps=1e-6) -> np.ndarray:

@@ -140,6 +140,58 @@ double orc_e8m0_to_double(uint8_t code) {
   return std::ldexp(1.0, (int)code - 127);
 }
 
+// Nearest E4M3 value: |v| = 2^e (1 + f), the mantissa rounded to 3 bits
+// (normal, e >= -6) or |v| rounded to a multiple of 2^-9 (subnormal), ties to
+// even, at most 448.
+uint8_t orc_double_to_e4m3(double v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  const double a = std::fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  int e2;
+  std::frexp(a, &e2);  // a = m 2^e2, m in [0.5, 1)
+  const int e = e2 - 1;  // a in [2^e, 2^(e+1))
+  if (e < -6) {
+    const double q = std::nearbyint(std::ldexp(a, 9));  // multiples of 2^-9, ties to even
+    return sign | (uint8_t)q;  // q == 8 is the smallest normal, code 0x08
+  }
+  double mant = std::nearbyint((std::ldexp(a, -e) - 1.0) * 8.0);
+  int eb = e + 7;
+  if (mant == 8.0) {
+    mant = 0.0;
+    eb += 1;
+  }
+  const int code = (eb << 3) | (int)mant;
+  return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes,
+                     uint8_t *scales) {
+  if (!x || !codes || !scales || block <= 0 || n % block) return -1;
+  for (int64_t b0 = 0; b0 < n; b0 += block) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < block; ++i) amax = std::max(amax, std::fabs(x[b0 + i]));
+    int shared = -127;
+    if (amax > 0.0) {
+      int e2;
+      std::frexp(amax, &e2);
+      shared = std::min(127, std::max(-127, (e2 - 1) - 8));
+    }
+    scales[b0 / block] = (uint8_t)(shared + 127);
+    for (int64_t i = 0; i < block; ++i)
+      codes[b0 + i] = orc_double_to_e4m3(std::ldexp(x[b0 + i], -shared));
+  }
+  return 0;
+}
+
+// x replaced by its MX FP8 quantisation (dequantised exactly), blocks of `block`.
+static void mx8_round_trip(double *x, int64_t n, int64_t block) {
+  std::vector<uint8_t> codes((size_t)n), scales((size_t)(n / block));
+  orc_mx8_quantize(x, n, block, codes.data(), scales.data());
+  for (int64_t i = 0; i < n; ++i)
+    x[i] = orc_e4m3_to_double(codes[i]) * orc_e8m0_to_double(scales[i / block]);
+}
+
 double orc_decode(const orc_mat *m, int64_t mat, int64_t r, int64_t c) {
   std::vector<double> row((size_t)m->cols);
   decode_row(m, mat, r, row.data());
@@ -269,11 +321,15 @@ int orc_dispatch(const int32_t *idx, int64_t bt, int64_t k, int64_t n_experts,
 int orc_expert(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
                const orc_mat *w_down, int64_t mat, const double *x_lat, double *o) {
   if (!s || !w_gate || !w_up || !w_down || !x_lat || !o) return -1;
-  const int64_t I = s->expert_inter;
+  const int64_t I = s->expert_inter, L = s->latent, qb = s->act_mx_block;
+  if (qb < 0 || (qb > 0 && (L % qb || I % qb))) return -1;
+  std::vector<double> xin(x_lat, x_lat + L);
+  if (qb > 0) mx8_round_trip(xin.data(), L, qb);  // the gate/up GEMMs read MX FP8 x_lat
   std::vector<double> g((size_t)I), u((size_t)I), h((size_t)I);
-  orc_matvec(w_gate, mat, x_lat, g.data());
-  orc_matvec(w_up, mat, x_lat, u.data());
+  orc_matvec(w_gate, mat, xin.data(), g.data());
+  orc_matvec(w_up, mat, xin.data(), u.data());
   for (int64_t i = 0; i < I; ++i) h[i] = orc_phi(g[i], s->beta) * orc_psi(u[i], s->beta_u);
+  if (qb > 0) mx8_round_trip(h.data(), I, qb);  // and the down GEMM MX FP8 h
   orc_matvec(w_down, mat, h.data(), o);
   return 0;
 }

@@ -67,6 +67,11 @@ typedef struct {
 typedef struct {
   int64_t d, latent, n_experts, top_k, expert_inter, n_shared, shared_inter;
   double beta, beta_u, rms_eps;
+  /* 0: the routed experts read their inputs exactly.  32: each expert GEMM
+   * reads its input (x_lat for gate/up, h for down) quantised to OCP MX FP8
+   * E4M3 with one E8M0 scale per 32 consecutive elements (orc_mx8_quantize),
+   * and the routing weight multiplies the expert output as always. */
+  int64_t act_mx_block;
 } orc_shape;
 
 typedef struct {
@@ -90,6 +95,18 @@ double orc_e4m3_to_double(uint8_t code);
  * code 255 is NaN. */
 double orc_e2m1_to_double(uint8_t code);
 double orc_e8m0_to_double(uint8_t code);
+
+/* OCP MX FP8 (E4M3) quantisation of x[n] in blocks of `block` consecutive
+ * elements (OCP Microscaling Formats (MX) Specification v1.0, the conversion
+ * of a vector of scalars to an MX block): per block the shared exponent is
+ * floor(log2(max |x|)) - 8 (8 = the largest E4M3 exponent), clamped to
+ * [-127, 127] (-127 for an all-zero block); each element is x / 2^shared
+ * rounded to the nearest E4M3 value, ties to even, magnitudes beyond 448
+ * saturating to 448.  codes[n] E4M3 bytes, scales[n / block] E8M0 codes
+ * (shared + 127).  n a multiple of block. */
+int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes, uint8_t *scales);
+/* Nearest E4M3 code of a double (ties to even, saturating at +-448). */
+uint8_t orc_double_to_e4m3(double v);
 
 /* out[r] = sum_c M[mat][r][c] in[c], fp64, c ascending. */
 void orc_matvec(const orc_mat *m, int64_t mat, const double *in, double *out);

@@ -69,6 +69,9 @@ class Config:
     router: str = "bf16"
     bias: str = "zero"          # "zero" or "zipf1.1"
     cutoff: str = "given"       # benchmark cutoff mode: "given" (alpha = 0) or "batch"
+    # "mxfp8": the expert GEMMs read their inputs (x_lat, h) as OCP MX FP8 with a scale
+    # per 32 (with weight="mxfp4": the block-scaled MFMA path); "none": exactly
+    act_quant: str = "none"
     beta: float = 4.0
     beta_u: float = 25.0
     rms_eps: float = 1e-6
@@ -118,6 +121,11 @@ CONFIGS: Dict[str, Config] = {
                                n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
                                shared_inter=3072, weight="mxfp4", bias="zipf1.1",
                                cutoff="batch"),
+    # MXFP4 experts read MX FP8 activations: the gfx950 block-scaled MFMA (W4A8)
+    "k3_prefill_mxfp4_a8": Config("k3_prefill_mxfp4_a8", bt=16384, d=7168, latent=3584,
+                                  n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                                  shared_inter=3072, weight="mxfp4", bias="zipf1.1",
+                                  cutoff="batch", act_quant="mxfp8"),
     # one GPU's share of K3 prefill under 8-way expert parallelism: its own 16384 tokens
     # through the replicated dense parts, and 262144 pairs over its 112 experts
     # (about 2341 rows per expert), so the grouped GEMMs run at the sharded shape

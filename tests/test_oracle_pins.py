@@ -633,3 +633,82 @@ def test_batch_quantile_balances_zipf_skewed_load():
     mean = cfg.bt * cfg.top_k / cfg.n_experts
     assert given.max() > 3 * mean
     assert batch.max() < 1.6 * mean and batch.min() > 0.4 * mean
+
+
+# ---- MX FP8 activations (the expert GEMMs' inputs in the block-scaled MFMA path) ---------
+
+def test_e4m3_encode_round_trips_every_code_and_rounds_to_even():
+    for code in list(range(0x7F)) + list(range(0x81, 0xFF)):
+        assert oracle.double_to_e4m3(oracle.e4m3_to_double(code)) == code, hex(code)
+    assert oracle.double_to_e4m3(-0.0) == 0x80
+    assert oracle.double_to_e4m3(1.0625) == 0x38      # tie 1.0 / 1.125 -> even (1.0)
+    assert oracle.double_to_e4m3(1.1875) == 0x3A      # tie 1.125 / 1.25 -> even (1.25)
+    assert oracle.double_to_e4m3(2.0 ** -10) == 0x00  # subnormal tie 0 / 2^-9 -> 0
+    assert oracle.double_to_e4m3(3 * 2.0 ** -10) == 0x02
+    assert oracle.double_to_e4m3(447.0) == 0x7E and oracle.double_to_e4m3(1e6) == 0x7E
+    assert oracle.double_to_e4m3(-1e6) == 0xFE
+
+
+def test_e4m3_encode_is_nearest_by_brute_force():
+    grid = np.array([oracle.e4m3_to_double(c) for c in range(0x7F)])  # 0 .. 448
+    rng = np.random.default_rng(40)
+    for v in np.concatenate([rng.normal(0, 30, 3000), rng.normal(0, 0.01, 1000)]):
+        c = oracle.double_to_e4m3(v)
+        d = np.abs(grid - min(abs(v), 448.0))
+        assert abs(oracle.e4m3_to_double(c & 0x7F) - abs(v)) <= d.min() + 1e-300
+        assert (c >> 7) == (v < 0)
+
+
+def test_mx8_block_rules():
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 3, 32 * 20) * np.repeat(2.0 ** rng.integers(-20, 20, 20), 32)
+    x[64:96] = 0.0  # an all-zero block
+    codes, sc = oracle.mx8_quantize(x, 32)
+    for b in range(20):
+        blk = x[32 * b:32 * (b + 1)]
+        amax = np.abs(blk).max()
+        if amax == 0:
+            assert sc[b] == 0 and not codes[32 * b:32 * (b + 1)].any()
+            continue
+        assert sc[b] == int(np.floor(np.log2(amax))) - 8 + 127
+        top = codes[32 * b + int(np.argmax(np.abs(blk)))] & 0x7F
+        assert 0x78 <= top <= 0x7E  # the block maximum lands in [256, 448]
+        deq = np.array([oracle.e4m3_to_double(c) for c in codes[32 * b:32 * (b + 1)]]) * \
+            2.0 ** (int(sc[b]) - 127)
+        step = 2.0 ** (int(sc[b]) - 127)
+        # within half an E4M3 ulp (relative 2^-4 for normals, 2^-10 * scale below them)
+        assert np.all(np.abs(deq - blk) <= np.maximum(np.abs(blk) * 2.0 ** -4, step * 2.0 ** -10)
+                      + np.where(np.abs(blk) > 448 * step, np.abs(blk) - 448 * step, 0))
+    # a power-of-two scaling of a block only moves its shared exponent
+    c2, s2 = oracle.mx8_quantize(x * 2.0 ** 5, 32)
+    np.testing.assert_array_equal(c2, codes)
+    nz = sc > 0
+    np.testing.assert_array_equal(s2[nz], sc[nz] + 5)
+
+
+def test_expert_with_mx8_inputs_is_the_quantised_composition():
+    """act_mx_block = 32: gate/up read MX FP8 x_lat, down reads MX FP8 h (each
+    quantised in blocks of 32), composed from the pinned pieces."""
+    rng = np.random.default_rng(42)
+    L, I = 64, 96
+    Wg, Wu = f32(rng.normal(size=(I, L)) / 8), f32(rng.normal(size=(I, L)) / 8)
+    Wd = f32(rng.normal(size=(L, I)) / 10)
+    x = rng.normal(size=L)
+
+    def q(v):
+        c, s = oracle.mx8_quantize(v, 32)
+        return np.array([oracle.e4m3_to_double(k) for k in c]) * np.repeat(
+            2.0 ** (s.astype(np.int64) - 127), 32)
+
+    s = Shape(latent=L, expert_inter=I)
+    s.act_quant = "mxfp8"
+    o = oracle.expert(s, oracle.Mat(Wg), oracle.Mat(Wu), oracle.Mat(Wd), x)
+    xq = q(x)
+    g, u = Wg.astype(np.float64) @ xq, Wu.astype(np.float64) @ xq
+    h = np.array([oracle.phi(a) * oracle.psi(b) for a, b in zip(g, u)])
+    np.testing.assert_allclose(o, Wd.astype(np.float64) @ q(h), rtol=1e-12, atol=1e-12)
+    # and it differs from the exact expert by the quantisation only (a few per cent)
+    s.act_quant = "none"
+    o_exact = oracle.expert(s, oracle.Mat(Wg), oracle.Mat(Wu), oracle.Mat(Wd), x)
+    rel = np.abs(o - o_exact).max() / np.abs(o_exact).max()
+    assert 1e-4 < rel < 0.1
