@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the block-scaled MFMA on fp8 operands)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "LatentMoE layer tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 
@@ -51,7 +52,12 @@ def phase_work(cfg, touched: int) -> dict:
     else:
         xw = lambda r, c: r * c * wb + sc(r, c)
     batch = cfg.cutoff == "batch"
-    return {
+    a8 = getattr(cfg, "act_quant", "none") == "mxfp8"
+    # MX FP8 expert inputs: the GEMMs read codes + E8M0 bytes, a quantiser writes them
+    qb = (lambda n: n + n // 32) if a8 else (lambda n: n * ab)
+    extra = {"xlat_quant": (0, bt * L * ab + bt * L * 33 // 32),
+             "h_quant": (0, P * I * ab + P * I * 33 // 32)} if a8 else {}
+    return {**extra,
         "shared_gateup": (2 * bt * d * 2 * S * Is,
                           bt * d * ab + 2 * S * (Is * d * wb + sc(Is, d)) + bt * S * Is * ab),
         "router_logits": (2 * bt * d * E, bt * d * ab + E * d * rb + bt * E * 4 * (2 if batch else 1)),
@@ -59,8 +65,8 @@ def phase_work(cfg, touched: int) -> dict:
         "topk": (0, bt * E * 4 + P * 8),
         "dispatch": (0, P * 4 + P * 8),
         "down_proj": (2 * bt * d * L, bt * d * ab + L * d * wb + sc(L, d) + bt * L * ab),
-        "expert_gateup": (2 * P * 2 * L * I, touched * 2 * xw(I, L) + bt * L * ab + P * I * ab),
-        "expert_down": (2 * P * L * I, touched * xw(L, I) + P * I * ab + P * L * ab),
+        "expert_gateup": (2 * P * 2 * L * I, touched * 2 * xw(I, L) + qb(bt * L) + P * I * ab),
+        "expert_down": (2 * P * L * I, touched * xw(L, I) + qb(P * I) + P * L * ab),
         "combine_norm": (0, P * L * ab + bt * L * ab),
         "output": (2 * bt * (L + S * Is) * d,
                    bt * (L + S * Is) * ab + d * (L + S * Is) * wb + sc(d, L) + S * sc(d, Is)
@@ -98,20 +104,20 @@ def measured_traffic(workload: str, kernel: str):
     return k["bytes_per_launch"]
 
 
-def roofline_of(name, flops, nbytes, ms):
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+def roofline_of(name, flops, nbytes, ms, peak_tflops=PEAK_BF16_TFLOPS):
+    t_mfma = flops / (peak_tflops * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
         ach = flops / (ms * 1e-3) / 1e12
-        out = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-               "frac": ach / PEAK_BF16_TFLOPS}
+        out = {"bound": "mfma", "achieved": ach, "peak": peak_tflops, "unit": "TFLOP/s",
+               "frac": ach / peak_tflops}
     else:
         ach = nbytes / (ms * 1e-3) / 1e9
         out = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                "frac": ach / PEAK_HBM_GBS}
     out.update({"traffic": None, "kernel": name, "ms": ms, "algorithmic_flops": flops,
                 "algorithmic_bytes": nbytes,
-                "mfma_frac": flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                "mfma_frac": flops / (ms * 1e-3) / (peak_tflops * 1e12),
                 "hbm_frac": nbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9)})
     return out
 
@@ -360,7 +366,10 @@ def main(argv=None):
 
     work = phase_work(cfg, touched)
     dom = max(phases, key=lambda n: phases[n][0])
-    roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0])
+    a8 = cfg.act_quant == "mxfp8"
+    # the routed experts' GEMMs on MX FP8 inputs run the block-scaled MFMA at the fp8 rate
+    peak = PEAK_FP8_TFLOPS if a8 and dom.startswith("expert_") else PEAK_BF16_TFLOPS
+    roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0], peak)
     roof["traffic"] = measured_traffic(cfg.name, dom)
     layer_flops = cfg.flops()
     line = {
@@ -374,12 +383,13 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "dtype": ("bf16+mxfp8-experts" if a8 else "bf16") if cfg.act == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "bt": cfg.bt, "d": cfg.d, "latent": cfg.latent,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k,
                    "expert_inter": cfg.expert_inter, "n_shared": cfg.n_shared,
                    "shared_inter": cfg.shared_inter, "weights": cfg.weight,
+                   "expert_inputs": "mxfp8" if a8 else cfg.act,
                    "cutoff": cfg.cutoff, "router_bias": cfg.bias,
                    "parallelism": "1 GPU", "streams": 2 if args.two_streams else 1},
         "roofline": roof,

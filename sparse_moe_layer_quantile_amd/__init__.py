@@ -19,9 +19,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4, MOE_MXFP4_A8 = 0, 1, 2, 3, 4
 CUTOFF_GIVEN, CUTOFF_BATCH = 0, 1
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128, "mxfp4": MOE_MXFP4}
+# "mxfp4_a8": MXFP4 experts with their inputs quantised to MX FP8 in the layer
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128, "mxfp4": MOE_MXFP4,
+          "mxfp4_a8": MOE_MXFP4_A8}
 CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH}
 
 _P = ctypes.c_void_p
@@ -98,6 +100,8 @@ def _load():
     lib.moe_ffn_forward.argtypes = [CP(MoeFfnConfig), CP(MoeFfnWeights), _P, _P, ctypes.c_int64,
                                     _P, _P, ctypes.c_size_t, _P]
     lib.moe_ffn_forward.restype = ctypes.c_int
+    lib.moe_mx8_quantize.argtypes = [_P, ctypes.c_int64, _P, _P, _P]
+    lib.moe_mx8_quantize.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_profile_enable.argtypes = [ctypes.c_int]
@@ -113,8 +117,28 @@ LIB = _load()
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_status_str", "moe_profile_enable", "moe_profile_read",
-            "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward")
-N_PHASES = 13
+            "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward",
+            "moe_mx8_quantize")
+
+
+def moe_mx8_quantize(x: int, n: int, codes: int, scales: int, stream: int) -> int:
+    return LIB.moe_mx8_quantize(_P(x or None), n, _P(codes or None), _P(scales or None),
+                                _P(stream or None))
+
+
+def mx8_quantize(x):
+    """MX FP8 codes (uint8, x's shape) and E8M0 scales (uint8, last dim / 32) of
+    a bf16 device tensor, blocks of 32 along the last dimension."""
+    import torch
+    x = x.contiguous()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((*x.shape[:-1], x.shape[-1] // 32), dtype=torch.uint8, device=x.device)
+    st = moe_mx8_quantize(x.data_ptr(), x.numel(), codes.data_ptr(), scales.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise MoeError(st, "moe_mx8_quantize")
+    return codes, scales
+N_PHASES = 15
 
 
 def status_str(status: int) -> str:

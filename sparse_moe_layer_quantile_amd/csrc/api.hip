@@ -38,7 +38,8 @@ int64_t elem_size(int32_t dt) {
     case MOE_F32: return 4;
     case MOE_BF16: return 2;
     case MOE_FP8E4M3_B128: return 1;
-    case MOE_MXFP4: return 2;  // the dense weights of an MXFP4 layer are bf16
+    case MOE_MXFP4:
+    case MOE_MXFP4_A8: return 2;  // the dense weights of an MXFP4 layer are bf16
   }
   return 0;
 }
@@ -51,7 +52,7 @@ struct Plan {
   int64_t act_bytes = 2;
   // byte offsets into the workspace
   size_t z, zT, alpha, idx, w, w_sorted, counts, offsets, tile_offsets, perm, inv_perm, masks,
-      xlat, h, o, n, hs, split, split_sh, total;
+      xlat, h, o, n, hs, split, split_sh, xq, xq_sc, hq, hq_sc, total;
   int64_t split_cap = 0;  // floats in each split-K region (0: split K off)
 };
 
@@ -81,8 +82,8 @@ moe_status check_config(const moe_config *c) {
     return MOE_ERR_UNSUPPORTED;
   // MXFP4 experts: K ranges (latent, expert_inter) of whole 128-element groups
   // (a dword of E8M0 codes), with the codes of a B row (K/32 <= 128) in LDS
-  if (c->weight_dtype == MOE_MXFP4 &&
-      (c->latent % 128 || c->expert_inter % 128 || c->expert_inter > 4096))
+  const bool mx4 = c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8;
+  if (mx4 && (c->latent % 128 || c->expert_inter % 128 || c->expert_inter > 4096))
     return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
   // fp8 GEMMs stage the block scales of up to 128 K blocks in LDS
@@ -102,11 +103,17 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->path = c->act_dtype == MOE_F32 ? PATH_F32 : PATH_BF16;
   p->fp8 = c->weight_dtype == MOE_FP8E4M3_B128;
   p->dense_wf = p->fp8 ? WF_FP8 : WF_BF16;
-  p->expert_wf = c->weight_dtype == MOE_MXFP4 ? WF_MX4 : p->dense_wf;
+  p->expert_wf = c->weight_dtype == MOE_MXFP4      ? WF_MX4
+                 : c->weight_dtype == MOE_MXFP4_A8 ? WF_MX4A8
+                                                   : p->dense_wf;
   p->act_bytes = elem_size(c->act_dtype);
   const int64_t E = c->n_experts, k = c->top_k, P = bt * k, L = c->latent;
   // the bf16 engine addresses gathered x_lat rows with 32-bit byte offsets
   if (p->path == PATH_BF16 && bt * L * 2 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // MX FP8 A: the E8M0 codes of A rows are addressed from the matrix start
+  // with 32-bit offsets
+  if (p->expert_wf == WF_MX4A8 && P * (c->expert_inter / 32) > (int64_t)UINT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
   const int64_t nb = (bt + 63) / 64;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -139,6 +146,12 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   }
   p->split = take(4 * p->split_cap);
   p->split_sh = take(4 * p->split_cap);
+  // MX FP8 inputs of the routed experts' GEMMs: codes and E8M0 scales
+  const bool a8 = p->expert_wf == WF_MX4A8;
+  p->xq = take(a8 ? bt * L : 0);
+  p->xq_sc = take(a8 ? bt * L / 32 : 0);
+  p->hq = take(a8 ? P * c->expert_inter : 0);
+  p->hq_sc = take(a8 ? P * c->expert_inter / 32 : 0);
   p->total = off + kAlign;
   return MOE_OK;
 }
@@ -167,7 +180,7 @@ bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts)
     if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
     if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;
   }
-  if (c->weight_dtype == MOE_MXFP4) {
+  if (c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8) {
     // E8M0 codes are copied a dword at a time
     for (const uint8_t *e8 : {w->e8_gate, w->e8_up, w->e8_down})
       if (!e8 || reinterpret_cast<uintptr_t>(e8) % 4) return false;
@@ -192,12 +205,13 @@ GemmArgs base_args(const moe_config *c) {
 // ---- phase timing (measurement support) -------------------------------------------
 enum Phase {
   PH_SHARED = 0, PH_ROUTER, PH_CUTOFF, PH_TOPK, PH_DISPATCH, PH_DOWN_PROJ, PH_EXPERT_GATEUP,
-  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT, PH_FFN_NORM, PH_FFN_GATEUP, PH_FFN_DOWN
+  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT, PH_FFN_NORM, PH_FFN_GATEUP, PH_FFN_DOWN, PH_XLAT_QUANT,
+  PH_H_QUANT
 };
 const char *kPhaseNames[MOE_N_PHASES] = {
     "shared_gateup", "router_logits", "cutoff", "topk", "dispatch", "down_proj",
     "expert_gateup", "expert_down", "combine_norm", "output", "ffn_norm", "ffn_gateup",
-    "ffn_down"};
+    "ffn_down", "xlat_quant", "h_quant"};
 
 struct Profiler {
   bool on = false;
@@ -401,6 +415,16 @@ MOE_API moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, 
   return MOE_OK;
 }
 
+MOE_API moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes,
+                                    uint8_t *scales, void *stream) {
+  if (n < 0 || n % 32) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!x || !codes || !scales || reinterpret_cast<uintptr_t>(x) % 16) return MOE_ERR_INVALID_ARG;
+  if (n / 8 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY_HIP(launch_mx8_quant(x, n, codes, scales, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                                int64_t bt, void *y, moe_route_out *route,
                                moe_dispatch_out *disp, void *ws, size_t ws_bytes, void *stream,
@@ -452,6 +476,14 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     PhaseScope ph(PH_DOWN_PROJ, side);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_DENSE, dwf, dense_mt, side));
   }
+  // MX FP8 experts' input: x_lat quantised once per token (the gate/up GEMM
+  // gathers each token's codes k times)
+  const bool a8 = ewf == WF_MX4A8;
+  uint8_t *xq = at<uint8_t>(ws, p.xq), *xq_sc = at<uint8_t>(ws, p.xq_sc);
+  if (a8) {
+    PhaseScope ph(PH_XLAT_QUANT, side);
+    MOE_TRY_HIP(launch_mx8_quant(xlat, bt * L, xq, xq_sc, side));
+  }
   if (two_streams) MOE_TRY_HIP(hipEventRecord(ev_lat, ss));
   void *hs = at<void>(ws, p.hs);
   if (S > 0) {
@@ -502,35 +534,51 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.M = P;
     a.N = I;
     a.nseg = 1;
-    a.seg[0] = GemmSeg{xlat, L, w->w_gate, L, w->s_gate, L};
+    a.seg[0] = GemmSeg{a8 ? (const void *)xq : xlat, L, w->w_gate, L, w->s_gate, L};
+    if (a8) {
+      a.a_sc = xq_sc;
+      a.lda_sc = L / 32;
+    }
     a.b_up = w->w_up;
     a.bscale_up = w->s_up;
     a.offsets = offsets;
     a.tile_offsets = tile_offsets;
     a.n_experts = (int32_t)E;
     a.b_estride = I * L;
-    a.s_estride = fp8 ? (I / 128) * (L / 128) : ewf == WF_MX4 ? I * (L / 32) : 0;
+    a.s_estride = fp8 ? (I / 128) * (L / 128) : (ewf == WF_MX4 || a8) ? I * (L / 32) : 0;
     a.e8 = w->e8_gate;
     a.e8_up = w->e8_up;
     a.gather = perm;
     a.gather_div = (int32_t)k;
-    a.row_scale = w_sorted;  // h rows carry the routing weight: W_d (w h) = w (W_d h)
+    // h rows carry the routing weight: W_d (w h) = w (W_d h); with MX FP8 h
+    // the down GEMM applies it instead (h is quantised as the unweighted row)
+    a.row_scale = a8 ? nullptr : w_sorted;
     a.out = h;
     a.ldo = I;
     PhaseScope ph(PH_EXPERT_GATEUP, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, ewf, grouped_mt, s));
+  }
+  uint8_t *hq = at<uint8_t>(ws, p.hq), *hq_sc = at<uint8_t>(ws, p.hq_sc);
+  if (a8) {
+    PhaseScope ph(PH_H_QUANT, s);
+    MOE_TRY_HIP(launch_mx8_quant(h, P * I, hq, hq_sc, s));
   }
   {
     GemmArgs a = base_args(cfg);
     a.M = P;
     a.N = L;
     a.nseg = 1;
-    a.seg[0] = GemmSeg{h, I, w->w_down, I, w->s_down, I};
+    a.seg[0] = GemmSeg{a8 ? (const void *)hq : h, I, w->w_down, I, w->s_down, I};
+    if (a8) {
+      a.a_sc = hq_sc;
+      a.lda_sc = I / 32;
+      a.row_scale = w_sorted;
+    }
     a.offsets = offsets;
     a.tile_offsets = tile_offsets;
     a.n_experts = (int32_t)E;
     a.b_estride = L * I;
-    a.s_estride = fp8 ? (L / 128) * (I / 128) : ewf == WF_MX4 ? L * (I / 32) : 0;
+    a.s_estride = fp8 ? (L / 128) * (I / 128) : (ewf == WF_MX4 || a8) ? L * (I / 32) : 0;
     a.e8 = w->e8_down;
     a.out = o;
     a.ldo = L;

@@ -46,9 +46,13 @@ struct GemmArgs {
   int64_t ldo;
   float *out_t;              // router: transposed copy [N][M] (may be NULL)
   const float *bias;         // router: [N] (may be NULL)
-  const float *row_scale;    // SiTU: factor of output row m (NULL = 1)
+  const float *row_scale;    // SiTU and store: factor of output row m (NULL = 1)
   const void *resid;         // store: out = acc + resid[m][ldr] (OutT; NULL = none; may be out)
   int64_t ldr;
+  // MX FP8 A (direct-to-LDS engine, BF_MX4A8): E8M0 codes a_sc[row][lda_sc] of the A
+  // rows (gathered rows indexed as the A rows), one per 32 elements along K
+  const uint8_t *a_sc;
+  int64_t lda_sc;
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;         // N tiles (direct-to-LDS engine: groups of nper N tiles)
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)
@@ -128,6 +132,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, int64_t row, int64_t
     store_out<OutT>(a.out, row * a.ldo + col,
                     f * situ(v, vu, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
   } else {
+    if (a.row_scale) v *= a.row_scale[row];
     if (a.resid) v += load_in<OutT>(a.resid, row * a.ldr + col);
     store_out<OutT>(a.out, row * a.ldo + col, v);
   }

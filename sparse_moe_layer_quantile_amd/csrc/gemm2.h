@@ -123,6 +123,8 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w, float s) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
 template <int W>
 __device__ __forceinline__ uint32_t word_of(const uint4 &v) {
   static_assert(W >= 0 && W < 4, "four words");
@@ -226,7 +228,9 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
 }
 
 // Storage format of the B operand.
-enum BFmt { BF_BF16 = 0, BF_FP8 = 1, BF_MX4 = 2 };
+// BF_MX4A8: MXFP4 B with MX FP8 A (e4m3 codes, an E8M0 scale per 32): the
+// gfx950 block-scaled MFMA, the B codes widened to e4m3 in registers.
+enum BFmt { BF_BF16 = 0, BF_FP8 = 1, BF_MX4 = 2, BF_MX4A8 = 3 };
 
 // fp8 B operands: block scales of up to this many 128-wide K blocks (K <= 16384)
 constexpr int kMaxKBlocks = 128;
@@ -248,11 +252,13 @@ template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int MA
           bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64 || BK == 128 || BK == 256, "K tile of 32 to 256");
-  constexpr int RB = BK * 2;          // bytes per A tile row
+  // A is bf16, or (A8) MX FP8: e4m3 codes with an E8M0 scale per 32 along K
+  constexpr bool A8 = BF == BF_MX4A8;
+  constexpr int RB = BK * (A8 ? 1 : 2);  // bytes per A tile row
   constexpr int CPR = RB / 16;        // 16 B chunks per A row
   constexpr int RPI = 1024 / RB;      // A rows per DMA wave instruction
   // B is bf16, fp8 e4m3 with 128 x 128 block scales (B8), or MXFP4 (MX4)
-  constexpr bool B8 = BF == BF_FP8, MX4 = BF == BF_MX4;
+  constexpr bool B8 = BF == BF_FP8, MX4 = BF == BF_MX4 || A8;
   constexpr int ESZ_B = B8 ? 1 : 2;   // bytes per B element (bf16, fp8)
   // B bytes of n elements: n * BNUM / BDEN
   constexpr int BNUM = MX4 ? 1 : ESZ_B, BDEN = MX4 ? 2 : 1;
@@ -277,10 +283,16 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // ones.  K tiles of 64 (2 bytes a row) take a whole-K table loaded up front.
   constexpr bool MXS = MX4 && BK >= 128;
   constexpr int SPR = MXS ? BK / 32 : 0;
-  constexpr int S_BYTES = TN * SPR;
-  constexpr int LS = S_BYTES / 256 / NW;
-  static_assert(S_BYTES == LS * NW * 256, "whole scale instructions for every wave");
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+  // whole rounds of scale instructions: rows past TN are loaded, never used
+  constexpr int LS = MXS ? ((TN * SPR + 255) / 256 + NW - 1) / NW : 0;
+  constexpr int S_BYTES = LS * NW * 256;
+  // A8: the A rows' E8M0 codes (SPR bytes a row) travel after the B codes,
+  // LSA dword instructions a wave (rows past TM are loaded and never used)
+  static_assert(!A8 || MXS, "MX FP8 A: in-stage scales");
+  constexpr int SA_RPI = A8 ? 256 / SPR : 1;  // A rows a scale instruction
+  constexpr int LSA = A8 ? ((TM + SA_RPI - 1) / SA_RPI + NW - 1) / NW : 0;
+  constexpr int SA_BYTES = LSA * NW * 256;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES + SA_BYTES;
   // A stage is TA + TB wave instructions of 1 KB each (A rows, then B rows,
   // in LDS order).  Instruction g is issued by wave g % NW as its (g / NW)-th,
   // so a wave issues LMAX or LMAX - 1 of them per stage (plus LS scale ones).
@@ -291,7 +303,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   static_assert(!DUAL || (TN / 2) % RPI_B == 0, "gate/up split on a DMA instruction");
   static_assert(!DUAL || !MXS || (TN / 2) % (256 / SPR) == 0,
                 "gate/up split on a scale instruction");
-  static_assert(LMAX + LS < 64 / (STAGES > 2 ? STAGES - 2 : 1), "vmcnt range");
+  static_assert(LMAX + LS + LSA < 64 / (STAGES > 2 ? STAGES - 2 : 1), "vmcnt range");
+  static_assert(!A8 || (BK >= 128 && MA == 0), "MX FP8 A: K tile of 128 or more");
   // multi-segment problems keep whole A and B rounds per wave
   constexpr int A_LD = TA / NW, B_LD = TB / NW;
   static_assert(!MSEG || (TA % NW == 0 && TB % NW == 0), "segmented: whole DMA rounds");
@@ -515,7 +528,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   if constexpr (!MSEG) {
     const int64_t a_first = GATHER ? 0 : tile.m0;
     const int64_t kb0 = (int64_t)k_begin * BK;
-    a_base = reinterpret_cast<const char *>(cur_a + a_first * cur_lda + kb0);
+    a_base = reinterpret_cast<const char *>(cur_a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
     const char *bsrc = static_cast<const char *>(args.seg[0].b);
     const char *busrc = static_cast<const char *>(args.b_up);
     if (args.offsets != nullptr) {
@@ -540,7 +553,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         int64_t m = tile.m0 + r;
         if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
         if constexpr (GATHER) m = args.gather[m] / args.gather_div;
-        o = (uint32_t)((m - a_first) * cur_lda * 2 + ch * 16);
+        o = (uint32_t)((m - a_first) * cur_lda * (A8 ? 1 : 2) + ch * 16);
       } else if (g < TT) {
         // B rows from TN/2 on are the up rows of a dual problem
         const int rb = (g - TA) * RPI_B + lane / CPR_B;
@@ -565,13 +578,30 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       const int gs = wave + NW * q;
       const int i = gs * 64 + lane;
       const int rr = i / (SPR / 4), w = i % (SPR / 4);
-      const bool up = DUAL && gs * 64 / (SPR / 4) >= TN / 2;
+      const bool up = DUAL && rr >= TN / 2 && rr < TN;
       int64_t n = tile.n0 + (up ? rr - TN / 2 : rr);
-      if (n >= args.N) n = tile.n0;
+      if (rr >= TN || n >= args.N) n = tile.n0;  // loaded, never used
       soff[q] = (uint32_t)(n * kb32 + 4 * w);
       sbase[q] = reinterpret_cast<uint64_t>((up ? args.e8_up : args.e8) +
                                             (int64_t)tile.e * args.s_estride +
                                             (int64_t)k_begin * BK / 32);
+    }
+  }
+  // A8: scale instructions of the A rows: instruction gs = wave + NW q, lane l
+  // copies dword w of the codes of tile row rr (gathered rows addressed from
+  // the matrix start, like the A rows)
+  uint32_t saoff[A8 ? LSA : 1];
+  const char *sa_base = nullptr;
+  if constexpr (A8) {
+    sa_base = reinterpret_cast<const char *>(args.a_sc) + (int64_t)k_begin * BK / 32;
+#pragma unroll
+    for (int q = 0; q < LSA; ++q) {
+      const int i = (wave + NW * q) * 64 + lane;
+      const int rr = i / (SPR / 4), w = i % (SPR / 4);
+      int64_t m = tile.m0 + rr;
+      if (rr >= TM || m >= tile.m_end) m = tile.m0;  // loaded, never used
+      if constexpr (GATHER) m = args.gather[m] / args.gather_div;
+      saoff[q] = (uint32_t)(m * args.lda_sc + 4 * w);
     }
   }
   // B bytes from one N tile to the next (persistent N tiles)
@@ -609,13 +639,23 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                     smem + st * STAGE_BYTES + A_BYTES + B_BYTES + (wave + NW * q) * 256);
     }
   };
+  // A8: the A scale instructions of K tile kt into stage st
+  auto dma_ascales = [&](int kt, int st) G2_INL {
+    if constexpr (A8) {
+#pragma unroll
+      for (int q = 0; q < LSA; ++q)
+        dma4_sb_asm(sa_base + (int64_t)kt * SPR, saoff[q],
+                    smem + st * STAGE_BYTES + A_BYTES + B_BYTES + S_BYTES +
+                        (wave + NW * q) * 256);
+    }
+  };
   // "tile kt landed": this wave's loads of later tiles may still be in flight
   auto wait_tile = [&]() G2_INL {
     if constexpr (EVEN) {
-      wait_vmcnt<(LMAX + LS) * (STAGES - 2)>();
+      wait_vmcnt<(LMAX + LS + LSA) * (STAGES - 2)>();
     } else {
-      if (has_last) wait_vmcnt<(LMAX + LS) * (STAGES - 2)>();
-      else wait_vmcnt<(LMAX - 1 + LS) * (STAGES - 2)>();
+      if (has_last) wait_vmcnt<(LMAX + LS + LSA) * (STAGES - 2)>();
+      else wait_vmcnt<(LMAX - 1 + LS + LSA) * (STAGES - 2)>();
     }
   };
 
@@ -724,15 +764,17 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           for (int j = 0; j < JN; ++j)
             if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
         } else {
-          // store, plus the residual row (read before the write: it may be the output)
+          // store (times the row's factor, when given), plus the residual row
+          // (read before the write: it may be the output)
           const void *rrow = args.resid ? static_cast<const char *>(args.resid) +
                                               row * args.ldr * (int64_t)sizeof(OutT)
                                         : nullptr;
+          const float f = args.row_scale ? args.row_scale[row] : 1.0f;
 #pragma unroll
           for (int j = 0; j < JN; ++j)
             if (col_ok[j])
               store_out<OutT>(orow, col[j],
-                              acc[i][j][r] + (rrow ? load_in<OutT>(rrow, col[j]) : 0.0f));
+                              f * acc[i][j][r] + (rrow ? load_in<OutT>(rrow, col[j]) : 0.0f));
         }
       }
     }
@@ -786,6 +828,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         const int jp = PN ? tp / ktiles : 0;
         static_for<L>([&](auto d) G2_INL { dma_one(d, tp - jp * ktiles, p, jp); });
         dma_scales(tp - jp * ktiles, p, jp);
+        dma_ascales(tp - jp * ktiles, p);
       }
       int kt = 0, jn = 0;  // K tile and N tile of t
       for (int t = 0; t < T; ++t) {
@@ -797,7 +840,53 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         const int dj = PN ? kdt / ktiles : 0;
         const int kdc = kdt - dj * ktiles;
         const int dst = kd % STAGES;
-        if constexpr (NS == 0) {
+        if constexpr (A8) {
+          // block-scaled MFMA: all loads of the tile STAGES - 1 ahead first, then
+          // per 64-wide k step the operands and scales of NS x FRN
+          // v_mfma_scale_f32_32x32x64_f8f6f4 (A e4m3, B E2M1 as stored).  Scale
+          // block b of the step (its k 32 b.. 32 b + 31, MX block 2 S + b) is B
+          // lane half b (one 16-byte chunk of 32 codes, 2 S + b) and bytes
+          // 16 b.. 16 b + 15 of both A lane halves (half h: k 32 b + 16 h ..+16,
+          // so a lane reads A chunks 4 S + h and 4 S + 2 + h); the scale of
+          // block b comes from lane half b, on both operands.
+          static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst, dj); });
+          dma_scales(kdc, dst, dj);
+          dma_ascales(kdc, dst);
+          if constexpr (NS > 0) {
+            const uint8_t *sa_st = reinterpret_cast<const uint8_t *>(
+                st + A_BYTES + B_BYTES + S_BYTES);
+            static_for<BK / 64>([&](auto s_tag) G2_INL {
+              constexpr int S = decltype(s_tag)::value;
+              i32x8 bq[FRN];
+              int bs[FRN];
+              static_for<FRN>([&](auto j) G2_INL {
+                uint4 raw[FRN];
+                read_b8(st, S, j, raw);
+                bq[j] = i32x8{(int)raw[j].x, (int)raw[j].y, (int)raw[j].z, (int)raw[j].w, 0, 0, 0, 0};
+                bs[j] = (int)*reinterpret_cast<const uint8_t *>(
+                    st + A_BYTES + B_BYTES + b_row_of(j) * SPR + 2 * S + (lane >> 5));
+              });
+#pragma unroll
+              for (int i = 0; i < NS; ++i) {
+                const int r = (i * WM + wm) * 32 + (lane & 31);
+                const int c0 = 4 * S + (lane >> 5);
+                const char *ar = st + r * RB;
+                const uint4 lo = *reinterpret_cast<const uint4 *>(ar + ((c0 ^ swz(r, CPR)) << 4));
+                const uint4 hi =
+                    *reinterpret_cast<const uint4 *>(ar + (((c0 + 2) ^ swz(r, CPR)) << 4));
+                const i32x8 aq = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                const int as = (int)sa_st[r * SPR + 2 * S + (lane >> 5)];
+#pragma unroll
+                for (int j = 0; j < FRN; ++j)
+                  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                      aq, bq[j], acc[i][j], 0 /* A e4m3 */, 4 /* B e2m1 */, 0, as, 0, bs[j]);
+              }
+              // keep the next k step's LDS reads after these MFMAs (registers)
+              __builtin_amdgcn_sched_barrier(0);
+            });
+          }
+        } else if constexpr (NS == 0) {
           static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst, dj); });
           dma_scales(kdc, dst, dj);
         } else {
@@ -1052,6 +1141,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a) {
       store_out<OutT>(a.out, row * a.ldo + col,
                       f * situ(g, u, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
     } else {
+      if (a.row_scale) g *= a.row_scale[row];
       if (a.resid) g += load_in<OutT>(a.resid, row * a.ldr + col);
       store_out<OutT>(a.out, row * a.ldo + col, g);
     }

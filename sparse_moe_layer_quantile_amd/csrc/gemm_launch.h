@@ -26,13 +26,21 @@ struct DmaShape {
   constexpr int tn() const { return wn * frn * 32; }
   // bytes of a B tile row in format bf (g2::BFmt): bf16, fp8 codes, MXFP4 bytes
   static constexpr int b_row_bytes(int bk, int bf) {
-    return bf == g2::BF_FP8 ? bk : bf == g2::BF_MX4 ? bk / 2 : bk * 2;
+    return bf == g2::BF_FP8 ? bk : (bf == g2::BF_MX4 || bf == g2::BF_MX4A8) ? bk / 2 : bk * 2;
   }
-  // stage ring: bf16 A rows and B rows (MXFP4 with K tiles of 128 or more:
-  // and the B rows' E8M0 codes)
+  // scale-code instructions (256 bytes) of `rows` rows of bk/32 codes, in whole
+  // rounds of the workgroup's waves
+  constexpr size_t code_bytes(int rows) const {
+    const int nw = wm * wn;
+    return (size_t)((rows * (bk / 32) + 255) / 256 + nw - 1) / nw * nw * 256;
+  }
+  // stage ring: A rows (bf16, or e4m3 codes with MX FP8 A) and B rows; MXFP4 B
+  // with K tiles of 128 or more also the B rows' E8M0 codes, MX FP8 A the A rows'
   constexpr size_t lds(int bf = g2::BF_BF16) const {
-    return (size_t)stages * (tm() * bk * 2 + tn() * b_row_bytes(bk, bf) +
-                             (bf == g2::BF_MX4 && bk >= 128 ? tn() * (bk / 32) : 0));
+    const bool mx = bf == g2::BF_MX4 || bf == g2::BF_MX4A8;
+    return (size_t)stages * (tm() * bk * (bf == g2::BF_MX4A8 ? 1 : 2) + tn() * b_row_bytes(bk, bf) +
+                             (mx && bk >= 128 ? code_bytes(tn()) : 0) +
+                             (bf == g2::BF_MX4A8 ? code_bytes(tm()) : 0));
   }
   // every wave issues whole rounds of A and of B DMA instructions (1 KB each)
   constexpr bool whole_rounds(int bf = g2::BF_BF16) const {
@@ -61,10 +69,16 @@ constexpr DmaShape kDma[] = {
     // room for a third stage of the grouped tiles
     {2, 4, 4, 2, 64, 3, 1},  // 9: 256 x 256, BK 64, 3 stages
     {2, 4, 3, 2, 64, 3, 1},  // 10: 192 x 256, BK 64, 3 stages
+    // MX FP8 A x MXFP4 B (block-scaled MFMA): K tiles of 128 (two 64-wide MFMA
+    // k steps), both operands' E8M0 codes in the stage
+    {2, 4, 4, 2, 128, 3, 1},  // 11: 256 x 256, 3 stages (156 KB)
+    {2, 4, 5, 2, 128, 2, 1},  // 12: 320 x 256, 2 stages (120 KB)
+    {2, 4, 3, 2, 128, 3, 1},  // 13: 192 x 256, 3 stages (132 KB)
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
 constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6,
-              kVTinyMX4 = 7, kVTinyMX4W = 8, kVQ256 = 9, kVQ192 = 10;
+              kVTinyMX4 = 7, kVTinyMX4W = 8, kVQ256 = 9, kVQ192 = 10, kVA8 = 11,
+              kVA8W = 12, kVA8S = 13;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 // shapes a bf16 B operand can take (6..8 are MXFP4-only)
 constexpr bool bf16_shape(int v) { return v >= 0 && v < 6; }
@@ -233,6 +247,27 @@ MOE_DMA_KINDS(MOE_DMA_EXTERN)
 #define MOE_B8_EXTERN(E, D, G, T, M) \
   extern template hipError_t launch_dma_b8<E, D, G, T, M>(int, const GemmArgs &, hipStream_t);
 MOE_B8_KINDS(MOE_B8_EXTERN)
+// MX FP8 A x MXFP4 B, the routed experts on the block-scaled MFMA: the tile
+// rows by the rows an expert holds on average (override MOE_GEMM_A8: 11-13)
+inline int a8_shape(int64_t rows, int64_t n_experts) {
+  const int dflt = rows <= 200 * n_experts ? kVA8S : rows <= 300 * n_experts ? kVA8W : kVA8;
+  const int v = env_int("MOE_GEMM_A8", dflt);
+  return (v == kVA8 || v == kVA8W || v == kVA8S) ? v : dflt;
+}
+template <int EPI, bool DUAL, bool GATHER, typename OutT>
+hipError_t launch_dma_b4a8(int shape, const GemmArgs &a, hipStream_t s) {
+  constexpr int F = g2::BF_MX4A8;
+  switch (shape) {
+    case kVA8W: return launch_dma_impl<kVA8W, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVA8S: return launch_dma_impl<kVA8S, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    default: return launch_dma_impl<kVA8, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+  }
+}
+extern template hipError_t launch_dma_b4a8<EPI_STORE, false, false, uint16_t>(int,
+                                                                            const GemmArgs &,
+                                                                            hipStream_t);
+extern template hipError_t launch_dma_b4a8<EPI_SITU, true, true, uint16_t>(int, const GemmArgs &,
+                                                                         hipStream_t);
 #define MOE_B4_KINDS(X)                     \
   X(EPI_STORE, false, false, uint16_t)      \
   X(EPI_SITU, true, true, uint16_t)

@@ -21,8 +21,9 @@ enum GemmKind {
 
 int gemm_bm(int path);
 // Storage format of a GEMM's weights (B operand): bf16 (fp32 on the fp32
-// path), fp8 e4m3 with 128 x 128 block scales, MXFP4 with E8M0 scales per 32.
-enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2 };
+// path), fp8 e4m3 with 128 x 128 block scales, MXFP4 with E8M0 scales per 32
+// (WF_MX4A8: and the A operand in MX FP8, for the block-scaled MFMA).
+enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2, WF_MX4A8 = 3 };
 // M-tile rows of the grouped GEMMs for rows (token, expert) pairs over
 // n_experts experts with weights in format wf (the dispatch lays its tile
 // table out in these units).
@@ -49,6 +50,12 @@ hipError_t launch_dispatch(const int32_t *idx, const float *w, int64_t bt, int64
                            int64_t n_experts, int tile_bm, uint64_t *masks, int32_t *counts,
                            int32_t *offsets, int32_t *tile_offsets, int32_t *perm,
                            int32_t *inv_perm, float *w_sorted, hipStream_t s);
+
+// ---- MX FP8 activations -------------------------------------------------------------
+// x: n bf16 elements (n a multiple of 32, 16-byte aligned) -> codes[n] E4M3 and
+// scales[n / 32] E8M0 (OCP MX, blocks of 32 consecutive elements).
+hipError_t launch_mx8_quant(const void *x, int64_t n, uint8_t *codes, uint8_t *scales,
+                            hipStream_t s);
 
 // ---- combine + latent RMSNorm ---------------------------------------------------
 // o [P][L] (act) rows already scaled by their routing weight; n [bt][L] (act).

@@ -36,14 +36,21 @@ MX_ABI = {"w_gate": "e8_gate", "w_up": "e8_up", "w_down": "e8_down"}
 def tol_of(cfg) -> float:
     if cfg.act == "f32":
         return TOL["f32"]
-    return TOL["fp8"] if cfg.weight == "fp8" else TOL["bf16"]
+    # fp8 weights, or MX FP8 expert inputs: e4m3 codes that a bf16 rounding
+    # upstream can move by one step
+    fp8 = cfg.weight == "fp8" or getattr(cfg, "act_quant", "none") == "mxfp8"
+    return TOL["fp8"] if fp8 else TOL["bf16"]
 
 
 def abi_config(cfg, cutoff=None):
     import sparse_moe_layer_quantile_amd as moe
+    weight = cfg.weight
+    if getattr(cfg, "act_quant", "none") == "mxfp8":
+        assert weight == "mxfp4", "MX FP8 expert inputs go with MXFP4 experts"
+        weight = "mxfp4_a8"
     return moe.make_config(cfg.d, cfg.latent, cfg.n_experts, cfg.top_k, cfg.expert_inter,
                            cfg.n_shared, cfg.shared_inter, cfg.beta, cfg.beta_u, cfg.rms_eps,
-                           act=cfg.act, weight=cfg.weight, router=cfg.router,
+                           act=cfg.act, weight=weight, router=cfg.router,
                            cutoff=cutoff or cfg.cutoff)
 
 

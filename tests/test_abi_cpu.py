@@ -22,7 +22,7 @@ moe = pytest.importorskip("sparse_moe_layer_quantile_amd")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -104,6 +104,35 @@ def test_dtype_combinations():
                                                weight="f32"), 64) > 0
     assert moe.workspace_bytes(moe.make_config(256, 2112, 16, 2, 64, 1, 128, act="f32",
                                                weight="f32"), 64) == 0
+
+
+def test_mxfp4_a8_workspace_and_limits():
+    """MX FP8 expert inputs add their codes and E8M0 scales to the workspace:
+    x_lat (bt L bytes + bt L / 32) and h (bt k I + bt k I / 32)."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4")
+    c4 = parity.abi_config(cfg)
+    c8 = parity.abi_config(cfg.with_(act_quant="mxfp8"))
+    assert c8.weight_dtype == moe.MOE_MXFP4_A8
+    bt = 1024
+    extra = bt * cfg.latent * 33 // 32 + bt * cfg.top_k * cfg.expert_inter * 33 // 32
+    diff = moe.workspace_bytes(c8, bt) - moe.workspace_bytes(c4, bt)
+    assert extra <= diff <= extra + 4 * 256
+    # K ranges of whole 128-element groups, as for MXFP4
+    assert moe.workspace_bytes(parity.abi_config(cfg.with_(act_quant="mxfp8", latent=576)),
+                               64) == 0
+    with pytest.raises(AssertionError):
+        parity.abi_config(synth.CONFIGS["mid_bf16"].with_(act_quant="mxfp8"))
+
+
+def test_mx8_quantize_argument_errors_on_host():
+    """Rejected before any launch: n not a multiple of 32, negative, NULL or
+    misaligned pointers; n = 0 is a no-op."""
+    assert moe.moe_mx8_quantize(256, 48, 256, 256, 0) == -1
+    assert moe.moe_mx8_quantize(256, -32, 256, 256, 0) == -1
+    assert moe.moe_mx8_quantize(0, 32, 256, 256, 0) == -1
+    assert moe.moe_mx8_quantize(256, 32, 0, 256, 0) == -1
+    assert moe.moe_mx8_quantize(258, 32, 256, 256, 0) == -1
+    assert moe.moe_mx8_quantize(0, 0, 0, 0, 0) == 0
 
 
 def test_argument_errors_before_any_launch():

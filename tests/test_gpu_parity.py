@@ -209,6 +209,98 @@ def _mxfp4_check(cfg, cutoff):
     assert err <= parity.tol_of(cfg)
 
 
+# ---- MX FP8 expert inputs (MXFP4 weights, block-scaled MFMA) --------------------------------
+
+def _mx8_inputs(n, seed):
+    """n bf16 values (uint16 bit patterns), blocks of 32 drawn from a mix that
+    reaches every branch of the conversion: normal data at scales 2^-133 ..
+    2^120 (bf16 subnormal to near the top of its range), all-zero blocks,
+    blocks with one non-zero, blocks with signed zeros, and values that sit
+    exactly on e4m3 rounding midpoints after scaling."""
+    rng = np.random.default_rng(seed)
+    nb = n // 32
+    v = rng.normal(size=(nb, 32)).astype(np.float32)
+    kind = rng.integers(0, 8, size=nb)
+    scale = np.ldexp(np.float32(1), rng.integers(-133, 121, size=nb)).astype(np.float32)
+    v *= scale[:, None]
+    v[kind == 0] = 0.0
+    v[kind == 1] = -0.0
+    one = kind == 2
+    v[one, 1:] = 0.0
+    # midpoints: m.5 steps of a 3-bit mantissa at the block's scale
+    mid = kind == 3
+    m = rng.integers(0, 16, size=(int(mid.sum()), 32)).astype(np.float32)
+    e = rng.integers(-10, 9, size=(int(mid.sum()), 32))
+    sign = np.where(rng.random((int(mid.sum()), 32)) < 0.5, -1, 1).astype(np.float32)
+    v[mid] = sign * np.ldexp((8 + m + 0.5) / 8, e).astype(np.float32) * 0.5
+    # bf16 of each value (round to nearest even; no overflow at these scales)
+    u = v.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16).reshape(-1)
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("n,seed", [(32, 0), (32 * 37, 1), (32 * 1000 + 32 * 3, 2),
+                                     ((1 << 21) + 32 * 5, 3)])
+def test_mx8_quantize_bit_exact(n, seed):
+    """The MX FP8 quantiser's codes and E8M0 scales equal the oracle's bit for
+    bit (its input is bf16, exact in the oracle's fp64; both compute the same
+    rounding), over one block, ragged grids and a 2M-element input."""
+    import sparse_moe_layer_quantile_amd as moe
+    say("mx8 quantize", n, seed)
+    bits = _mx8_inputs(n, seed)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    codes, scales = moe.mx8_quantize(x)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx8_quantize(_bf16_to_f64(bits))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != rc)[0]
+    assert bad.size == 0, (f"{bad.size} codes differ, first at {bad[:4]}: got "
+                           f"{got[bad[:4]]} want {rc[bad[:4]]} from {_bf16_to_f64(bits)[bad[:4]]}")
+
+
+def test_mx8_quantize_argument_errors():
+    import sparse_moe_layer_quantile_amd as moe
+    x = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(64, dtype=torch.uint8, device="cuda")
+    s = torch.empty(2, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    assert moe.moe_mx8_quantize(x.data_ptr(), 48, c.data_ptr(), s.data_ptr(), stream) == -1
+    assert moe.moe_mx8_quantize(x.data_ptr(), -32, c.data_ptr(), s.data_ptr(), stream) == -1
+    assert moe.moe_mx8_quantize(0, 32, c.data_ptr(), s.data_ptr(), stream) == -1
+    assert moe.moe_mx8_quantize(x.data_ptr() + 2, 32, c.data_ptr(), s.data_ptr(), stream) == -1
+    assert moe.moe_mx8_quantize(0, 0, 0, 0, stream) == 0
+
+
+@pytest.mark.parametrize("bt,cutoff,shape", [(4096, "batch", None), (64, "given", None),
+                                             (300, "batch", (640, 384)), (8, "batch", None)])
+def test_forward_mxfp4_mx8_inputs_mid(bt, cutoff, shape):
+    """MXFP4 experts with MX FP8 inputs (x_lat and h quantised in the layer, the
+    block-scaled MFMA): the oracle quantises its fp64 x_lat and h the same
+    way.  256-row tiles: several per expert at 4096 tokens, a partial one
+    at 64; (640, 384) has a partial N tile in the down GEMM and K ranges of
+    five and three 128-wide K tiles."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", act_quant="mxfp8", bt=bt)
+    if shape is not None:
+        cfg = cfg.with_(latent=shape[0], expert_inter=shape[1])
+    say("forward mxfp4 + mx8 inputs", bt, cutoff, cfg.latent, cfg.expert_inter)
+    _mxfp4_check(cfg, cutoff)
+
+
+@pytest.mark.parametrize("shape_id", ["11", "12", "13"])
+def test_forward_mxfp4_mx8_every_tile_shape(shape_id, monkeypatch):
+    """Each tile shape of the block-scaled engine (forced): 256, 320 and 192 rows
+    on a batch of 512 rows an expert (several M tiles each, a ragged last one)."""
+    monkeypatch.setenv("MOE_GEMM_A8", shape_id)
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", act_quant="mxfp8", bt=4096)
+    say("forward mxfp4 + mx8 inputs, forced shape", shape_id)
+    _mxfp4_check(cfg, "batch")
+
+
 # ---- edge cases ----------------------------------------------------------------------------
 
 def _small_forward_check(cfg, cutoff, seed=0, alpha=None, routing="normal"):
