@@ -77,6 +77,7 @@ def lib():
             "orc_rmsnorm": ([P, I64, P, D, P], None),
             "orc_mx8_quantize": ([P, I64, I64, P, P], ctypes.c_int),
             "orc_double_to_e4m3": ([D], ctypes.c_uint8),
+            "orc_round_bf16": ([D], D),
             "orc_dense_ffn": ([P, P, P, P, P, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -290,6 +291,11 @@ def output(cfg, w: Weights, n, x_t) -> np.ndarray:
 
 def double_to_e4m3(v) -> int:
     return int(lib().orc_double_to_e4m3(float(v)))
+
+
+def round_bf16(v: float) -> float:
+    """Nearest bf16 value of v (ties to even)."""
+    return float(lib().orc_round_bf16(float(v)))
 
 
 def mx8_quantize(x, block=32):

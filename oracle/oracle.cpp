@@ -165,6 +165,14 @@ uint8_t orc_double_to_e4m3(double v) {
   return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
+double orc_round_bf16(double v) {
+  if (v == 0.0 || !std::isfinite(v)) return v;
+  int e2;
+  std::frexp(v, &e2);                          // |v| in [2^(e2-1), 2^e2)
+  const int q = std::max(e2 - 1 - 7, -133);    // weight of the last bf16 bit
+  return std::ldexp(std::nearbyint(std::ldexp(v, -q)), q);  // exact scaling; RNE
+}
+
 int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes,
                      uint8_t *scales) {
   if (!x || !codes || !scales || block <= 0 || n % block) return -1;
@@ -184,9 +192,11 @@ int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes,
   return 0;
 }
 
-// x replaced by its MX FP8 quantisation (dequantised exactly), blocks of `block`.
+// x replaced by its MX FP8 quantisation (dequantised exactly), blocks of
+// `block`, the codes decided on x rounded to bf16.
 static void mx8_round_trip(double *x, int64_t n, int64_t block) {
   std::vector<uint8_t> codes((size_t)n), scales((size_t)(n / block));
+  for (int64_t i = 0; i < n; ++i) x[i] = orc_round_bf16(x[i]);
   orc_mx8_quantize(x, n, block, codes.data(), scales.data());
   for (int64_t i = 0; i < n; ++i)
     x[i] = orc_e4m3_to_double(codes[i]) * orc_e8m0_to_double(scales[i / block]);

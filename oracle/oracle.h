@@ -70,7 +70,9 @@ typedef struct {
   /* 0: the routed experts read their inputs exactly.  32: each expert GEMM
    * reads its input (x_lat for gate/up, h for down) quantised to OCP MX FP8
    * E4M3 with one E8M0 scale per 32 consecutive elements (orc_mx8_quantize),
-   * and the routing weight multiplies the expert output as always. */
+   * and the routing weight multiplies the expert output as always.  The codes
+   * are decided on the input rounded to bf16 (orc_round_bf16): the precision
+   * in which the GPU path holds x_lat and h when it quantises them. */
   int64_t act_mx_block;
 } orc_shape;
 
@@ -107,6 +109,9 @@ double orc_e8m0_to_double(uint8_t code);
 int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes, uint8_t *scales);
 /* Nearest E4M3 code of a double (ties to even, saturating at +-448). */
 uint8_t orc_double_to_e4m3(double v);
+/* Nearest bf16 value of a finite double within the bf16 range (8 significant
+ * bits, ties to even; below 2^-126 multiples of 2^-133). */
+double orc_round_bf16(double v);
 
 /* out[r] = sum_c M[mat][r][c] in[c], fp64, c ascending. */
 void orc_matvec(const orc_mat *m, int64_t mat, const double *in, double *out);

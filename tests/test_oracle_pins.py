@@ -686,9 +686,42 @@ def test_mx8_block_rules():
     np.testing.assert_array_equal(s2[nz], sc[nz] + 5)
 
 
+def _bf16_rne(v):
+    """bf16 rounding (ties to even) of normal doubles on their bit patterns:
+    keep the top 7 of the 52 fraction bits."""
+    u = np.asarray(v, np.float64).view(np.uint64)
+    low = u & np.uint64((1 << 45) - 1)
+    keep = u >> np.uint64(45)
+    half = np.uint64(1 << 44)
+    up = (low > half) | ((low == half) & ((keep & np.uint64(1)) == 1))
+    return ((keep + up.astype(np.uint64)) << np.uint64(45)).view(np.float64)
+
+
+def test_round_bf16():
+    """The oracle's bf16 rounding: ties to even at 8 significant bits, carries
+    into the exponent, subnormal steps of 2^-133, and agreement with torch's
+    fp32 -> bf16 conversion (RNE) on fp32-exact values."""
+    r = oracle.round_bf16
+    assert r(1.0 + 2.0 ** -8) == 1.0                     # tie, even below
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6     # tie, even above
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7
+    assert r(-(2.0 - 2.0 ** -9)) == -2.0                 # carry into the exponent
+    assert r(3 * 2.0 ** -134) == 2.0 ** -132             # subnormal tie, even above
+    assert r(2.0 ** -134) == 0.0                         # subnormal tie, even below
+    assert r(0.0) == 0.0 and math.copysign(1.0, r(-0.0)) == -1.0
+    torch = pytest.importorskip("torch")
+    v = np.random.default_rng(5).normal(size=4000).astype(np.float32) * \
+        np.float32(2.0) ** np.random.default_rng(6).integers(-30, 30, 4000).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([r(float(a)) for a in v])
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(_bf16_rne(v.astype(np.float64)), want)
+
+
 def test_expert_with_mx8_inputs_is_the_quantised_composition():
     """act_mx_block = 32: gate/up read MX FP8 x_lat, down reads MX FP8 h (each
-    quantised in blocks of 32), composed from the pinned pieces."""
+    rounded to bf16, then quantised in blocks of 32), composed from the pinned
+    pieces."""
     rng = np.random.default_rng(42)
     L, I = 64, 96
     Wg, Wu = f32(rng.normal(size=(I, L)) / 8), f32(rng.normal(size=(I, L)) / 8)
@@ -696,7 +729,7 @@ def test_expert_with_mx8_inputs_is_the_quantised_composition():
     x = rng.normal(size=L)
 
     def q(v):
-        c, s = oracle.mx8_quantize(v, 32)
+        c, s = oracle.mx8_quantize(_bf16_rne(v), 32)
         return np.array([oracle.e4m3_to_double(k) for k in c]) * np.repeat(
             2.0 ** (s.astype(np.int64) - 127), 32)
 
