@@ -44,11 +44,13 @@ def phase_work(cfg, touched: int) -> dict:
     I, S, Is = cfg.expert_inter, cfg.n_shared, cfg.shared_inter
     P = bt * k
     ab = 4 if cfg.act == "f32" else 2
-    wb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2}[cfg.weight]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2, "mxfp8": 2}[cfg.weight]
     rb = {"f32": 4, "bf16": 2}[cfg.router]
     sc = (lambda r, c: (r // 128) * (c // 128) * 4) if cfg.weight == "fp8" else (lambda r, c: 0)
     if cfg.weight == "mxfp4":
         xw = lambda r, c: r * c // 2 + r * (c // 32)  # an expert matrix, codes + scales
+    elif cfg.weight == "mxfp8":
+        xw = lambda r, c: r * c + r * (c // 32)
     else:
         xw = lambda r, c: r * c * wb + sc(r, c)
     batch = cfg.cutoff == "batch"
@@ -383,7 +385,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16+mxfp8-experts" if a8 else "bf16") if cfg.act == "bf16" else "f32",
+        "dtype": (("bf16+mxfp8" if cfg.weight == "mxfp8" else "bf16+mxfp8xmxfp4") if a8
+                  else "bf16") if cfg.act == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "bt": cfg.bt, "d": cfg.d, "latent": cfg.latent,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k,
@@ -396,8 +399,8 @@ def main(argv=None):
         "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": layer_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                   "experts_touched": touched,
-                  "weight_gb": sum(sp.nbytes + (sp.n_scale_blocks * (1 if sp.dtype == synth.MXFP4 else 4)
-                                                if sp.dtype in (synth.FP8, synth.MXFP4) else 0)
+                  "weight_gb": sum(sp.nbytes + (sp.n_scale_blocks * (1 if sp.dtype in synth.MX_DTYPES else 4)
+                                                if sp.dtype in (synth.FP8, *synth.MX_DTYPES) else 0)
                                    for n, sp in synth.specs(cfg).items() if n != "x") / 1e9},
         "phases_ms": {n: round(v[0], 4) for n, v in phases.items()},
         "kernel_sources": kernel_source_hash(),

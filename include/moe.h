@@ -71,7 +71,13 @@ typedef enum {
    * MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) at the fp8 rate.  Same weight
    * buffers as MOE_MXFP4; the routing weight multiplies the down GEMM's output
    * rows instead of h. */
-  MOE_MXFP4_A8 = 4
+  MOE_MXFP4_A8 = 4,
+  /* Routed experts in OCP MX FP8: each [out][in] matrix stored as [out][in]
+   * OCP e4m3fn codes plus uint8 E8M0 codes [out][in/32] (the same scale layout
+   * as MOE_MXFP4); every other weight bf16.  The experts' inputs are quantised
+   * to MX FP8 as with MOE_MXFP4_A8, and both operands go to the block-scaled
+   * MFMA as stored (W8A8). */
+  MOE_MXFP8 = 5
 } moe_dtype;
 
 /* Quantile Balancing cutoff (tech.news18a.com page, third technique): BATCH
@@ -95,7 +101,7 @@ typedef struct moe_config {
   int32_t weight_dtype; /* W_down_proj, experts, W_up_proj, shared: MOE_F32 (with f32
                            act), MOE_BF16 or MOE_FP8E4M3_B128 (with bf16 act); or
                            MOE_MXFP4 or MOE_MXFP4_A8 (bf16 act): MXFP4 experts,
-                           the rest bf16 */
+                           the rest bf16; MOE_MXFP8 (bf16 act): MX FP8 experts */
   int32_t router_dtype; /* W_r: equal to act_dtype */
   int32_t cutoff_mode;  /* moe_cutoff_mode */
 } moe_config;
@@ -103,8 +109,8 @@ typedef struct moe_config {
  * multiples of 64 (of 128 with fp8 weights); latent at most 4096 (2048 with
  * fp32 activations); with fp8 weights d, latent, expert_inter and
  * shared_inter at most 16384; with MXFP4 experts latent and expert_inter
- * multiples of 128 and expert_inter at most 4096 (MOE_MXFP4_A8: bt * top_k *
- * expert_inter / 32 below 2^32); bt * top_k below 2^31; with bf16
+ * multiples of 128 and expert_inter at most 4096 (MOE_MXFP4_A8 and MOE_MXFP8:
+ * bt * top_k * expert_inter / 32 below 2^32); bt * top_k below 2^31; with bf16
  * activations the latent activations bt * latent * 2 bytes stay below 4 GiB
  * (bt < 599186 at latent 3584).  Else MOE_ERR_UNSUPPORTED. */
 
@@ -125,7 +131,7 @@ typedef struct moe_weights {
    * block of each [out][in] matrix, laid out [matrices][out/128][in/128]. */
   const float *s_down_proj, *s_gate, *s_up, *s_down, *s_up_proj, *s_sh_gate, *s_sh_up,
       *s_sh_down;
-  /* MOE_MXFP4 and MOE_MXFP4_A8 only (else NULL): E8M0 codes of the routed experts' matrices,
+  /* MOE_MXFP4, MOE_MXFP4_A8 and MOE_MXFP8 only (else NULL): E8M0 codes of the routed experts' matrices,
    * [E][I][L/32] (gate, up) and [E][L][I/32] (down), 4-byte aligned. */
   const uint8_t *e8_gate, *e8_up, *e8_down;
 } moe_weights;
@@ -212,7 +218,7 @@ moe_status moe_ffn_forward(const moe_ffn_config *cfg, const moe_ffn_weights *w, 
 /* ---- MX FP8 quantisation -----------------------------------------------------
  * OCP Microscaling Formats (MX) Specification v1.0, conversion of a vector of
  * scalars to MX blocks, with e4m3 elements and block 32 -- the step
- * MOE_MXFP4_A8 applies to the routed experts' GEMM inputs.  x: n bf16 values
+ * MOE_MXFP4_A8 and MOE_MXFP8 apply to the routed experts' GEMM inputs.  x: n bf16 values
  * (device, 16-byte aligned; n a multiple of 32, blocks = 32 consecutive
  * elements); codes: n bytes of OCP e4m3fn (device); scales: n / 32 E8M0 bytes
  * (device).  Per block: shared exponent s = floor(log2 max|x|) - 8, clamped to
@@ -232,7 +238,7 @@ moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes, uint8_t *s
  * record.  Phases: 0 shared gate/up, 1 router logits, 2 cutoffs, 3 top-k,
  * 4 dispatch, 5 W_down_proj, 6 expert gate/up, 7 expert down, 8 combine +
  * RMSNorm, 9 output projection; dense FFN: 10 RMSNorm, 11 gate/up, 12 down;
- * MOE_MXFP4_A8: 13 MX FP8 quantisation of x_lat, 14 of h.
+ * MOE_MXFP4_A8 and MOE_MXFP8: 13 MX FP8 quantisation of x_lat, 14 of h.
  * Events are created by the library and kept for reuse (no device memory).
  * Not thread-safe against concurrent forwards. */
 #define MOE_N_PHASES 15

@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+F32, BF16, FP8, MXFP4, MXFP8 = 0, 1, 2, 3, 4
 GIVEN, BATCH = 0, 1
 
 _NP_DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): FP8}
@@ -108,8 +108,10 @@ def shape_of(cfg) -> OrcShape:
 
 
 class Mat:
-    """Keeps the arrays behind an OrcMat alive.  A uint8 `scale` (E8M0 codes)
-    marks `data` as MXFP4: bytes [.., rows, cols / 2] of two codes each."""
+    """Keeps the arrays behind an OrcMat alive.  A uint8 `scale` (E8M0 codes
+    [.., rows, cols / 32]) marks `data` as an MX format: MXFP4 when its rows
+    are cols / 2 bytes of two codes each, MX FP8 when they are cols e4m3
+    codes."""
 
     def __init__(self, data: np.ndarray, scale: np.ndarray | None = None, n_mats=None,
                  rows=None, cols=None):
@@ -119,13 +121,19 @@ class Mat:
             self.scale = None
         else:
             self.scale = np.ascontiguousarray(scale, np.uint8 if mx else np.float32)
-        dt = MXFP4 if mx else _NP_DT[self.data.dtype]
+        dt = _NP_DT[self.data.dtype]
         if data.ndim == 3:
             n_mats, rows, cols = data.shape
         elif data.ndim == 2:
             n_mats, rows, cols = 1, data.shape[0], data.shape[1]
         if mx:
-            cols *= 2
+            blocks = self.scale.shape[-1]
+            if cols * 2 == blocks * 32:
+                dt, cols = MXFP4, cols * 2
+            elif cols == blocks * 32:
+                dt = MXFP8
+            else:
+                raise ValueError("E8M0 scales do not match the MX data's row length")
         self.c = OrcMat(self.data.ctypes.data, dt,
                         None if self.scale is None else self.scale.ctypes.data,
                         n_mats, rows, cols)

@@ -23,6 +23,7 @@ int64_t elem_bytes(int32_t dt) {
     case ORC_BF16: return 2;
     case ORC_FP8E4M3: return 1;
     case ORC_MXFP4: return 1;  // (half a byte per element)
+    case ORC_MXFP8: return 1;
     case ORC_F64: return 8;
   }
   return 0;
@@ -32,7 +33,8 @@ bool valid_mat(const orc_mat *m) {
   if (!m || !m->data || m->rows <= 0 || m->cols <= 0 || m->n_mats <= 0) return false;
   if (elem_bytes(m->dtype) == 0) return false;
   if (m->dtype == ORC_FP8E4M3 && (!m->scale || m->rows % 128 || m->cols % 128)) return false;
-  if (m->dtype == ORC_MXFP4 && (!m->scale || m->cols % 32)) return false;
+  if ((m->dtype == ORC_MXFP4 || m->dtype == ORC_MXFP8) && (!m->scale || m->cols % 32))
+    return false;
   return true;
 }
 
@@ -68,6 +70,14 @@ void decode_row(const orc_mat *m, int64_t mat, int64_t r, double *buf) {
         const uint8_t code = (c & 1) ? (uint8_t)(p[c / 2] >> 4) : (uint8_t)(p[c / 2] & 0xF);
         buf[c] = orc_e2m1_to_double(code) * orc_e8m0_to_double(srow[c / 32]);
       }
+      break;
+    }
+    case ORC_MXFP8: {
+      // element c: e4m3 code c of the row times the E8M0 scale of its block
+      const uint8_t *p = static_cast<const uint8_t *>(m->data) + base;
+      const uint8_t *srow = static_cast<const uint8_t *>(m->scale) + (mat * m->rows + r) * (cols / 32);
+      for (int64_t c = 0; c < cols; ++c)
+        buf[c] = orc_e4m3_to_double(p[c]) * orc_e8m0_to_double(srow[c / 32]);
       break;
     }
     case ORC_F64: {

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8E4M3 = 2, ORC_MXFP4 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8E4M3 = 2, ORC_MXFP4 = 3, ORC_MXFP8 = 4 };
 enum { ORC_CUTOFF_GIVEN = 0, ORC_CUTOFF_BATCH = 1 };
 
 /* n_mats matrices of rows x cols, row-major, raw storage.
@@ -55,8 +55,9 @@ enum { ORC_CUTOFF_GIVEN = 0, ORC_CUTOFF_BATCH = 1 };
  *                the low nibble of byte i, 2i+1 in the high nibble (a row is
  *                cols/2 bytes); scale -> uint8 E8M0 codes [n_mats][rows][cols/32],
  *                one per 32 consecutive elements of a row.
- * (OCP Microscaling Formats (MX) Specification v1.0: element type FP4 E2M1,
- * scale type E8M0, block size 32.) */
+ *   ORC_MXFP8:   OCP MX FP8 -- one e4m3fn code per byte; scale as for ORC_MXFP4.
+ * (OCP Microscaling Formats (MX) Specification v1.0: element types FP4 E2M1 and
+ * FP8 E4M3, scale type E8M0, block size 32.) */
 typedef struct {
   const void *data;
   int32_t dtype;

@@ -19,11 +19,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4, MOE_MXFP4_A8 = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4, MOE_MXFP4_A8, MOE_MXFP8 = 0, 1, 2, 3, 4, 5
 CUTOFF_GIVEN, CUTOFF_BATCH = 0, 1
-# "mxfp4_a8": MXFP4 experts with their inputs quantised to MX FP8 in the layer
+# "mxfp4_a8": MXFP4 experts with their inputs quantised to MX FP8 in the layer;
+# "mxfp8": MX FP8 experts, inputs likewise
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128, "mxfp4": MOE_MXFP4,
-          "mxfp4_a8": MOE_MXFP4_A8}
+          "mxfp4_a8": MOE_MXFP4_A8, "mxfp8": MOE_MXFP8}
 CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH}
 
 _P = ctypes.c_void_p

@@ -39,7 +39,8 @@ int64_t elem_size(int32_t dt) {
     case MOE_BF16: return 2;
     case MOE_FP8E4M3_B128: return 1;
     case MOE_MXFP4:
-    case MOE_MXFP4_A8: return 2;  // the dense weights of an MXFP4 layer are bf16
+    case MOE_MXFP4_A8:
+    case MOE_MXFP8: return 2;  // the dense weights of an MX layer are bf16
   }
   return 0;
 }
@@ -82,8 +83,9 @@ moe_status check_config(const moe_config *c) {
     return MOE_ERR_UNSUPPORTED;
   // MXFP4 experts: K ranges (latent, expert_inter) of whole 128-element groups
   // (a dword of E8M0 codes), with the codes of a B row (K/32 <= 128) in LDS
-  const bool mx4 = c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8;
-  if (mx4 && (c->latent % 128 || c->expert_inter % 128 || c->expert_inter > 4096))
+  const bool mx = c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8 ||
+                  c->weight_dtype == MOE_MXFP8;
+  if (mx && (c->latent % 128 || c->expert_inter % 128 || c->expert_inter > 4096))
     return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype == MOE_FP8E4M3_B128 && c->d % 128) return MOE_ERR_UNSUPPORTED;
   // fp8 GEMMs stage the block scales of up to 128 K blocks in LDS
@@ -105,6 +107,7 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->dense_wf = p->fp8 ? WF_FP8 : WF_BF16;
   p->expert_wf = c->weight_dtype == MOE_MXFP4      ? WF_MX4
                  : c->weight_dtype == MOE_MXFP4_A8 ? WF_MX4A8
+                 : c->weight_dtype == MOE_MXFP8    ? WF_MX8A8
                                                    : p->dense_wf;
   p->act_bytes = elem_size(c->act_dtype);
   const int64_t E = c->n_experts, k = c->top_k, P = bt * k, L = c->latent;
@@ -112,7 +115,8 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   if (p->path == PATH_BF16 && bt * L * 2 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   // MX FP8 A: the E8M0 codes of A rows are addressed from the matrix start
   // with 32-bit offsets
-  if (p->expert_wf == WF_MX4A8 && P * (c->expert_inter / 32) > (int64_t)UINT32_MAX)
+  const bool a8 = p->expert_wf == WF_MX4A8 || p->expert_wf == WF_MX8A8;
+  if (a8 && P * (c->expert_inter / 32) > (int64_t)UINT32_MAX)
     return MOE_ERR_UNSUPPORTED;
   const int64_t nb = (bt + 63) / 64;
   size_t off = 0;
@@ -147,7 +151,6 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->split = take(4 * p->split_cap);
   p->split_sh = take(4 * p->split_cap);
   // MX FP8 inputs of the routed experts' GEMMs: codes and E8M0 scales
-  const bool a8 = p->expert_wf == WF_MX4A8;
   p->xq = take(a8 ? bt * L : 0);
   p->xq_sc = take(a8 ? bt * L / 32 : 0);
   p->hq = take(a8 ? P * c->expert_inter : 0);
@@ -180,7 +183,8 @@ bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts)
     if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
     if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;
   }
-  if (c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8) {
+  if (c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8 ||
+      c->weight_dtype == MOE_MXFP8) {
     // E8M0 codes are copied a dword at a time
     for (const uint8_t *e8 : {w->e8_gate, w->e8_up, w->e8_down})
       if (!e8 || reinterpret_cast<uintptr_t>(e8) % 4) return false;
@@ -478,7 +482,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   }
   // MX FP8 experts' input: x_lat quantised once per token (the gate/up GEMM
   // gathers each token's codes k times)
-  const bool a8 = ewf == WF_MX4A8;
+  const bool a8 = ewf == WF_MX4A8 || ewf == WF_MX8A8;
   uint8_t *xq = at<uint8_t>(ws, p.xq), *xq_sc = at<uint8_t>(ws, p.xq_sc);
   if (a8) {
     PhaseScope ph(PH_XLAT_QUANT, side);

@@ -10,7 +10,8 @@
 namespace moe {
 
 static_assert((int)WF_BF16 == g2::BF_BF16 && (int)WF_FP8 == g2::BF_FP8 &&
-                  (int)WF_MX4 == g2::BF_MX4 && (int)WF_MX4A8 == g2::BF_MX4A8,
+                  (int)WF_MX4 == g2::BF_MX4 && (int)WF_MX4A8 == g2::BF_MX4A8 &&
+                  (int)WF_MX8A8 == g2::BF_MX8A8,
               "weight format codes");
 
 int gemm_bm(int path) { return path == PATH_F32 ? sf::BM : mf::BM; }
@@ -62,6 +63,7 @@ int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts) {
   const int v = dma_variant(GK_EXPERT_SITU, rows, n_experts);
   // the MXFP4 engine's shapes (launch_dma_b4, launch_dma_b4a8)
   if (wf == WF_MX4A8) return kDma[a8_shape(rows, n_experts)].tm();
+  if (wf == WF_MX8A8) return kDma[mx8_shape(rows, n_experts)].tm();
   if (wf == WF_MX4) return kDma[mx4_shape(v, rows, n_experts)].tm();
   // the fp8 engine's shapes (launch_dma_b8)
   if (wf == WF_FP8) return kDma[fp8_shape(v, true)].tm();
@@ -77,6 +79,15 @@ hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64
     switch (kind) {
       case GK_EXPERT_SITU: return launch_dma_b4a8<EPI_SITU, true, true, uint16_t>(v, a, s);
       case GK_EXPERT_DOWN: return launch_dma_b4a8<EPI_STORE, false, false, uint16_t>(v, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (path == PATH_BF16 && wf == WF_MX8A8) {
+    // MX FP8 activations x MX FP8 weights: the routed experts only
+    const int v = mx8_shape(a.M, a.n_experts);
+    switch (kind) {
+      case GK_EXPERT_SITU: return launch_dma_b8a8<EPI_SITU, true, true, uint16_t>(v, a, s);
+      case GK_EXPERT_DOWN: return launch_dma_b8a8<EPI_STORE, false, false, uint16_t>(v, a, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -227,10 +227,11 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
   return t;
 }
 
-// Storage format of the B operand.
-// BF_MX4A8: MXFP4 B with MX FP8 A (e4m3 codes, an E8M0 scale per 32): the
-// gfx950 block-scaled MFMA, the B codes widened to e4m3 in registers.
-enum BFmt { BF_BF16 = 0, BF_FP8 = 1, BF_MX4 = 2, BF_MX4A8 = 3 };
+// Storage format of the B operand (and of A).
+// BF_MX4A8: MXFP4 B with MX FP8 A (e4m3 codes, an E8M0 scale per 32);
+// BF_MX8A8: MX FP8 B (e4m3 codes, an E8M0 scale per 32) with MX FP8 A.  Both
+// run the gfx950 block-scaled MFMA on the codes as stored.
+enum BFmt { BF_BF16 = 0, BF_FP8 = 1, BF_MX4 = 2, BF_MX4A8 = 3, BF_MX8A8 = 4 };
 
 // fp8 B operands: block scales of up to this many 128-wide K blocks (K <= 16384)
 constexpr int kMaxKBlocks = 128;
@@ -253,13 +254,15 @@ template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int MA
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64 || BK == 128 || BK == 256, "K tile of 32 to 256");
   // A is bf16, or (A8) MX FP8: e4m3 codes with an E8M0 scale per 32 along K
-  constexpr bool A8 = BF == BF_MX4A8;
+  constexpr bool A8 = BF == BF_MX4A8 || BF == BF_MX8A8;
   constexpr int RB = BK * (A8 ? 1 : 2);  // bytes per A tile row
   constexpr int CPR = RB / 16;        // 16 B chunks per A row
   constexpr int RPI = 1024 / RB;      // A rows per DMA wave instruction
-  // B is bf16, fp8 e4m3 with 128 x 128 block scales (B8), or MXFP4 (MX4)
-  constexpr bool B8 = BF == BF_FP8, MX4 = BF == BF_MX4 || A8;
-  constexpr int ESZ_B = B8 ? 1 : 2;   // bytes per B element (bf16, fp8)
+  // B is bf16, fp8 e4m3 with 128 x 128 block scales (B8), MXFP4 (MX4) or MX
+  // FP8 (MX8); MXB: B with an E8M0 scale per 32 along K
+  constexpr bool B8 = BF == BF_FP8, MX4 = BF == BF_MX4 || BF == BF_MX4A8;
+  constexpr bool MX8 = BF == BF_MX8A8, MXB = MX4 || MX8;
+  constexpr int ESZ_B = (B8 || MX8) ? 1 : 2;  // bytes per B element (bf16, e4m3)
   // B bytes of n elements: n * BNUM / BDEN
   constexpr int BNUM = MX4 ? 1 : ESZ_B, BDEN = MX4 ? 2 : 1;
   constexpr int RB_B = BK * BNUM / BDEN;  // bytes per B tile row
@@ -273,7 +276,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   static_assert(!B8 || (BK == 64 && TN_OUT % 128 == 0),
                 "fp8 B: K tile 64, whole 128-row scale blocks");
   // MXFP4 B: a lane's 16-byte read of a B row holds 32 codes, one E8M0 block
-  static_assert(!MX4 || (BK >= 64 && !MSEG && TN % 64 == 0),
+  static_assert(!MXB || (BK >= 64 && !MSEG && TN % 64 == 0),
                 "MXFP4 B: K tile of 64 or more, single segment");
   constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -281,7 +284,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // (SPR bytes a row) travel with the tile, after its B rows, copied a dword a
   // lane: LS instructions of 256 bytes a wave a tile, besides the operand
   // ones.  K tiles of 64 (2 bytes a row) take a whole-K table loaded up front.
-  constexpr bool MXS = MX4 && BK >= 128;
+  constexpr bool MXS = MXB && BK >= 128;
   constexpr int SPR = MXS ? BK / 32 : 0;
   // whole rounds of scale instructions: rows past TN are loaded, never used
   constexpr int LS = MXS ? ((TN * SPR + 255) / 256 + NW - 1) / NW : 0;
@@ -384,10 +387,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // Persistent N tiles (short tiles with bf16 or in-stage-scaled MXFP4 B): a
   // workgroup runs nper consecutive N tiles of its M tile, one ring over all
   // of their K tiles, storing each N tile's outputs inside the loop
-  constexpr bool PN = MA > 0 && !B8 && !MSEG && EPI != EPI_ROUTER && (!MX4 || MXS);
+  constexpr bool PN = MA > 0 && !B8 && !MSEG && EPI != EPI_ROUTER && (!MXB || MXS);
   const int nper = PN ? max((int)args.nper, 1) : 1;
   uint8_t *mx_lds = reinterpret_cast<uint8_t *>(sc_lds);
-  const int kb32 = MX4 ? (int)(args.seg[0].k / 32) : 0;
+  const int kb32 = MXB ? (int)(args.seg[0].k / 32) : 0;
   if constexpr (MX4 && !MXS) {
     const int wpr = kb32 / 4;  // dwords a row
     const int total = TN * wpr;
@@ -843,12 +846,13 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         if constexpr (A8) {
           // block-scaled MFMA: all loads of the tile STAGES - 1 ahead first, then
           // per 64-wide k step the operands and scales of NS x FRN
-          // v_mfma_scale_f32_32x32x64_f8f6f4 (A e4m3, B E2M1 as stored).  Scale
-          // block b of the step (its k 32 b.. 32 b + 31, MX block 2 S + b) is B
-          // lane half b (one 16-byte chunk of 32 codes, 2 S + b) and bytes
-          // 16 b.. 16 b + 15 of both A lane halves (half h: k 32 b + 16 h ..+16,
-          // so a lane reads A chunks 4 S + h and 4 S + 2 + h); the scale of
-          // block b comes from lane half b, on both operands.
+          // v_mfma_scale_f32_32x32x64_f8f6f4 (A e4m3, B E2M1 or e4m3 as stored).
+          // Scale block b of the step (its k 32 b.. 32 b + 31, MX block 2 S + b)
+          // is, for E2M1 B, B lane half b (one 16-byte chunk of 32 codes,
+          // 2 S + b), and for e4m3 operands bytes 16 b.. 16 b + 15 of both lane
+          // halves (half h: k 32 b + 16 h ..+16, so a lane reads chunks 4 S + h
+          // and 4 S + 2 + h); the scale of block b comes from lane half b, on
+          // both operands.
           static_for<L>([&](auto d) G2_INL { dma_one(d, kdc, dst, dj); });
           dma_scales(kdc, dst, dj);
           dma_ascales(kdc, dst);
@@ -860,9 +864,23 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
               i32x8 bq[FRN];
               int bs[FRN];
               static_for<FRN>([&](auto j) G2_INL {
-                uint4 raw[FRN];
-                read_b8(st, S, j, raw);
-                bq[j] = i32x8{(int)raw[j].x, (int)raw[j].y, (int)raw[j].z, (int)raw[j].w, 0, 0, 0, 0};
+                if constexpr (MX8) {
+                  // e4m3 B: the A lane layout (chunks 4 S + h and 4 S + 2 + h)
+                  const int rb = b_row_of(j);
+                  const char *br = st + A_BYTES + rb * RB_B;
+                  const int c0 = 4 * S + (lane >> 5);
+                  const uint4 lo =
+                      *reinterpret_cast<const uint4 *>(br + ((c0 ^ swz(rb, CPR_B)) << 4));
+                  const uint4 hi =
+                      *reinterpret_cast<const uint4 *>(br + (((c0 + 2) ^ swz(rb, CPR_B)) << 4));
+                  bq[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                } else {
+                  uint4 raw[FRN];
+                  read_b8(st, S, j, raw);
+                  bq[j] = i32x8{(int)raw[j].x, (int)raw[j].y, (int)raw[j].z, (int)raw[j].w,
+                                0, 0, 0, 0};
+                }
                 bs[j] = (int)*reinterpret_cast<const uint8_t *>(
                     st + A_BYTES + B_BYTES + b_row_of(j) * SPR + 2 * S + (lane >> 5));
               });
@@ -880,7 +898,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
 #pragma unroll
                 for (int j = 0; j < FRN; ++j)
                   acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                      aq, bq[j], acc[i][j], 0 /* A e4m3 */, 4 /* B e2m1 */, 0, as, 0, bs[j]);
+                      aq, bq[j], acc[i][j], 0 /* A e4m3 */, MX8 ? 0 /* B e4m3 */ : 4 /* B e2m1 */,
+                      0, as, 0, bs[j]);
               }
               // keep the next k step's LDS reads after these MFMAs (registers)
               __builtin_amdgcn_sched_barrier(0);

@@ -26,7 +26,9 @@ struct DmaShape {
   constexpr int tn() const { return wn * frn * 32; }
   // bytes of a B tile row in format bf (g2::BFmt): bf16, fp8 codes, MXFP4 bytes
   static constexpr int b_row_bytes(int bk, int bf) {
-    return bf == g2::BF_FP8 ? bk : (bf == g2::BF_MX4 || bf == g2::BF_MX4A8) ? bk / 2 : bk * 2;
+    return (bf == g2::BF_FP8 || bf == g2::BF_MX8A8)    ? bk
+           : (bf == g2::BF_MX4 || bf == g2::BF_MX4A8) ? bk / 2
+                                                      : bk * 2;
   }
   // scale-code instructions (256 bytes) of `rows` rows of bk/32 codes, in whole
   // rounds of the workgroup's waves
@@ -37,10 +39,11 @@ struct DmaShape {
   // stage ring: A rows (bf16, or e4m3 codes with MX FP8 A) and B rows; MXFP4 B
   // with K tiles of 128 or more also the B rows' E8M0 codes, MX FP8 A the A rows'
   constexpr size_t lds(int bf = g2::BF_BF16) const {
-    const bool mx = bf == g2::BF_MX4 || bf == g2::BF_MX4A8;
-    return (size_t)stages * (tm() * bk * (bf == g2::BF_MX4A8 ? 1 : 2) + tn() * b_row_bytes(bk, bf) +
+    const bool a8 = bf == g2::BF_MX4A8 || bf == g2::BF_MX8A8;
+    const bool mx = bf == g2::BF_MX4 || a8;
+    return (size_t)stages * (tm() * bk * (a8 ? 1 : 2) + tn() * b_row_bytes(bk, bf) +
                              (mx && bk >= 128 ? code_bytes(tn()) : 0) +
-                             (bf == g2::BF_MX4A8 ? code_bytes(tm()) : 0));
+                             (a8 ? code_bytes(tm()) : 0));
   }
   // every wave issues whole rounds of A and of B DMA instructions (1 KB each)
   constexpr bool whole_rounds(int bf = g2::BF_BF16) const {
@@ -74,11 +77,14 @@ constexpr DmaShape kDma[] = {
     {2, 4, 4, 2, 128, 3, 1},  // 11: 256 x 256, 3 stages (156 KB)
     {2, 4, 5, 2, 128, 2, 1},  // 12: 320 x 256, 2 stages (120 KB)
     {2, 4, 3, 2, 128, 3, 1},  // 13: 192 x 256, 3 stages (132 KB)
+    // MX FP8 A x MX FP8 B (twice the B bytes of MXFP4): 2-stage rings
+    {2, 4, 4, 2, 128, 2, 1},  // 14: 256 x 256 (136 KB)
+    {2, 4, 3, 2, 128, 2, 1},  // 15: 192 x 256 (120 KB)
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
 constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6,
               kVTinyMX4 = 7, kVTinyMX4W = 8, kVQ256 = 9, kVQ192 = 10, kVA8 = 11,
-              kVA8W = 12, kVA8S = 13;
+              kVA8W = 12, kVA8S = 13, kVB8 = 14, kVB8S = 15;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 // shapes a bf16 B operand can take (6..8 are MXFP4-only)
 constexpr bool bf16_shape(int v) { return v >= 0 && v < 6; }
@@ -267,6 +273,27 @@ extern template hipError_t launch_dma_b4a8<EPI_STORE, false, false, uint16_t>(in
                                                                             const GemmArgs &,
                                                                             hipStream_t);
 extern template hipError_t launch_dma_b4a8<EPI_SITU, true, true, uint16_t>(int, const GemmArgs &,
+                                                                         hipStream_t);
+// MX FP8 A x MX FP8 B: 320-row tiles for 201-300 rows an expert, else 192
+// (<= 200) or 256 (override MOE_GEMM_A8: 12, 14, 15)
+inline int mx8_shape(int64_t rows, int64_t n_experts) {
+  const int dflt = rows <= 200 * n_experts ? kVB8S : rows <= 300 * n_experts ? kVA8W : kVB8;
+  const int v = env_int("MOE_GEMM_A8", dflt);
+  return (v == kVA8W || v == kVB8 || v == kVB8S) ? v : dflt;
+}
+template <int EPI, bool DUAL, bool GATHER, typename OutT>
+hipError_t launch_dma_b8a8(int shape, const GemmArgs &a, hipStream_t s) {
+  constexpr int F = g2::BF_MX8A8;
+  switch (shape) {
+    case kVA8W: return launch_dma_impl<kVA8W, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVB8S: return launch_dma_impl<kVB8S, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    default: return launch_dma_impl<kVB8, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+  }
+}
+extern template hipError_t launch_dma_b8a8<EPI_STORE, false, false, uint16_t>(int,
+                                                                            const GemmArgs &,
+                                                                            hipStream_t);
+extern template hipError_t launch_dma_b8a8<EPI_SITU, true, true, uint16_t>(int, const GemmArgs &,
                                                                          hipStream_t);
 #define MOE_B4_KINDS(X)                     \
   X(EPI_STORE, false, false, uint16_t)      \

@@ -22,8 +22,9 @@ enum GemmKind {
 int gemm_bm(int path);
 // Storage format of a GEMM's weights (B operand): bf16 (fp32 on the fp32
 // path), fp8 e4m3 with 128 x 128 block scales, MXFP4 with E8M0 scales per 32
-// (WF_MX4A8: and the A operand in MX FP8, for the block-scaled MFMA).
-enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2, WF_MX4A8 = 3 };
+// (WF_MX4A8: and the A operand in MX FP8, for the block-scaled MFMA); WF_MX8A8:
+// MX FP8 (e4m3 with E8M0 scales per 32) for both operands.
+enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2, WF_MX4A8 = 3, WF_MX8A8 = 4 };
 // M-tile rows of the grouped GEMMs for rows (token, expert) pairs over
 // n_experts experts with weights in format wf (the dispatch lays its tile
 // table out in these units).

@@ -27,6 +27,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 F32, BF16, FP8, MXFP4, E8M0 = 0, 1, 2, 3, 4
+# MX FP8 weights: e4m3 codes (generated as FP8 storage) with E8M0 scales per 32;
+# a Python-side tag only (the generators see FP8 for the codes)
+MXFP8 = 5
+MX_DTYPES = (MXFP4, MXFP8)
 NORMAL, DYADIC = 0, 1
 NORMAL_INT_STD = 107022.329313
 NORMAL_INT_MAX = 524280
@@ -38,11 +42,14 @@ MX_CODE_SIGMA = 2.0  # MXFP4: standard deviation of the draws rounded to E2M1 co
 # to the grid, saturating at 6), and the rms of 2^u, u uniform in {-1, 0, 1}
 MX_CODE_STD = 1.9885
 MX_SCALE_RMS = math.sqrt((0.25 + 1.0 + 4.0) / 3.0)
+MX8_CODE_SIGMA = 16.0  # MX FP8: standard deviation of the draws rounded to e4m3 codes
 
-# weight="mxfp4": the routed experts in MXFP4, every other weight bf16
-DTYPE_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
-NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8, MXFP4: np.uint8}
-ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, MXFP4: 1}  # per storage unit (MXFP4: 2 elements)
+# weight="mxfp4": the routed experts in MXFP4, every other weight bf16;
+# weight="mxfp8": the routed experts in MX FP8 (with MX FP8 inputs), the rest bf16
+DTYPE_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4, "mxfp8": MXFP8}
+NP_STORAGE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8, MXFP4: np.uint8, MXFP8: np.uint8}
+# per storage unit (MXFP4: 2 elements)
+ELEM_BYTES = {F32: 4, BF16: 2, FP8: 1, MXFP4: 1, MXFP8: 1}
 MX_NAMES = ("w_gate", "w_up", "w_down")
 
 # Tensor ids: distinct Philox counter words per tensor.
@@ -70,7 +77,8 @@ class Config:
     bias: str = "zero"          # "zero" or "zipf1.1"
     cutoff: str = "given"       # benchmark cutoff mode: "given" (alpha = 0) or "batch"
     # "mxfp8": the expert GEMMs read their inputs (x_lat, h) as OCP MX FP8 with a scale
-    # per 32 (with weight="mxfp4": the block-scaled MFMA path); "none": exactly
+    # per 32 (with weight="mxfp4" or "mxfp8": the block-scaled MFMA path; weight="mxfp8"
+    # requires it); "none": exactly
     act_quant: str = "none"
     beta: float = 4.0
     beta_u: float = 25.0
@@ -126,6 +134,12 @@ CONFIGS: Dict[str, Config] = {
                                   n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
                                   shared_inter=3072, weight="mxfp4", bias="zipf1.1",
                                   cutoff="batch", act_quant="mxfp8"),
+    # the routed experts in MX FP8 (e4m3 codes, E8M0 scale per 32 inputs) reading MX
+    # FP8 activations: both operands on the block-scaled MFMA (W8A8)
+    "k3_prefill_mxfp8": Config("k3_prefill_mxfp8", bt=16384, d=7168, latent=3584,
+                               n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                               shared_inter=3072, weight="mxfp8", bias="zipf1.1",
+                               cutoff="batch", act_quant="mxfp8"),
     # one GPU's share of K3 prefill under 8-way expert parallelism: its own 16384 tokens
     # through the replicated dense parts, and 262144 pairs over its 112 experts
     # (about 2341 rows per expert), so the grouped GEMMs run at the sharded shape
@@ -162,13 +176,13 @@ class Spec:
 
     @property
     def n_scale_blocks(self) -> int:
-        if self.dtype == MXFP4:
+        if self.dtype in MX_DTYPES:
             return self.n_mats * self.mat_rows * (self.mat_cols // MX_BLOCK)
         return self.n_mats * (self.mat_rows // FP8_BLOCK) * (self.mat_cols // FP8_BLOCK)
 
     @property
     def scale_shape(self) -> tuple:
-        if self.dtype == MXFP4:
+        if self.dtype in MX_DTYPES:
             return (self.n_mats, self.mat_rows, self.mat_cols // MX_BLOCK)
         return (self.n_mats, self.mat_rows // FP8_BLOCK, self.mat_cols // FP8_BLOCK)
 
@@ -177,9 +191,9 @@ def specs(cfg: Config) -> Dict[str, Spec]:
     d, L, E, I, S, Is = (cfg.d, cfg.latent, cfg.n_experts, cfg.expert_inter, cfg.n_shared,
                          cfg.shared_inter)
     a, w, r = DTYPE_NAMES[cfg.act], DTYPE_NAMES[cfg.weight], DTYPE_NAMES[cfg.router]
-    # MXFP4 applies to the routed experts; the dense weights stay bf16
+    # MXFP4 / MX FP8 apply to the routed experts; the dense weights stay bf16
     xw = w
-    if w == MXFP4:
+    if w in MX_DTYPES:
         w = BF16
     h = 2 if xw == MXFP4 else 1  # elements per storage unit of the experts
     return {
@@ -219,16 +233,20 @@ def draw_params(cfg: Config, name: str, routing: str = "normal"):
         return NORMAL, FP8_MAX / NORMAL_INT_MAX, 0
     if sp.dtype == MXFP4:
         return NORMAL, float(np.float32(MX_CODE_SIGMA / NORMAL_INT_STD)), 0
+    if sp.dtype == MXFP8:
+        return NORMAL, float(np.float32(MX8_CODE_SIGMA / NORMAL_INT_STD)), 0
     sigma = 1.0 if (name == "x" or sp.fan_in == 0) else 1.0 / math.sqrt(sp.fan_in)
     return NORMAL, float(np.float32(sigma / NORMAL_INT_STD)), 0
 
 
 def mx_centre(cfg: Config, name: str) -> int:
-    """Centre E8M0 code of the MXFP4 block scales of `name`: decoded weights
-    then have standard deviation ~ 1/sqrt(fan_in) (within a factor sqrt 2)."""
+    """Centre E8M0 code of the MXFP4 / MX FP8 block scales of `name`: decoded
+    weights then have standard deviation ~ 1/sqrt(fan_in) (within a factor
+    sqrt 2)."""
     sp = specs(cfg)[name]
     sigma = 1.0 / math.sqrt(max(sp.fan_in, 1))
-    return 127 + int(round(math.log2(sigma / (MX_CODE_STD * MX_SCALE_RMS))))
+    code_std = MX_CODE_STD if sp.dtype == MXFP4 else MX8_CODE_SIGMA
+    return 127 + int(round(math.log2(sigma / (code_std * MX_SCALE_RMS))))
 
 
 def scale_base(cfg: Config, name: str) -> float:
@@ -300,8 +318,8 @@ def lib_dev():
 def host_fill(dtype: int, n: int, seed: int, tid: int, offset: int, kind: int, scale: float,
               rng: int) -> np.ndarray:
     out = np.empty(n, dtype=np.uint8 if dtype == E8M0 else NP_STORAGE[dtype])
-    rc = lib_host().synth_fill_host(out.ctypes.data, dtype, n, seed, tid, offset, kind,
-                                    scale, rng)
+    rc = lib_host().synth_fill_host(out.ctypes.data, FP8 if dtype == MXFP8 else dtype, n, seed,
+                                    tid, offset, kind, scale, rng)
     if rc != 0:
         raise ValueError("synth_fill_host rejected its arguments")
     return out
@@ -339,9 +357,9 @@ def host_rows(cfg: Config, name: str, rows, seed: int = 0, routing: str = "norma
 
 def host_scales(cfg: Config, name: str, seed: int = 0) -> Optional[np.ndarray]:
     """fp32 block scales [n_mats][rows/128][cols/128] of an fp8 tensor, uint8
-    E8M0 codes [n_mats][rows][cols/32] of an MXFP4 tensor, else None."""
+    E8M0 codes [n_mats][rows][cols/32] of an MXFP4 or MX FP8 tensor, else None."""
     sp = specs(cfg)[name]
-    if sp.dtype == MXFP4:
+    if sp.dtype in MX_DTYPES:
         return host_fill(E8M0, sp.n_scale_blocks, seed, SCALE_TID_BASE + TID[name], 0, NORMAL,
                          0.0, mx_centre(cfg, name)).reshape(sp.scale_shape)
     if sp.dtype != FP8:
@@ -401,11 +419,13 @@ def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cu
     """Every tensor of the layer generated directly in device memory (torch
     tensors of the raw storage dtype).  Same bits as host_layer()."""
     import torch
-    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP4: torch.uint8}
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.uint8, MXFP4: torch.uint8,
+           MXFP8: torch.uint8}
     stream = torch.cuda.current_stream().cuda_stream
 
     def fill(t, dtype, n, tid, kind, scale, rng, what):
-        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()), dtype, n, seed, tid, 0,
+        rc = lib_dev().synth_fill_device(ctypes.c_void_p(t.data_ptr()),
+                                         FP8 if dtype == MXFP8 else dtype, n, seed, tid, 0,
                                          kind, scale, rng, ctypes.c_void_p(stream))
         if rc != 0:
             raise RuntimeError(f"synth_fill_device failed ({rc}) for {what}")
@@ -418,7 +438,7 @@ def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cu
         kind, scale, rng = draw_params(cfg, name, routing)
         fill(t, sp.dtype, sp.numel, TID[name], kind, scale, rng, name)
         out[name] = t
-        if sp.dtype == MXFP4:
+        if sp.dtype in MX_DTYPES:
             sc = torch.empty(sp.scale_shape, dtype=torch.uint8, device=device)
             fill(sc, E8M0, sp.n_scale_blocks, SCALE_TID_BASE + TID[name], NORMAL, 0.0,
                  mx_centre(cfg, name), "scale:" + name)

@@ -45,8 +45,11 @@ def tol_of(cfg) -> float:
 def abi_config(cfg, cutoff=None):
     import sparse_moe_layer_quantile_amd as moe
     weight = cfg.weight
-    if getattr(cfg, "act_quant", "none") == "mxfp8":
-        assert weight == "mxfp4", "MX FP8 expert inputs go with MXFP4 experts"
+    mx8_in = getattr(cfg, "act_quant", "none") == "mxfp8"
+    if weight == "mxfp8":
+        assert mx8_in, "MX FP8 experts read MX FP8 inputs"
+    elif mx8_in:
+        assert weight == "mxfp4", "MX FP8 expert inputs go with MX experts"
         weight = "mxfp4_a8"
     return moe.make_config(cfg.d, cfg.latent, cfg.n_experts, cfg.top_k, cfg.expert_inter,
                            cfg.n_shared, cfg.shared_inter, cfg.beta, cfg.beta_u, cfg.rms_eps,
@@ -65,7 +68,7 @@ def device_layer(cfg, seed=0, routing="normal", cutoff=None, alpha=None, names=N
         if k == "x" or v is None:
             continue
         if k.startswith("scale:"):
-            mx = cfg.weight == "mxfp4" and k[6:] in MX_ABI
+            mx = cfg.weight in ("mxfp4", "mxfp8") and k[6:] in MX_ABI
             t[(MX_ABI if mx else SCALE_ABI)[k[6:]]] = v
         else:
             t[ABI_NAME[k]] = v

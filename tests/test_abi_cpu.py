@@ -122,6 +122,12 @@ def test_mxfp4_a8_workspace_and_limits():
                                64) == 0
     with pytest.raises(AssertionError):
         parity.abi_config(synth.CONFIGS["mid_bf16"].with_(act_quant="mxfp8"))
+    # MX FP8 experts (W8A8): the same workspace as W4A8, MX FP8 inputs required
+    c88 = parity.abi_config(cfg.with_(weight="mxfp8", act_quant="mxfp8"))
+    assert c88.weight_dtype == moe.MOE_MXFP8
+    assert moe.workspace_bytes(c88, bt) == moe.workspace_bytes(c8, bt)
+    with pytest.raises(AssertionError):
+        parity.abi_config(cfg.with_(weight="mxfp8"))
 
 
 def test_mx8_quantize_argument_errors_on_host():

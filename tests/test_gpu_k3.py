@@ -99,6 +99,11 @@ def test_k3_prefill_mxfp4_mx8_inputs():
     _run_k3("k3_prefill_mxfp4_a8", n_sample=10)
 
 
+def test_k3_prefill_mxfp8_experts():
+    """MX FP8 experts with MX FP8 inputs (W8A8 on the block-scaled MFMA)."""
+    _run_k3("k3_prefill_mxfp8", n_sample=10)
+
+
 def test_k3_expert_parallel_share():
     """One GPU's share of 8-way expert parallelism: 112 experts with about 2341
     rows each, so every expert spans several M tiles of the grouped GEMMs."""

@@ -25,18 +25,23 @@ def _need_gpu():
 
 @pytest.mark.parametrize("name,routing", [("x", "normal"), ("w_gate", "normal"),
                                           ("x", "dyadic"), ("w_router", "dyadic")])
-@pytest.mark.parametrize("cfg_name", ["tiny_fp32", "mid_bf16", "k3_prefill_fp8"])
+@pytest.mark.parametrize("cfg_name", ["tiny_fp32", "mid_bf16", "k3_prefill_fp8",
+                                      "k3_prefill_mxfp4", "k3_prefill_mxfp8"])
 def test_synth_device_matches_host(cfg_name, name, routing):
     cfg = synth.CONFIGS[cfg_name]
-    if cfg_name == "k3_prefill_fp8":
+    if cfg_name.startswith("k3_prefill"):
         cfg = cfg.with_(bt=64, n_experts=2)
     say("synth", cfg_name, name, routing)
-    dev = synth.device_layer(cfg, seed=3, routing=routing, names=[name])[name]
+    lay = synth.device_layer(cfg, seed=3, routing=routing, names=[name])
+    dev = lay[name]
     torch.cuda.synchronize()
     host = synth.host_tensor(cfg, name, seed=3, routing=routing)
     got = dev.view(torch.uint8 if dev.dtype == torch.uint8 else
                    (torch.int16 if dev.dtype == torch.bfloat16 else torch.int32)).cpu().numpy()
     np.testing.assert_array_equal(got.reshape(-1).view(host.dtype), host)
+    if "scale:" + name in lay:  # block scales / E8M0 codes too
+        hs = synth.host_scales(cfg, name, seed=3)
+        np.testing.assert_array_equal(lay["scale:" + name].cpu().numpy(), hs)
 
 
 # ---- routing -------------------------------------------------------------------------------
@@ -298,6 +303,29 @@ def test_forward_mxfp4_mx8_every_tile_shape(shape_id, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_A8", shape_id)
     cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp4", act_quant="mxfp8", bt=4096)
     say("forward mxfp4 + mx8 inputs, forced shape", shape_id)
+    _mxfp4_check(cfg, "batch")
+
+
+@pytest.mark.parametrize("bt,cutoff,shape", [(4096, "batch", None), (64, "given", None),
+                                             (300, "batch", (640, 384)), (8, "batch", None)])
+def test_forward_mxfp8_experts_mid(bt, cutoff, shape):
+    """MX FP8 experts (e4m3 codes, E8M0 scales per 32) reading MX FP8 inputs: both
+    operands on the block-scaled MFMA (W8A8).  The 4096-token batch runs the
+    320-row tiles, the others the 192-row ones; (640, 384) has a partial N tile
+    in the down GEMM."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp8", act_quant="mxfp8", bt=bt)
+    if shape is not None:
+        cfg = cfg.with_(latent=shape[0], expert_inter=shape[1])
+    say("forward mxfp8 experts", bt, cutoff, cfg.latent, cfg.expert_inter)
+    _mxfp4_check(cfg, cutoff)
+
+
+@pytest.mark.parametrize("shape_id", ["12", "14", "15"])
+def test_forward_mxfp8_every_tile_shape(shape_id, monkeypatch):
+    """Each tile shape of the W8A8 engine (forced): 320, 256 and 192 rows."""
+    monkeypatch.setenv("MOE_GEMM_A8", shape_id)
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp8", act_quant="mxfp8", bt=4096)
+    say("forward mxfp8 experts, forced shape", shape_id)
     _mxfp4_check(cfg, "batch")
 
 

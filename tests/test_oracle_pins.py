@@ -181,6 +181,55 @@ def test_mxfp4_expert_equals_expert_on_decoded_values():
         np.testing.assert_array_equal(a, b)
 
 
+def _mx8_table_decode(codes, e8):
+    """MX FP8 decode for the layout pins: the element values from the e4m3
+    decoder (pinned above on the OCP table and on every code), the scale from
+    the E8M0 doubling rule, placed here per row and 32-wide block."""
+    table = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    sc = np.ldexp(1.0, e8.astype(np.int64) - 127)
+    return table[codes] * np.repeat(sc, 32, axis=-1)
+
+
+def test_mxfp8_matrix_element_and_block_scale():
+    """An MX FP8 matrix holds one e4m3 code a byte; each element takes the E8M0
+    scale of its own row and 32-wide column block (not a neighbour's)."""
+    rows, cols = 3, 96
+    codes = np.arange(rows * cols, dtype=np.int64).reshape(rows, cols) % 0x7E
+    codes = (codes | ((np.arange(cols) % 3 == 0) * 0x80)).astype(np.uint8)  # some negatives
+    e8 = np.array([[120, 127, 130], [1, 200, 126], [127, 127, 128]], np.uint8)
+    m = oracle.Mat(codes, e8)
+    assert m.c.cols == cols and m.c.dtype == oracle.MXFP8
+    want = _mx8_table_decode(codes, e8)
+    for r in range(rows):
+        for c in (0, 1, 30, 31, 32, 33, 63, 64, 95):
+            assert oracle.lib().orc_decode(m.ref, 0, r, c) == want[r, c]
+    with pytest.raises(ValueError):
+        oracle.Mat(codes[:, :80], e8)  # scales of a different row length
+
+
+def test_mxfp8_expert_equals_expert_on_decoded_values():
+    """An expert with MX FP8 matrices gives exactly the expert on the same values
+    written out in fp64-exact fp32 (decoded here from the spec tables)."""
+    rng = np.random.default_rng(23)
+    E, L, I = 2, 64, 96
+    def mx(rows, cols):
+        codes = rng.integers(0, 256, size=(E, rows, cols), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x00  # no NaN codes
+        e8 = rng.integers(110, 118, size=(E, rows, cols // 32), dtype=np.uint8)
+        return codes, e8
+    (gc, ge), (uc, ue), (dc, de) = mx(I, L), mx(I, L), mx(L, I)
+    x = rng.normal(size=L)
+    s = Shape(latent=L, expert_inter=I)
+    for e in range(E):
+        a = oracle.expert(s, oracle.Mat(gc, ge), oracle.Mat(uc, ue), oracle.Mat(dc, de), x,
+                          index=e)
+        dec = [f32(_mx8_table_decode(c[e], sc[e])) for c, sc in ((gc, ge), (uc, ue), (dc, de))]
+        assert all((d.astype(np.float64) == _mx8_table_decode(c[e], sc[e])).all()
+                   for d, (c, sc) in zip(dec, ((gc, ge), (uc, ue), (dc, de))))
+        b = oracle.expert(s, *(oracle.Mat(d) for d in dec), x)
+        np.testing.assert_array_equal(a, b)
+
+
 # ---- scalar functions -----------------------------------------------------------------
 
 def test_sigmoid_closed_forms():

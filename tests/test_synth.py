@@ -96,6 +96,31 @@ def test_mxfp4_layer_packing_and_scales():
     assert abs(deq.std() * math.sqrt(cfg.latent) - 1.0) < 0.45
 
 
+def test_mxfp8_layer_codes_and_scales():
+    """MX FP8 experts: one e4m3 code a weight (the draw at standard deviation 16,
+    rounded as the fp8 path rounds), E8M0 codes per row and 32 inputs around a
+    centre that gives decoded weights ~ 1/sqrt(fan_in); dense weights bf16."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight="mxfp8", act_quant="mxfp8", n_experts=2,
+                                          latent=256, expert_inter=128)
+    sp = synth.specs(cfg)
+    assert sp["w_gate"].shape == (2, 128, 256) and sp["w_down"].shape == (2, 256, 128)
+    assert sp["w_gate"].dtype == synth.MXFP8 and sp["w_down_proj"].dtype == synth.BF16
+    codes = synth.host_matrix(cfg, "w_gate", 1)
+    assert codes.dtype == np.uint8 and codes.shape == (128, 256)
+    kind, scale, _ = synth.draw_params(cfg, "w_gate")
+    off = sp["w_gate"].mat_rows * sp["w_gate"].mat_cols  # first element of expert 1
+    for i in (0, 1, 77, codes.size - 1):
+        v = synth.lib_host().synth_normal_int_host(0, synth.TID["w_gate"], off + i)
+        want = oracle.double_to_e4m3(float(np.float32(v) * np.float32(scale)))
+        assert codes.ravel()[i] == want, i
+    sc = synth.host_scales(cfg, "w_gate")
+    assert sc.dtype == np.uint8 and sc.shape == (2, 128, 8)
+    c = synth.mx_centre(cfg, "w_gate")
+    assert set(np.unique(sc)) == {c - 1, c, c + 1}
+    deq = oracle.decode(codes, sc[1])
+    assert abs(deq.std() * math.sqrt(cfg.latent) - 1.0) < 0.45
+
+
 def test_normal_draw_statistics():
     cfg = synth.CONFIGS["tiny_fp32"]
     x = synth.host_tensor(cfg, "x")
