@@ -221,6 +221,110 @@ def bench_ffn(args) -> int:
     return 0
 
 
+def bench_tier(args, cfg) -> int:
+    """Low-batch decode with the routed experts in pinned host memory and an HBM
+    cache of cfg.tier_slots experts (moe_tier_*).  Each step is one forward of a
+    new token batch (a pool of 16 seeded batches), with the cache's plan and
+    observe calls around it, and ends with the host waiting for the step's
+    output, as an autoregressive decode loop does before its next step; the
+    cache warms during 4 x warmup steps.  Reported beside it: the same steps
+    with every expert resident in HBM, and with none cached (every expert read
+    over PCIe)."""
+    import torch
+    import sparse_moe_layer_quantile_amd as moe
+    import synth
+    from tests import parity
+
+    torch.cuda.set_device(0)
+    layer, _ = parity.device_layer(cfg, seed=args.seed)
+    pool = [synth.device_layer(cfg, seed=1000 + i, names=["x"])["x"] for i in range(16)]
+    mx = cfg.weight != "bf16"
+    names = ["w_gate", "w_up", "w_down"] + (["e8_gate", "e8_up", "e8_down"] if mx else [])
+    host = {n: layer.tensors[n].cpu().pin_memory() for n in names}
+    host_bytes = sum(t.numel() * t.element_size() for t in host.values())
+    E, P = cfg.n_experts, cfg.bt * cfg.top_k
+    bufs = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                perm=torch.empty(P, dtype=torch.int32, device="cuda"),
+                inv_perm=torch.empty(P, dtype=torch.int32, device="cuda"))
+    y = torch.empty((cfg.bt, cfg.d), dtype=torch.bfloat16, device="cuda")
+
+    def run(step_fn, warm, steps):
+        for i in range(warm):
+            step_fn(pool[i % len(pool)])
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step_fn(pool[(warm + i) % len(pool)])
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms_resident = run(lambda x: layer.forward(x, out=y), args.warmup, args.steps)
+    copy = torch.cuda.Stream()
+    out = {}
+    for n_slots in (0, cfg.tier_slots):
+        tier = moe.ExpertTier(layer.cfg, host, n_slots, decay=0.9, max_loads=32)
+        t = {n: v for n, v in layer.tensors.items() if n not in names}
+        t["expert_tab"] = tier.table
+        tl = moe.StableLatentMoE(layer.cfg, t)
+
+        def step(x):
+            tier.plan(copy)
+            tl.forward(x, out=y, dispatch=bufs)
+            tier.observe(bufs["counts"])
+
+        warm = 4 * args.warmup if n_slots else args.warmup
+        for i in range(warm):
+            step(pool[i % len(pool)])
+            torch.cuda.synchronize()
+        s0 = tier.stats()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(pool[(warm + i) % len(pool)])
+            torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for _ in range(2):  # fold the timed steps' last counts
+            tier.plan(copy)
+            torch.cuda.synchronize()
+        s1 = tier.stats()
+        d = {k: s1[k] - s0[k] for k in s1}
+        out[n_slots] = dict(ms=ms, hbm_pair_frac=d["pairs_hbm"] / max(d["pairs"], 1),
+                            loads_per_step=d["loads"] / args.steps,
+                            bytes_loaded_per_step=d["bytes_loaded"] / args.steps,
+                            resident=s1["resident"])
+        tier.close()
+        del tl, tier
+    tiered = out[cfg.tier_slots]
+    line = {
+        "metric": "tiered-expert decode tokens/s (experts in host DRAM, HBM cache)",
+        "value": cfg.bt / (tiered["ms"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": tiered["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "bt": cfg.bt, "d": cfg.d, "latent": cfg.latent,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "expert_inter": cfg.expert_inter, "weights": cfg.weight,
+                   "router_bias": cfg.bias, "cutoff": cfg.cutoff, "parallelism": "1 GPU"},
+        "tiering": {"cache_slots": cfg.tier_slots,
+                    "cache_bytes": cfg.tier_slots * moe.tier_slot_bytes(layer.cfg),
+                    "host_expert_bytes": host_bytes,
+                    "tiered": tiered, "host_only": out[0],
+                    "all_resident_ms": ms_resident},
+        "roofline": None,
+        "kernel_sources": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
     """The fp64 CPU oracle on a bounded sample of the same workload."""
     import oracle
@@ -331,6 +435,8 @@ def main(argv=None):
     from tests import parity
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.tier_slots > 0:
+        return bench_tier(args, cfg)
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)

@@ -134,6 +134,16 @@ typedef struct moe_weights {
   /* MOE_MXFP4, MOE_MXFP4_A8 and MOE_MXFP8 only (else NULL): E8M0 codes of the routed experts' matrices,
    * [E][I][L/32] (gate, up) and [E][L][I/32] (down), 4-byte aligned. */
   const uint8_t *e8_gate, *e8_up, *e8_down;
+  /* Optional (NULL: the stacked arrays above): per-expert addresses of the
+   * routed experts' matrices, a device array [6][E] of device-visible
+   * addresses -- rows gate, up, down, e8_gate, e8_up, e8_down (the e8 rows for
+   * the MX dtypes only, else ignored).  Entry e of a row is the start of expert
+   * e's matrix in the per-expert form of the stacked layout ([I][L] etc.), in
+   * device memory or in device-visible pinned host memory (256-byte aligned;
+   * E8M0 codes 4-byte aligned).  When set, w_gate, w_up, w_down and e8_* are
+   * not read and may be NULL.  Weight dtypes MOE_BF16 and the MX ones only
+   * (else MOE_ERR_UNSUPPORTED).  moe_tier_* maintains such a table. */
+  const uint64_t *expert_tab;
 } moe_weights;
 
 /* Router results.  The router "computes scores and indices" (tech.news18a.com
@@ -214,6 +224,89 @@ size_t moe_ffn_workspace_bytes(const moe_ffn_config *cfg, int64_t bt);
 moe_status moe_ffn_forward(const moe_ffn_config *cfg, const moe_ffn_weights *w, const void *x,
                            const void *r, int64_t bt, void *y, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* ---- Expert tiering: cold experts in host DRAM, hot ones cached in HBM -----
+ * akashbajwa.co "稀疏设计" (the tiered-memory paragraphs near its end): at low
+ * batch, the most used experts can sit in HBM and the rarely used ones in
+ * cheaper DRAM, hot experts being loaded as needed -- worthwhile when routing
+ * concentrates on popular experts (a power law), not when a large batch
+ * lights up most of them.
+ *
+ * The routed experts live in pinned host memory (hipHostMalloc, e.g. torch
+ * pin_memory), stacked as moe_weights' w_gate / w_up / w_down / e8_*.  A
+ * caller-allocated HBM cache of n_slots experts holds the popular ones, and
+ * moe_forward reads every expert through the address table `table` (pass it
+ * as moe_weights.expert_tab): a cached expert from its slot, any other one
+ * straight from host memory over PCIe.  A forward is therefore correct
+ * whatever the cache holds, and never waits for the host.  Popularity is the
+ * routed-pair count of each expert (the dispatch counts of the forwards),
+ * decayed by `decay` per observed forward.  Call
+ *   moe_tier_plan(t, stream, copy_stream)   before each forward, and
+ *   moe_tier_observe(t, counts, stream)     after it (counts: the forward's
+ *                                           moe_dispatch_out.counts).
+ * Neither blocks the host.  observe adds the counts on the device into
+ * counts_acc (and the pairs whose expert the forward read from HBM), so no
+ * observation is lost however far the host runs ahead.  plan harvests that
+ * accumulator into counts_host (an async copy, then zeroes it) when no harvest
+ * is in flight, folds a landed harvest into the scores, points the table at
+ * the slots of experts whose copies have landed, and, when no copy is in
+ * flight, picks experts to load with moe_tier_select and starts their copies
+ * on copy_stream (NULL: stream).
+ * Those copies are ordered after the forwards already enqueued on stream,
+ * which may still read a slot being reused.  Every table change is a small
+ * kernel on `stream`.  The library allocates no device memory; it keeps
+ * host-side state and a few events.  Not thread-safe; one tier per layer. */
+typedef struct moe_tier moe_tier;
+
+typedef struct moe_tier_desc {
+  const void *h_gate, *h_up, *h_down;             /* pinned host, stacked [E][..] */
+  const uint8_t *h_e8_gate, *h_e8_up, *h_e8_down; /* pinned host, MX dtypes only */
+  int64_t n_slots;      /* experts the HBM cache holds, 0..E */
+  void *slots;          /* device, n_slots * moe_tier_slot_bytes(cfg) bytes, 256-aligned */
+  uint64_t *table;      /* device, 6 * E entries (moe_weights.expert_tab) */
+  uint32_t *counts_acc; /* device, E + 2 entries: counts observed since the last
+                           harvest, then the pairs read from HBM and all pairs */
+  uint32_t *counts_host;/* pinned host, E + 2 entries: where harvests land */
+  float decay;          /* popularity decay per observed forward, in (0, 1] */
+  int64_t max_loads;    /* experts a plan call may start loading, >= 1 */
+} moe_tier_desc;
+
+typedef struct moe_tier_stats {
+  int64_t forwards;     /* observed forwards */
+  int64_t harvested;    /* ... whose counts have been folded into the scores */
+  int64_t pairs;        /* routed (token, expert) pairs of the harvested forwards */
+  int64_t pairs_hbm;    /* ... whose expert the forward read from HBM */
+  int64_t loads;        /* experts copied into the cache */
+  int64_t evictions;    /* experts switched back to host memory */
+  int64_t bytes_loaded; /* host -> HBM bytes copied */
+  int64_t resident;     /* experts the table currently points at HBM for */
+} moe_tier_stats;
+
+/* Device bytes of one cache slot (one expert's matrices, plus E8M0 codes for
+ * the MX dtypes, each 256-byte aligned); 0 for a config tiering does not take. */
+size_t moe_tier_slot_bytes(const moe_config *cfg);
+/* Validates desc (host buffers must be pinned and device-visible:
+ * MOE_ERR_INVALID_ARG otherwise), fills the table with every expert's host
+ * address (an empty cache) and zeroes counts_acc on `stream`, returns the
+ * handle in *out. */
+moe_status moe_tier_create(const moe_config *cfg, const moe_tier_desc *desc, void *stream,
+                           moe_tier **out);
+moe_status moe_tier_plan(moe_tier *t, void *stream, void *copy_stream);
+moe_status moe_tier_observe(moe_tier *t, const int32_t *counts, void *stream);
+moe_status moe_tier_get_stats(const moe_tier *t, moe_tier_stats *out);
+/* Waits for the tier's copies in flight, then frees its host-side state. */
+moe_status moe_tier_destroy(moe_tier *t);
+/* The cache policy moe_tier_plan applies (host only; no GPU call).  score[E]
+ * >= 0, resident[E] in {0, 1}.  Candidates are the non-resident experts with
+ * score > 0, best first; victims the resident ones, worst first (ties: lower
+ * id first as candidate, higher id first as victim).  Up to max_loads
+ * candidates are chosen: into a free slot while fewer than n_slots experts
+ * are resident (victim -1), else replacing the next victim if the candidate's
+ * score exceeds 1.25 x the victim's (hysteresis against thrashing), stopping
+ * at the first that does not.  Writes load[i], victim[i]; returns the count,
+ * or -1 for invalid arguments. */
+int64_t moe_tier_select(const float *score, const uint8_t *resident, int64_t E, int64_t n_slots,
+                        int64_t max_loads, int32_t *load, int32_t *victim);
 
 /* ---- MX FP8 quantisation -----------------------------------------------------
  * OCP Microscaling Formats (MX) Specification v1.0, conversion of a vector of

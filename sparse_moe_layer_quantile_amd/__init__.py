@@ -43,7 +43,7 @@ class MoeConfig(ctypes.Structure):
 WEIGHT_FIELDS = ("w_router", "router_bias", "cutoff", "w_down_proj", "w_gate", "w_up",
                  "w_down", "latent_gamma", "w_up_proj", "sh_gate", "sh_up", "sh_down",
                  "s_down_proj", "s_gate", "s_up", "s_down", "s_up_proj", "s_sh_gate",
-                 "s_sh_up", "s_sh_down", "e8_gate", "e8_up", "e8_down")
+                 "s_sh_up", "s_sh_down", "e8_gate", "e8_up", "e8_down", "expert_tab")
 
 
 class MoeWeights(ctypes.Structure):
@@ -58,6 +58,22 @@ class MoeFfnConfig(ctypes.Structure):
 
 class MoeFfnWeights(ctypes.Structure):
     _fields_ = [("w_gate", _P), ("w_up", _P), ("w_down", _P), ("gamma", _P)]
+
+
+class MoeTierDesc(ctypes.Structure):
+    _fields_ = [("h_gate", _P), ("h_up", _P), ("h_down", _P), ("h_e8_gate", _P),
+                ("h_e8_up", _P), ("h_e8_down", _P), ("n_slots", ctypes.c_int64),
+                ("slots", _P), ("table", _P), ("counts_acc", _P), ("counts_host", _P),
+                ("decay", ctypes.c_float),
+                ("max_loads", ctypes.c_int64)]
+
+
+TIER_STATS = ("forwards", "harvested", "pairs", "pairs_hbm", "loads", "evictions",
+              "bytes_loaded", "resident")
+
+
+class MoeTierStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in TIER_STATS]
 
 
 class MoeRouteOut(ctypes.Structure):
@@ -101,6 +117,21 @@ def _load():
     lib.moe_ffn_forward.argtypes = [CP(MoeFfnConfig), CP(MoeFfnWeights), _P, _P, ctypes.c_int64,
                                     _P, _P, ctypes.c_size_t, _P]
     lib.moe_ffn_forward.restype = ctypes.c_int
+    lib.moe_tier_slot_bytes.argtypes = [CP(MoeConfig)]
+    lib.moe_tier_slot_bytes.restype = ctypes.c_size_t
+    lib.moe_tier_create.argtypes = [CP(MoeConfig), CP(MoeTierDesc), _P, CP(_P)]
+    lib.moe_tier_create.restype = ctypes.c_int
+    lib.moe_tier_plan.argtypes = [_P, _P, _P]
+    lib.moe_tier_plan.restype = ctypes.c_int
+    lib.moe_tier_observe.argtypes = [_P, _P, _P]
+    lib.moe_tier_observe.restype = ctypes.c_int
+    lib.moe_tier_get_stats.argtypes = [_P, CP(MoeTierStats)]
+    lib.moe_tier_get_stats.restype = ctypes.c_int
+    lib.moe_tier_destroy.argtypes = [_P]
+    lib.moe_tier_destroy.restype = ctypes.c_int
+    lib.moe_tier_select.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P,
+                                    _P]
+    lib.moe_tier_select.restype = ctypes.c_int64
     lib.moe_mx8_quantize.argtypes = [_P, ctypes.c_int64, _P, _P, _P]
     lib.moe_mx8_quantize.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -119,7 +150,95 @@ LIB = _load()
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_status_str", "moe_profile_enable", "moe_profile_read",
             "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward",
-            "moe_mx8_quantize")
+            "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
+            "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select")
+
+
+# ---- expert tiering -----------------------------------------------------------------
+
+def tier_slot_bytes(cfg: MoeConfig) -> int:
+    return int(LIB.moe_tier_slot_bytes(ctypes.byref(cfg)))
+
+
+def tier_select(score, resident, n_slots: int, max_loads: int):
+    """The cache policy alone (host only): (load ids, victim ids or -1)."""
+    import numpy as np
+    score = np.ascontiguousarray(score, np.float32)
+    resident = np.ascontiguousarray(resident, np.uint8)
+    load = np.empty(max(max_loads, 1), np.int32)
+    victim = np.empty(max(max_loads, 1), np.int32)
+    n = LIB.moe_tier_select(score.ctypes.data, resident.ctypes.data, score.size, n_slots,
+                            max_loads, load.ctypes.data, victim.ctypes.data)
+    if n < 0:
+        raise MoeError(-1, "moe_tier_select")
+    return load[:n].copy(), victim[:n].copy()
+
+
+class ExpertTier:
+    """Routed experts in pinned host memory with an HBM cache of n_slots experts
+    (moe_tier_*).  `host` maps w_gate / w_up / w_down (and e8_* for the MX
+    dtypes) to pinned CPU tensors in the stacked layout.  Pass `table` as the
+    layer's expert_tab; call plan() before and observe(counts) after each
+    forward."""
+
+    def __init__(self, cfg: MoeConfig, host: dict, n_slots: int, decay: float = 0.9,
+                 max_loads: int = 32):
+        import torch
+        self.cfg = cfg
+        self.host = dict(host)
+        E = cfg.n_experts
+        sb = tier_slot_bytes(cfg)
+        if sb == 0:
+            raise MoeError(-2, "moe_tier_slot_bytes")
+        self.slots = torch.empty(max(n_slots * sb, 256), dtype=torch.uint8, device="cuda")
+        self.table = torch.empty(6 * E, dtype=torch.int64, device="cuda")
+        self.counts_acc = torch.empty(E + 2, dtype=torch.int32, device="cuda")
+        self.counts_host = torch.empty(E + 2, dtype=torch.int32, pin_memory=True)
+        desc = MoeTierDesc(*(_ptr(self.host.get(n)) for n in ("w_gate", "w_up", "w_down",
+                                                              "e8_gate", "e8_up", "e8_down")),
+                           n_slots, self.slots.data_ptr(), self.table.data_ptr(),
+                           self.counts_acc.data_ptr(), self.counts_host.data_ptr(), decay,
+                           max_loads)
+        h = _P()
+        st = LIB.moe_tier_create(ctypes.byref(cfg), ctypes.byref(desc),
+                                 _P(torch.cuda.current_stream().cuda_stream), ctypes.byref(h))
+        if st != 0:
+            raise MoeError(st, "moe_tier_create")
+        self.handle = h
+
+    def plan(self, copy_stream=None):
+        import torch
+        st = LIB.moe_tier_plan(self.handle, _P(torch.cuda.current_stream().cuda_stream),
+                               _P(copy_stream.cuda_stream if copy_stream is not None else 0))
+        if st != 0:
+            raise MoeError(st, "moe_tier_plan")
+
+    def observe(self, counts):
+        import torch
+        st = LIB.moe_tier_observe(self.handle, _P(counts.data_ptr()),
+                                  _P(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise MoeError(st, "moe_tier_observe")
+
+    def stats(self) -> dict:
+        s = MoeTierStats()
+        st = LIB.moe_tier_get_stats(self.handle, ctypes.byref(s))
+        if st != 0:
+            raise MoeError(st, "moe_tier_get_stats")
+        return {n: getattr(s, n) for n in TIER_STATS}
+
+    def close(self):
+        if self.handle:
+            st = LIB.moe_tier_destroy(self.handle)
+            self.handle = None
+            if st != 0:
+                raise MoeError(st, "moe_tier_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_mx8_quantize(x: int, n: int, codes: int, scales: int, stream: int) -> int:
@@ -262,7 +381,10 @@ class StableLatentMoE:
             raise MoeError(st, "moe_dispatch")
         return res
 
-    def forward(self, x, shared_stream=None, return_routing=False, out=None):
+    def forward(self, x, shared_stream=None, return_routing=False, out=None, dispatch=None):
+        """y; with return_routing also the routing and dispatch results (new
+        tensors).  `dispatch` may instead hold caller-owned counts / offsets /
+        perm / inv_perm tensors to receive the dispatch results."""
         import torch
         bt = x.shape[0]
         E, k, P = self.cfg.n_experts, self.cfg.top_k, x.shape[0] * self.cfg.top_k
@@ -283,6 +405,9 @@ class StableLatentMoE:
                                                                 "logits")))
             disp = MoeDispatchOut(*(extra[n].data_ptr() for n in ("counts", "offsets", "perm",
                                                                   "inv_perm")))
+        elif dispatch is not None:
+            disp = MoeDispatchOut(*(dispatch[n].data_ptr() for n in ("counts", "offsets", "perm",
+                                                                     "inv_perm")))
         ws = self.workspace(bt)
         st = moe_forward(self.cfg, self.w, _ptr(x), bt, y.data_ptr(), route, disp,
                          ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream,

@@ -174,17 +174,17 @@ bool check_weights(const moe_config *c, const moe_weights *w, bool need_experts)
   if (!w || !w->w_router) return false;
   if (c->cutoff_mode == MOE_CUTOFF_GIVEN) { /* cutoff may be NULL */ }
   if (!need_experts) return true;
-  if (!w->w_down_proj || !w->w_gate || !w->w_up || !w->w_down || !w->latent_gamma ||
-      !w->w_up_proj)
-    return false;
+  const bool tab = w->expert_tab != nullptr;  // per-expert addresses instead
+  if (!w->w_down_proj || !w->latent_gamma || !w->w_up_proj) return false;
+  if (!tab && (!w->w_gate || !w->w_up || !w->w_down)) return false;
   if (c->n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return false;
   if (reinterpret_cast<uintptr_t>(w->latent_gamma) % 16) return false;  // read as float4
   if (c->weight_dtype == MOE_FP8E4M3_B128) {
     if (!w->s_down_proj || !w->s_gate || !w->s_up || !w->s_down || !w->s_up_proj) return false;
     if (c->n_shared > 0 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down)) return false;
   }
-  if (c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8 ||
-      c->weight_dtype == MOE_MXFP8) {
+  if (!tab && (c->weight_dtype == MOE_MXFP4 || c->weight_dtype == MOE_MXFP4_A8 ||
+               c->weight_dtype == MOE_MXFP8)) {
     // E8M0 codes are copied a dword at a time
     for (const uint8_t *e8 : {w->e8_gate, w->e8_up, w->e8_down})
       if (!e8 || reinterpret_cast<uintptr_t>(e8) % 4) return false;
@@ -442,6 +442,9 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   if (disp && (!disp->counts || !disp->offsets || !disp->perm || !disp->inv_perm))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  // per-expert address tables: the direct-to-LDS engine with bf16 or MX experts
+  const uint64_t *tab = w->expert_tab;
+  if (tab && (p.path != PATH_BF16 || p.expert_wf == WF_FP8)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t ss = shared_stream ? static_cast<hipStream_t>(shared_stream) : s;
   if (bt == 0) return MOE_OK;
@@ -552,6 +555,12 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.s_estride = fp8 ? (I / 128) * (L / 128) : (ewf == WF_MX4 || a8) ? I * (L / 32) : 0;
     a.e8 = w->e8_gate;
     a.e8_up = w->e8_up;
+    if (tab) {  // rows gate, up, down, e8_gate, e8_up, e8_down of [6][E]
+      a.b_tab = tab;
+      a.bu_tab = tab + E;
+      a.e8_tab = tab + 3 * E;
+      a.e8u_tab = tab + 4 * E;
+    }
     a.gather = perm;
     a.gather_div = (int32_t)k;
     // h rows carry the routing weight: W_d (w h) = w (W_d h); with MX FP8 h
@@ -584,6 +593,10 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.b_estride = L * I;
     a.s_estride = fp8 ? (L / 128) * (I / 128) : (ewf == WF_MX4 || a8) ? L * (I / 32) : 0;
     a.e8 = w->e8_down;
+    if (tab) {
+      a.b_tab = tab + 2 * E;
+      a.e8_tab = tab + 5 * E;
+    }
     a.out = o;
     a.ldo = L;
     PhaseScope ph(PH_EXPERT_DOWN, s);

@@ -40,6 +40,10 @@ struct GemmArgs {
   // MXFP4 B: E8M0 codes [rows][k/32] of seg[0].b and of b_up (expert 0; 4-byte
   // aligned); consecutive experts s_estride codes apart
   const uint8_t *e8, *e8_up;
+  // grouped, direct-to-LDS engine: per-expert addresses of seg[0].b, b_up, e8 and
+  // e8_up ([n_experts] each; NULL = the stacked layout above).  An address may be
+  // device memory or device-visible pinned host memory.
+  const uint64_t *b_tab, *bu_tab, *e8_tab, *e8u_tab;
   const int32_t *gather;     // A row of position p = gather[p] / gather_div
   int32_t gather_div;
   void *out;

@@ -394,8 +394,11 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   if constexpr (MX4 && !MXS) {
     const int wpr = kb32 / 4;  // dwords a row
     const int total = TN * wpr;
-    const uint8_t *e8g = args.e8 + (int64_t)tile.e * args.s_estride;
-    const uint8_t *e8u = DUAL ? args.e8_up + (int64_t)tile.e * args.s_estride : e8g;
+    const uint8_t *e8g = args.e8_tab ? reinterpret_cast<const uint8_t *>(args.e8_tab[tile.e])
+                                     : args.e8 + (int64_t)tile.e * args.s_estride;
+    const uint8_t *e8u = !DUAL        ? e8g
+                         : args.e8u_tab ? reinterpret_cast<const uint8_t *>(args.e8u_tab[tile.e])
+                                        : args.e8_up + (int64_t)tile.e * args.s_estride;
     for (int q = wave; q * 64 < total; q += NW) {
       const int i0 = q * 64 + lane;
       const int i = i0 < total ? i0 : 0;  // past the table: loaded, never used
@@ -534,7 +537,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     a_base = reinterpret_cast<const char *>(cur_a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
     const char *bsrc = static_cast<const char *>(args.seg[0].b);
     const char *busrc = static_cast<const char *>(args.b_up);
-    if (args.offsets != nullptr) {
+    if (args.b_tab != nullptr) {  // per-expert addresses (tiered experts)
+      bsrc = reinterpret_cast<const char *>(args.b_tab[tile.e]);
+      if (DUAL) busrc = reinterpret_cast<const char *>(args.bu_tab[tile.e]);
+    } else if (args.offsets != nullptr) {
       bsrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
       if (DUAL) busrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
     }
@@ -585,9 +591,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       int64_t n = tile.n0 + (up ? rr - TN / 2 : rr);
       if (rr >= TN || n >= args.N) n = tile.n0;  // loaded, never used
       soff[q] = (uint32_t)(n * kb32 + 4 * w);
-      sbase[q] = reinterpret_cast<uint64_t>((up ? args.e8_up : args.e8) +
-                                            (int64_t)tile.e * args.s_estride +
-                                            (int64_t)k_begin * BK / 32);
+      const uint8_t *e8x =
+          args.e8_tab ? reinterpret_cast<const uint8_t *>((up ? args.e8u_tab : args.e8_tab)[tile.e])
+                      : (up ? args.e8_up : args.e8) + (int64_t)tile.e * args.s_estride;
+      sbase[q] = reinterpret_cast<uint64_t>(e8x + (int64_t)k_begin * BK / 32);
     }
   }
   // A8: scale instructions of the A rows: instruction gs = wave + NW q, lane l

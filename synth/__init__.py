@@ -80,6 +80,9 @@ class Config:
     # per 32 (with weight="mxfp4" or "mxfp8": the block-scaled MFMA path; weight="mxfp8"
     # requires it); "none": exactly
     act_quant: str = "none"
+    # > 0: the routed experts live in pinned host memory with an HBM cache of this
+    # many experts (moe_tier_*), the benchmark's tiered-decode workload
+    tier_slots: int = 0
     beta: float = 4.0
     beta_u: float = 25.0
     rms_eps: float = 1e-6
@@ -134,6 +137,12 @@ CONFIGS: Dict[str, Config] = {
                                   n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
                                   shared_inter=3072, weight="mxfp4", bias="zipf1.1",
                                   cutoff="batch", act_quant="mxfp8"),
+    # low-batch decode with Zipf-skewed routing (popular experts), the MXFP4 experts
+    # in host DRAM and 112 of them (1/8) cached in HBM
+    "k3_decode_mxfp4_tier": Config("k3_decode_mxfp4_tier", bt=8, d=7168, latent=3584,
+                                   n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                                   shared_inter=3072, weight="mxfp4", bias="zipf1.1",
+                                   cutoff="given", tier_slots=112),
     # the routed experts in MX FP8 (e4m3 codes, E8M0 scale per 32 inputs) reading MX
     # FP8 activations: both operands on the block-scaled MFMA (W8A8)
     "k3_prefill_mxfp8": Config("k3_prefill_mxfp8", bt=16384, d=7168, latent=3584,

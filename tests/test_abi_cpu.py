@@ -8,6 +8,7 @@ import re
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import synth
@@ -40,7 +41,8 @@ def test_struct_layouts_match_header():
     ctypes mirrors used by the binding."""
     structs = {"moe_config": moe.MoeConfig, "moe_weights": moe.MoeWeights,
                "moe_route_out": moe.MoeRouteOut, "moe_dispatch_out": moe.MoeDispatchOut,
-               "moe_ffn_config": moe.MoeFfnConfig, "moe_ffn_weights": moe.MoeFfnWeights}
+               "moe_ffn_config": moe.MoeFfnConfig, "moe_ffn_weights": moe.MoeFfnWeights,
+               "moe_tier_desc": moe.MoeTierDesc, "moe_tier_stats": moe.MoeTierStats}
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
     for s, cls in structs.items():
         src.append(f'printf("{s} %zu\\n", sizeof({s}));')
@@ -139,6 +141,59 @@ def test_mx8_quantize_argument_errors_on_host():
     assert moe.moe_mx8_quantize(256, 32, 0, 256, 0) == -1
     assert moe.moe_mx8_quantize(258, 32, 256, 256, 0) == -1
     assert moe.moe_mx8_quantize(0, 0, 0, 0, 0) == 0
+
+
+def test_tier_select_policy():
+    """The expert cache policy (host only): free slots fill with the best
+    candidates; a full cache swaps only when a candidate beats the worst
+    resident by more than 1.25x; max_loads caps a call; ties are ordered by id."""
+    sel = moe.tier_select
+    score = np.array([0, 5, 3, 3, 9, 0, 1], np.float32)
+    res = np.zeros(7, np.uint8)
+    load, vic = sel(score, res, 3, 8)
+    assert load.tolist() == [4, 1, 2] and vic.tolist() == [-1, -1, -1]
+    load, vic = sel(score, res, 3, 2)  # max_loads
+    assert load.tolist() == [4, 1]
+    # full cache {1, 2, 4}: candidate 3 (3.0) does not beat victim 2 (3.0) x 1.25
+    res[[1, 2, 4]] = 1
+    load, vic = sel(score, res, 3, 8)
+    assert load.size == 0
+    score[3] = 3.8  # beats 3.0 x 1.25 = 3.75
+    load, vic = sel(score, res, 3, 8)
+    assert load.tolist() == [3] and vic.tolist() == [2]
+    # equal-score victims: the higher id goes first
+    score = np.array([4, 4, 0, 9, 9], np.float32)
+    res = np.array([1, 1, 0, 0, 0], np.uint8)
+    load, vic = sel(score, res, 2, 8)
+    assert load.tolist() == [3, 4] and vic.tolist() == [1, 0]
+    # a free slot first, then a swap
+    res = np.array([1, 0, 0, 0, 0], np.uint8)
+    load, vic = sel(score, res, 2, 8)
+    assert load.tolist() == [3, 4] and vic.tolist() == [-1, 0]
+    # zero scores are never loaded; invalid arguments
+    load, vic = sel(np.zeros(4, np.float32), np.zeros(4, np.uint8), 4, 4)
+    assert load.size == 0
+    with pytest.raises(moe.MoeError):
+        sel(score, np.ones(5, np.uint8), 2, 8)  # more resident than slots
+
+
+def test_tier_slot_bytes_and_unsupported_dtypes():
+    """A slot holds one expert's three matrices (and E8M0 codes for MX dtypes),
+    each 256-byte aligned; fp32 and fp8-block experts are not tiered, and a
+    forward with an expert table on them is rejected before any launch."""
+    base = synth.CONFIGS["mid_bf16"]
+    n = base.expert_inter * base.latent
+    assert moe.tier_slot_bytes(parity.abi_config(base)) == 3 * 2 * n
+    mx4 = parity.abi_config(base.with_(weight="mxfp4"))
+    assert moe.tier_slot_bytes(mx4) == 3 * (n // 2) + 3 * (n // 32)
+    mx8 = parity.abi_config(base.with_(weight="mxfp8", act_quant="mxfp8"))
+    assert moe.tier_slot_bytes(mx8) == 3 * n + 3 * (n // 32)
+    fp8 = parity.abi_config(synth.CONFIGS["k3_prefill_fp8"])
+    assert moe.tier_slot_bytes(fp8) == 0
+    assert moe.tier_slot_bytes(parity.abi_config(synth.CONFIGS["tiny_fp32"])) == 0
+    need = moe.workspace_bytes(fp8, 64)
+    w = moe.MoeWeights(**{f: 256 for f in moe.WEIGHT_FIELDS})
+    assert moe.moe_forward(fp8, w, 256, 64, 256, None, None, 256, need, 0) == -2
 
 
 def test_argument_errors_before_any_launch():
