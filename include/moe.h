@@ -83,8 +83,16 @@ typedef enum {
 /* Quantile Balancing cutoff (tech.news18a.com page, third technique): BATCH
  * takes alpha[e] = the m-th largest fp32 logit of expert e over the batch,
  * m = clamp(ceil(bt*top_k/E), 1, bt), so each expert's load is driven to
- * bt*top_k/E; GIVEN takes a caller-held alpha (e.g. a running estimate). */
-typedef enum { MOE_CUTOFF_GIVEN = 0, MOE_CUTOFF_BATCH = 1 } moe_cutoff_mode;
+ * bt*top_k/E; GIVEN takes a caller-held alpha (e.g. a running estimate).
+ * RUNNING selects with the caller-held alpha, as GIVEN, and also computes this
+ * batch's quantile zeta (as BATCH would use it) into moe_route_out.cutoff
+ * (required), so the caller can move its running alpha toward it
+ * (moe_cutoff_update) -- the cutoff "dynamically adjusted" across steps. */
+typedef enum {
+  MOE_CUTOFF_GIVEN = 0,
+  MOE_CUTOFF_BATCH = 1,
+  MOE_CUTOFF_RUNNING = 2
+} moe_cutoff_mode;
 
 typedef struct moe_config {
   int64_t d;            /* model width (7168 for K3) */
@@ -153,7 +161,8 @@ typedef struct moe_weights {
 typedef struct moe_route_out {
   int32_t *topk_idx; /* [bt][k] required */
   float *topk_w;     /* [bt][k] required */
-  float *cutoff;     /* [E] optional: the alpha used (the batch quantile in BATCH mode) */
+  float *cutoff;     /* [E] optional: the alpha used (the batch quantile in BATCH mode);
+                        RUNNING: required, the batch quantile zeta (alpha when bt = 0) */
   float *logits;     /* [bt][E] optional: fp32 z */
 } moe_route_out;
 
@@ -224,6 +233,15 @@ size_t moe_ffn_workspace_bytes(const moe_ffn_config *cfg, int64_t bt);
 moe_status moe_ffn_forward(const moe_ffn_config *cfg, const moe_ffn_weights *w, const void *x,
                            const void *r, int64_t bt, void *y, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* Running cutoff step for MOE_CUTOFF_RUNNING: alpha[e] += rate * (zeta[e] -
+ * alpha[e]) for e < n_experts, in fp32 with each operation rounded (device
+ * arrays, on `stream`; rate in [0, 1]: 1 follows the last batch, 0 freezes).
+ * An exponential moving average of the batch quantiles: the "dynamic
+ * adjustment" of the cutoff across steps, which the news18a page names
+ * without a rule (the reading taken here). */
+moe_status moe_cutoff_update(float *alpha, const float *zeta, int64_t n_experts, float rate,
+                             void *stream);
 
 /* ---- Expert tiering: cold experts in host DRAM, hot ones cached in HBM -----
  * akashbajwa.co "稀疏设计" (the tiered-memory paragraphs near its end): at low

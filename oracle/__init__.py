@@ -234,6 +234,17 @@ def quantile(z32: np.ndarray, m: int) -> np.ndarray:
     return out
 
 
+def cutoff_update(alpha, zeta, rate: float) -> np.ndarray:
+    """One step of the running cutoff (an exponential moving average of the
+    batch quantiles; the news18a page's third technique adjusts the cutoff
+    dynamically without giving a rule): alpha + rate * (zeta - alpha) in fp32,
+    each operation rounded."""
+    a = np.asarray(alpha, np.float32)
+    z = np.asarray(zeta, np.float32)
+    r = np.float32(rate)
+    return (a + r * (z - a)).astype(np.float32)
+
+
 def topk(z32: np.ndarray, k: int, alpha=None, z64=None):
     z32 = _c(z32, np.float32)
     alpha = _c(alpha, np.float32)

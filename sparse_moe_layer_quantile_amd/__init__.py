@@ -20,12 +20,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8E4M3_B128, MOE_MXFP4, MOE_MXFP4_A8, MOE_MXFP8 = 0, 1, 2, 3, 4, 5
-CUTOFF_GIVEN, CUTOFF_BATCH = 0, 1
+CUTOFF_GIVEN, CUTOFF_BATCH, CUTOFF_RUNNING = 0, 1, 2
 # "mxfp4_a8": MXFP4 experts with their inputs quantised to MX FP8 in the layer;
 # "mxfp8": MX FP8 experts, inputs likewise
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8E4M3_B128, "mxfp4": MOE_MXFP4,
           "mxfp4_a8": MOE_MXFP4_A8, "mxfp8": MOE_MXFP8}
-CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH}
+CUTOFFS = {"given": CUTOFF_GIVEN, "batch": CUTOFF_BATCH, "running": CUTOFF_RUNNING}
 
 _P = ctypes.c_void_p
 
@@ -117,6 +117,8 @@ def _load():
     lib.moe_ffn_forward.argtypes = [CP(MoeFfnConfig), CP(MoeFfnWeights), _P, _P, ctypes.c_int64,
                                     _P, _P, ctypes.c_size_t, _P]
     lib.moe_ffn_forward.restype = ctypes.c_int
+    lib.moe_cutoff_update.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_float, _P]
+    lib.moe_cutoff_update.restype = ctypes.c_int
     lib.moe_tier_slot_bytes.argtypes = [CP(MoeConfig)]
     lib.moe_tier_slot_bytes.restype = ctypes.c_size_t
     lib.moe_tier_create.argtypes = [CP(MoeConfig), CP(MoeTierDesc), _P, CP(_P)]
@@ -151,7 +153,17 @@ EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_status_str", "moe_profile_enable", "moe_profile_read",
             "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward",
             "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
-            "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select")
+            "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select",
+            "moe_cutoff_update")
+
+
+def cutoff_update(alpha, zeta, rate: float):
+    """alpha += rate * (zeta - alpha) on the device (fp32 tensors of E)."""
+    import torch
+    st = LIB.moe_cutoff_update(_P(alpha.data_ptr()), _P(zeta.data_ptr()), alpha.numel(),
+                               float(rate), _P(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise MoeError(st, "moe_cutoff_update")
 
 
 # ---- expert tiering -----------------------------------------------------------------

@@ -62,7 +62,8 @@ moe_status check_config(const moe_config *c) {
   if (c->d <= 0 || c->latent <= 0 || c->n_experts <= 0 || c->top_k <= 0 ||
       c->expert_inter <= 0 || c->n_shared < 0 || (c->n_shared > 0 && c->shared_inter <= 0))
     return MOE_ERR_INVALID_ARG;
-  if (c->cutoff_mode != MOE_CUTOFF_GIVEN && c->cutoff_mode != MOE_CUTOFF_BATCH)
+  if (c->cutoff_mode != MOE_CUTOFF_GIVEN && c->cutoff_mode != MOE_CUTOFF_BATCH &&
+      c->cutoff_mode != MOE_CUTOFF_RUNNING)
     return MOE_ERR_INVALID_ARG;
   if (elem_size(c->act_dtype) == 0 || elem_size(c->weight_dtype) == 0 ||
       elem_size(c->router_dtype) == 0)
@@ -260,7 +261,10 @@ moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, c
                      int64_t bt, float *z, int32_t *idx, float *wts, float *cutoff_out, void *ws,
                      hipStream_t s) {
   const int64_t E = c->n_experts;
-  const bool batch = c->cutoff_mode == MOE_CUTOFF_BATCH;
+  // BATCH and RUNNING compute this batch's quantile; RUNNING selects with the
+  // caller's alpha and only reports the quantile (in cutoff_out)
+  const bool batch = c->cutoff_mode != MOE_CUTOFF_GIVEN;
+  const bool running = c->cutoff_mode == MOE_CUTOFF_RUNNING;
   float *zT = at<float>(ws, p.zT);
   GemmArgs a = base_args(c);
   a.M = bt;
@@ -286,7 +290,7 @@ moe_status run_route(const moe_config *c, const Plan &p, const moe_weights *w, c
       m = m < 1 ? 1 : (m > bt ? bt : m);
       float *zeta = cutoff_out ? cutoff_out : at<float>(ws, p.alpha);
       MOE_TRY_HIP(launch_quantile(zT, bt, E, m, zeta, s));
-      alpha = zeta;
+      alpha = running ? w->cutoff : zeta;
     } else {
       alpha = w->cutoff;
       if (cutoff_out) MOE_TRY_HIP(launch_copy_or_zero_f32(cutoff_out, w->cutoff, E, s));
@@ -389,11 +393,12 @@ MOE_API moe_status moe_route(const moe_config *cfg, const moe_weights *w, const 
   if (st != MOE_OK) return st;
   if (!check_weights(cfg, w, false) || !out || !out->topk_idx || !out->topk_w)
     return MOE_ERR_INVALID_ARG;
+  if (cfg->cutoff_mode == MOE_CUTOFF_RUNNING && !out->cutoff) return MOE_ERR_INVALID_ARG;
   if (bt > 0 && !x) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bt == 0) {
-    if (out->cutoff && cfg->cutoff_mode == MOE_CUTOFF_GIVEN)
+    if (out->cutoff && cfg->cutoff_mode != MOE_CUTOFF_BATCH)  // GIVEN, RUNNING: alpha
       MOE_TRY_HIP(launch_copy_or_zero_f32(out->cutoff, w->cutoff, cfg->n_experts, s));
     return MOE_OK;
   }
@@ -419,6 +424,15 @@ MOE_API moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, 
   return MOE_OK;
 }
 
+MOE_API moe_status moe_cutoff_update(float *alpha, const float *zeta, int64_t n_experts,
+                                     float rate, void *stream) {
+  if (n_experts < 0 || !(rate >= 0.0f && rate <= 1.0f)) return MOE_ERR_INVALID_ARG;
+  if (n_experts == 0) return MOE_OK;
+  if (!alpha || !zeta) return MOE_ERR_INVALID_ARG;
+  MOE_TRY_HIP(launch_cutoff_update(alpha, zeta, n_experts, rate, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes,
                                     uint8_t *scales, void *stream) {
   if (n < 0 || n % 32) return MOE_ERR_INVALID_ARG;
@@ -439,6 +453,8 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   if (!check_weights(cfg, w, true)) return MOE_ERR_INVALID_ARG;
   if (bt > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
   if (route && (!route->topk_idx || !route->topk_w)) return MOE_ERR_INVALID_ARG;
+  if (cfg->cutoff_mode == MOE_CUTOFF_RUNNING && (!route || !route->cutoff))
+    return MOE_ERR_INVALID_ARG;
   if (disp && (!disp->counts || !disp->offsets || !disp->perm || !disp->inv_perm))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
@@ -447,7 +463,11 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   if (tab && (p.path != PATH_BF16 || p.expert_wf == WF_FP8)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t ss = shared_stream ? static_cast<hipStream_t>(shared_stream) : s;
-  if (bt == 0) return MOE_OK;
+  if (bt == 0) {
+    if (route && route->cutoff && cfg->cutoff_mode != MOE_CUTOFF_BATCH)
+      MOE_TRY_HIP(launch_copy_or_zero_f32(route->cutoff, w->cutoff, cfg->n_experts, s));
+    return MOE_OK;
+  }
 
   const int64_t E = cfg->n_experts, k = cfg->top_k, P = bt * k, d = cfg->d, L = cfg->latent;
   const int64_t I = cfg->expert_inter, S = cfg->n_shared, Is = cfg->shared_inter;

@@ -42,6 +42,9 @@ hipError_t launch_topk(const float *z, const float *alpha, int64_t bt, int64_t n
                        int64_t k, int32_t *idx, float *w, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_copy_or_zero_f32(float *dst, const float *src, int64_t n, hipStream_t s);
+// alpha[i] += rate * (zeta[i] - alpha[i]) in fp32, each operation rounded
+hipError_t launch_cutoff_update(float *alpha, const float *zeta, int64_t n, float rate,
+                                hipStream_t s);
 hipError_t launch_zero_i32(int32_t *dst, int64_t n, hipStream_t s);
 
 // ---- dispatch -------------------------------------------------------------------

@@ -171,6 +171,26 @@ hipError_t launch_copy_or_zero_f32(float *dst, const float *src, int64_t n, hipS
   return launch_kernel(copy_or_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        dst, src, n);
 }
+// alpha += rate * (zeta - alpha), rounded at each step (no fused multiply-add:
+// the pragma keeps the compiler from contracting the product and the sum)
+__global__ void __launch_bounds__(256) cutoff_update_kernel(float *alpha, const float *zeta,
+                                                            int64_t n, float rate) {
+#pragma clang fp contract(off)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const float a = alpha[i];
+    const float step = rate * (zeta[i] - a);
+    alpha[i] = a + step;
+  }
+}
+
+hipError_t launch_cutoff_update(float *alpha, const float *zeta, int64_t n, float rate,
+                                hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  return launch_kernel(cutoff_update_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       alpha, zeta, n, rate);
+}
+
 hipError_t launch_zero_i32(int32_t *dst, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   return launch_kernel(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst,

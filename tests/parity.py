@@ -145,15 +145,16 @@ def oracle_routing_full(cfg, seed=0, routing="normal", cutoff=None, alpha=None, 
     z64 = oracle.router_logits(cfg, w, x)
     z32 = z64.astype(np.float32)
     mode = cutoff or cfg.cutoff
+    zeta = oracle.quantile(z32, cfg.quantile_rank) if mode in ("batch", "running") else None
     if mode == "batch":
-        a = oracle.quantile(z32, cfg.quantile_rank)
+        a = zeta
     else:
         a = np.zeros(cfg.n_experts, np.float32) if alpha is None else np.asarray(alpha,
                                                                                   np.float32)
     idx, wts = oracle.topk(z32, cfg.top_k, alpha=a, z64=z64)
     counts, offsets, perm, inv = oracle.dispatch(idx, cfg.n_experts)
-    return dict(z64=z64, z32=z32, alpha=a, idx=idx, w=wts, counts=counts, offsets=offsets,
-                perm=perm, inv_perm=inv, x=x)
+    return dict(z64=z64, z32=z32, alpha=a, zeta=zeta, idx=idx, w=wts, counts=counts,
+                offsets=offsets, perm=perm, inv_perm=inv, x=x)
 
 
 def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None):

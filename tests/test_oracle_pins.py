@@ -405,6 +405,22 @@ def test_topk_cutoff_moves_selection():
 
 # ---- step 4: dispatch -----------------------------------------------------------------
 
+def test_running_cutoff_step():
+    """rate 1 follows the batch quantile, rate 0 keeps alpha; with dyadic values
+    every step is exact: from alpha 0 toward zeta 1 at rate 1/2, alpha_n =
+    1 - 2^-n (the geometric closed form of the moving average)."""
+    z = np.array([1.0, -3.0, 0.25], np.float32)
+    a = np.array([0.5, 2.0, -1.0], np.float32)
+    np.testing.assert_array_equal(oracle.cutoff_update(a, z, 1.0), z)
+    np.testing.assert_array_equal(oracle.cutoff_update(a, z, 0.0), a)
+    alpha = np.zeros(1, np.float32)
+    for n in range(1, 20):
+        alpha = oracle.cutoff_update(alpha, np.ones(1, np.float32), 0.5)
+        assert alpha[0] == 1.0 - 2.0 ** -n
+    # a constant zeta is a fixed point
+    np.testing.assert_array_equal(oracle.cutoff_update(z, z, 0.3), z)
+
+
 def test_dispatch_invariants():
     for hot in (0, 5):
         idx = synth.routing_fixture(300, 4, 24, seed=3, hot=hot)
