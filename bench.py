@@ -57,8 +57,7 @@ def phase_work(cfg, touched: int) -> dict:
     a8 = getattr(cfg, "act_quant", "none") == "mxfp8"
     # MX FP8 expert inputs: the GEMMs read codes + E8M0 bytes, a quantiser writes them
     qb = (lambda n: n + n // 32) if a8 else (lambda n: n * ab)
-    extra = {"xlat_quant": (0, bt * L * ab + bt * L * 33 // 32),
-             "h_quant": (0, P * I * ab + P * I * 33 // 32)} if a8 else {}
+    extra = {"xlat_quant": (0, bt * L * ab + bt * L * 33 // 32)} if a8 else {}
     return {**extra,
         "shared_gateup": (2 * bt * d * 2 * S * Is,
                           bt * d * ab + 2 * S * (Is * d * wb + sc(Is, d)) + bt * S * Is * ab),
@@ -67,7 +66,7 @@ def phase_work(cfg, touched: int) -> dict:
         "topk": (0, bt * E * 4 + P * 8),
         "dispatch": (0, P * 4 + P * 8),
         "down_proj": (2 * bt * d * L, bt * d * ab + L * d * wb + sc(L, d) + bt * L * ab),
-        "expert_gateup": (2 * P * 2 * L * I, touched * 2 * xw(I, L) + qb(bt * L) + P * I * ab),
+        "expert_gateup": (2 * P * 2 * L * I, touched * 2 * xw(I, L) + qb(bt * L) + qb(P * I)),
         "expert_down": (2 * P * L * I, touched * xw(L, I) + qb(P * I) + P * L * ab),
         "combine_norm": (0, P * L * ab + bt * L * ab),
         "output": (2 * bt * (L + S * Is) * d,

@@ -349,10 +349,11 @@ moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes, uint8_t *s
  * record.  Phases: 0 shared gate/up, 1 router logits, 2 cutoffs, 3 top-k,
  * 4 dispatch, 5 W_down_proj, 6 expert gate/up, 7 expert down, 8 combine +
  * RMSNorm, 9 output projection; dense FFN: 10 RMSNorm, 11 gate/up, 12 down;
- * MOE_MXFP4_A8 and MOE_MXFP8: 13 MX FP8 quantisation of x_lat, 14 of h.
+ * MOE_MXFP4_A8 and MOE_MXFP8: 13 MX FP8 quantisation of x_lat (h is written
+ * in MX FP8 by the expert gate/up epilogue).
  * Events are created by the library and kept for reuse (no device memory).
  * Not thread-safe against concurrent forwards. */
-#define MOE_N_PHASES 15
+#define MOE_N_PHASES 14
 moe_status moe_profile_enable(int on);
 moe_status moe_profile_read(double *ms_avg, int64_t *calls); /* arrays of MOE_N_PHASES */
 const char *moe_profile_phase_name(int phase);

@@ -270,7 +270,7 @@ def mx8_quantize(x):
     if st != 0:
         raise MoeError(st, "moe_mx8_quantize")
     return codes, scales
-N_PHASES = 15
+N_PHASES = 14
 
 
 def status_str(status: int) -> str:

@@ -116,8 +116,8 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   if (p->path == PATH_BF16 && bt * L * 2 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   // MX FP8 A: the E8M0 codes of A rows are addressed from the matrix start
   // with 32-bit offsets
-  const bool a8 = p->expert_wf == WF_MX4A8 || p->expert_wf == WF_MX8A8;
-  if (a8 && P * (c->expert_inter / 32) > (int64_t)UINT32_MAX)
+  if ((p->expert_wf == WF_MX4A8 || p->expert_wf == WF_MX8A8) &&
+      P * (c->expert_inter / 32) > (int64_t)UINT32_MAX)
     return MOE_ERR_UNSUPPORTED;
   const int64_t nb = (bt + 63) / 64;
   size_t off = 0;
@@ -139,7 +139,9 @@ moe_status make_plan(const moe_config *c, int64_t bt, Plan *p) {
   p->inv_perm = take(4 * P);
   p->masks = take(8 * E * nb);
   p->xlat = take(p->act_bytes * bt * L);
-  p->h = take(p->act_bytes * P * c->expert_inter);
+  // MX FP8 experts' h goes straight to its codes (hq below): no bf16 copy
+  const bool a8 = p->expert_wf == WF_MX4A8 || p->expert_wf == WF_MX8A8;
+  p->h = take(a8 ? 0 : p->act_bytes * P * c->expert_inter);
   p->o = take(p->act_bytes * P * L);
   p->n = take(p->act_bytes * bt * L);
   p->hs = take(p->act_bytes * bt * c->n_shared * c->shared_inter);
@@ -210,13 +212,12 @@ GemmArgs base_args(const moe_config *c) {
 // ---- phase timing (measurement support) -------------------------------------------
 enum Phase {
   PH_SHARED = 0, PH_ROUTER, PH_CUTOFF, PH_TOPK, PH_DISPATCH, PH_DOWN_PROJ, PH_EXPERT_GATEUP,
-  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT, PH_FFN_NORM, PH_FFN_GATEUP, PH_FFN_DOWN, PH_XLAT_QUANT,
-  PH_H_QUANT
+  PH_EXPERT_DOWN, PH_COMBINE, PH_OUTPUT, PH_FFN_NORM, PH_FFN_GATEUP, PH_FFN_DOWN, PH_XLAT_QUANT
 };
 const char *kPhaseNames[MOE_N_PHASES] = {
     "shared_gateup", "router_logits", "cutoff", "topk", "dispatch", "down_proj",
     "expert_gateup", "expert_down", "combine_norm", "output", "ffn_norm", "ffn_gateup",
-    "ffn_down", "xlat_quant", "h_quant"};
+    "ffn_down", "xlat_quant"};
 
 struct Profiler {
   bool on = false;
@@ -552,6 +553,7 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   }
   if (two_streams) MOE_TRY_HIP(hipStreamWaitEvent(s, ev_lat, 0));  // x_lat ready
 
+  uint8_t *hq = at<uint8_t>(ws, p.hq), *hq_sc = at<uint8_t>(ws, p.hq_sc);
   // ---- routed experts ---------------------------------------------------------------
   const int64_t grouped_mt = (P + bm - 1) / bm + E;
   void *h = at<void>(ws, p.h);
@@ -588,13 +590,14 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
     a.row_scale = a8 ? nullptr : w_sorted;
     a.out = h;
     a.ldo = I;
+    if (a8) {  // the epilogue writes h as MX FP8 (codes + E8M0 scales) directly
+      a.q_codes = hq;
+      a.q_scales = hq_sc;
+      a.ldq = I;
+      a.ldq_sc = I / 32;
+    }
     PhaseScope ph(PH_EXPERT_GATEUP, s);
     MOE_TRY_HIP(gemm_launch(a, p.path, GK_EXPERT_SITU, ewf, grouped_mt, s));
-  }
-  uint8_t *hq = at<uint8_t>(ws, p.hq), *hq_sc = at<uint8_t>(ws, p.hq_sc);
-  if (a8) {
-    PhaseScope ph(PH_H_QUANT, s);
-    MOE_TRY_HIP(launch_mx8_quant(h, P * I, hq, hq_sc, s));
   }
   {
     GemmArgs a = base_args(cfg);

@@ -54,6 +54,44 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __uint_as_float(__float_as_uint(v) | sign);
 }
 
+// ---- OCP MX FP8 (e4m3 elements, E8M0 scale per 32) ---------------------------
+// Nearest E4M3 code of a finite fp32 value (OCP e4m3fn: bias 7, 3 mantissa
+// bits, largest 448), ties to even, saturating.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448
+  const int e = (int)(a >> 23) - 127;
+  if (e < -126) return sign;  // zero or fp32 subnormal: far below half the least E4M3 step
+  const uint32_t f = a & 0x7FFFFFu;
+  if (e < -6) {
+    // subnormal E4M3: |v| / 2^-9 rounded to an integer in [0, 8] (8 = least normal)
+    const uint32_t m = f | 0x800000u;  // |v| = m 2^(e - 23)
+    const int shift = 14 - e;          // |v| / 2^-9 = m / 2^shift
+    if (shift > 24) return sign;
+    const uint32_t q = (m + (1u << (shift - 1)) - 1u + ((m >> shift) & 1u)) >> shift;
+    return sign | q;
+  }
+  uint32_t mant = (f + 0x7FFFFu + ((f >> 20) & 1u)) >> 20;  // 23 -> 3 bits, ties to even
+  int eb = e + 7;
+  if (mant == 8u) {
+    mant = 0u;
+    ++eb;
+  }
+  const uint32_t code = ((uint32_t)eb << 3) | mant;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Shared exponent of an MX block from its largest magnitude (OCP MX v1.0):
+// floor(log2 amax) - 8 (8 = the largest e4m3 exponent), clamped to [-127, 127];
+// -127 for an all-zero block.  The E8M0 scale byte is shared + 127.
+__device__ __forceinline__ int mx8_shared_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int e = (int)(__float_as_uint(amax) >> 23) - 127;  // floor(log2); subnormal: -127
+  return max(-127, min(127, e - 8));
+}
+
 // ---- elementary functions (from their definitions via exp) ------------------
 // exp(x) = 2^(x log2 e) on the hardware exp2 unit.
 __device__ __forceinline__ float exp_fast(float x) {

@@ -57,6 +57,12 @@ struct GemmArgs {
   // rows (gathered rows indexed as the A rows), one per 32 elements along K
   const uint8_t *a_sc;
   int64_t lda_sc;
+  // SiTU epilogue of the MX FP8 engine: when q_codes is set, the output is
+  // written as MX FP8 instead (the next GEMM's A): e4m3 codes q_codes[row][ldq]
+  // and E8M0 codes q_scales[row][ldq_sc], blocks of 32 output columns, decided
+  // on the bf16-rounded value (as a separate quantisation of the bf16 output)
+  uint8_t *q_codes, *q_scales;
+  int64_t ldq, ldq_sc;
   float beta, inv_beta, beta_u, inv_beta_u;
   int32_t n_tiles_n;         // N tiles (direct-to-LDS engine: groups of nper N tiles)
   int32_t group_m;           // M tiles per rasterisation group (tiles of a group share B)

@@ -752,6 +752,67 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
     }
     OutT *out = static_cast<OutT *>(args.out);
+    if constexpr (A8 && EPI == EPI_SITU) {
+      if (args.q_codes != nullptr) {
+        // MX FP8 output.  The 32 columns of this wave's block column make one
+        // MX block per row: each wave stages its SiTU outputs (bf16, as they
+        // would be stored) in LDS as [rows][32], then every lane quantises
+        // whole rows -- no cross-lane exchange.  The ring is reused for the
+        // staging once every DMA has landed and every wave has left the loop.
+        static_assert(JN == 1, "one 32-column block column a wave");
+        static_assert(NW * SUBM * 32 * 32 * 2 <= STAGES * STAGE_BYTES, "staging fits the ring");
+        wait_vmcnt<0>();
+        barrier();
+        uint16_t *wl = reinterpret_cast<uint16_t *>(smem) + wave * (SUBM * 32 * 32);
+#pragma unroll
+        for (int i = 0; i < SUBM; ++i) {
+          if (i >= sub_valid) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const float f = use_rs ? rs_lds[(i * WM + wm) * 32 + lr - i * 32] : 1.0f;
+            wl[lr * 32 + (lane & 31)] =
+                f32_to_bf16(f * situ(acc[i][0][r], acc[i][FRN / 2][r], args.beta, args.inv_beta,
+                                     args.beta_u, args.inv_beta_u));
+          }
+        }
+        const int64_t c0 = n0 + wn * 32;  // first column of this wave's block
+        if (c0 < args.N) {
+          for (int lr = lane; lr < sub_valid * 32; lr += 64) {
+            const int64_t row = tile.m0 + ((lr >> 5) * WM + wm) * 32 + (lr & 31);
+            if (row >= tile.m_end) continue;
+            const uint4 *src = reinterpret_cast<const uint4 *>(wl + lr * 32);
+            float v[32];
+            float amax = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint4 w4 = src[q];
+              const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                v[8 * q + 2 * h] = bf16_to_f32((uint16_t)(w[h] & 0xFFFFu));
+                v[8 * q + 2 * h + 1] = bf16_to_f32((uint16_t)(w[h] >> 16));
+                amax = fmaxf(amax, fmaxf(fabsf(v[8 * q + 2 * h]), fabsf(v[8 * q + 2 * h + 1])));
+              }
+            }
+            const int shared = mx8_shared_exp(amax);
+            const float inv = __uint_as_float((uint32_t)(127 - shared) << 23);
+            uint32_t code[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              code[q] = 0;
+#pragma unroll
+              for (int b = 0; b < 4; ++b) code[q] |= f32_to_e4m3_sat(v[4 * q + b] * inv) << (8 * b);
+            }
+            uint4 *dst = reinterpret_cast<uint4 *>(args.q_codes + row * args.ldq + c0);
+            dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+            dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+            args.q_scales[row * args.ldq_sc + c0 / 32] = (uint8_t)(shared + 127);
+          }
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < SUBM; ++i) {
       if (i >= sub_valid) continue;

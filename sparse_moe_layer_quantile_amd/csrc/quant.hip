@@ -16,34 +16,6 @@
 
 namespace moe {
 
-// Nearest E4M3 code of a finite fp32 value (OCP e4m3fn: bias 7, 3 mantissa
-// bits, largest 448), ties to even, saturating.
-__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448
-  const int e = (int)(a >> 23) - 127;
-  if (e < -126) return sign;  // zero or fp32 subnormal: far below half the least E4M3 step
-  const uint32_t f = a & 0x7FFFFFu;
-  if (e < -6) {
-    // subnormal E4M3: |v| / 2^-9 rounded to an integer in [0, 8] (8 = least normal)
-    const uint32_t m = f | 0x800000u;  // |v| = m 2^(e - 23)
-    const int shift = 14 - e;          // |v| / 2^-9 = m / 2^shift
-    if (shift > 24) return sign;
-    const uint32_t q = (m + (1u << (shift - 1)) - 1u + ((m >> shift) & 1u)) >> shift;
-    return sign | q;
-  }
-  uint32_t mant = (f + 0x7FFFFu + ((f >> 20) & 1u)) >> 20;  // 23 -> 3 bits, ties to even
-  int eb = e + 7;
-  if (mant == 8u) {
-    mant = 0u;
-    ++eb;
-  }
-  const uint32_t code = ((uint32_t)eb << 3) | mant;
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
 __global__ void __launch_bounds__(256) mx8_quant_kernel(const uint16_t *__restrict__ x,
                                                         int64_t n8, uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ scales) {
@@ -63,11 +35,7 @@ __global__ void __launch_bounds__(256) mx8_quant_kernel(const uint16_t *__restri
   // the four lanes of a 32-element block (groups of 4 consecutive lanes)
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  int shared = -127;
-  if (amax > 0.0f) {
-    const int e = (int)(__float_as_uint(amax) >> 23) - 127;  // floor(log2 amax); subnormal: -127
-    shared = max(-127, min(127, e - 8));
-  }
+  const int shared = mx8_shared_exp(amax);
   if (!live) return;
   const float inv = __uint_as_float((uint32_t)(127 - shared) << 23);  // 2^-shared
   uint32_t lo = 0, hi = 0;
