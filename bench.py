@@ -426,10 +426,18 @@ def main(argv=None):
         return 2
 
     import synth
+    import torch
+    if args.calibrate_copy:
+        torch.cuda.set_device(0)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.config in synth.FFN_CONFIGS:
         return bench_ffn(args)
 
-    import torch
     import sparse_moe_layer_quantile_amd as moe
     from tests import parity
 
@@ -437,13 +445,6 @@ def main(argv=None):
     if cfg.tier_slots > 0:
         return bench_tier(args, cfg)
     torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     layer, x = parity.device_layer(cfg, seed=args.seed)
     y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
     side = torch.cuda.Stream() if args.two_streams else None
