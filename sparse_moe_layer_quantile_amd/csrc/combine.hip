@@ -20,7 +20,8 @@
 
 namespace moe {
 
-template <bool BF16, int NCH>
+// GATHER: rows o[inv_perm[t k + j]] (the combine); else row t (plain RMSNorm)
+template <bool BF16, int NCH, bool GATHER>
 __global__ void __launch_bounds__(256) combine_norm_kernel(const void *__restrict__ o_,
                                                            const int32_t *__restrict__ inv_perm,
                                                            int64_t bt, int k, int L,
@@ -31,7 +32,7 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const void *__restric
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= bt) return;
   const int nch = L / V;
-  const int32_t *ip = inv_perm + t * k;
+  const int32_t *ip = GATHER ? inv_perm + t * k : nullptr;
   float acc[NCH][V];
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
@@ -42,7 +43,7 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const void *__restric
     int64_t pos[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      pos[u] = j0 + u < k ? (inv_perm ? (int64_t)ip[j0 + u] : t) : -1;
+      pos[u] = j0 + u < k ? (GATHER ? (int64_t)ip[j0 + u] : t) : -1;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
@@ -118,20 +119,26 @@ static hipError_t launch_cn(const void *o, const int32_t *inv_perm, int64_t bt, 
   constexpr int V = BF16 ? 8 : 4;
   const int64_t per_lane = (L / V + 63) / 64;
   const dim3 grid((unsigned)((bt + 3) / 4)), block(256);
+  if (inv_perm == nullptr) {  // plain RMSNorm rows (k = 1), up to 16 chunks a lane
+    if (per_lane <= 8)
+      return launch_kernel(combine_norm_kernel<BF16, 8, false>, grid, block, 0, s, o, inv_perm, bt,
+                           (int)k, (int)L, gamma, eps, n);
+    if (per_lane <= 16)
+      return launch_kernel(combine_norm_kernel<BF16, 16, false>, grid, block, 0, s, o, inv_perm,
+                           bt, (int)k, (int)L, gamma, eps, n);
+    return hipErrorInvalidValue;
+  }
   if (per_lane <= 1)
-    return launch_kernel(combine_norm_kernel<BF16, 1>, grid, block, 0, s, o, inv_perm, bt, (int)k,
-                         (int)L, gamma, eps, n);
+    return launch_kernel(combine_norm_kernel<BF16, 1, true>, grid, block, 0, s, o, inv_perm, bt,
+                         (int)k, (int)L, gamma, eps, n);
   if (per_lane <= 2)
-    return launch_kernel(combine_norm_kernel<BF16, 2>, grid, block, 0, s, o, inv_perm, bt, (int)k,
-                         (int)L, gamma, eps, n);
+    return launch_kernel(combine_norm_kernel<BF16, 2, true>, grid, block, 0, s, o, inv_perm, bt,
+                         (int)k, (int)L, gamma, eps, n);
   if (per_lane <= 4)
-    return launch_kernel(combine_norm_kernel<BF16, 4>, grid, block, 0, s, o, inv_perm, bt, (int)k,
-                         (int)L, gamma, eps, n);
+    return launch_kernel(combine_norm_kernel<BF16, 4, true>, grid, block, 0, s, o, inv_perm, bt,
+                         (int)k, (int)L, gamma, eps, n);
   if (per_lane <= 8)
-    return launch_kernel(combine_norm_kernel<BF16, 8>, grid, block, 0, s, o, inv_perm, bt, (int)k,
-                         (int)L, gamma, eps, n);
-  if (per_lane <= 16 && inv_perm == nullptr)  // plain RMSNorm rows up to 16 chunks a lane
-    return launch_kernel(combine_norm_kernel<BF16, 16>, grid, block, 0, s, o, inv_perm, bt,
+    return launch_kernel(combine_norm_kernel<BF16, 8, true>, grid, block, 0, s, o, inv_perm, bt,
                          (int)k, (int)L, gamma, eps, n);
   return hipErrorInvalidValue;
 }

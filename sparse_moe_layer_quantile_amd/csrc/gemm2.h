@@ -752,6 +752,9 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
     }
     OutT *out = static_cast<OutT *>(args.out);
+    // the plain store (no row factor, no residual): the common case, kept free
+    // of the per-row loads of the general one
+    const bool plain_store = args.resid == nullptr && args.row_scale == nullptr;
     if constexpr (A8 && EPI == EPI_SITU) {
       if (args.q_codes != nullptr) {
         // MX FP8 output.  The 32 columns of this wave's block column make one
@@ -813,41 +816,56 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         return;
       }
     }
+    // one loop nest per store form, so that the plain store's code carries
+    // none of the waits that the general form's loads would put at every join
+    auto rows_loop = [&](auto general_tag) G2_INL {
+      constexpr bool GEN = decltype(general_tag)::value;
 #pragma unroll
-    for (int i = 0; i < SUBM; ++i) {
-      if (i >= sub_valid) continue;
+      for (int i = 0; i < SUBM; ++i) {
+        if (i >= sub_valid) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t row = tile.m0 + rr;
-        if (row >= tile.m_end) continue;
-        OutT *orow = out + row * args.ldo;
-        if constexpr (EPI == EPI_SITU) {
-          const float f = use_rs ? rs_lds[rr] : 1.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int rr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t row = tile.m0 + rr;
+          if (row >= tile.m_end) continue;
+          OutT *orow = out + row * args.ldo;
+          if constexpr (EPI == EPI_SITU) {
+            const float f = use_rs ? rs_lds[rr] : 1.0f;
 #pragma unroll
-          for (int j = 0; j < JN; ++j)
-            if (col_ok[j])
-              store_out<OutT>(orow, col[j],
-                              f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
-                                       args.inv_beta, args.beta_u, args.inv_beta_u));
-        } else if constexpr (EPI == EPI_ROUTER) {
+            for (int j = 0; j < JN; ++j)
+              if (col_ok[j])
+                store_out<OutT>(orow, col[j],
+                                f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
+                                         args.inv_beta, args.beta_u, args.inv_beta_u));
+          } else if constexpr (EPI == EPI_ROUTER) {
 #pragma unroll
-          for (int j = 0; j < JN; ++j)
-            if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
-        } else {
-          // store (times the row's factor, when given), plus the residual row
-          // (read before the write: it may be the output)
-          const void *rrow = args.resid ? static_cast<const char *>(args.resid) +
-                                              row * args.ldr * (int64_t)sizeof(OutT)
-                                        : nullptr;
-          const float f = args.row_scale ? args.row_scale[row] : 1.0f;
+            for (int j = 0; j < JN; ++j)
+              if (col_ok[j]) store_out<float>(orow, col[j], acc[i][j][r] + bias[j]);
+          } else if constexpr (!GEN) {
 #pragma unroll
-          for (int j = 0; j < JN; ++j)
-            if (col_ok[j])
-              store_out<OutT>(orow, col[j],
-                              f * acc[i][j][r] + (rrow ? load_in<OutT>(rrow, col[j]) : 0.0f));
+            for (int j = 0; j < JN; ++j)
+              if (col_ok[j]) store_out<OutT>(orow, col[j], acc[i][j][r]);
+          } else {
+            // store (times the row's factor, when given), plus the residual row
+            // (read before the write: it may be the output)
+            const void *rrow = args.resid ? static_cast<const char *>(args.resid) +
+                                                row * args.ldr * (int64_t)sizeof(OutT)
+                                          : nullptr;
+            const float f = args.row_scale ? args.row_scale[row] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+              if (col_ok[j])
+                store_out<OutT>(orow, col[j],
+                                f * acc[i][j][r] + (rrow ? load_in<OutT>(rrow, col[j]) : 0.0f));
+          }
         }
       }
+    };
+    if constexpr (EPI == EPI_STORE) {
+      if (plain_store) rows_loop(std::false_type{});
+      else rows_loop(std::true_type{});
+    } else {
+      rows_loop(std::false_type{});
     }
     if constexpr (EPI == EPI_ROUTER) {
       if (args.out_t != nullptr) {
