@@ -137,6 +137,14 @@ CONFIGS: Dict[str, Config] = {
                                   n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
                                   shared_inter=3072, weight="mxfp4", bias="zipf1.1",
                                   cutoff="batch", act_quant="mxfp8"),
+    # decode with MX FP8 expert inputs (MXFP4 or MX FP8 experts)
+    "k3_decode_mxfp4_a8": Config("k3_decode_mxfp4_a8", bt=64, d=7168, latent=3584,
+                                 n_experts=896, top_k=16, expert_inter=3072, n_shared=2,
+                                 shared_inter=3072, weight="mxfp4", cutoff="given",
+                                 act_quant="mxfp8"),
+    "k3_decode_mxfp8": Config("k3_decode_mxfp8", bt=64, d=7168, latent=3584, n_experts=896,
+                              top_k=16, expert_inter=3072, n_shared=2, shared_inter=3072,
+                              weight="mxfp8", cutoff="given", act_quant="mxfp8"),
     # low-batch decode with Zipf-skewed routing (popular experts), the MXFP4 experts
     # in host DRAM and 112 of them (1/8) cached in HBM
     "k3_decode_mxfp4_tier": Config("k3_decode_mxfp4_tier", bt=8, d=7168, latent=3584,

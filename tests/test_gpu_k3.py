@@ -104,6 +104,12 @@ def test_k3_prefill_mxfp8_experts():
     _run_k3("k3_prefill_mxfp8", n_sample=10)
 
 
+@pytest.mark.parametrize("weight", ["mxfp4", "mxfp8"])
+def test_k3_decode_mx8_inputs(weight):
+    """K3 decode (64 tokens) with MX FP8 expert inputs, every token checked."""
+    _run_k3("k3_decode_mxfp4_a8" if weight == "mxfp4" else "k3_decode_mxfp8", n_sample=64)
+
+
 def test_k3_expert_parallel_share():
     """One GPU's share of 8-way expert parallelism: 112 experts with about 2341
     rows each, so every expert spans several M tiles of the grouped GEMMs."""

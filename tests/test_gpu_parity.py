@@ -296,6 +296,16 @@ def test_forward_mxfp4_mx8_inputs_mid(bt, cutoff, shape):
     _mxfp4_check(cfg, cutoff)
 
 
+@pytest.mark.parametrize("weight", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("bt", [1, 2, 63, 129])
+def test_forward_mx8_inputs_ragged_batches(weight, bt):
+    """MX FP8 expert inputs on ragged batches: one row in most experts' tiles,
+    a single token (BATCH mode: the k lowest ids), partial 32-row sub-blocks."""
+    cfg = synth.CONFIGS["mid_bf16"].with_(weight=weight, act_quant="mxfp8", bt=bt)
+    say("forward mx8 inputs ragged", weight, bt)
+    _mxfp4_check(cfg, "batch")
+
+
 @pytest.mark.parametrize("shape_id", ["11", "12", "13"])
 def test_forward_mxfp4_mx8_every_tile_shape(shape_id, monkeypatch):
     """Each tile shape of the block-scaled engine (forced): 256, 320 and 192 rows
