@@ -120,6 +120,30 @@ def test_tiered_forward_equals_resident(weight, frac, side_copy):
     tier.close()
 
 
+def test_tiered_forward_equals_resident_k3_mxfp4_decode():
+    """K3 decode with MXFP4 experts (15.7 GB of pinned host experts, 112 cached):
+    four steps of fresh tokens, each equal to the resident layer's output."""
+    import sparse_moe_layer_quantile_amd as moe
+    cfg = synth.CONFIGS["k3_decode_mxfp4_tier"]
+    say("tier K3 mxfp4 decode")
+    layer, _ = parity.device_layer(cfg, seed=0)
+    tier = moe.ExpertTier(layer.cfg, _host_experts(layer, True), cfg.tier_slots, max_loads=64)
+    tl = _tiered_layer(moe, layer, tier)
+    bufs = _dispatch_bufs(cfg, cfg.bt)
+    for step in range(4):
+        x = synth.device_layer(cfg, seed=300 + step, names=["x"])["x"]
+        y_ref = layer.forward(x)
+        tier.plan()
+        y = tl.forward(x, dispatch=bufs)
+        tier.observe(bufs["counts"])
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"step {step}"
+    st = tier.stats()
+    say("  stats", st)
+    assert st["resident"] > 0
+    tier.close()
+
+
 def test_tier_rejects_pageable_host_memory():
     import sparse_moe_layer_quantile_amd as moe
     cfg = synth.CONFIGS["mid_bf16"].with_(bt=8)
