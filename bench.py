@@ -401,6 +401,76 @@ def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
                        f"token; extrapolated to tokens/s")}
 
 
+def backward_flops(cfg) -> float:
+    """Multiply-adds x 2 of one backward call: the recomputed forward GEMMs
+    (x_lat, the experts' gate / up / down, the shared gate / up) and the
+    gradient GEMMs (two per forward GEMM: the input's and the weight's, the
+    router's included)."""
+    bt, d, L, E = cfg.bt, cfg.d, cfg.latent, cfg.n_experts
+    P, I, SI = cfg.bt * cfg.top_k, cfg.expert_inter, cfg.n_shared * cfg.shared_inter
+    recompute = 2 * bt * d * L + 3 * 2 * P * L * I + 2 * 2 * bt * d * SI
+    grads = 2 * (2 * bt * d * L          # W_up
+                 + 2 * bt * d * SI       # shared down
+                 + 3 * 2 * P * L * I     # expert down, gate, up
+                 + 2 * bt * d * L        # W_down_proj
+                 + 2 * bt * d * E        # router
+                 + 2 * 2 * bt * d * SI)  # shared gate, up
+    return float(recompute + grads)
+
+
+def bench_backward(args, cfg) -> int:
+    """moe_backward on the workload's batch: the routing from one route() call
+    (outside the timed region, as a training step takes it from its forward),
+    gradients into preallocated fp32 tensors."""
+    import torch
+    from tests import parity
+    torch.cuda.set_device(0)
+    layer, x = parity.device_layer(cfg, seed=args.seed)
+    gen = torch.Generator(device="cuda").manual_seed(args.seed + 7)
+    dy = torch.randn((cfg.bt, cfg.d), generator=gen, device="cuda").to(torch.bfloat16)
+    r = layer.route(x)
+    grads = {n: torch.empty(s, dtype=torch.float32, device="cuda")
+             for n, s in layer.grad_shapes(cfg.bt).items()}
+    for _ in range(args.warmup):
+        layer.backward(x, dy, route=r, grads=grads)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.backward(x, dy, route=r, grads=grads)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    flops = backward_flops(cfg)
+    tf = flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "backward tokens/s (gradients of x and every weight)",
+        "value": cfg.bt * args.steps / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + " backward", "bt": cfg.bt, "d": cfg.d,
+                   "latent": cfg.latent, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "expert_inter": cfg.expert_inter, "n_shared": cfg.n_shared,
+                   "shared_inter": cfg.shared_inter, "cutoff": cfg.cutoff,
+                   "parallelism": "1 GPU"},
+        "roofline": {"bound": "mfma", "kernel": "whole backward call", "achieved": tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": None, "flops_per_call": flops},
+        "kernel_sources": kernel_source_hash(),
+        # the fp64 oracle would need the experts' 30 G parameters as fp64 on the host
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +484,8 @@ def main(argv=None):
                     help="run W_down_proj and the shared experts on a second stream (the "
                          "default keeps one stream: the GEMMs fill the GPU either way, and "
                          "each kernel's time is then its own)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward (bf16 workloads) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -442,6 +514,8 @@ def main(argv=None):
     from tests import parity
 
     cfg = synth.CONFIGS[args.config]
+    if args.backward:
+        return bench_backward(args, cfg)
     if cfg.tier_slots > 0:
         return bench_tier(args, cfg)
     torch.cuda.set_device(0)

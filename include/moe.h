@@ -198,6 +198,50 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                        void *y, moe_route_out *route, moe_dispatch_out *disp, void *ws,
                        size_t ws_bytes, void *stream, void *shared_stream);
 
+/* ---- backward pass ---------------------------------------------------------------
+ * Gradients of a loss with respect to x and every weight, given dL/dy.  The
+ * pages describe the forward only (tech.news18a.com page: the architecture
+ * figure, the SiTU formula, the quantile-balancing passage; the gradient
+ * explosion passage of that page is why its caps exist); the gradients are the
+ * chain rule of that forward.  The chosen expert set is piecewise constant in
+ * the scores and gets no gradient; each chosen weight w = sigmoid(z) does, and
+ * through it the router weights and bias.  Every array is fp32, dense, in the
+ * layout of the weight it belongs to (moe_weights), overwritten (not
+ * accumulated), all required (sh_* only when n_shared > 0). */
+typedef struct moe_grads {
+  float *dx;           /* [bt][d] (may be NULL when bt == 0) */
+  float *w_router;     /* [E][d] */
+  float *router_bias;  /* [E] */
+  float *w_down_proj;  /* [L][d] */
+  float *w_gate;       /* [E][I][L] */
+  float *w_up;         /* [E][I][L] */
+  float *w_down;       /* [E][L][I] */
+  float *latent_gamma; /* [L] */
+  float *w_up_proj;    /* [d][L] */
+  float *sh_gate;      /* [S][I_s][d] */
+  float *sh_up;        /* [S][I_s][d] */
+  float *sh_down;      /* [S][d][I_s] */
+} moe_grads;
+
+/* Device bytes of workspace moe_backward needs for bt tokens; 0 for an invalid
+ * or unsupported config. */
+size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t bt);
+
+/* Backward of moe_forward for bf16 activations, weights and router
+ * (MOE_ERR_UNSUPPORTED otherwise, and for an expert_tab).  x[bt][d] and
+ * dy[bt][d] are bf16; topk_idx / topk_w [bt][k] the routing moe_route (or
+ * moe_forward) returned for x.  The forward's intermediate values are
+ * recomputed from x, so no activations are kept between the calls.  The call
+ * copies the dispatch offsets to the host (it synchronises `stream` once),
+ * then enqueues the rest on `stream` and returns: the gradients are complete
+ * when `stream` reaches that point.  The GEMMs run on rocBLAS (bf16 inputs, fp32
+ * accumulation), the routed experts' ones one expert at a time.  bt == 0
+ * writes zero weight gradients.  The workspace (256-byte aligned) holds the
+ * recomputed activations, about 2 (L + I) * 10 bytes a (token, expert) pair. */
+moe_status moe_backward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
+                        const int32_t *topk_idx, const float *topk_w, const void *dy,
+                        const moe_grads *g, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_str(int status);
 

@@ -84,6 +84,14 @@ class MoeDispatchOut(ctypes.Structure):
     _fields_ = [("counts", _P), ("offsets", _P), ("perm", _P), ("inv_perm", _P)]
 
 
+GRAD_FIELDS = ("dx", "w_router", "router_bias", "w_down_proj", "w_gate", "w_up", "w_down",
+               "latent_gamma", "w_up_proj", "sh_gate", "sh_up", "sh_down")
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)} ({status})")
@@ -102,6 +110,11 @@ def _load():
     CP = ctypes.POINTER
     lib.moe_workspace_bytes.argtypes = [CP(MoeConfig), ctypes.c_int64]
     lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_backward_workspace_bytes.argtypes = [CP(MoeConfig), ctypes.c_int64]
+    lib.moe_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_backward.argtypes = [CP(MoeConfig), CP(MoeWeights), _P, ctypes.c_int64, _P, _P, _P,
+                                 CP(MoeGrads), _P, ctypes.c_size_t, _P]
+    lib.moe_backward.restype = ctypes.c_int
     lib.moe_route.argtypes = [CP(MoeConfig), CP(MoeWeights), _P, ctypes.c_int64,
                               CP(MoeRouteOut), _P, ctypes.c_size_t, _P]
     lib.moe_route.restype = ctypes.c_int
@@ -154,7 +167,7 @@ EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward",
             "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
             "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select",
-            "moe_cutoff_update")
+            "moe_cutoff_update", "moe_backward_workspace_bytes", "moe_backward")
 
 
 def cutoff_update(alpha, zeta, rate: float):
@@ -292,6 +305,17 @@ def workspace_bytes(cfg: MoeConfig, bt: int) -> int:
     return int(LIB.moe_workspace_bytes(ctypes.byref(cfg), bt))
 
 
+def backward_workspace_bytes(cfg: MoeConfig, bt: int) -> int:
+    return int(LIB.moe_backward_workspace_bytes(ctypes.byref(cfg), bt))
+
+
+def moe_backward(cfg, weights: MoeWeights, x: int, bt: int, topk_idx: int, topk_w: int, dy: int,
+                 grads: MoeGrads, ws: int, ws_bytes: int, stream: int) -> int:
+    return LIB.moe_backward(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None), bt,
+                            _P(topk_idx or None), _P(topk_w or None), _P(dy or None),
+                            ctypes.byref(grads), _P(ws or None), ws_bytes, _P(stream or None))
+
+
 def moe_route(cfg, weights: MoeWeights, x: int, bt: int, out: MoeRouteOut, ws: int,
               ws_bytes: int, stream: int) -> int:
     return LIB.moe_route(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None), bt,
@@ -427,6 +451,38 @@ class StableLatentMoE:
         if st != 0:
             raise MoeError(st, "moe_forward")
         return (y, extra) if return_routing else y
+
+    def grad_shapes(self, bt: int) -> dict:
+        c = self.cfg
+        E, d, L, I = c.n_experts, c.d, c.latent, c.expert_inter
+        S, Is = c.n_shared, c.shared_inter
+        return dict(dx=(bt, d), w_router=(E, d), router_bias=(E,), w_down_proj=(L, d),
+                    w_gate=(E, I, L), w_up=(E, I, L), w_down=(E, L, I), latent_gamma=(L,),
+                    w_up_proj=(d, L), sh_gate=(S, Is, d), sh_up=(S, Is, d),
+                    sh_down=(S, d, Is))
+
+    def backward(self, x, dy, route=None, grads=None):
+        """fp32 gradients of sum(dy * y) (a dict keyed by GRAD_FIELDS) for y =
+        forward(x), given the routing of x (route(x) when None).  `grads` may
+        hold caller-owned fp32 tensors of grad_shapes() to receive them."""
+        import torch
+        bt = x.shape[0]
+        if route is None:
+            route = self.route(x)
+        if grads is None:
+            grads = {n: torch.empty(s, dtype=torch.float32, device=x.device)
+                     for n, s in self.grad_shapes(bt).items()}
+        need = backward_workspace_bytes(self.cfg, bt)
+        if need == 0:
+            raise MoeError(-2, "moe_backward_workspace_bytes")
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        gs = MoeGrads(*(_ptr(grads.get(n)) for n in GRAD_FIELDS))
+        st = moe_backward(self.cfg, self.w, _ptr(x), bt, route["idx"].data_ptr(),
+                          route["w"].data_ptr(), _ptr(dy), gs, ws.data_ptr(), ws.numel(),
+                          torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise MoeError(st, "moe_backward")
+        return grads
 
 
 # ---- dense layer-1 FFN -----------------------------------------------------------------

@@ -42,7 +42,8 @@ def test_struct_layouts_match_header():
     structs = {"moe_config": moe.MoeConfig, "moe_weights": moe.MoeWeights,
                "moe_route_out": moe.MoeRouteOut, "moe_dispatch_out": moe.MoeDispatchOut,
                "moe_ffn_config": moe.MoeFfnConfig, "moe_ffn_weights": moe.MoeFfnWeights,
-               "moe_tier_desc": moe.MoeTierDesc, "moe_tier_stats": moe.MoeTierStats}
+               "moe_tier_desc": moe.MoeTierDesc, "moe_tier_stats": moe.MoeTierStats,
+               "moe_grads": moe.MoeGrads}
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
     for s, cls in structs.items():
         src.append(f'printf("{s} %zu\\n", sizeof({s}));')
@@ -215,6 +216,37 @@ def test_argument_errors_before_any_launch():
     assert moe.moe_forward(c, w, 1, 64, 1, None, None, 256, need, 0) == -1  # no expert weights
     assert moe.status_str(-3).startswith("workspace")
     assert moe.status_str(7) == "unknown status"
+
+
+def test_backward_workspace_and_argument_errors():
+    """moe_backward: bf16 only; every error returned before any launch."""
+    mid = synth.CONFIGS["mid_bf16"]
+    c = parity.abi_config(mid)
+    need = moe.backward_workspace_bytes(c, 64)
+    P, L, I = 64 * mid.top_k, mid.latent, mid.expert_inter
+    assert need > 2 * P * (L + I) * 8  # the recomputed pair activations dominate
+    assert moe.backward_workspace_bytes(c, 0) > 0
+    assert moe.backward_workspace_bytes(c, -1) == 0
+    for other in (synth.CONFIGS["tiny_fp32"], mid.with_(weight="fp8", router="bf16"),
+                  mid.with_(weight="mxfp4")):
+        assert moe.backward_workspace_bytes(parity.abi_config(other), 64) == 0
+    full = moe.MoeGrads(*([1] * len(moe.GRAD_FIELDS)))
+    w = moe.MoeWeights(**{n: 1 for n in ("w_router", "w_down_proj", "w_gate", "w_up",
+                                         "w_down", "w_up_proj", "sh_gate", "sh_up",
+                                         "sh_down")})
+    ok = (c, w, 1, 64, 1, 1, 1)
+    assert moe.moe_backward(*ok, moe.MoeGrads(), 256, need, 0) == -1         # no gradients
+    assert moe.moe_backward(*ok, moe.MoeGrads(*([1] * 11)), 256, need, 0) == -1  # no sh_down
+    assert moe.moe_backward(c, moe.MoeWeights(), 1, 64, 1, 1, 1, full, 256, need, 0) == -1
+    assert moe.moe_backward(c, w, 1, 64, 0, 1, 1, full, 256, need, 0) == -1  # no routing
+    assert moe.moe_backward(*ok, full, 0, need, 0) == -3
+    assert moe.moe_backward(*ok, full, 256, need - 1, 0) == -3
+    assert moe.moe_backward(*ok, full, 257, need, 0) == -3                  # misaligned
+    tab = moe.MoeWeights(**{f: getattr(w, f) or 0 for f, _ in moe.MoeWeights._fields_})
+    tab.expert_tab = 1
+    assert moe.moe_backward(c, tab, 1, 64, 1, 1, 1, full, 256, need, 0) == -2
+    f32 = parity.abi_config(synth.CONFIGS["tiny_fp32"])
+    assert moe.moe_backward(f32, w, 1, 64, 1, 1, 1, full, 256, need, 0) == -2
 
 
 def test_ffn_workspace_and_validation():
