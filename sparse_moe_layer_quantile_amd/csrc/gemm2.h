@@ -757,16 +757,17 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     const bool plain_store = args.resid == nullptr && args.row_scale == nullptr;
     if constexpr (A8 && EPI == EPI_SITU) {
       if (args.q_codes != nullptr) {
-        // MX FP8 output.  The 32 columns of this wave's block column make one
-        // MX block per row: each wave stages its SiTU outputs (bf16, as they
-        // would be stored) in LDS as [rows][32], then every lane quantises
-        // whole rows -- no cross-lane exchange.  The ring is reused for the
-        // staging once every DMA has landed and every wave has left the loop.
-        static_assert(JN == 1, "one 32-column block column a wave");
-        static_assert(NW * SUBM * 32 * 32 * 2 <= STAGES * STAGE_BYTES, "staging fits the ring");
+        // MX FP8 output.  The 32 columns of each of this wave's JN block
+        // columns make one MX block per row: each wave stages its SiTU outputs
+        // (bf16, as they would be stored) in LDS as [rows][JN * 32], then every
+        // lane quantises whole (row, block) pairs -- no cross-lane exchange.
+        // The ring is reused for the staging once every DMA has landed and
+        // every wave has left the loop.
+        constexpr int RW = JN * 32;  // staged columns a row
+        static_assert(NW * SUBM * 32 * RW * 2 <= STAGES * STAGE_BYTES, "staging fits the ring");
         wait_vmcnt<0>();
         barrier();
-        uint16_t *wl = reinterpret_cast<uint16_t *>(smem) + wave * (SUBM * 32 * 32);
+        uint16_t *wl = reinterpret_cast<uint16_t *>(smem) + wave * (SUBM * 32 * RW);
 #pragma unroll
         for (int i = 0; i < SUBM; ++i) {
           if (i >= sub_valid) continue;
@@ -774,17 +775,19 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           for (int r = 0; r < 16; ++r) {
             const int lr = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const float f = use_rs ? rs_lds[(i * WM + wm) * 32 + lr - i * 32] : 1.0f;
-            wl[lr * 32 + (lane & 31)] =
-                f32_to_bf16(f * situ(acc[i][0][r], acc[i][FRN / 2][r], args.beta, args.inv_beta,
-                                     args.beta_u, args.inv_beta_u));
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+              wl[lr * RW + j * 32 + (lane & 31)] = f32_to_bf16(
+                  f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta, args.inv_beta,
+                           args.beta_u, args.inv_beta_u));
           }
         }
-        const int64_t c0 = n0 + wn * 32;  // first column of this wave's block
-        if (c0 < args.N) {
-          for (int lr = lane; lr < sub_valid * 32; lr += 64) {
-            const int64_t row = tile.m0 + ((lr >> 5) * WM + wm) * 32 + (lr & 31);
-            if (row >= tile.m_end) continue;
-            const uint4 *src = reinterpret_cast<const uint4 *>(wl + lr * 32);
+        for (int it = lane; it < sub_valid * 32 * JN; it += 64) {
+          const int lr = it / JN, j = it % JN;
+          const int64_t c0 = n0 + (wn * JN + j) * 32;  // first column of the block
+          const int64_t row = tile.m0 + ((lr >> 5) * WM + wm) * 32 + (lr & 31);
+          if (c0 < args.N && row < tile.m_end) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(wl + lr * RW + j * 32);
             float v[32];
             float amax = 0.0f;
 #pragma unroll
