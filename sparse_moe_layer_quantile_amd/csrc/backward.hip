@@ -14,14 +14,17 @@
 // the routing that moe_route returned, so a caller keeps no activations.  The
 // contractions are plain GEMMs with transposed operands and run on rocBLAS
 // (bf16 inputs, fp32 accumulation); the routed experts' GEMMs are issued per
-// expert from the dispatch counts, which the call copies to the host.  Every
+// expert from the dispatch counts, which the call copies to the host, over
+// four side streams.  Every
 // elementwise step, gather, reduction and normalisation runs in the kernels
 // below.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -121,17 +124,62 @@ T *at(void *ws, size_t off) {
     if ((expr) != rocblas_status_success) return MOE_ERR_HIP; \
   } while (0)
 
-// ---- rocBLAS -------------------------------------------------------------------------
-// One handle a device, created on first use with that device current.
-rocblas_handle blas_handle() {
+// ---- rocBLAS and the expert streams ---------------------------------------------------
+// One expert's GEMM (a few hundred rows at prefill, a few at decode) covers a
+// small part of the 256 CUs, so consecutive experts go round-robin to kSide
+// streams and run side by side.  Per device, created on first use with that
+// device current: a handle for the caller's stream, and a stream + handle +
+// event for each side; all at the default priority.
+constexpr int kSide = 4;
+struct Blas {
+  rocblas_handle main = nullptr;
+  rocblas_handle side[kSide] = {};
+  hipStream_t ss[kSide] = {};
+  hipEvent_t done[kSide] = {};
+  hipEvent_t fork = nullptr;
+  bool ok = false;
+};
+
+Blas *blas() {
   static std::mutex mu;
-  static rocblas_handle handles[64] = {};
+  static Blas per_dev[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   std::lock_guard<std::mutex> lk(mu);
-  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success)
-    handles[dev] = nullptr;
-  return handles[dev];
+  Blas &b = per_dev[dev];
+  if (!b.ok) {
+    if (!b.main && rocblas_create_handle(&b.main) != rocblas_status_success) return nullptr;
+    if (!b.fork && hipEventCreateWithFlags(&b.fork, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    for (int i = 0; i < kSide; ++i) {
+      if (!b.ss[i] && hipStreamCreateWithFlags(&b.ss[i], hipStreamNonBlocking) != hipSuccess)
+        return nullptr;
+      if (!b.done[i] && hipEventCreateWithFlags(&b.done[i], hipEventDisableTiming) != hipSuccess)
+        return nullptr;
+      if (!b.side[i]) {
+        if (rocblas_create_handle(&b.side[i]) != rocblas_status_success) return nullptr;
+        if (rocblas_set_stream(b.side[i], b.ss[i]) != rocblas_status_success) return nullptr;
+      }
+    }
+    b.ok = true;
+  }
+  return &b;
+}
+
+// the side streams start after the work enqueued on s so far ...
+hipError_t fork_sides(const Blas &b, hipStream_t s) {
+  hipError_t e = hipEventRecord(b.fork, s);
+  for (int i = 0; i < kSide && e == hipSuccess; ++i) e = hipStreamWaitEvent(b.ss[i], b.fork, 0);
+  return e;
+}
+// ... and s continues after everything enqueued on them
+hipError_t join_sides(const Blas &b, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < kSide && e == hipSuccess; ++i) {
+    e = hipEventRecord(b.done[i], b.ss[i]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, b.done[i], 0);
+  }
+  return e;
 }
 
 // Row-major C[M][N] = op(A) op(B) + beta C with op(A) [M][K], op(B) [K][N]; ta / tb
@@ -351,6 +399,29 @@ hipError_t colsum(const float *a, const float *b, const float *rs, int64_t rows,
                        (const float *)part, nchunk, cols, out);
 }
 
+// Runs fn(e, handle, stream) for every expert e, expert e on side e % kSide;
+// each side's experts are issued by a host thread of its own (a library call
+// per GEMM costs microseconds of host time, comparable to a small expert's
+// GEMM).  The sides start after the work on s so far, and s waits for them.
+template <typename Fn>
+moe_status for_experts(const Blas &b, hipStream_t s, int64_t E, Fn fn) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || fork_sides(b, s) != hipSuccess) return MOE_ERR_HIP;
+  std::atomic<int> status{MOE_OK};
+  std::thread th[kSide];
+  for (int i = 0; i < kSide; ++i)
+    th[i] = std::thread([&, i] {
+      if (hipSetDevice(dev) != hipSuccess) status.store(MOE_ERR_HIP);  // the caller's device
+      for (int64_t e = i; e < E && status.load() == MOE_OK; e += kSide) {
+        const moe_status st = fn(e, b.side[i], b.ss[i]);
+        if (st != MOE_OK) status.store(st);
+      }
+    });
+  for (auto &t : th) t.join();
+  if (join_sides(b, s) != hipSuccess) return MOE_ERR_HIP;
+  return static_cast<moe_status>(status.load());
+}
+
 bool grads_complete(const moe_config *c, const moe_grads *g, int64_t bt) {
   return g && (g->dx || bt == 0) && g->w_router && g->router_bias && g->w_down_proj && g->w_gate &&
          g->w_up && g->w_down && g->latent_gamma && g->w_up_proj &&
@@ -394,8 +465,9 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
       if (a.first) MOE_TRY(fill_f32(a.first, a.second, s));
     return MOE_OK;
   }
-  rocblas_handle hd = blas_handle();
-  if (!hd) return MOE_ERR_HIP;
+  Blas *bl = blas();
+  if (!bl) return MOE_ERR_HIP;
+  rocblas_handle hd = bl->main;
   MOE_TRY_BLAS(rocblas_set_stream(hd, s));
   const float beta = cfg->beta, ib = 1.0f / cfg->beta, bu = cfg->beta_u, ibu = 1.0f / cfg->beta_u;
 
@@ -429,22 +501,28 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
                        BF, L));
   MOE_TRY(launch_kernel(gather_rows_kernel, grid_for(P * L / 8), dim3(256), 0, s,
                         (const uint16_t *)xlat, (const int32_t *)perm, (int)k, P, L, xg));
-  for (int64_t e = 0; e < E; ++e) {
+  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
+    (void)se;
     const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) continue;
-    MOE_TRY_BLAS(gemm_rm(hd, false, true, ne, I, L, xg + q0 * L, BF, L, Wg + e * I * L, BF, L,
+    if (ne == 0) return MOE_OK;
+    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, I, L, xg + q0 * L, BF, L, Wg + e * I * L, BF, L,
                          0.0f, G + q0 * I, F32, I));
-    MOE_TRY_BLAS(gemm_rm(hd, false, true, ne, I, L, xg + q0 * L, BF, L, Wu + e * I * L, BF, L,
+    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, I, L, xg + q0 * L, BF, L, Wu + e * I * L, BF, L,
                          0.0f, U + q0 * I, F32, I));
-  }
+    return MOE_OK;
+  });
+  if (st != MOE_OK) return st;
   MOE_TRY(launch_kernel(situ_h_kernel, grid_for(P * I), dim3(256), 0, s, (const float *)G,
                         (const float *)U, (const float *)w_sorted, P, I, beta, ib, bu, ibu, h));
-  for (int64_t e = 0; e < E; ++e) {
+  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
+    (void)se;
     const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) continue;
-    MOE_TRY_BLAS(gemm_rm(hd, false, true, ne, L, I, h + q0 * I, BF, I, Wd + e * L * I, BF, I,
+    if (ne == 0) return MOE_OK;
+    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, L, I, h + q0 * I, BF, I, Wd + e * L * I, BF, I,
                          0.0f, o + q0 * L, BF, L));
-  }
+    return MOE_OK;
+  });
+  if (st != MOE_OK) return st;
   MOE_TRY(launch_kernel(combine_ylat_kernel, dim3((unsigned)bt), dim3(256), 0, s,
                         (const uint16_t *)o, (const int32_t *)inv_perm, (int)k, L,
                         w->latent_gamma, cfg->rms_eps, ylat, rinv, n));
@@ -478,37 +556,43 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
   MOE_TRY(launch_kernel(gather_rows_kernel, grid_for(P * L / 8), dim3(256), 0, s,
                         (const uint16_t *)dylat, (const int32_t *)perm, (int)k, P, L, dyg));
   MOE_TRY(fill_f32(dz, bt * E, s));
-  for (int64_t e = 0; e < E; ++e) {
+  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
+    (void)se;
     const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
     if (ne == 0) {  // no pair chose the expert
-      MOE_TRY(fill_f32(g->w_down + e * L * I, L * I, s));
-      continue;
+      MOE_TRY(fill_f32(g->w_down + e * L * I, L * I, se));
+      return MOE_OK;
     }
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, L, I, ne, dyg + q0 * L, BF, L, h + q0 * I, BF, I, 0.0f,
+    MOE_TRY_BLAS(gemm_rm(he, true, false, L, I, ne, dyg + q0 * L, BF, L, h + q0 * I, BF, I, 0.0f,
                          g->w_down + e * L * I, F32, I));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, ne, I, L, dyg + q0 * L, BF, L, Wd + e * L * I, BF, I,
+    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, I, L, dyg + q0 * L, BF, L, Wd + e * L * I, BF, I,
                          0.0f, dh + q0 * I, F32, I));
-  }
+    return MOE_OK;
+  });
+  if (st != MOE_OK) return st;
   MOE_TRY(launch_kernel(situ_bwd_kernel, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s, (const float *)dh,
                         (const float *)G, (const float *)U, (const float *)w_sorted,
                         (const int32_t *)perm, topk_idx, (int)k, E, P, I, beta, ib, bu, ibu, dg,
                         du, dz));
-  for (int64_t e = 0; e < E; ++e) {
+  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
+    (void)se;
     const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
     if (ne == 0) {
-      MOE_TRY(fill_f32(g->w_gate + e * I * L, I * L, s));
-      MOE_TRY(fill_f32(g->w_up + e * I * L, I * L, s));
-      continue;
+      MOE_TRY(fill_f32(g->w_gate + e * I * L, I * L, se));
+      MOE_TRY(fill_f32(g->w_up + e * I * L, I * L, se));
+      return MOE_OK;
     }
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, I, L, ne, dg + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
+    MOE_TRY_BLAS(gemm_rm(he, true, false, I, L, ne, dg + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
                          g->w_gate + e * I * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, I, L, ne, du + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
+    MOE_TRY_BLAS(gemm_rm(he, true, false, I, L, ne, du + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
                          g->w_up + e * I * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, ne, L, I, dg + q0 * I, BF, I, Wg + e * I * L, BF, L,
+    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, L, I, dg + q0 * I, BF, I, Wg + e * I * L, BF, L,
                          0.0f, dxg + q0 * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, ne, L, I, du + q0 * I, BF, I, Wu + e * I * L, BF, L,
+    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, L, I, du + q0 * I, BF, I, Wu + e * I * L, BF, L,
                          1.0f, dxg + q0 * L, F32, L));
-  }
+    return MOE_OK;
+  });
+  if (st != MOE_OK) return st;
   MOE_TRY(launch_kernel(combine_rows_kernel, grid_for(bt * L), dim3(256), 0, s,
                         (const float *)dxg, (const int32_t *)inv_perm, (int)k, bt, L, dxlat));
   // ---- x_lat = W_down_proj x, and the router ------------------------------------------
