@@ -198,7 +198,8 @@ def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None):
 # ---- smoke -------------------------------------------------------------------------------
 
 def smoke_check():
-    """One small forward on cuda:0 through the C ABI, checked against the oracle."""
+    """One small forward and one small backward on cuda:0 through the C ABI,
+    checked against the oracle."""
     import torch
     cfg = synth.CONFIGS["tiny_fp32"]
     layer, x = device_layer(cfg, seed=0)
@@ -211,3 +212,26 @@ def smoke_check():
     err = normwise_err(y_to_f64(y)[keep], ref["y"][keep])
     assert err <= tol_of(cfg), f"normwise error {err:.3e} above {tol_of(cfg)}"
     print(f"smoke ok: {cfg.name} bt={cfg.bt} normwise err {err:.2e}", flush=True)
+
+    # backward of a small bf16 layer: every gradient against the fp64 backward oracle
+    from oracle import backward as ob
+    bcfg = synth.CONFIGS["mid_bf16"].with_(name="smoke_bwd", bt=64, d=256, latent=64,
+                                           n_experts=16, top_k=2, expert_inter=64, n_shared=1,
+                                           shared_inter=128, cutoff="batch")
+    layer, x = device_layer(bcfg, seed=0)
+    dy = torch.from_numpy(np.random.default_rng(1).normal(0, 1, (bcfg.bt, bcfg.d))
+                          .astype(np.float32)).cuda().to(torch.bfloat16)
+    r = layer.route(x)
+    g = layer.backward(x, dy, route=r)
+    torch.cuda.synchronize()
+    idx = to_np(r["idx"])
+    rr = oracle_routing_full(bcfg, seed=0, cutoff="batch")
+    _, bad = routing_mismatches(idx, rr["idx"], rr["z32"], rr["alpha"])
+    assert not bad, f"backward smoke: routing differs beyond near ties: tokens {bad}"
+    host = synth.host_layer(bcfg, 0)
+    ref = ob.backward(bcfg, ob.decode_layer(bcfg, host), oracle.decode(host["x"]),
+                      idx.astype(np.int64), dy.float().cpu().numpy().astype(np.float64))
+    worst = max(normwise_err(to_np(g[n]).astype(np.float64), ref[n]) for n in ob.GRAD_NAMES)
+    assert worst <= TOL["bf16"], f"backward normwise error {worst:.3e} above {TOL['bf16']}"
+    print(f"smoke ok: backward {bcfg.name} bt={bcfg.bt} worst normwise err {worst:.2e}",
+          flush=True)
