@@ -80,3 +80,36 @@ def test_unchosen_expert_has_zero_gradient():
         nz = any(np.abs(gr[m][e]).max() > 0 for m in ("w_gate", "w_up", "w_down"))
         assert nz == (e in chosen), e
         assert (gr["router_bias"][e] != 0) == (e in chosen)
+
+
+def test_finite_differences_catch_a_planted_mistake(monkeypatch):
+    """Plant a mistake in the oracle (phi' without its tanh-cap term; the
+    forward only uses phi and psi, so it stays right): the finite difference
+    agrees with the true gradient and not with the planted one."""
+    _, ref, p, x = _setup(SMALL)
+    idx = ref["idx"]
+    dy = np.random.default_rng(5).normal(0, 1, (SMALL.bt, SMALL.d))
+    good = ob.backward(SMALL, p, x, idx, dy)["w_gate"]
+    orig = ob.situ_parts
+
+    def planted(g, u, beta, beta_u):
+        phi, dphi, psi, dpsi = orig(g, u, beta, beta_u)
+        s = 1.0 / (1.0 + np.exp(-g))
+        return phi, dphi - s * (1.0 - np.tanh(g / beta) ** 2), psi, dpsi
+
+    monkeypatch.setattr(ob, "situ_parts", planted)
+    wrong = ob.backward(SMALL, p, x, idx, dy)["w_gate"]
+    monkeypatch.undo()
+    pos = np.unravel_index(int(np.abs(good - wrong).argmax()), good.shape)
+    h = 1e-5
+    t = p["w_gate"]
+    o = float(t[pos])
+    t[pos] = o + h
+    lp = _loss(SMALL, p, x, idx, dy)
+    t[pos] = o - h
+    lm = _loss(SMALL, p, x, idx, dy)
+    t[pos] = o
+    fd = (lp - lm) / (2 * h)
+    scale = max(1.0, float(np.abs(good).max()))
+    assert abs(fd - good[pos]) <= 1e-6 * scale
+    assert abs(fd - wrong[pos]) > 1e-3 * scale
