@@ -103,3 +103,66 @@ def test_backward_zero_tokens_writes_zero_gradients():
         if n != "dx":
             assert bool((t == 0).all()), n
     del route, x
+
+
+def _reduced_host_layer(cfg, tokens, idx, seed):
+    """The host layer cut down to what the listed tokens touch: the dense
+    weights whole, and the router rows, biases and matrices of the experts those
+    tokens chose (re-indexed in ascending id).  A token's forward and its dx only
+    involve its own experts, and an expert's weight gradients only the tokens
+    that chose it."""
+    experts = sorted({int(e) for t in tokens for e in idx[t]})
+    remap = {e: i for i, e in enumerate(experts)}
+    sp = synth.specs(cfg)
+    lay = {n: synth.host_tensor(cfg, n, seed).reshape(sp[n].shape)
+           for n in ("w_down_proj", "w_up_proj", "sh_gate", "sh_up", "sh_down")}
+    lay["w_router"] = synth.host_tensor(cfg, "w_router", seed).reshape(sp["w_router"].shape)[
+        experts]
+    for n in ("w_gate", "w_up", "w_down"):
+        lay[n] = np.stack([synth.host_matrix(cfg, n, e, seed) for e in experts])
+    bias = synth.router_bias(cfg)
+    if bias is not None:
+        lay["router_bias"] = np.asarray(bias)[experts]
+    lay["gamma"] = synth.gamma(cfg)
+    sub_idx = np.array([[remap[int(e)] for e in idx[t]] for t in tokens], np.int64)
+    return cfg.with_(n_experts=len(experts), bt=len(tokens)), lay, remap, sub_idx
+
+
+def test_backward_k3_decode_sampled():
+    """K3 decode shapes (64 tokens, 896 experts of 3072 x 3584, top 16, d 7168):
+    an expert chosen by two tokens, and those tokens.  The oracle computes the
+    two tokens' dx and the expert's gate / up / down / router gradients in full
+    from the 32 or fewer experts they touch."""
+    cfg = synth.CONFIGS["k3_decode_bf16"]
+    seed = 0
+    say("backward K3 decode, sampled")
+    layer, x = parity.device_layer(cfg, seed=seed)
+    bits, dy64 = _bf16_dy(cfg, seed + 7)
+    dy = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    r = layer.route(x)
+    g = layer.backward(x, dy, route=r)
+    torch.cuda.synchronize()
+    idx = parity.to_np(r["idx"])
+    ref_route = parity.oracle_routing_full(cfg, seed=seed)
+    _, bad = parity.routing_mismatches(idx, ref_route["idx"], ref_route["z32"],
+                                       ref_route["alpha"])
+    assert not bad, f"tokens whose expert set is not a valid top-k: {bad[:8]}"
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)
+    e_star = int(np.nonzero(counts == 2)[0][0])
+    tokens = [int(t) for t in np.nonzero((idx == e_star).any(axis=1))[0]]
+    say("  expert", e_star, "tokens", tokens)
+    sub, lay, remap, sub_idx = _reduced_host_layer(cfg, tokens, idx, seed)
+    p = ob.decode_layer(sub, lay)
+    xs = oracle.decode(synth.host_rows(cfg, "x", tokens, seed))
+    ref = ob.backward(sub, p, xs, sub_idx, dy64[tokens])
+    es = remap[e_star]
+    pairs = [("dx", parity.to_np(g["dx"][tokens]), ref["dx"])]
+    for n in ("w_gate", "w_up", "w_down", "w_router"):
+        pairs.append((n, parity.to_np(g[n][e_star]), ref[n][es]))
+    for name, got, want in pairs:
+        err = parity.normwise_err(got.astype(np.float64), want)
+        say(f"  {name:9s} normwise {err:.2e}")
+        assert err <= TOL, (name, err)
+    gb = float(g["router_bias"][e_star])
+    assert abs(gb - ref["router_bias"][es]) <= TOL * max(1e-30, abs(ref["router_bias"][es]))
+    del layer, g

@@ -113,3 +113,25 @@ def test_finite_differences_catch_a_planted_mistake(monkeypatch):
     scale = max(1.0, float(np.abs(good).max()))
     assert abs(fd - good[pos]) <= 1e-6 * scale
     assert abs(fd - wrong[pos]) > 1e-3 * scale
+
+
+def test_token_and_expert_locality_of_the_gradients():
+    """What the full-size sampled GPU check relies on: the oracle on the layer
+    cut down to the experts some tokens chose gives those tokens' dx, and the
+    full weight gradients of an expert all of whose tokens are among them,
+    equal to the oracle on the whole layer."""
+    from tests.test_gpu_backward import _reduced_host_layer
+    cfg = SMALL.with_(bt=48)
+    lay, ref, p, x = _setup(cfg)
+    idx = ref["idx"]
+    dy = np.random.default_rng(9).normal(0, 1, (cfg.bt, cfg.d))
+    full = ob.backward(cfg, p, x, idx, dy)
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)
+    e_star = int(np.argmin(np.where(counts > 0, counts, 10 ** 9)))
+    tokens = [int(t) for t in np.nonzero((idx == e_star).any(axis=1))[0]]
+    sub, small, remap, sub_idx = _reduced_host_layer(cfg, tokens, idx, 0)
+    part = ob.backward(sub, ob.decode_layer(sub, small), x[tokens], sub_idx, dy[tokens])
+    np.testing.assert_allclose(part["dx"], full["dx"][tokens], rtol=1e-9, atol=1e-12)
+    es = remap[e_star]
+    for n in ("w_gate", "w_up", "w_down", "w_router", "router_bias"):
+        np.testing.assert_allclose(part[n][es], full[n][e_star], rtol=1e-9, atol=1e-12)
