@@ -166,3 +166,33 @@ def test_backward_k3_decode_sampled():
     gb = float(g["router_bias"][e_star])
     assert abs(gb - ref["router_bias"][es]) <= TOL * max(1e-30, abs(ref["router_bias"][es]))
     del layer, g
+
+
+def test_backward_k3_prefill_sampled_tokens():
+    """K3 prefill shapes (16384 tokens, Zipf(1.1) offsets, batch quantile
+    cutoffs), the launch the backward bench times: the first and the last
+    token's dx against the oracle on the experts they chose."""
+    cfg = synth.CONFIGS["k3_prefill_bf16"]
+    seed = 0
+    say("backward K3 prefill, sampled tokens")
+    layer, x = parity.device_layer(cfg, seed=seed)
+    bits, dy64 = _bf16_dy(cfg, seed + 7)
+    dy = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    r = layer.route(x)
+    g = layer.backward(x, dy, route=r)
+    torch.cuda.synchronize()
+    idx = parity.to_np(r["idx"])
+    tokens = [0, cfg.bt - 1]
+    dx = parity.to_np(g["dx"][tokens])
+    del g, layer
+    torch.cuda.empty_cache()
+    ref_route = parity.oracle_routing_full(cfg, seed=seed)
+    _, bad = parity.routing_mismatches(idx, ref_route["idx"], ref_route["z32"],
+                                       ref_route["alpha"])
+    assert not bad, f"tokens whose expert set is not a valid top-k: {bad[:8]}"
+    sub, lay, _, sub_idx = _reduced_host_layer(cfg, tokens, idx, seed)
+    xs = oracle.decode(synth.host_rows(cfg, "x", tokens, seed))
+    ref = ob.backward(sub, ob.decode_layer(sub, lay), xs, sub_idx, dy64[tokens])
+    err = parity.normwise_err(dx.astype(np.float64), ref["dx"])
+    say(f"  dx normwise {err:.2e}")
+    assert err <= TOL
