@@ -240,7 +240,8 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t bt);
  * their rocBLAS handles; default priority) that start after the work already
  * on `stream` and that `stream` waits for.  Those streams and handles are
  * per device and shared by every call: calls of moe_backward on one device
- * must not overlap from several host threads.  bt == 0
+ * must not overlap from several host threads.  The call synchronises the
+ * stream, so it cannot be captured into a HIP graph.  bt == 0
  * writes zero weight gradients.  The workspace (256-byte aligned) holds the
  * recomputed activations, about 2 (L + I) * 10 bytes a (token, expert) pair. */
 moe_status moe_backward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
