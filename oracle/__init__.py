@@ -34,7 +34,7 @@ class OrcShape(ctypes.Structure):
                 ("expert_inter", ctypes.c_int64), ("n_shared", ctypes.c_int64),
                 ("shared_inter", ctypes.c_int64), ("beta", ctypes.c_double),
                 ("beta_u", ctypes.c_double), ("rms_eps", ctypes.c_double),
-                ("act_mx_block", ctypes.c_int64)]
+                ("act_mx_block", ctypes.c_int64), ("act_mx_exact", ctypes.c_int64)]
 
 
 class OrcWeights(ctypes.Structure):
@@ -79,6 +79,8 @@ def lib():
             "orc_double_to_e4m3": ([D], ctypes.c_uint8),
             "orc_round_bf16": ([D], D),
             "orc_dense_ffn": ([P, P, P, P, P, P, P, P], ctypes.c_int),
+            "orc_set_threads": ([ctypes.c_int], None),
+            "orc_get_threads": ([], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -99,12 +101,28 @@ def _c(a, dt=None):
     return a
 
 
-def shape_of(cfg) -> OrcShape:
+# MX FP8 expert inputs: decide each code on the input rounded to bf16 (the
+# precision the layer stores x_lat and h in) or, when False, on the exact value
+MX_CODES_ON_BF16 = True
+
+
+def shape_of(cfg, mx_codes_on_bf16=None) -> OrcShape:
     g = lambda n, dflt=0: getattr(cfg, n, dflt)
     mx = 32 if getattr(cfg, "act_quant", "none") == "mxfp8" else 0
+    on_bf16 = MX_CODES_ON_BF16 if mx_codes_on_bf16 is None else mx_codes_on_bf16
     return OrcShape(g("d"), g("latent"), g("n_experts"), g("top_k"), g("expert_inter"),
                     g("n_shared"), g("shared_inter"), float(g("beta", 4.0)),
-                    float(g("beta_u", 25.0)), float(g("rms_eps", 1e-6)), mx)
+                    float(g("beta_u", 25.0)), float(g("rms_eps", 1e-6)), mx,
+                    0 if on_bf16 else 1)
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
 
 
 class Mat:
@@ -270,11 +288,12 @@ def dispatch(idx: np.ndarray, n_experts: int):
     return counts, offsets, perm, inv
 
 
-def expert(cfg, gate: Mat, up: Mat, down: Mat, x_lat, index=0) -> np.ndarray:
+def expert(cfg, gate: Mat, up: Mat, down: Mat, x_lat, index=0,
+           mx_codes_on_bf16=None) -> np.ndarray:
     x_lat = _c(x_lat, np.float64)
     o = np.empty(cfg.latent, np.float64)
-    if lib().orc_expert(ctypes.byref(shape_of(cfg)), gate.ref, up.ref, down.ref, index,
-                        _ptr(x_lat), _ptr(o)):
+    if lib().orc_expert(ctypes.byref(shape_of(cfg, mx_codes_on_bf16)), gate.ref, up.ref,
+                        down.ref, index, _ptr(x_lat), _ptr(o)):
         raise ValueError("orc_expert rejected its arguments")
     return o
 

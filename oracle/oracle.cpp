@@ -114,6 +114,9 @@ double dot(const double *a, const double *b, int64_t n) {
 
 extern "C" {
 
+void orc_set_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
+int orc_get_threads(void) { return omp_get_max_threads(); }
+
 double orc_bf16_to_double(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;
   float f;
@@ -203,10 +206,11 @@ int orc_mx8_quantize(const double *x, int64_t n, int64_t block, uint8_t *codes,
 }
 
 // x replaced by its MX FP8 quantisation (dequantised exactly), blocks of
-// `block`, the codes decided on x rounded to bf16.
-static void mx8_round_trip(double *x, int64_t n, int64_t block) {
+// `block`, the codes decided on x rounded to bf16 (on_bf16) or on x itself.
+static void mx8_round_trip(double *x, int64_t n, int64_t block, bool on_bf16) {
   std::vector<uint8_t> codes((size_t)n), scales((size_t)(n / block));
-  for (int64_t i = 0; i < n; ++i) x[i] = orc_round_bf16(x[i]);
+  if (on_bf16)
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_round_bf16(x[i]);
   orc_mx8_quantize(x, n, block, codes.data(), scales.data());
   for (int64_t i = 0; i < n; ++i)
     x[i] = orc_e4m3_to_double(codes[i]) * orc_e8m0_to_double(scales[i / block]);
@@ -344,12 +348,13 @@ int orc_expert(const orc_shape *s, const orc_mat *w_gate, const orc_mat *w_up,
   const int64_t I = s->expert_inter, L = s->latent, qb = s->act_mx_block;
   if (qb < 0 || (qb > 0 && (L % qb || I % qb))) return -1;
   std::vector<double> xin(x_lat, x_lat + L);
-  if (qb > 0) mx8_round_trip(xin.data(), L, qb);  // the gate/up GEMMs read MX FP8 x_lat
+  const bool on_bf16 = s->act_mx_exact == 0;
+  if (qb > 0) mx8_round_trip(xin.data(), L, qb, on_bf16);  // gate/up read MX FP8 x_lat
   std::vector<double> g((size_t)I), u((size_t)I), h((size_t)I);
   orc_matvec(w_gate, mat, xin.data(), g.data());
   orc_matvec(w_up, mat, xin.data(), u.data());
   for (int64_t i = 0; i < I; ++i) h[i] = orc_phi(g[i], s->beta) * orc_psi(u[i], s->beta_u);
-  if (qb > 0) mx8_round_trip(h.data(), I, qb);  // and the down GEMM MX FP8 h
+  if (qb > 0) mx8_round_trip(h.data(), I, qb, on_bf16);  // and the down GEMM MX FP8 h
   orc_matvec(w_down, mat, h.data(), o);
   return 0;
 }

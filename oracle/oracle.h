@@ -32,9 +32,10 @@
  * its power-of-two E8M0 block scale.
  *
  * Parity pins (tests/test_oracle_pins.py): closed forms, invariants and
- * brute force as listed there.  The layer output as a whole is pinned only
- * through those properties: the pages print no worked numeric example of
- * it.
+ * brute force as listed there; step 8 (orc_output) by exact dyadic closed
+ * forms at the SiTU caps, where phi * psi is exactly beta * beta_u.  The
+ * layer output as a whole is pinned only through those properties: the
+ * pages print no worked numeric example of it.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -71,10 +72,14 @@ typedef struct {
   /* 0: the routed experts read their inputs exactly.  32: each expert GEMM
    * reads its input (x_lat for gate/up, h for down) quantised to OCP MX FP8
    * E4M3 with one E8M0 scale per 32 consecutive elements (orc_mx8_quantize),
-   * and the routing weight multiplies the expert output as always.  The codes
-   * are decided on the input rounded to bf16 (orc_round_bf16): the precision
-   * in which the GPU path holds x_lat and h when it quantises them. */
+   * and the routing weight multiplies the expert output as always.  Where
+   * floating point decides a code, the decision is taken in the precision of
+   * the stored input: by default the input rounded to bf16 (orc_round_bf16),
+   * the precision in which the layer holds x_lat and h when it quantises
+   * them (the pages fix none).  act_mx_exact = 1 decides the codes on the
+   * exact fp64 input instead, the plain reading of the MX conversion. */
   int64_t act_mx_block;
+  int64_t act_mx_exact;
 } orc_shape;
 
 typedef struct {
@@ -88,6 +93,11 @@ typedef struct {
   orc_mat sh_gate, sh_up;           /* [S][I_s][d] */
   orc_mat sh_down;                  /* [S][d][I_s] */
 } orc_weights;
+
+/* OpenMP threads of the oracle's parallel loops (n >= 1), and the current
+ * count: the CPU baseline is timed at the host's core count and at one core. */
+void orc_set_threads(int n);
+int orc_get_threads(void);
 
 /* One element, decoded exactly. */
 double orc_decode(const orc_mat *m, int64_t mat, int64_t r, int64_t c);

@@ -810,3 +810,72 @@ def test_expert_with_mx8_inputs_is_the_quantised_composition():
     o_exact = oracle.expert(s, oracle.Mat(Wg), oracle.Mat(Wu), oracle.Mat(Wd), x)
     rel = np.abs(o - o_exact).max() / np.abs(o_exact).max()
     assert 1e-4 < rel < 0.1
+
+
+# ---- step 8: output projection plus the shared experts -----------------------------------
+#
+# y = W_up n + sum_j W_ds,j (phi(W_gs,j x) psi(W_us,j x)).  At g = u = +-1000 the
+# SiTU factors sit exactly on their caps in fp64 (sigmoid(1000) = 1, tanh(250) =
+# tanh(40) = 1, sigmoid(-1000) = 0), so every hidden value is exactly
+# beta * beta_u = 100, -100 or 0, and with dyadic weights the whole output is an
+# exact dyadic number: the expected values below are exact sums.
+
+def _output_case(S=2):
+    d, L, Is = 6, 4, 3
+    # shared gate/up rows read x[0] only, with weight +1 or -1: g, u = +-1000
+    sg = np.zeros((S, Is, d), np.float32)
+    su = np.zeros((S, Is, d), np.float32)
+    signs_g = np.array([[1, 1, -1], [1, -1, 1], [-1, 1, 1]][:S], np.float32)
+    signs_u = np.array([[1, -1, 1], [-1, 1, 1], [1, 1, -1]][:S], np.float32)
+    sg[:, :, 0], su[:, :, 0] = signs_g, signs_u
+    # the hidden values those signs give at the caps: phi(+1000) = 4, phi(-1000) = 0,
+    # psi(+-1000) = +-25
+    h = np.where(signs_g > 0, 4.0, 0.0) * 25.0 * signs_u
+    rng = np.random.default_rng(50)
+    sd = (rng.integers(-8, 9, (S, d, Is)) / 8.0).astype(np.float32)   # dyadic
+    wup = (rng.integers(-8, 9, (d, L)) / 16.0).astype(np.float32)     # dyadic
+    n = rng.integers(-6, 7, L) / 4.0                                   # dyadic
+    x = np.zeros(d)
+    x[0], x[3] = 1000.0, 7.0  # x[3] meets only zero weights
+    shp = Shape(d=d, latent=L, n_shared=S, shared_inter=Is)
+    mats = {"w_up_proj": wup, "sh_gate": sg, "sh_up": su, "sh_down": sd}
+    return shp, mats, x, n, h
+
+
+def test_output_at_the_situ_caps_is_exact():
+    """y equals W_up n plus every shared expert's W_ds h, bit for bit: a dropped
+    routed term, a dropped or single shared expert, swapped gate/up, or a
+    transposed W_ds or W_up all change y."""
+    shp, mats, x, n, h = _output_case()
+    y = oracle.output(shp, oracle.Weights(mats), n, x)
+    routed = mats["w_up_proj"].astype(np.float64) @ n
+    shared = sum(mats["sh_down"][j].astype(np.float64) @ h[j] for j in range(2))
+    np.testing.assert_array_equal(y, routed + shared)
+    assert np.abs(routed).max() > 0 and np.abs(shared).max() > 0
+    assert not np.array_equal(y, routed) and not np.array_equal(y, shared)
+    assert not np.array_equal(y, routed + mats["sh_down"][0].astype(np.float64) @ h[0])
+    # the shared term alone (W_up = 0) is orc_shared, exactly
+    z = dict(mats, w_up_proj=np.zeros_like(mats["w_up_proj"]))
+    np.testing.assert_array_equal(oracle.output(shp, oracle.Weights(z), n, x), shared)
+    np.testing.assert_array_equal(oracle.shared(shp, oracle.Weights(mats), x), shared)
+
+
+def test_output_without_shared_experts_selects_latent_entries():
+    """S = 0 and a one-hot W_up (row r picks entry p(r) of n): y is those entries
+    of n, exactly."""
+    d, L = 5, 4
+    pick = [2, 0, 3, 3, 1]
+    wup = np.zeros((d, L), np.float32)
+    wup[np.arange(d), pick] = 1.0
+    n = np.array([0.5, -1.25, 3.0, -0.75])
+    shp = Shape(d=d, latent=L, n_shared=0, shared_inter=8)
+    y = oracle.output(shp, oracle.Weights({"w_up_proj": wup}), n, np.ones(d))
+    np.testing.assert_array_equal(y, n[pick])
+
+
+def test_output_is_linear_in_w_up_only_through_the_routed_term():
+    """Doubling W_up adds exactly W_up n: the shared term does not move."""
+    shp, mats, x, n, _ = _output_case()
+    y1 = oracle.output(shp, oracle.Weights(mats), n, x)
+    y2 = oracle.output(shp, oracle.Weights(dict(mats, w_up_proj=2 * mats["w_up_proj"])), n, x)
+    np.testing.assert_array_equal(y2 - y1, mats["w_up_proj"].astype(np.float64) @ n)
