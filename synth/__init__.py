@@ -470,6 +470,52 @@ def device_layer(cfg: Config, seed: int = 0, routing: str = "normal", device="cu
     return out
 
 
+# ---- the C ABI's names for a generated layer ----------------------------------------
+# (name mapping only: a generated tensor goes to the moe_weights field of the
+# same meaning; fp8 block scales to s_*, MX E8M0 codes of the experts to e8_*)
+
+ABI_NAME = {"w_router": "w_router", "router_bias": "router_bias", "w_down_proj": "w_down_proj",
+            "w_gate": "w_gate", "w_up": "w_up", "w_down": "w_down", "gamma": "latent_gamma",
+            "w_up_proj": "w_up_proj", "sh_gate": "sh_gate", "sh_up": "sh_up",
+            "sh_down": "sh_down"}
+SCALE_ABI = {"w_down_proj": "s_down_proj", "w_gate": "s_gate", "w_up": "s_up",
+             "w_down": "s_down", "w_up_proj": "s_up_proj", "sh_gate": "s_sh_gate",
+             "sh_up": "s_sh_up", "sh_down": "s_sh_down"}
+MX_ABI = {"w_gate": "e8_gate", "w_up": "e8_up", "w_down": "e8_down"}
+
+
+def abi_config_args(cfg: Config, cutoff: Optional[str] = None) -> dict:
+    """Keyword arguments of the binding's make_config for this workload: the
+    weight dtype names the ABI's (MXFP4 experts with MX FP8 inputs are
+    "mxfp4_a8")."""
+    weight = cfg.weight
+    mx8_in = cfg.act_quant == "mxfp8"
+    if weight == "mxfp8":
+        assert mx8_in, "MX FP8 experts read MX FP8 inputs"
+    elif mx8_in:
+        assert weight == "mxfp4", "MX FP8 expert inputs go with MX experts"
+        weight = "mxfp4_a8"
+    return dict(d=cfg.d, latent=cfg.latent, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                expert_inter=cfg.expert_inter, n_shared=cfg.n_shared,
+                shared_inter=cfg.shared_inter, beta=cfg.beta, beta_u=cfg.beta_u,
+                rms_eps=cfg.rms_eps, act=cfg.act, weight=weight, router=cfg.router,
+                cutoff=cutoff or cfg.cutoff)
+
+
+def abi_tensors(cfg: Config, lay: dict) -> dict:
+    """A device_layer() dict re-keyed by moe_weights field names (x left out)."""
+    t = {}
+    for k, v in lay.items():
+        if k == "x" or v is None:
+            continue
+        if k.startswith("scale:"):
+            mx = cfg.weight in ("mxfp4", "mxfp8") and k[6:] in MX_ABI
+            t[(MX_ABI if mx else SCALE_ABI)[k[6:]]] = v
+        else:
+            t[ABI_NAME[k]] = v
+    return t
+
+
 # ---- dense layer-1 FFN workloads ----------------------------------------------------------
 # mkdocs.reaper.mx "Vue d'ensemble de l'architecture": layer 1 is a dense SiTU-GLU FFN
 # of intermediate width 33 792 (section "Le décompte des couches"), pre-RMSNorm with

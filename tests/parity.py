@@ -23,14 +23,7 @@ import synth
 TIE_BAND = 1e-6
 TOL = {"bf16": 2e-2, "fp8": 6e-2, "f32": 1e-4}
 
-ABI_NAME = {"w_router": "w_router", "router_bias": "router_bias", "w_down_proj": "w_down_proj",
-            "w_gate": "w_gate", "w_up": "w_up", "w_down": "w_down", "gamma": "latent_gamma",
-            "w_up_proj": "w_up_proj", "sh_gate": "sh_gate", "sh_up": "sh_up",
-            "sh_down": "sh_down"}
-SCALE_ABI = {"w_down_proj": "s_down_proj", "w_gate": "s_gate", "w_up": "s_up",
-             "w_down": "s_down", "w_up_proj": "s_up_proj", "sh_gate": "s_sh_gate",
-             "sh_up": "s_sh_up", "sh_down": "s_sh_down"}
-MX_ABI = {"w_gate": "e8_gate", "w_up": "e8_up", "w_down": "e8_down"}
+ELEM_FLOOR = 1e-3
 
 
 def tol_of(cfg) -> float:
@@ -44,17 +37,7 @@ def tol_of(cfg) -> float:
 
 def abi_config(cfg, cutoff=None):
     import sparse_moe_layer_quantile_amd as moe
-    weight = cfg.weight
-    mx8_in = getattr(cfg, "act_quant", "none") == "mxfp8"
-    if weight == "mxfp8":
-        assert mx8_in, "MX FP8 experts read MX FP8 inputs"
-    elif mx8_in:
-        assert weight == "mxfp4", "MX FP8 expert inputs go with MX experts"
-        weight = "mxfp4_a8"
-    return moe.make_config(cfg.d, cfg.latent, cfg.n_experts, cfg.top_k, cfg.expert_inter,
-                           cfg.n_shared, cfg.shared_inter, cfg.beta, cfg.beta_u, cfg.rms_eps,
-                           act=cfg.act, weight=weight, router=cfg.router,
-                           cutoff=cutoff or cfg.cutoff)
+    return moe.make_config(**synth.abi_config_args(cfg, cutoff))
 
 
 def device_layer(cfg, seed=0, routing="normal", cutoff=None, alpha=None, names=None):
@@ -63,15 +46,7 @@ def device_layer(cfg, seed=0, routing="normal", cutoff=None, alpha=None, names=N
     import torch
     import sparse_moe_layer_quantile_amd as moe
     lay = synth.device_layer(cfg, seed, routing, names=names)
-    t = {}
-    for k, v in lay.items():
-        if k == "x" or v is None:
-            continue
-        if k.startswith("scale:"):
-            mx = cfg.weight in ("mxfp4", "mxfp8") and k[6:] in MX_ABI
-            t[(MX_ABI if mx else SCALE_ABI)[k[6:]]] = v
-        else:
-            t[ABI_NAME[k]] = v
+    t = synth.abi_tensors(cfg, lay)
     if alpha is not None:
         t["cutoff"] = torch.as_tensor(np.asarray(alpha, np.float32), device="cuda")
     layer = moe.StableLatentMoE(abi_config(cfg, cutoff), t)
@@ -91,6 +66,32 @@ def y_to_f64(y):
 def normwise_err(y, ref) -> float:
     den = float(np.abs(ref).max())
     return float(np.abs(y - ref).max()) / (den if den > 0 else 1.0)
+
+
+def elementwise_err(y, ref, floor=ELEM_FLOOR) -> float:
+    """max_i |y_i - ref_i| / max(|ref_i|, floor * max|ref|): the error of each
+    element relative to its own magnitude, with small elements judged against
+    a floor at a fraction of the largest one."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    top = float(np.abs(ref).max())
+    if top == 0.0:
+        return float(np.abs(y).max())
+    den = np.maximum(np.abs(ref), floor * top)
+    return float((np.abs(y - ref) / den).max())
+
+
+def assert_close(y, ref, tol, what=""):
+    """Normwise error within tol, and the element-wise errors at the floors
+    ELEM_CHECKS lists within theirs; every figure is printed."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nw = normwise_err(y, ref)
+    ew = {f: elementwise_err(y, ref, f) for f in (1e-3, 1e-2, 1e-1, 0.25)}
+    print(f"  {what} normwise {nw:.3e} (tol {tol}); elementwise "
+          + " ".join(f"floor {f:g}: {v:.3e}" for f, v in ew.items()), flush=True)
+    assert nw <= tol, f"{what}: normwise error {nw:.3e} above {tol}"
+    return nw, ew
 
 
 def sigmoid64(x):
@@ -157,7 +158,8 @@ def oracle_routing_full(cfg, seed=0, routing="normal", cutoff=None, alpha=None, 
                 offsets=offsets, perm=perm, inv_perm=inv, x=x)
 
 
-def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None):
+def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None,
+                  mx_codes_on_bf16=None):
     """Oracle y (fp64) of the listed tokens given their routing (steps 5-8),
     regenerating each touched expert's matrices on the host."""
     sp = synth.specs(cfg)
@@ -187,7 +189,7 @@ def oracle_tokens(cfg, tokens, idx, wts, seed=0, routing="normal", x=None):
                                None if esc[n] is None else esc[n][e])
                     for n in ("w_gate", "w_up", "w_down"))
         for i, j in pairs:
-            o[i, j] = oracle.expert(cfg, g, u, dn, xlat[i])
+            o[i, j] = oracle.expert(cfg, g, u, dn, xlat[i], mx_codes_on_bf16=mx_codes_on_bf16)
     ys = []
     for i, t in enumerate(tokens):
         _, n = oracle.combine_norm(cfg, o[i], wts[t], mats["gamma"])

@@ -61,10 +61,9 @@ class _Ref:
 def _check(cfg, y, ref, tokens, with_r=True):
     yg = parity.y_to_f64(y)[tokens]
     yr = ref.rows(tokens, with_r)
-    err = parity.normwise_err(yg, yr)
     tol = parity.TOL["f32" if cfg.act == "f32" else "bf16"]
-    say(f"  {cfg.name} bt {cfg.bt}: normwise err {err:.3e} (tol {tol}) on {len(tokens)} rows")
-    assert err <= tol
+    say(f"  {cfg.name} bt {cfg.bt}: {len(tokens)} rows")
+    err, _ = parity.assert_close(yg, yr, tol, "y")
     return err
 
 

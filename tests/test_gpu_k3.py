@@ -7,6 +7,7 @@ token (decode) or on a seeded sample of tokens the oracle computes one by one
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from tests import parity
 
@@ -26,6 +27,25 @@ def _need_gpu():
     torch.cuda.empty_cache()
 
 
+def _selection_on_gpu_logits(cfg, got):
+    """Routing stage 1, free of any tolerance: the oracle's quantile, top-k and
+    dispatch run on the GPU's own fp32 logits of the whole batch, and the
+    cutoffs, expert ids, counts, offsets and both permutations must equal the
+    GPU's bit for bit; the combine weights are the sigmoid of the same logits."""
+    z = got["logits"]
+    if cfg.cutoff == "batch":
+        alpha = oracle.quantile(z, cfg.quantile_rank)
+    else:
+        alpha = np.zeros(cfg.n_experts, np.float32)
+    np.testing.assert_array_equal(got["cutoff"], alpha, err_msg="cutoffs")
+    idx, w = oracle.topk(z, cfg.top_k, alpha=alpha)
+    np.testing.assert_array_equal(got["idx"], idx, err_msg="expert ids")
+    for n, v in zip(("counts", "offsets", "perm", "inv_perm"), oracle.dispatch(idx, cfg.n_experts)):
+        np.testing.assert_array_equal(got[n], v, err_msg=n)
+    np.testing.assert_allclose(got["w"], w, rtol=2e-6, atol=0)
+    say(f"  stage 1: cutoffs, ids and dispatch bit-exact on {cfg.bt} tokens")
+
+
 def _run_k3(cfg_name, n_sample, seed=0, two_streams=False):
     cfg = synth.CONFIGS[cfg_name]
     say("k3 parity", cfg.name, "bt", cfg.bt, "sample", n_sample, "two streams", two_streams)
@@ -37,7 +57,9 @@ def _run_k3(cfg_name, n_sample, seed=0, two_streams=False):
     got = {n: parity.to_np(v) for n, v in r.items()}
     del layer, x, y, r
     torch.cuda.empty_cache()
-    say("  gpu done; oracle routing")
+    say("  gpu done; oracle selection on the GPU's logits")
+    _selection_on_gpu_logits(cfg, got)
+    say("  oracle routing")
     ref = parity.oracle_routing_full(cfg, seed=seed)
     dz = np.abs(got["logits"].astype(np.float64) - ref["z64"]).max()
     say(f"  max |z - z_ref| = {dz:.3e}")
@@ -60,9 +82,7 @@ def _run_k3(cfg_name, n_sample, seed=0, two_streams=False):
         tokens = np.unique(np.concatenate([tokens, [pool[0], pool[-1]]]))
     say(f"  oracle y on {len(tokens)} tokens")
     yref = parity.oracle_tokens(cfg, tokens, ref["idx"], ref["w"], seed=seed, x=ref["x"])
-    err = parity.normwise_err(yg[tokens], yref)
-    say(f"  normwise err {err:.3e} (tol {parity.tol_of(cfg)})")
-    assert err <= parity.tol_of(cfg)
+    parity.assert_close(yg[tokens], yref, parity.tol_of(cfg), "y")
     return cfg, got
 
 

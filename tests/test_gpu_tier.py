@@ -3,8 +3,8 @@ memory, an HBM cache of the popular ones, every expert read through the
 address table.  Reading an expert from its slot or from host memory gives the
 same bytes to the same kernels, so a tiered forward must equal the forward on
 HBM-resident weights bit for bit, whatever the cache holds at that moment.
-The resident forward itself is checked against the oracle by the parity
-tests."""
+Tiered outputs are also checked against the oracle directly: the oracle's
+routing of the same tokens and its output on them, from regenerated weights."""
 import numpy as np
 import pytest
 
@@ -47,6 +47,21 @@ def _expert_bytes(cfg):
             "mxfp8": 3 * (n + n // 32)}[cfg.weight]
 
 
+def _check_against_oracle(cfg, tl, x, x_seed, y):
+    """The tiered layer's routing and output on this batch against the oracle
+    (weights of seed 0, tokens of x_seed), every token."""
+    r = tl.route(x)
+    torch.cuda.synchronize()
+    xh = synth.host_tensor(cfg, "x", x_seed).reshape(cfg.bt, cfg.d)
+    ref = parity.oracle_routing_full(cfg, seed=0, x=xh)
+    idx = parity.to_np(r["idx"])
+    diff, bad = parity.routing_mismatches(idx, ref["idx"], ref["z32"], ref["alpha"])
+    assert not bad
+    keep = np.setdiff1d(np.arange(cfg.bt), diff)
+    yref = parity.oracle_tokens(cfg, keep, ref["idx"], ref["w"], seed=0, x=xh)
+    parity.assert_close(parity.y_to_f64(y)[keep], yref, parity.tol_of(cfg), "tiered y")
+
+
 def _dispatch_bufs(cfg, bt):
     E, P = cfg.n_experts, bt * cfg.top_k
     return dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
@@ -84,6 +99,8 @@ def test_tiered_forward_equals_resident(weight, frac, side_copy):
         torch.cuda.synchronize()
         same = torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
         assert same, f"step {step}: tiered output differs"
+        if step in (0, 7):
+            _check_against_oracle(cfg, tl, x, 100 + step, y)
     for _ in range(2):  # start the last harvest, then fold it
         tier.plan(copy)
         torch.cuda.synchronize()
@@ -138,6 +155,8 @@ def test_tiered_forward_equals_resident_k3_mxfp4_decode():
         tier.observe(bufs["counts"])
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"step {step}"
+        if step in (0, 3):
+            _check_against_oracle(cfg, tl, x, 300 + step, y)
     st = tier.stats()
     say("  stats", st)
     assert st["resident"] > 0
