@@ -184,8 +184,12 @@ size_t moe_workspace_bytes(const moe_config *cfg, int64_t bt);
 moe_status moe_route(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
                      moe_route_out *out, void *ws, size_t ws_bytes, void *stream);
 
-/* Dispatch of given routing indices topk_idx[bt][k] (each in [0, E), distinct
- * and ascending per token).  All four outputs are required. */
+/* Dispatch of given routing indices topk_idx[bt][k] (each in [0, E) and
+ * distinct within a token's row, in any order).  All four outputs are
+ * required.  An id out of range, or repeated in its row, leaves that pair out
+ * of the grouping: offsets[E] is then below bt * k (the caller's check; the
+ * call does not wait for the device), the pair's inv_perm entry is 0, and
+ * every write stays inside the four arrays. */
 moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int64_t bt,
                         moe_dispatch_out *out, void *ws, size_t ws_bytes, void *stream);
 
@@ -390,6 +394,22 @@ int64_t moe_tier_select(const float *score, const uint8_t *resident, int64_t E, 
  * MOE_ERR_UNSUPPORTED for n >= 2^35. */
 moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes, uint8_t *scales,
                             void *stream);
+
+/* ---- SiTU-GLU numerics ---------------------------------------------------------
+ * The SiTU-GLU factors on the device, elementwise, by the same inline device
+ * functions the GEMM epilogues use (tech.news18a.com page, first technique:
+ * sigmoid limiting combined with tanh scaling, an output range strictly
+ * bounded by beta = 4 and beta_u = 25):
+ *   phi[i] = sigmoid(g[i]) beta tanh(g[i] / beta)
+ *   psi[i] = beta_u tanh(u[i] / beta_u)
+ *   h[i]   = phi[i] psi[i]
+ * g, u: n fp32 device values; phi, psi, h: n fp32 device outputs, each may be
+ * NULL (not all three).  For every finite input phi <= beta (phi > -0.2698 at
+ * beta = 4), |psi| <= beta_u and |h| <= beta beta_u.  Asynchronous on `stream`.
+ * MOE_ERR_INVALID_ARG for n < 0, beta or beta_u not positive, or NULL inputs
+ * with n > 0. */
+moe_status moe_situ_eval(const float *g, const float *u, int64_t n, float beta, float beta_u,
+                         float *phi, float *psi, float *h, void *stream);
 
 /* ---- Measurement support (not part of the layer) ----------------------------
  * While enabled, moe_forward and moe_ffn_forward record a timing hipEvent pair

@@ -149,6 +149,9 @@ def _load():
     lib.moe_tier_select.restype = ctypes.c_int64
     lib.moe_mx8_quantize.argtypes = [_P, ctypes.c_int64, _P, _P, _P]
     lib.moe_mx8_quantize.restype = ctypes.c_int
+    lib.moe_situ_eval.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_float, _P, _P,
+                                  _P, _P]
+    lib.moe_situ_eval.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_profile_enable.argtypes = [ctypes.c_int]
@@ -167,7 +170,8 @@ EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_profile_phase_name", "moe_ffn_workspace_bytes", "moe_ffn_forward",
             "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
             "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select",
-            "moe_cutoff_update", "moe_backward_workspace_bytes", "moe_backward")
+            "moe_cutoff_update", "moe_backward_workspace_bytes", "moe_backward",
+            "moe_situ_eval")
 
 
 def cutoff_update(alpha, zeta, rate: float):
@@ -264,6 +268,27 @@ class ExpertTier:
             self.close()
         except Exception:
             pass
+
+
+def moe_situ_eval(g: int, u: int, n: int, beta: float, beta_u: float, phi: int, psi: int,
+                  h: int, stream: int) -> int:
+    return LIB.moe_situ_eval(_P(g or None), _P(u or None), n, float(beta), float(beta_u),
+                             _P(phi or None), _P(psi or None), _P(h or None),
+                             _P(stream or None))
+
+
+def situ_eval(g, u, beta=4.0, beta_u=25.0):
+    """(phi(g), psi(u), phi(g) psi(u)) of fp32 device tensors, by the device
+    functions of the GEMM epilogues."""
+    import torch
+    g = g.contiguous()
+    u = u.contiguous()
+    phi, psi, h = (torch.empty_like(g) for _ in range(3))
+    st = moe_situ_eval(g.data_ptr(), u.data_ptr(), g.numel(), beta, beta_u, phi.data_ptr(),
+                       psi.data_ptr(), h.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise MoeError(st, "moe_situ_eval")
+    return phi, psi, h
 
 
 def moe_mx8_quantize(x: int, n: int, codes: int, scales: int, stream: int) -> int:

@@ -106,11 +106,15 @@ __device__ __forceinline__ float tanh_f(float x) {
   return copysignf((1.0f - e) * rcp_fast(1.0f + e), x);
 }
 // SiTU-GLU factors: phi(g) = sigmoid(g) beta tanh(g / beta), psi(u) = beta_u tanh(u / beta_u)
+__device__ __forceinline__ float situ_phi(float g, float beta, float inv_beta) {
+  return sigmoid_f(g) * beta * tanh_f(g * inv_beta);
+}
+__device__ __forceinline__ float situ_psi(float u, float beta_u, float inv_beta_u) {
+  return beta_u * tanh_f(u * inv_beta_u);
+}
 __device__ __forceinline__ float situ(float g, float u, float beta, float inv_beta,
                                       float beta_u, float inv_beta_u) {
-  const float phi = sigmoid_f(g) * beta * tanh_f(g * inv_beta);
-  const float psi = beta_u * tanh_f(u * inv_beta_u);
-  return phi * psi;
+  return situ_phi(g, beta, inv_beta) * situ_psi(u, beta_u, inv_beta_u);
 }
 
 // Order-preserving map of an fp32 value to uint32 (larger value -> larger

@@ -15,6 +15,10 @@
 //   3. one workgroup per expert walks its masks in token order: a prefix
 //      over the blocks' popcounts places every pair at its stable position
 //      (and, for the forward pass, copies the pair's routing weight there).
+// Caller-given ids may be out of range or repeated within a token's row: such
+// pairs are left out (offsets[E] < bt * k then tells), every write stays in
+// its array, and inv_perm of a left-out pair is 0.  The order of the ids in a
+// row does not matter.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,7 +27,8 @@ namespace moe {
 __global__ void __launch_bounds__(256) dispatch_mask_kernel(const int32_t *__restrict__ idx,
                                                             int64_t bt, int k, int E, int nb,
                                                             uint64_t *__restrict__ masks,
-                                                            int32_t *__restrict__ counts) {
+                                                            int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ inv_perm) {
   extern __shared__ uint64_t bits[];  // [E]
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) bits[e] = 0;
@@ -31,9 +36,17 @@ __global__ void __launch_bounds__(256) dispatch_mask_kernel(const int32_t *__res
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int ntok = (int)min((int64_t)64, bt - t0);
   for (int p = tid; p < ntok * k; p += 256) {
-    const int tl = p / k;
-    const int e = idx[t0 * k + p];
-    if (e >= 0 && e < E) atomicOr((unsigned long long *)&bits[e], 1ull << tl);
+    const int tl = p / k, j = p - tl * k;
+    const int32_t *row = idx + (t0 + tl) * k;
+    const int e = row[j];
+    // a pair counts when its id is in range and not repeated earlier in the
+    // row; any other pair (caller-given ids only) is dropped from the
+    // grouping, and its inv_perm slot is pointed at position 0 so that no
+    // consumer of inv_perm reads outside the pair range
+    bool ok = e >= 0 && e < E;
+    for (int q = 0; q < j && ok; ++q) ok = row[q] != e;
+    if (ok) atomicOr((unsigned long long *)&bits[e], 1ull << tl);
+    else inv_perm[t0 * k + p] = 0;
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -75,14 +88,12 @@ __global__ void __launch_bounds__(1024) dispatch_scan_kernel(const int32_t *__re
   }
 }
 
-__device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int32_t v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < v) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
+// Slot j of expert e in a token's row of k ids: its first occurrence (the
+// mask kernel counted only that one), in any id order.
+__device__ __forceinline__ int slot_of(const int32_t *row, int k, int32_t e) {
+  int j = 0;
+  while (j < k - 1 && row[j] != e) ++j;
+  return j;
 }
 
 __global__ void __launch_bounds__(256) dispatch_scatter_kernel(
@@ -117,7 +128,7 @@ __global__ void __launch_bounds__(256) dispatch_scatter_kernel(
       const int tl = __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
       const int64_t t = (int64_t)b * 64 + tl;
-      const int j = lower_bound_i32(idx + t * k, k, e);
+      const int j = slot_of(idx + t * k, k, e);
       const int32_t p = (int32_t)(t * k + j);
       perm[pos] = p;
       inv_perm[p] = pos;
@@ -139,7 +150,7 @@ hipError_t launch_dispatch(const int32_t *idx, const float *w, int64_t bt, int64
   const int nb = (int)((bt + 63) / 64);
   if (nb > 0) {
     err = launch_kernel(dispatch_mask_kernel, dim3(nb), dim3(256), sizeof(uint64_t) * E, s, idx,
-                        bt, (int)k, E, nb, masks, counts);
+                        bt, (int)k, E, nb, masks, counts, inv_perm);
     if (err != hipSuccess) return err;
   }
   err = launch_kernel(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, tile_bm, offsets,

@@ -265,3 +265,13 @@ def test_ffn_workspace_and_validation():
     w = moe.MoeFfnWeights(0, 0, 0, 0)
     # NULL weights are rejected before anything touches the device
     assert moe.moe_ffn_forward(c, w, 0, 0, 8, 0, 0, 0, 0) == -1
+
+
+def test_situ_eval_argument_errors_on_host():
+    """moe_situ_eval validates before any launch (no GPU needed)."""
+    assert moe.moe_situ_eval(0, 0, 0, 4.0, 25.0, 0, 0, 0, 0) == 0      # nothing to do
+    assert moe.moe_situ_eval(0, 0, -1, 4.0, 25.0, 0, 0, 0, 0) == -1
+    assert moe.moe_situ_eval(0, 0, 16, 4.0, 25.0, 0, 0, 0, 0) == -1     # NULL inputs
+    assert moe.moe_situ_eval(8, 8, 16, 4.0, 25.0, 0, 0, 0, 0) == -1     # no output
+    assert moe.moe_situ_eval(8, 8, 16, 0.0, 25.0, 8, 0, 0, 0) == -1     # beta <= 0
+    assert moe.moe_situ_eval(8, 8, 16, 4.0, -1.0, 8, 0, 0, 0) == -1     # beta_u <= 0
