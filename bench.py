@@ -92,17 +92,22 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when it is missing or the GEMM sources changed
-    since the counters were taken."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel sources changed since
+    the counters were taken.  Reads are the L2-to-memory read requests
+    (TCC_EA0_RDREQ_{32B,64B,128B} x their sizes) when the summary has them, else
+    FETCH_SIZE scaled by its reading for a plain copy of known size; writes are
+    WRITE_SIZE scaled the same way.  Returns (bytes, method)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     rec = json.load(open(path))
     k = rec.get("kernels", {}).get(kernel)
     if not k or rec.get("gemm_source_hash") != kernel_source_hash():
-        return None
-    return k["bytes_per_launch"]
+        return None, None
+    if k.get("ea_read_bytes") is not None:
+        return k["ea_read_bytes"] + k["write_bytes"], "TCC_EA0_RDREQ_* bytes + WRITE_SIZE (copy-calibrated)"
+    return k["bytes_per_launch"], "FETCH_SIZE + WRITE_SIZE (copy-calibrated)"
 
 
 def roofline_of(name, flops, nbytes, ms, peak_tflops=PEAK_BF16_TFLOPS):
@@ -191,7 +196,7 @@ def bench_ffn(args) -> int:
     work = ffn_phase_work(cfg)
     dom = max(phases, key=lambda n: phases[n][0])
     roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0])
-    roof["traffic"] = measured_traffic(cfg.name, dom)
+    roof["traffic"], roof["traffic_method"] = measured_traffic(cfg.name, dom)
     line = {
         "metric": "dense layer-1 FFN tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)",
         "value": cfg.bt * args.steps / dt,
@@ -232,10 +237,9 @@ def bench_tier(args, cfg) -> int:
     import torch
     import sparse_moe_layer_quantile_amd as moe
     import synth
-    from tests import parity
 
     torch.cuda.set_device(0)
-    layer, _ = parity.device_layer(cfg, seed=args.seed)
+    layer, _ = device_layer(cfg, args.seed)
     pool = [synth.device_layer(cfg, seed=1000 + i, names=["x"])["x"] for i in range(16)]
     mx = cfg.weight != "bf16"
     names = ["w_gate", "w_up", "w_down"] + (["e8_gate", "e8_up", "e8_down"] if mx else [])
@@ -324,12 +328,27 @@ def bench_tier(args, cfg) -> int:
     return 0
 
 
-def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
-    """The fp64 CPU oracle on a bounded sample of the same workload."""
+def cpu_baseline(cfg, seed: int, n_tokens: int, logits=None, threads=None) -> dict:
+    """The fp64 CPU oracle on a bounded sample of the same workload: on the
+    host's cores (OMP_NUM_THREADS) or on `threads` of them.  The batch
+    quantile runs on this batch's logits when given (else on a matrix of the
+    same shape)."""
     import oracle
     import synth
-    from tests import parity
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    saved = oracle.get_threads()
+    if threads is not None:
+        oracle.set_threads(threads)
+    try:
+        out = _cpu_baseline(cfg, seed, n_tokens, logits)
+    finally:
+        oracle.set_threads(saved)
+    return out
+
+
+def _cpu_baseline(cfg, seed, n_tokens, logits):
+    import oracle
+    import synth
+    cores = oracle.get_threads()
     n_params = sum(sp.numel for n, sp in synth.specs(cfg).items() if n != "x")
     if n_params <= 2e8:  # small layers: the whole oracle forward (weights held as fp64)
         lay = synth.host_layer(cfg, seed)
@@ -360,7 +379,8 @@ def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
     # batch quantile over a full-size logit matrix, amortised over the batch
     q = 0.0
     if cfg.cutoff == "batch":
-        zfull = rng.standard_normal((cfg.bt, cfg.n_experts), dtype=np.float32)
+        zfull = (np.ascontiguousarray(logits, np.float32) if logits is not None else
+                 rng.standard_normal((cfg.bt, cfg.n_experts), dtype=np.float32))
         t0 = time.perf_counter()
         alpha = oracle.quantile(zfull, cfg.quantile_rank)
         q = time.perf_counter() - t0
@@ -396,9 +416,9 @@ def cpu_baseline(cfg, seed: int, n_tokens: int) -> dict:
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"{len(tokens)} of {cfg.bt} tokens through router logits, top-k, "
                        f"W_down, {cfg.top_k} experts, combine+RMSNorm, W_up and shared "
-                       f"experts ({timed:.1f} s), plus the batch quantile over a full "
-                       f"{cfg.bt}x{cfg.n_experts} logit matrix ({q:.2f} s) amortised per "
-                       f"token; extrapolated to tokens/s")}
+                       f"experts ({timed:.1f} s), plus the batch quantile over the "
+                       f"{cfg.bt}x{cfg.n_experts} logits of the batch ({q:.2f} s) amortised "
+                       f"per token; extrapolated to tokens/s")}
 
 
 def backward_flops(cfg) -> float:
@@ -423,9 +443,8 @@ def bench_backward(args, cfg) -> int:
     (outside the timed region, as a training step takes it from its forward),
     gradients into preallocated fp32 tensors."""
     import torch
-    from tests import parity
     torch.cuda.set_device(0)
-    layer, x = parity.device_layer(cfg, seed=args.seed)
+    layer, x = device_layer(cfg, args.seed)
     gen = torch.Generator(device="cuda").manual_seed(args.seed + 7)
     dy = torch.randn((cfg.bt, cfg.d), generator=gen, device="cuda").to(torch.bfloat16)
     r = layer.route(x)
@@ -479,6 +498,10 @@ def main(argv=None):
     ap.add_argument("--config", default="k3_prefill_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens-1core", type=int, default=8,
+                    help="tokens of the one-core oracle timing")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the K3 decode and K3 fp8 prefill lines of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-streams", action="store_true",
                     help="run W_down_proj and the shared experts on a second stream (the "
@@ -510,57 +533,117 @@ def main(argv=None):
     if args.config in synth.FFN_CONFIGS:
         return bench_ffn(args)
 
-    import sparse_moe_layer_quantile_amd as moe
-    from tests import parity
-
     cfg = synth.CONFIGS[args.config]
     if args.backward:
         return bench_backward(args, cfg)
     if cfg.tier_slots > 0:
         return bench_tier(args, cfg)
     torch.cuda.set_device(0)
-    layer, x = parity.device_layer(cfg, seed=args.seed)
-    y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
-    side = torch.cuda.Stream() if args.two_streams else None
+    res = time_forward(cfg, args.seed, args.steps, args.warmup, args.two_streams,
+                       want_routing=True)
+    line = forward_line(cfg, args, res)
+    line["routing"] = routing_stats(cfg, res)
+    if not args.no_secondary and args.config == "k3_prefill_bf16":
+        line["secondary"] = {}
+        for name, steps in (("k3_decode_bf16", args.steps), ("k3_prefill_fp8", args.steps)):
+            c2 = synth.CONFIGS[name]
+            r2 = time_forward(c2, args.seed, steps, args.warmup, False)
+            l2 = forward_line(c2, args, r2)
+            line["secondary"][name] = {k: l2[k] for k in ("value", "unit", "ms_per_step",
+                                                           "roofline", "layer", "phases_ms")}
+    del res
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens,
+                                            logits=line["routing"].pop("_logits", None))
+        line["cpu_baseline_1core"] = cpu_baseline(cfg, args.seed, args.cpu_tokens_1core,
+                                                  threads=1)
+    line["routing"].pop("_logits", None)
+    print(json.dumps(line), flush=True)
+    return 0
 
-    # routing of this batch: experts touched (for the algorithmic byte count)
+
+def device_layer(cfg, seed):
+    """The layer's weights and tokens generated in HBM, as a StableLatentMoE."""
+    import torch
+    import sparse_moe_layer_quantile_amd as moe
+    import synth
+    lay = synth.device_layer(cfg, seed)
+    layer = moe.StableLatentMoE(moe.make_config(**synth.abi_config_args(cfg)),
+                                synth.abi_tensors(cfg, lay))
+    torch.cuda.synchronize()
+    return layer, lay["x"]
+
+
+def time_forward(cfg, seed, steps, warmup, two_streams, want_routing=False):
+    """steps timed forwards of the workload after warmup ones, inputs resident
+    in HBM.  Wall time per step between two device synchronisations, and each
+    phase's average from the HIP events the library records on the stream that
+    phase runs on."""
+    import torch
+    import sparse_moe_layer_quantile_amd as moe
+    layer, x = device_layer(cfg, seed)
+    y = torch.empty((cfg.bt, cfg.d), dtype=x.dtype, device="cuda")
+    side = torch.cuda.Stream() if two_streams else None
+    # this batch's routing: experts touched (for the algorithmic byte count)
     _, r = layer.forward(x, shared_stream=side, return_routing=True, out=y)
     counts = r["counts"].cpu().numpy()
-    touched = int((counts > 0).sum())
+    extra = {}
+    if want_routing:
+        extra = dict(logits=r["logits"].cpu().numpy(), cutoff=r["cutoff"].cpu().numpy(),
+                     idx=r["idx"].cpu().numpy())
     del r
-
     # warmup with phase events on, so the event pool is filled before timing
     moe.profile_enable(True)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.forward(x, shared_stream=side, out=y)
     torch.cuda.synchronize()
     moe.profile_read()
-    # timed region; every phase is bracketed by HIP events recorded on the
-    # stream that phase runs on, read back after the region
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         layer.forward(x, shared_stream=side, out=y)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    ms_step = dt * 1e3 / args.steps
     phases = moe.profile_read()
     moe.profile_enable(False)
+    del layer, x, y
+    torch.cuda.empty_cache()
+    return dict(dt=dt, steps=steps, warmup=warmup, ms_step=dt * 1e3 / steps, phases=phases,
+                counts=counts, two_streams=two_streams, **extra)
 
+
+def forward_line(cfg, args, res) -> dict:
+    """The JSON line of one forward workload from time_forward's result."""
+    import synth
+    counts = res["counts"]
+    touched = int((counts > 0).sum())
+    phases = res["phases"]
+    ms_step = res["ms_step"]
     work = phase_work(cfg, touched)
     dom = max(phases, key=lambda n: phases[n][0])
     a8 = cfg.act_quant == "mxfp8"
     # the routed experts' GEMMs on MX FP8 inputs run the block-scaled MFMA at the fp8 rate
     peak = PEAK_FP8_TFLOPS if a8 and dom.startswith("expert_") else PEAK_BF16_TFLOPS
     roof = roofline_of(dom, work[dom][0], work[dom][1], phases[dom][0], peak)
-    roof["traffic"] = measured_traffic(cfg.name, dom)
+    roof["traffic"], roof["traffic_method"] = measured_traffic(cfg.name, dom)
     layer_flops = cfg.flops()
-    line = {
+    weight_bytes = sum(sp.nbytes + (sp.n_scale_blocks * (1 if sp.dtype in synth.MX_DTYPES else 4)
+                                    if sp.dtype in (synth.FP8, *synth.MX_DTYPES) else 0)
+                       for n, sp in synth.specs(cfg).items() if n != "x")
+    # weights a step reads: the dense ones and each touched expert once
+    sp = synth.specs(cfg)
+    per_expert = sum(sp[n].nbytes + (sp[n].n_scale_blocks * (1 if sp[n].dtype in synth.MX_DTYPES
+                                                              else 4)
+                                     if sp[n].dtype in (synth.FP8, *synth.MX_DTYPES) else 0)
+                     for n in ("w_gate", "w_up", "w_down")) / cfg.n_experts
+    read_bytes = weight_bytes - (cfg.n_experts - touched) * per_expert + 2 * cfg.bt * cfg.d * 2
+    return {
         "metric": METRIC,
-        "value": cfg.bt * args.steps / dt,
+        "value": cfg.bt * res["steps"] / res["dt"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": res["steps"],
+        "warmup": res["warmup"],
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -574,22 +657,40 @@ def main(argv=None):
                    "shared_inter": cfg.shared_inter, "weights": cfg.weight,
                    "expert_inputs": "mxfp8" if a8 else cfg.act,
                    "cutoff": cfg.cutoff, "router_bias": cfg.bias,
-                   "parallelism": "1 GPU", "streams": 2 if args.two_streams else 1},
+                   "parallelism": "1 GPU", "streams": 2 if res["two_streams"] else 1},
         "roofline": roof,
         "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": layer_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                   "experts_touched": touched,
-                  "weight_gb": sum(sp.nbytes + (sp.n_scale_blocks * (1 if sp.dtype in synth.MX_DTYPES else 4)
-                                                if sp.dtype in (synth.FP8, *synth.MX_DTYPES) else 0)
-                                   for n, sp in synth.specs(cfg).items() if n != "x") / 1e9},
+                  "weight_gb": weight_bytes / 1e9,
+                  # weight-streaming view: every byte a step must read (touched
+                  # experts once, dense weights, x and y) over the step time
+                  "read_gb": read_bytes / 1e9,
+                  "hbm_gbs": read_bytes / (ms_step * 1e-3) / 1e9,
+                  "hbm_frac": read_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9)},
         "phases_ms": {n: round(v[0], 4) for n, v in phases.items()},
         "kernel_sources": kernel_source_hash(),
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens)
-    print(json.dumps(line), flush=True)
-    return 0
+
+
+def routing_stats(cfg, res) -> dict:
+    """Per-expert load of the timed batch (max and min over the mean bt k / E)
+    and its near ties: tokens whose k-th and (k+1)-th best cutoff-adjusted
+    scores sigmoid(z - alpha) are within 1e-6 (the band inside which the
+    selection is allowed to differ from the oracle's)."""
+    counts = res["counts"].astype(np.float64)
+    mean = cfg.bt * cfg.top_k / cfg.n_experts
+    out = {"load_max_over_mean": float(counts.max() / mean),
+           "load_min_over_mean": float(counts.min() / mean)}
+    z = res.get("logits")
+    if z is not None and cfg.top_k < cfg.n_experts:
+        r = (z - res["cutoff"][None, :].astype(np.float32)).astype(np.float32)
+        part = -np.partition(-r, (cfg.top_k - 1, cfg.top_k), axis=1)
+        s = 1.0 / (1.0 + np.exp(-part[:, cfg.top_k - 1:cfg.top_k + 1].astype(np.float64)))
+        out["near_tie_tokens"] = int((s[:, 0] - s[:, 1] <= 1e-6).sum())
+        out["_logits"] = z
+    return out
 
 
 if __name__ == "__main__":
