@@ -202,6 +202,25 @@ moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *
                        void *y, moe_route_out *route, moe_dispatch_out *disp, void *ws,
                        size_t ws_bytes, void *stream, void *shared_stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results, with the workspace taken from a library-held
+ * device array of MOE_NOALLOC_SCRATCH_BYTES (128 MiB) instead of a caller
+ * buffer.  Each GPU the library runs on holds its own array from the first
+ * call there until the process ends; the call allocates nothing (no hipMalloc,
+ * no hipFree).  Every call on a GPU shares that GPU's array and leaves its
+ * contents behind: calls that overlap on one GPU (on different streams or
+ * from several host threads) race and give undefined results, so order them
+ * on one stream.  A batch whose moe_workspace_bytes(cfg, bt) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE before anything is
+ * enqueued (K3 decode shapes, d 7168 and 896 experts, fit up to 64 tokens).
+ * The two-stream join takes events from the library's pool (created on first
+ * use; events are not device memory). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                               int64_t bt, void *y, moe_route_out *route,
+                               moe_dispatch_out *disp, void *stream, void *shared_stream);
+
 /* ---- backward pass ---------------------------------------------------------------
  * Gradients of a loss with respect to x and every weight, given dL/dy.  The
  * pages describe the forward only (tech.news18a.com page: the architecture

@@ -125,6 +125,9 @@ def _load():
                                 CP(MoeRouteOut), CP(MoeDispatchOut), _P, ctypes.c_size_t, _P,
                                 _P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [CP(MoeConfig), CP(MoeWeights), _P, ctypes.c_int64, _P,
+                                        CP(MoeRouteOut), CP(MoeDispatchOut), _P, _P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_ffn_workspace_bytes.argtypes = [CP(MoeFfnConfig), ctypes.c_int64]
     lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_ffn_forward.argtypes = [CP(MoeFfnConfig), CP(MoeFfnWeights), _P, _P, ctypes.c_int64,
@@ -171,7 +174,10 @@ EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
             "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select",
             "moe_cutoff_update", "moe_backward_workspace_bytes", "moe_backward",
-            "moe_situ_eval")
+            "moe_situ_eval", "moe_forward_noalloc")
+
+# bytes of the library-held workspace of moe_forward_noalloc (one array per GPU)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def cutoff_update(alpha, zeta, rate: float):
@@ -359,6 +365,15 @@ def moe_forward(cfg, weights: MoeWeights, x: int, bt: int, y: int, route, disp, 
                            _P(y or None), ctypes.byref(route) if route is not None else None,
                            ctypes.byref(disp) if disp is not None else None, _P(ws or None),
                            ws_bytes, _P(stream or None), _P(shared_stream or None))
+
+
+def moe_forward_noalloc(cfg, weights: MoeWeights, x: int, bt: int, y: int, route, disp,
+                        stream: int, shared_stream: int = 0) -> int:
+    return LIB.moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _P(x or None), bt,
+                                   _P(y or None),
+                                   ctypes.byref(route) if route is not None else None,
+                                   ctypes.byref(disp) if disp is not None else None,
+                                   _P(stream or None), _P(shared_stream or None))
 
 
 def profile_enable(on: bool) -> None:

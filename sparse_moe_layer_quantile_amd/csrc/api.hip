@@ -667,6 +667,54 @@ MOE_API moe_status moe_forward(const moe_config *cfg, const moe_weights *w, cons
   return MOE_OK;
 }
 
+// ---- moe_forward without a caller workspace ------------------------------------------
+// For callers that cannot allocate device memory: the workspace is a
+// file-scope device array of MOE_NOALLOC_SCRATCH_BYTES, one per GPU, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+
+namespace {
+
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void *>> g_scratch_ptr;  // (device, address of scratch there)
+
+moe_status scratch_of_current_device(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  for (auto &dp : g_scratch_ptr)
+    if (dp.first == dev) {
+      *out = dp.second;
+      return MOE_OK;
+    }
+  void *ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+    return MOE_ERR_HIP;
+  g_scratch_ptr.emplace_back(dev, ptr);
+  *out = ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w,
+                                       const void *x, int64_t bt, void *y, moe_route_out *route,
+                                       moe_dispatch_out *disp, void *stream,
+                                       void *shared_stream) {
+  Plan p;
+  moe_status st = make_plan(cfg, bt, &p);
+  if (st != MOE_OK) return st;
+  if (p.total - kAlign > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  // moe_forward zeroes what must start at zero (the per-expert counts) itself
+  return moe_forward(cfg, w, x, bt, y, route, disp, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
+                     shared_stream);
+}
+
 // ---- dense layer-1 FFN ------------------------------------------------------------
 // RMSNorm -> n, gate/up + SiTU -> h, down + residual -> y, all on `stream`
 // (mkdocs.reaper.mx "Vue d'ensemble de l'architecture": layer 1 is a dense
