@@ -7,7 +7,8 @@ Comparison rules:
     sigmoid(z - alpha) within TIE_BAND, and such tokens are logged.
   * floating-point outputs: normwise max relative error
     max|y - y_ref| / max|y_ref| within TOL[dtype] (bf16 2e-2, fp8-weight 6e-2,
-    fp32 1e-4), on the tokens whose routing matches.  MXFP4 experts take the
+    fp32 1e-4), on the tokens whose routing matches; and every element within
+    the same tolerance of max(|y_ref_i|, max|y_ref| / 2) (ELEM_FLOOR_ASSERT).  MXFP4 experts take the
     bf16 bound: their weights widen to bf16 exactly, so the arithmetic and its
     roundings are those of the bf16 path.
 """
@@ -81,16 +82,32 @@ def elementwise_err(y, ref, floor=ELEM_FLOOR) -> float:
     return float((np.abs(y - ref) / den).max())
 
 
-def assert_close(y, ref, tol, what=""):
-    """Normwise error within tol, and the element-wise errors at the floors
-    ELEM_CHECKS lists within theirs; every figure is printed."""
+# Element-wise bound asserted beside the normwise one: every element within tol
+# of max(|its reference|, ELEM_FLOOR_ASSERT * max|reference|).  The GPU holds
+# x_lat, h, o, n, hs and y in bf16, so each output element carries rounding
+# noise of a fixed absolute size (about 1e-3 of the largest output; measured
+# normwise errors 3-5e-3 over 1e5-1e6 elements), not one proportional to the
+# element: elements far below the maximum cannot be held to tol of their own
+# size, and the 1e-3 floor of the plain reading is reported, not asserted.  At
+# half the maximum, the bound is twice as strict as the normwise one on every
+# smaller element and relative on the largest.
+ELEM_FLOOR_ASSERT = 0.5
+
+
+def assert_close(y, ref, tol, what="", elem_floor=ELEM_FLOOR_ASSERT):
+    """Normwise error within tol, and (unless elem_floor is None) the
+    element-wise error with that floor within tol; the element-wise errors at
+    several floors are printed."""
     y = np.asarray(y, np.float64)
     ref = np.asarray(ref, np.float64)
     nw = normwise_err(y, ref)
-    ew = {f: elementwise_err(y, ref, f) for f in (1e-3, 1e-2, 1e-1, 0.25)}
+    ew = {f: elementwise_err(y, ref, f) for f in (ELEM_FLOOR, 1e-2, 1e-1, 0.25, 0.5)}
     print(f"  {what} normwise {nw:.3e} (tol {tol}); elementwise "
           + " ".join(f"floor {f:g}: {v:.3e}" for f, v in ew.items()), flush=True)
     assert nw <= tol, f"{what}: normwise error {nw:.3e} above {tol}"
+    if elem_floor is not None:
+        e = elementwise_err(y, ref, elem_floor)
+        assert e <= tol, f"{what}: element-wise error {e:.3e} (floor {elem_floor}) above {tol}"
     return nw, ew
 
 

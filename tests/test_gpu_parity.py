@@ -197,7 +197,7 @@ def test_forward_mxfp4_every_tile_shape(shape_id, monkeypatch):
     _mxfp4_check(cfg, "batch")
 
 
-def _mxfp4_check(cfg, cutoff):
+def _mxfp4_check(cfg, cutoff, elem_floor=parity.ELEM_FLOOR_ASSERT):
     layer, x = parity.device_layer(cfg, seed=0, cutoff=cutoff)
     y, r = layer.forward(x, return_routing=True)
     torch.cuda.synchronize()
@@ -208,7 +208,8 @@ def _mxfp4_check(cfg, cutoff):
     assert not bad
     keep = np.setdiff1d(np.arange(cfg.bt), diff)
     say(f"  near ties {len(diff)}")
-    parity.assert_close(parity.y_to_f64(y)[keep], ref["y"][keep], parity.tol_of(cfg), "y")
+    parity.assert_close(parity.y_to_f64(y)[keep], ref["y"][keep], parity.tol_of(cfg), "y",
+                        elem_floor=elem_floor)
 
 
 # ---- MX FP8 expert inputs (MXFP4 weights, block-scaled MFMA) --------------------------------
@@ -303,7 +304,10 @@ def test_forward_mx8_inputs_against_codes_on_exact_values(weight, monkeypatch):
     monkeypatch.setattr(oracle, "MX_CODES_ON_BF16", False)
     cfg = synth.CONFIGS["mid_bf16"].with_(weight=weight, act_quant="mxfp8", bt=4096)
     say("forward mx8 inputs, oracle codes on exact values", weight)
-    _mxfp4_check(cfg, "batch")
+    # normwise only: a code decided on a value one bf16 rounding away moves by a
+    # whole e4m3 step (about 6 %), and the two oracles differ by 2-5 % of an
+    # expert's largest output (measured on the CPU)
+    _mxfp4_check(cfg, "batch", elem_floor=None)
 
 
 @pytest.mark.parametrize("weight", ["mxfp4", "mxfp8"])
