@@ -149,6 +149,14 @@ __device__ __forceinline__ void dma4(const void *g, void *lds_wave_base) {
 __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
 }
+// A wave-uniform address, moved to scalar registers (the SGPR-base form of
+// the DMA needs it there when the compiler cannot prove it uniform).
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char *>((uint64_t)hi << 32 | lo);
+}
 __device__ __forceinline__ void dma16_asm(const char *sbase, uint32_t voff, void *lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -308,10 +316,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
                 "gate/up split on a scale instruction");
   static_assert(LMAX + LS + LSA < 64 / (STAGES > 2 ? STAGES - 2 : 1), "vmcnt range");
   static_assert(!A8 || (BK >= 128 && MA == 0), "MX FP8 A: K tile of 128 or more");
-  // multi-segment problems keep whole A and B rounds per wave
-  constexpr int A_LD = TA / NW, B_LD = TB / NW;
-  static_assert(!MSEG || (TA % NW == 0 && TB % NW == 0), "segmented: whole DMA rounds");
-  static_assert(!MSEG || !DUAL, "segmented problems are single");
+  static_assert(!MSEG || (!DUAL && !A8 && !MXB && MA == 0), "segmented problems: single, bf16 A");
   constexpr int L = LMAX;
   static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
   static_assert(!GATHER || !MSEG, "gathered A has one K segment");
@@ -413,37 +418,6 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // the last instruction slot of this wave carries an instruction
   const bool has_last = EVEN || wave + NW * (LMAX - 1) < TT;
 
-  // ---- per-lane source rows (segmented problems) ----------------------------
-  // A: instruction i of this wave fills tile rows (wave + NW i) * RPI + rsub.
-  int32_t a_row[MSEG ? A_LD : 1];
-  int32_t b_row[MSEG ? B_LD : 1];
-  if constexpr (MSEG) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int r = (wave + NW * i) * RPI + rsub;
-      int64_t m = tile.m0 + r;
-      if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
-      a_row[i] = (int32_t)m;
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int r = (wave + NW * i) * RPI_B + lane / CPR_B;
-      int64_t n = tile.n0 + r;
-      if (n >= args.N) n = tile.n0;
-      b_row[i] = (int32_t)n;
-    }
-  }
-  // B chunk of a segmented problem's lanes (same argument as for A)
-  const int fetch_chunk_b = (lane % CPR_B) ^ swz(wave * RPI_B + lane / CPR_B, CPR_B);
-  // (segmented problems are dense: no expert offset)
-  const uint16_t *b0 = static_cast<const uint16_t *>(args.seg[0].b);
-  // chunk a lane of a segmented problem fetches so that the DMA slot order
-  // realises the swizzle: instruction i of the wave fills region rows
-  // (wave + NW i) RPI + rsub, whose swizzle key (4 (wave + NW i) + rsub /
-  // (16 / CPR)) % CPR does not depend on i (CPR divides 4 NW)
-  static_assert(!MSEG || CPR <= 16, "segmented problems: K tile up to 64");
-  const int fetch_chunk = slot ^ swz(wave * RPI + rsub, CPR);
-
   // ---- K segments -------------------------------------------------------------
   int ktiles = (int)(args.seg[0].k / BK);
   if constexpr (MSEG) {
@@ -459,50 +433,6 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     k_begin = (int)blockIdx.y * kper;
     ktiles = min(ktiles - k_begin, kper);
   }
-
-  // Prefetch cursor over (segment, K tile); segment fields are reloaded from
-  // the kernel arguments (scalar loads) only when it crosses a boundary.
-  int cur_seg = 0, cur_k = 0, cur_nk = (int)(args.seg[0].k / BK);
-  const uint16_t *cur_a = static_cast<const uint16_t *>(args.seg[0].a);
-  const char *cur_b = reinterpret_cast<const char *>(b0);
-  int64_t cur_lda = args.seg[0].lda, cur_ldb = args.seg[0].ldb;
-  if constexpr (MSEG) {
-    int skip = k_begin;
-    while (skip >= cur_nk) {
-      skip -= cur_nk;
-      const GemmSeg *sg = &args.seg[++cur_seg];
-      cur_a = static_cast<const uint16_t *>(sg->a);
-      cur_b = static_cast<const char *>(sg->b);
-      cur_lda = sg->lda;
-      cur_ldb = sg->ldb;
-      cur_nk = (int)(sg->k / BK);
-    }
-    cur_k = skip;
-  }
-
-  auto issue = [&](int kt) G2_INL {
-    if (MSEG && cur_k == cur_nk) {
-      ++cur_seg;
-      const GemmSeg *sg = &args.seg[cur_seg];
-      cur_a = static_cast<const uint16_t *>(sg->a);
-      cur_b = static_cast<const char *>(sg->b);
-      cur_lda = sg->lda;
-      cur_ldb = sg->ldb;
-      cur_nk = (int)(sg->k / BK);
-      cur_k = 0;
-    }
-    const int64_t k0 = (int64_t)cur_k * BK + fetch_chunk * 8;
-    char *st = smem + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      dma16(cur_a + (int64_t)a_row[i] * cur_lda + k0, st + (wave + NW * i) * 1024);
-    static_assert(RPI * RB == 1024, "one DMA instruction fills 1 KB");
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      dma16(cur_b + ((int64_t)b_row[i] * cur_ldb + (int64_t)cur_k * BK) * BNUM / BDEN + fetch_chunk_b * 16,
-            st + A_BYTES + (wave + NW * i) * 1024);
-    ++cur_k;
-  };
 
   // valid 32-row sub-blocks of this wave: sub-block i of wave row wm covers
   // tile rows (i WM + wm) 32 ..+32, so a partial tile spreads over both wave
@@ -521,20 +451,23 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Single-segment problems: every DMA source is a uniform base plus a 32-bit
-  // per-lane byte offset (global_load_lds with an SGPR base).  Contiguous A
-  // and B are addressed from the tile's first row, so the offsets stay below
-  // TM (TN) rows; gathered A is addressed from the matrix start, which holds
-  // as long as the gathered matrix is under 4 GiB.
+  // Every DMA source is a uniform base plus a 32-bit per-lane byte offset
+  // (global_load_lds with an SGPR base).  Contiguous A and B are addressed
+  // from the tile's first row, so the offsets stay below TM (TN) rows;
+  // gathered A is addressed from the matrix start, which holds as long as the
+  // gathered matrix is under 4 GiB.
+  const int64_t cur_lda = args.seg[0].lda, cur_ldb = args.seg[0].ldb;
   const char *a_base = nullptr, *b_base = nullptr, *bu_base = nullptr;
-  uint32_t off[MSEG ? 1 : LMAX];
+  // single segment: byte offset of each instruction slot; K-segmented: the
+  // slot's tile row << 8 | its 16-byte chunk (the row stride is the segment's)
+  uint32_t off[LMAX];
   // uniform source base of each instruction slot (an integer: a select
   // between captured pointers would be lowered through the stack)
   uint64_t dbase[MSEG ? 1 : LMAX];
   if constexpr (!MSEG) {
     const int64_t a_first = GATHER ? 0 : tile.m0;
     const int64_t kb0 = (int64_t)k_begin * BK;
-    a_base = reinterpret_cast<const char *>(cur_a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
+    a_base = static_cast<const char *>(args.seg[0].a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
     const char *bsrc = static_cast<const char *>(args.seg[0].b);
     const char *busrc = static_cast<const char *>(args.b_up);
     if (args.b_tab != nullptr) {  // per-expert addresses (tiered experts)
@@ -546,34 +479,88 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
     b_base = bsrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
     if constexpr (DUAL) bu_base = busrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
+  }
 #pragma unroll
-    for (int d = 0; d < LMAX; ++d) {
-      const int g = wave + NW * d;
-      uint32_t o = 0;
+  for (int d = 0; d < LMAX; ++d) {
+    const int g = wave + NW * d;
+    uint32_t o = 0;
+    if constexpr (!MSEG) {
       uint64_t bsel = reinterpret_cast<uint64_t>(a_base);
       if (g >= TA)
         bsel = reinterpret_cast<uint64_t>((DUAL && g - TA >= TB / 2) ? bu_base : b_base);
       dbase[d] = bsel;
-      // lane l of an instruction fills 16 B slot l % CPR of tile row l / CPR
-      // and fetches the chunk that the swizzle puts there
-      if (g < TA) {
-        const int r = g * RPI + lane / CPR;
-        const int ch = (lane % CPR) ^ swz(r, CPR);
-        int64_t m = tile.m0 + r;
-        if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+    }
+    // lane l of an instruction fills 16 B slot l % CPR of tile row l / CPR
+    // and fetches the chunk that the swizzle puts there
+    if (g < TA) {
+      const int r = g * RPI + lane / CPR;
+      const int ch = (lane % CPR) ^ swz(r, CPR);
+      int64_t m = tile.m0 + r;
+      if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+      if constexpr (MSEG) {
+        o = (uint32_t)(m - tile.m0) << 8 | (uint32_t)ch;
+      } else {
+        const int64_t a_first = GATHER ? 0 : tile.m0;
         if constexpr (GATHER) m = args.gather[m] / args.gather_div;
         o = (uint32_t)((m - a_first) * cur_lda * (A8 ? 1 : 2) + ch * 16);
-      } else if (g < TT) {
-        // B rows from TN/2 on are the up rows of a dual problem
-        const int rb = (g - TA) * RPI_B + lane / CPR_B;
-        const int ch = (lane % CPR_B) ^ swz(rb, CPR_B);
-        int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
-        if (n >= args.N) n = tile.n0;
-        o = (uint32_t)((n - tile.n0) * cur_ldb * BNUM / BDEN + ch * 16);
       }
-      off[d] = o;
+    } else if (g < TT) {
+      // B rows from TN/2 on are the up rows of a dual problem
+      const int rb = (g - TA) * RPI_B + lane / CPR_B;
+      const int ch = (lane % CPR_B) ^ swz(rb, CPR_B);
+      int64_t n = tile.n0 + ((DUAL && rb >= TN / 2) ? rb - TN / 2 : rb);
+      if (n >= args.N) n = tile.n0;
+      if constexpr (MSEG) o = (uint32_t)(n - tile.n0) << 8 | (uint32_t)ch;
+      else o = (uint32_t)((n - tile.n0) * cur_ldb * BNUM / BDEN + ch * 16);
+    }
+    off[d] = o;
+  }
+  // K-segmented problems: first global K tile, sources and strides of each
+  // segment, read from the kernel arguments once (scalar registers), so that
+  // the DMAs select a segment with scalar compares inside the K loop
+  int seg_k0[MSEG ? 5 : 1];
+  uint64_t seg_a[MSEG ? 5 : 1], seg_b[MSEG ? 5 : 1];
+  uint32_t seg_lda[MSEG ? 5 : 1], seg_ldb[MSEG ? 5 : 1];
+  if constexpr (MSEG) {
+    int k0 = 0;
+#pragma unroll
+    for (int sgi = 0; sgi < 5; ++sgi) {
+      const GemmSeg &sg = args.seg[sgi];
+      const bool used = sgi < args.nseg;
+      seg_k0[sgi] = used ? k0 : INT32_MAX;
+      seg_a[sgi] = reinterpret_cast<uint64_t>(static_cast<const char *>(sg.a) + tile.m0 * sg.lda * 2);
+      seg_b[sgi] =
+          reinterpret_cast<uint64_t>(static_cast<const char *>(sg.b) + tile.n0 * sg.ldb * BNUM / BDEN);
+      seg_lda[sgi] = (uint32_t)(sg.lda * 2);
+      seg_ldb[sgi] = (uint32_t)(sg.ldb * BNUM / BDEN);
+      if (used) k0 += (int)(sg.k / BK);
     }
   }
+  // the sources of the K tile whose DMAs are issued next (K-segmented
+  // problems; set once per tile by seg_select, branch-free)
+  uint64_t ms_a = 0, ms_b = 0;
+  uint32_t ms_lda = 0, ms_ldb = 0;
+  auto seg_select = [&](int kt) G2_INL {
+    if constexpr (MSEG) {
+      const int kg = k_begin + kt;
+      uint64_t a = seg_a[0], b = seg_b[0];
+      uint32_t la = seg_lda[0], lb = seg_ldb[0];
+      int k0 = 0;
+#pragma unroll
+      for (int sgi = 1; sgi < 5; ++sgi) {
+        const bool in = kg >= seg_k0[sgi];
+        a = in ? seg_a[sgi] : a;
+        b = in ? seg_b[sgi] : b;
+        la = in ? seg_lda[sgi] : la;
+        lb = in ? seg_ldb[sgi] : lb;
+        k0 = in ? seg_k0[sgi] : k0;
+      }
+      ms_a = a + (uint64_t)(kg - k0) * RB;
+      ms_b = b + (uint64_t)(kg - k0) * RB_B;
+      ms_lda = la;
+      ms_ldb = lb;
+    }
+  };
   // MXFP4 scale instructions of this wave: instruction gs = wave + NW q fills
   // bytes 256 gs.. of the stage's code area; lane l copies dword w of the
   // codes of tile row rr (the B row numbering: dual up rows from TN/2), from
@@ -624,7 +611,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       if (!has_last) return;
     }
     const int g = wave + NW * d;
-    const char *base = reinterpret_cast<const char *>(dbase[d]);
+    if constexpr (MSEG) {
+      // the sources seg_select chose for this K tile
+      const bool is_a = g < TA;
+      const char *base = uniform_ptr(reinterpret_cast<const char *>(is_a ? ms_a : ms_b));
+      uint32_t o = __umul24(off[d] >> 8, is_a ? ms_lda : ms_ldb) + (off[d] & 0xFFu) * 16u;
+      if constexpr (BF != BF_BF16) {
+        dma16_asm(base, o, smem + st * STAGE_BYTES + g * 1024);
+      } else {
+        asm volatile("" : "+v"(o));
+        dma16(base + o, smem + st * STAGE_BYTES + g * 1024);
+      }
+      return;
+    }
+    const char *base = reinterpret_cast<const char *>(dbase[MSEG ? 0 : d]);
     // (builtin form: the empty asm re-issues the 32-bit offset inside the loop
     // body, so the instruction selector sees uniform base + zext(offset) there
     // (SGPR-base form) instead of a 64-bit address hoisted out of the loop)
@@ -910,7 +910,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     constexpr int KS = BK / 16;   // k steps per stage
     constexpr int NF = NS + FRN;  // fragment reads per k step
     constexpr int Q = NS * FRN;   // MFMAs per k step
-    if constexpr (!MSEG) {
+    {
       // tile t of the T = nper ktiles of this workgroup: N tile t / ktiles,
       // K tile t % ktiles
       const int T = nper * ktiles;
@@ -918,6 +918,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       for (int p = 0; p < STAGES - 1; ++p) {
         const int tp = p < T ? p : T - 1;
         const int jp = PN ? tp / ktiles : 0;
+        seg_select(tp - jp * ktiles);
         static_for<L>([&](auto d) G2_INL { dma_one(d, tp - jp * ktiles, p, jp); });
         dma_scales(tp - jp * ktiles, p, jp);
         dma_ascales(tp - jp * ktiles, p);
@@ -932,6 +933,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         const int dj = PN ? kdt / ktiles : 0;
         const int kdc = kdt - dj * ktiles;
         const int dst = kd % STAGES;
+        seg_select(kdc);
         if constexpr (A8) {
           // block-scaled MFMA: all loads of the tile STAGES - 1 ahead first, then
           // per 64-wide k step the operands and scales of NS x FRN
@@ -1120,48 +1122,6 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         }
       }
       wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
-    } else {
-#pragma unroll
-      for (int p = 0; p < STAGES - 1; ++p)
-        if (p < ktiles) issue(p);
-      for (int kt = 0; kt < ktiles; ++kt) {
-        // tile kt landed: at most (STAGES - 2) later tiles may still be in flight
-        if (kt + STAGES - 2 < ktiles) wait_vmcnt<L * (STAGES - 2)>();
-        else wait_vmcnt<0>();
-        barrier();
-        const char *st = smem + (kt % STAGES) * STAGE_BYTES;
-        // a segment switch waits on scalar loads (lgkmcnt), which would also
-        // wait for LDS reads in flight: issue first, then read fragments
-        if (kt + STAGES - 1 < ktiles) issue(kt + STAGES - 1);
-        if constexpr (NS > 0) {
-          bf16x8 fa[NA], fb[FRN];
-          uint4 braw[B8 ? FRN : 1];
-          float bsc[B8 ? FRN : 1];
-          if constexpr (B8) static_for<FRN>([&](auto j) G2_INL { bsc[j] = scale_b8(kt, j); });
-          static_for<KS>([&](auto ks_tag) G2_INL {
-            constexpr int ks = decltype(ks_tag)::value;
-            static_for<NF>([&](auto f) G2_INL {
-              if constexpr (f >= FRN || !B8) read_frag(st, ks, f, fa, fb);
-            });
-            if constexpr (B8) {
-              // fp8 B: an even step reads the codes of the step pair
-              static_for<FRN>([&](auto j) G2_INL {
-                if constexpr (ks % 2 == 0) {
-                  read_b8(st, ks / 2, j, braw);
-                  fb[j] = e4m3x8_to_bf16(braw[j].x, braw[j].y, bsc[j]);
-                } else {
-                  fb[j] = e4m3x8_to_bf16(braw[j].z, braw[j].w, bsc[j]);
-                }
-              });
-            }
-#pragma unroll
-            for (int i = 0; i < NS; ++i)
-#pragma unroll
-              for (int j = 0; j < FRN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-          });
-        }
-      }
     }
   };
   // one specialised copy of the K loop per number of active sub-blocks
