@@ -414,6 +414,36 @@ int64_t moe_tier_select(const float *score, const uint8_t *resident, int64_t E, 
 moe_status moe_mx8_quantize(const void *x, int64_t n, uint8_t *codes, uint8_t *scales,
                             void *stream);
 
+/* ---- bf16 contraction on the layer's GEMM engine --------------------------------
+ * C = op(A) op(B) (+ C_in) with bf16 operands, fp32 accumulation and output:
+ * the forms the backward pass runs its contractions in.  A is [M][K]
+ * (a_kouter = 0, row stride lda >= K) or K-outer [K][M] (a_kouter = 1, lda >=
+ * M); B is [N][K] (b_kouter = 0, ldb >= K) or K-outer [K][N] (b_kouter = 1,
+ * ldb >= N); C [M][ldc] fp32.  c_in (may be c) is added when given.
+ * With k_offsets (device, n_experts + 1 ascending row indices), both operands
+ * K-outer: n_experts outputs C_e = [M][N] at c + e M ldc, each over the K rows
+ * k_offsets[e] .. k_offsets[e + 1] of A and B (an expert without rows gets
+ * zeros) -- the routed experts' weight gradients; K is then unused.
+ * Limits: K-outer operands' rows (M or N) and the strides multiples of 8;
+ * unless both operands are K-outer, K a multiple of 64; a K-outer A needs a
+ * K-outer B.  Else MOE_ERR_UNSUPPORTED.  Asynchronous on `stream`; no
+ * workspace, no allocation. */
+typedef struct moe_gemm_desc {
+  int64_t M, N, K;
+  const void *a;
+  int64_t lda;
+  int32_t a_kouter;
+  const void *b;
+  int64_t ldb;
+  int32_t b_kouter;
+  float *c;
+  int64_t ldc;
+  const float *c_in;
+  const int32_t *k_offsets;
+  int64_t n_experts;
+} moe_gemm_desc;
+moe_status moe_gemm_bf16(const moe_gemm_desc *desc, void *stream);
+
 /* ---- SiTU-GLU numerics ---------------------------------------------------------
  * The SiTU-GLU factors on the device, elementwise, by the same inline device
  * functions the GEMM epilogues use (tech.news18a.com page, first technique:

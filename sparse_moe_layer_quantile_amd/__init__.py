@@ -92,6 +92,14 @@ class MoeGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
+class MoeGemmDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a", _P), ("lda", ctypes.c_int64), ("a_kouter", ctypes.c_int32),
+                ("b", _P), ("ldb", ctypes.c_int64), ("b_kouter", ctypes.c_int32),
+                ("c", _P), ("ldc", ctypes.c_int64), ("c_in", _P), ("k_offsets", _P),
+                ("n_experts", ctypes.c_int64)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)} ({status})")
@@ -152,6 +160,8 @@ def _load():
     lib.moe_tier_select.restype = ctypes.c_int64
     lib.moe_mx8_quantize.argtypes = [_P, ctypes.c_int64, _P, _P, _P]
     lib.moe_mx8_quantize.restype = ctypes.c_int
+    lib.moe_gemm_bf16.argtypes = [CP(MoeGemmDesc), _P]
+    lib.moe_gemm_bf16.restype = ctypes.c_int
     lib.moe_situ_eval.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_float, _P, _P,
                                   _P, _P]
     lib.moe_situ_eval.restype = ctypes.c_int
@@ -174,7 +184,7 @@ EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_forward",
             "moe_mx8_quantize", "moe_tier_slot_bytes", "moe_tier_create", "moe_tier_plan",
             "moe_tier_observe", "moe_tier_get_stats", "moe_tier_destroy", "moe_tier_select",
             "moe_cutoff_update", "moe_backward_workspace_bytes", "moe_backward",
-            "moe_situ_eval", "moe_forward_noalloc")
+            "moe_situ_eval", "moe_forward_noalloc", "moe_gemm_bf16")
 
 # bytes of the library-held workspace of moe_forward_noalloc (one array per GPU)
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -281,6 +291,25 @@ def moe_situ_eval(g: int, u: int, n: int, beta: float, beta_u: float, phi: int, 
     return LIB.moe_situ_eval(_P(g or None), _P(u or None), n, float(beta), float(beta_u),
                              _P(phi or None), _P(psi or None), _P(h or None),
                              _P(stream or None))
+
+
+def gemm_bf16(a, b, a_kouter=False, b_kouter=False, c_in=None, k_offsets=None, out=None):
+    """fp32 op(A) op(B) (+ c_in) on the engine: A [M][K] or, K-outer, [K][M];
+    B [N][K] or, K-outer, [K][N] (bf16 device tensors).  With k_offsets
+    (int32 [E + 1]): E outputs [M][N], expert e over K rows k_offsets[e]..[e+1]."""
+    import torch
+    M = a.shape[1] if a_kouter else a.shape[0]
+    K = a.shape[0] if a_kouter else a.shape[1]
+    N = b.shape[1] if b_kouter else b.shape[0]
+    E = 0 if k_offsets is None else k_offsets.numel() - 1
+    if out is None:
+        out = torch.empty(((E,) if E else ()) + (M, N), dtype=torch.float32, device=a.device)
+    d = MoeGemmDesc(M, N, K, a.data_ptr(), a.stride(0), int(a_kouter), b.data_ptr(), b.stride(0),
+                    int(b_kouter), out.data_ptr(), N, _ptr(c_in), _ptr(k_offsets), E)
+    st = LIB.moe_gemm_bf16(ctypes.byref(d), _P(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise MoeError(st, "moe_gemm_bf16")
+    return out
 
 
 def situ_eval(g, u, beta=4.0, beta_u=25.0):

@@ -235,6 +235,25 @@ __device__ __forceinline__ Tile map_tile_xcd(const GemmArgs &a) {
   return t;
 }
 
+// Tiles of one [M][N] output per expert (the expert-batched weight
+// gradients): the experts' outputs stacked along M, M tile mt being tile
+// mt % mte of expert mt / mte.
+template <int TM, int TN_OUT>
+__device__ __forceinline__ Tile map_tile_kgrp(const GemmArgs &args) {
+  GemmArgs ga = args;
+  const int64_t mte = (args.M + TM - 1) / TM;
+  ga.M = mte * TM * args.n_experts;
+  ga.offsets = nullptr;
+  Tile t = map_tile_xcd<TM, TN_OUT>(ga);
+  if (t.valid) {
+    const int64_t mt = t.m0 / TM;
+    t.e = (int32_t)(mt / mte);
+    t.m0 = (mt % mte) * TM;
+    t.m_end = min(args.M, t.m0 + TM);
+  }
+  return t;
+}
+
 // Storage format of the B operand (and of A).
 // BF_MX4A8: MXFP4 B with MX FP8 A (e4m3 codes, an E8M0 scale per 32);
 // BF_MX8A8: MX FP8 B (e4m3 codes, an E8M0 scale per 32) with MX FP8 A.  Both
@@ -257,8 +276,14 @@ constexpr int extra_lds_bytes() {
                        : (BF == BF_MX4 && BK < 128) ? TN * kMaxK32 : 0);
 }
 
+// AKO / BKO: operand A / B stored K-outer ([K][M] / [K][N] row-major, the
+// transposed layouts of the backward pass) instead of [M][K] / [N][K];
+// KGRP: one [M][N] output per expert e, over the K rows offsets[e] ..
+// offsets[e + 1] of K-outer operands (weight gradients of the routed
+// experts).
 template <int WM, int WN, int SUBM, int FRN, int BK, int STAGES, int OCC, int MA, int EPI,
-          bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
+          bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT, bool AKO = false,
+          bool BKO = false, bool KGRP = false>
 __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs args) {
   static_assert(BK == 32 || BK == 64 || BK == 128 || BK == 256, "K tile of 32 to 256");
   // A is bf16, or (A8) MX FP8: e4m3 codes with an E8M0 scale per 32 along K
@@ -318,11 +343,26 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   static_assert(!A8 || (BK >= 128 && MA == 0), "MX FP8 A: K tile of 128 or more");
   static_assert(!MSEG || (!DUAL && !A8 && !MXB && MA == 0), "segmented problems: single, bf16 A");
   constexpr int L = LMAX;
+  // K-outer operands: a tile row is one k (T bf16 values, T = TM or TN), in
+  // rows of whole 16-byte chunks whose index is XORed with 4 (k mod 4), so
+  // the transposing fragment reads hit every bank once
+  constexpr int RB_AK = TM * 2, RB_BK = TN * 2;  // bytes of a K-outer tile row
+  constexpr int RPI_AK = AKO ? 1024 / RB_AK : 1, RPI_BK = BKO ? 1024 / RB_BK : 1;
+  constexpr int CPR_AK = RB_AK / 16, CPR_BK = RB_BK / 16;
+  static_assert(!AKO || (BF == BF_BF16 && MA == 0 && !GATHER && !MSEG && 1024 % RB_AK == 0 &&
+                         RB_AK >= 256),
+                "K-outer A: bf16, a tile of 128, 256 or 512 rows");
+  static_assert(!BKO || (BF == BF_BF16 && !DUAL && !MSEG && 1024 % RB_BK == 0 && RB_BK >= 256),
+                "K-outer B: bf16 single, a tile of 128, 256 or 512 columns");
+  static_assert(!KGRP || (AKO && BKO && EPI == EPI_STORE), "expert-batched K: K-outer operands");
+  // K tiles past the end of K (or of an expert's rows) are masked on the B
+  // fragments; only layouts that can have such a tail carry the code
+  constexpr bool KTAIL = AKO || BKO;
   static_assert(!DUAL || FRN % 2 == 0, "dual needs gate and up fragments");
   static_assert(!GATHER || !MSEG, "gathered A has one K segment");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const Tile tile = map_tile_xcd<TM, TN_OUT>(args);
+  const Tile tile = KGRP ? map_tile_kgrp<TM, TN_OUT>(args) : map_tile_xcd<TM, TN_OUT>(args);
   if (!tile.valid) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -393,6 +433,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   // workgroup runs nper consecutive N tiles of its M tile, one ring over all
   // of their K tiles, storing each N tile's outputs inside the loop
   constexpr bool PN = MA > 0 && !B8 && !MSEG && EPI != EPI_ROUTER && (!MXB || MXS);
+  static_assert(!(PN && (AKO || BKO)), "persistent N tiles: K-inner operands");
   const int nper = PN ? max((int)args.nper, 1) : 1;
   uint8_t *mx_lds = reinterpret_cast<uint8_t *>(sc_lds);
   const int kb32 = MXB ? (int)(args.seg[0].k / 32) : 0;
@@ -419,7 +460,16 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   const bool has_last = EVEN || wave + NW * (LMAX - 1) < TT;
 
   // ---- K segments -------------------------------------------------------------
-  int ktiles = (int)(args.seg[0].k / BK);
+  // K range: K-outer operands run over the rows kr0 .. kr0 + klen (KGRP: the
+  // expert's pair rows), in K tiles of BK, the last possibly partial
+  int64_t kr0 = 0, klen = args.seg[0].k;
+  if constexpr (KGRP) {
+    kr0 = args.offsets[tile.e];
+    klen = args.offsets[tile.e + 1] - kr0;
+  }
+  int ktiles = (int)((klen + BK - 1) / BK);
+  const int ktiles_all = ktiles;
+  const int klast = (int)(klen - (int64_t)(ktiles - 1) * BK);  // k values in the last K tile
   if constexpr (MSEG) {
 #pragma unroll
     for (int s = 1; s < 5; ++s)
@@ -467,7 +517,10 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   if constexpr (!MSEG) {
     const int64_t a_first = GATHER ? 0 : tile.m0;
     const int64_t kb0 = (int64_t)k_begin * BK;
-    a_base = static_cast<const char *>(args.seg[0].a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
+    if constexpr (AKO)
+      a_base = static_cast<const char *>(args.seg[0].a) + ((kr0 + kb0) * cur_lda + tile.m0) * 2;
+    else
+      a_base = static_cast<const char *>(args.seg[0].a) + (a_first * cur_lda + kb0) * (A8 ? 1 : 2);
     const char *bsrc = static_cast<const char *>(args.seg[0].b);
     const char *busrc = static_cast<const char *>(args.b_up);
     if (args.b_tab != nullptr) {  // per-expert addresses (tiered experts)
@@ -477,7 +530,8 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       bsrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
       if (DUAL) busrc += (int64_t)tile.e * args.b_estride * BNUM / BDEN;
     }
-    b_base = bsrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
+    if constexpr (BKO) b_base = bsrc + ((kr0 + kb0) * cur_ldb + tile.n0) * 2;
+    else b_base = bsrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
     if constexpr (DUAL) bu_base = busrc + (tile.n0 * cur_ldb + kb0) * BNUM / BDEN;
   }
 #pragma unroll
@@ -492,7 +546,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
     // lane l of an instruction fills 16 B slot l % CPR of tile row l / CPR
     // and fetches the chunk that the swizzle puts there
-    if (g < TA) {
+    if (AKO && g < TA) {
+      // K-outer A: k row kr of the tile, 16-byte chunk ch of its TM columns
+      const int kr = g * RPI_AK + lane / CPR_AK;
+      const int ch = (lane % CPR_AK) ^ (4 * (kr & 3));
+      int64_t m = tile.m0 + 8 * ch;
+      if (m >= tile.m_end) m = tile.m0;  // clamp: loaded, never stored
+      o = (uint32_t)kr << 16 | (uint32_t)((m - tile.m0) * 2);
+    } else if (BKO && g >= TA && g < TT) {
+      const int kr = (g - TA) * RPI_BK + lane / CPR_BK;
+      const int ch = (lane % CPR_BK) ^ (4 * (kr & 3));
+      int64_t n = tile.n0 + 8 * ch;
+      if (n >= args.N) n = tile.n0;
+      o = (uint32_t)kr << 16 | (uint32_t)((n - tile.n0) * 2);
+    } else if (g < TA) {
       const int r = g * RPI + lane / CPR;
       const int ch = (lane % CPR) ^ swz(r, CPR);
       int64_t m = tile.m0 + r;
@@ -629,6 +696,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     // body, so the instruction selector sees uniform base + zext(offset) there
     // (SGPR-base form) instead of a 64-bit address hoisted out of the loop)
     uint32_t o = off[d];
+    if constexpr (AKO || BKO) {
+      const bool ko = (AKO && g < TA) || (BKO && g >= TA);
+      if (ko) {
+        // k rows past the end of K (last tile) re-read the last row; the B
+        // fragments mask those k
+        const int kv = k_begin + kt == ktiles_all - 1 ? klast : BK;
+        const uint32_t kr = min((int)(o >> 16), kv - 1);
+        const int64_t ldx = g < TA ? cur_lda : cur_ldb;
+        o = __umul24(kr, (uint32_t)(ldx * 2)) + (o & 0xFFFFu);
+        asm volatile("" : "+v"(o));
+        dma16(base + (int64_t)kt * BK * ldx * 2 + o, smem + st * STAGE_BYTES + g * 1024);
+        return;
+      }
+    }
     int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
     if constexpr (PN) kb += g < TA ? 0 : jn * nstep_b;
     if constexpr (BF != BF_BF16) {
@@ -694,7 +775,30 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       r = MA > 0 ? (lane & 31) % MA : ((f - FRN) * WM + wm) * 32 + (lane & 31);
       base = st;
     }
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ swz(r, CPR)) << 4));
+    bf16x8 v;
+    constexpr bool KO = f < FRN ? BKO : AKO;
+    if constexpr (KO) {
+      // K-outer operand: the fragment's 32 columns c0.. over k 16 ks ..+16,
+      // two transposing reads of four k each.  Lane (g, s) of a 16-lane group
+      // g supplies k row 8 (g / 2) + s / 4 (+ 4), columns 16 (g % 2) + 4 (s % 4)
+      // ..+4; lane i of the group receives element i % 4 of the chunks of
+      // lanes i / 4 + 4 j, j = 0..3: column c0 + (lane % 32), k 8 (lane / 32) + j
+      constexpr int RBX = f < FRN ? RB_BK : RB_AK;
+      const int c0 = r - (lane & 31);
+      const int g16 = lane >> 4, sx = lane & 15;
+      const int col = c0 + 16 * (g16 & 1) + 4 * (sx & 3);
+      const int kr = 16 * ks + 8 * (g16 >> 1) + (sx >> 2);  // kr % 4 == sx / 4
+      const char *p0 = base + kr * RBX + (((col >> 3) ^ (4 * (sx >> 2))) << 4) + (col & 7) * 2;
+      typedef __attribute__((ext_vector_type(4))) short s4;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4 *)(uintptr_t)lds_addr(p0));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4 *)(uintptr_t)lds_addr(p0 + 4 * RBX));
+      typedef __attribute__((ext_vector_type(8))) short s8;
+      v = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    } else {
+      v = *reinterpret_cast<const bf16x8 *>(base + r * RB + ((chunk ^ swz(r, CPR)) << 4));
+    }
     if constexpr (f < FRN) bfr[f] = v;
     else af[f - FRN] = v;
   };
@@ -751,7 +855,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
       col_ok[j] = col[j] < args.N;
       bias[j] = (EPI == EPI_ROUTER && args.bias && col_ok[j]) ? args.bias[col[j]] : 0.0f;
     }
-    OutT *out = static_cast<OutT *>(args.out);
+    OutT *out = static_cast<OutT *>(args.out) + (KGRP ? (int64_t)tile.e * args.M * args.ldo : 0);
     // the plain store (no row factor, no residual): the common case, kept free
     // of the per-row loads of the general one
     const bool plain_store = args.resid == nullptr && args.row_scale == nullptr;
@@ -1032,8 +1136,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
           } else {
             static_for<NF>([&](auto f) G2_INL { read_frag(st, 0, f, fa[0], fb[0]); });
           }
+          // a partial last K tile: k values past the end read as zero on B
+          const bool tail = KTAIL && k_begin + kt == ktiles_all - 1 && klast < BK;
           static_for<KS>([&](auto s_tag) G2_INL {
             constexpr int S = decltype(s_tag)::value;
+            if constexpr (KTAIL) {
+              if (tail) {
+                const int k8 = 16 * S + 8 * (lane >> 5);
+                static_for<FRN>([&](auto j) G2_INL {
+#pragma unroll
+                  for (int e = 0; e < 8; ++e)
+                    if (k8 + e >= klast) fb[S & 1][j][e] = (__bf16)0.0f;
+                });
+              }
+            }
             static_for<Q>([&](auto q_tag) G2_INL {
               constexpr int q = decltype(q_tag)::value;
               constexpr int i = q / FRN, j = q % FRN;
@@ -1126,7 +1242,7 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   };
   // one specialised copy of the K loop per number of active sub-blocks
   static_assert(SUBM <= 5, "mainloop dispatch covers up to 5 sub-blocks");
-  switch (sub_valid) {
+  if (!KGRP || ktiles > 0) switch (sub_valid) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
     case 2: if constexpr (SUBM >= 2) mainloop(std::integral_constant<int, 2>{}); break;

@@ -89,11 +89,12 @@ constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 // shapes a bf16 B operand can take (6..8 are MXFP4-only)
 constexpr bool bf16_shape(int v) { return v >= 0 && v < 6; }
 
-template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT>
+template <int V, int EPI, bool DUAL, bool GATHER, bool MSEG, int BF, typename OutT,
+          bool AKO = false, bool BKO = false, bool KGRP = false>
 hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   constexpr DmaShape sh = kDma[V];
   auto kern = g2::gemm_dma_kernel<sh.wm, sh.wn, sh.subm, sh.frn, sh.bk, sh.stages, sh.occ, sh.ma,
-                                  EPI, DUAL, GATHER, MSEG, BF, OutT>;
+                                  EPI, DUAL, GATHER, MSEG, BF, OutT, AKO, BKO, KGRP>;
   constexpr size_t lds = sh.lds(BF) + g2::extra_lds_bytes<EPI, sh.tm(), sh.tn(), BF, sh.bk>();
   static_assert(lds <= 160 * 1024, "LDS of a gfx950 workgroup");
   static bool attr_set = false;
@@ -122,16 +123,17 @@ hipError_t launch_dma_impl(GemmArgs a, hipStream_t s) {
   a.group_m = env_int("MOE_GROUP_M_DENSE", 4);
   if (a.group_m < 1) a.group_m = 1;
   int64_t m_tiles;
-  if (a.offsets == nullptr) m_tiles = (a.M + sh.tm() - 1) / sh.tm();
+  if (KGRP) m_tiles = (a.M + sh.tm() - 1) / sh.tm() * a.n_experts;  // every expert's [M][N]
+  else if (a.offsets == nullptr) m_tiles = (a.M + sh.tm() - 1) / sh.tm();
   else m_tiles = (a.M + sh.tm() - 1) / sh.tm() + a.n_experts;  // upper bound
   int64_t blocks = m_tiles * a.n_tiles_n;
   // split K when a dense problem has too few tiles to spread its weight
   // stream over the chip (short batches): about 256 workgroups, two or more
   // K tiles each, within the partial-sum buffer
   a.ksplit = 1;
-  if (a.offsets == nullptr && a.partial != nullptr && blocks > 0 && blocks < 128) {
+  if (!KGRP && a.offsets == nullptr && a.partial != nullptr && blocks > 0 && blocks < 128) {
     int64_t ktiles = 0;
-    for (int i = 0; i < a.nseg; ++i) ktiles += a.seg[i].k / sh.bk;
+    for (int i = 0; i < a.nseg; ++i) ktiles += (a.seg[i].k + sh.bk - 1) / sh.bk;
     const int64_t ldp = DUAL ? 2 * a.N : a.N;
     int64_t ks = std::min((256 + blocks - 1) / blocks, ktiles / 2);
     ks = std::min(ks, a.partial_cap / (a.M * ldp));
@@ -235,13 +237,48 @@ hipError_t launch_dma(int v, const GemmArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Operands stored K-outer (the backward pass): AKO: A is [K][M], BKO: B is
+// [K][N] (per expert for a grouped problem), both bf16; KGRP: the routed
+// experts' weight gradients, one [M][N] output per expert over its pair rows
+// (offsets) of K-outer A and B.  fp32 output.  K-outer A needs 256-row tiles
+// (the dense shape); K-outer B takes every bf16 shape (256 columns).
+template <int EPI, bool AKO, bool BKO, bool KGRP, bool GATHER, typename OutT>
+hipError_t launch_dma_ko(int v, const GemmArgs &a, hipStream_t s) {
+  constexpr int F = g2::BF_BF16;
+  if constexpr (AKO) {
+    return launch_dma_impl<kVDense, EPI, false, GATHER, false, F, OutT, AKO, BKO, KGRP>(a, s);
+  } else {
+    switch (v) {
+      case kVGrouped:
+        return launch_dma_impl<kVGrouped, EPI, false, GATHER, false, F, OutT, AKO, BKO, KGRP>(a, s);
+      case kVGroupedShort:
+        return launch_dma_impl<kVGroupedShort, EPI, false, GATHER, false, F, OutT, AKO, BKO, KGRP>(
+            a, s);
+      case kVSmallM:
+        return launch_dma_impl<kVSmallM, EPI, false, GATHER, false, F, OutT, AKO, BKO, KGRP>(a, s);
+      default:
+        return launch_dma_impl<kVDense, EPI, false, GATHER, false, F, OutT, AKO, BKO, KGRP>(a, s);
+    }
+  }
+}
+#define MOE_KO_KINDS(X)                         \
+  X(EPI_STORE, false, true, false, false, float) \
+  X(EPI_STORE, false, true, false, true, float)  \
+  X(EPI_STORE, true, true, false, false, float)  \
+  X(EPI_STORE, true, true, true, false, float)
+#define MOE_KO_EXTERN(E, A, B, K, G, T) \
+  extern template hipError_t launch_dma_ko<E, A, B, K, G, T>(int, const GemmArgs &, hipStream_t);
+MOE_KO_KINDS(MOE_KO_EXTERN)
+
 // launch_dma instantiations, one per problem kind (gemm_dma_*.hip)
 #define MOE_DMA_KINDS(X)                                  \
   X(EPI_ROUTER, false, false, float, false)               \
   X(EPI_STORE, false, false, uint16_t, true)              \
   X(EPI_STORE, false, false, uint16_t, false)             \
   X(EPI_SITU, true, false, uint16_t, false)               \
-  X(EPI_SITU, true, true, uint16_t, false)
+  X(EPI_SITU, true, true, uint16_t, false)                \
+  X(EPI_STORE, false, false, float, false)                \
+  X(EPI_STORE, false, true, float, false)
 #define MOE_DMA_EXTERN(E, D, G, T, M) \
   extern template hipError_t launch_dma<E, D, G, T, M>(int, const GemmArgs &, hipStream_t);
 MOE_DMA_KINDS(MOE_DMA_EXTERN)
