@@ -251,22 +251,20 @@ typedef struct moe_grads {
 size_t moe_backward_workspace_bytes(const moe_config *cfg, int64_t bt);
 
 /* Backward of moe_forward for bf16 activations, weights and router
- * (MOE_ERR_UNSUPPORTED otherwise, and for an expert_tab).  x[bt][d] and
- * dy[bt][d] are bf16; topk_idx / topk_w [bt][k] the routing moe_route (or
- * moe_forward) returned for x.  The forward's intermediate values are
- * recomputed from x, so no activations are kept between the calls.  The call
- * copies the dispatch offsets to the host (it synchronises `stream` once),
- * then enqueues the rest on `stream` and returns: the gradients are complete
- * when `stream` reaches that point.  The GEMMs run on rocBLAS (bf16 inputs, fp32
- * accumulation); the routed experts' ones are issued one expert at a time,
- * round-robin over four library-held streams (created on first use, with
- * their rocBLAS handles; default priority) that start after the work already
- * on `stream` and that `stream` waits for.  Those streams and handles are
- * per device and shared by every call: calls of moe_backward on one device
- * must not overlap from several host threads.  The call synchronises the
- * stream, so it cannot be captured into a HIP graph.  bt == 0
- * writes zero weight gradients.  The workspace (256-byte aligned) holds the
- * recomputed activations, about 2 (L + I) * 10 bytes a (token, expert) pair. */
+ * (MOE_ERR_UNSUPPORTED otherwise, for an expert_tab, and unless d, latent,
+ * expert_inter and shared_inter are multiples of 64 and n_experts of 8).
+ * x[bt][d] and dy[bt][d] are bf16; topk_idx / topk_w [bt][k] the routing
+ * moe_route (or moe_forward) returned for x (ids in range and distinct per
+ * token: a pair with an id out of range or repeated is left out of the
+ * gradients).  The forward's intermediate values are recomputed from x, so no
+ * activations are kept between the calls.  Same conventions as moe_forward:
+ * everything is enqueued on `stream` (the call neither allocates nor waits
+ * for the device), and the gradients are complete when `stream` reaches that
+ * point.  The contractions run on the layer's GEMM engine, the routed
+ * experts' ones grouped by expert from the dispatch offsets on the device.
+ * bt == 0 writes zero weight gradients.  The workspace (256-byte aligned)
+ * holds the recomputed activations, about 2 (L + I) * 10 bytes a (token,
+ * expert) pair. */
 moe_status moe_backward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
                         const int32_t *topk_idx, const float *topk_w, const void *dy,
                         const moe_grads *g, void *ws, size_t ws_bytes, void *stream);

@@ -11,23 +11,22 @@
 //
 // The forward quantities the gradients need (x_lat, each pair's g and u, h,
 // o, y_lat and r, the shared experts' g and u) are recomputed here from x and
-// the routing that moe_route returned, so a caller keeps no activations.  The
-// contractions are plain GEMMs with transposed operands and run on rocBLAS
-// (bf16 inputs, fp32 accumulation); the routed experts' GEMMs are issued per
-// expert from the dispatch counts, which the call copies to the host, over
-// four side streams.  Every
-// elementwise step, gather, reduction and normalisation runs in the kernels
-// below.
+// the routing that moe_route returned, so a caller keeps no activations.
+// Every contraction runs on the layer's GEMM engine, in one of three forms:
+// the forward's ([M][K] x [N][K]), the input gradients' (the weight operand
+// read K-outer, as stored: dx = dy W), and the weight gradients' (both
+// operands K-outer, K = tokens; for the routed experts one output per expert
+// over its pairs).  The routed experts' contractions are grouped by expert
+// from the dispatch offsets on the device, one launch each: nothing waits for
+// the host.  Every elementwise step, gather, reduction and normalisation runs
+// in the kernels below.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
-#include <atomic>
-#include <mutex>
-#include <thread>
-#include <vector>
 
 #include "common.h"
+#include "gemm.h"
+#include "gemm_launch.h"
 #include "kernels.h"
 #include "moe.h"
 
@@ -43,7 +42,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct BwdPlan {
   size_t masks, counts, offsets, tile_offsets, perm, inv_perm, w_sorted, xlat, xg, G, U, h, o,
       ylat, rinv, n, Gs, Us, hs, dn, dylat, dyg, dh, dg, du, dz, dz16, dxg, dxlat, dhs, dgs, dus,
-      part, total;
+      part, split, total;
+  int64_t e_pad = 0;      // router gradient columns, padded to the K tile (zeros past E)
+  int64_t split_cap = 0;  // floats of split-K partial sums (short batches)
 };
 
 bool backward_supported(const moe_config *c) {
@@ -58,15 +59,19 @@ moe_status bwd_plan(const moe_config *c, int64_t bt, BwdPlan *p) {
   if (!backward_supported(c) || bt < 0) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_BF16 || c->router_dtype != MOE_BF16)
     return MOE_ERR_UNSUPPORTED;
-  // the row gathers move 8 bf16 values a thread; rocBLAS takes 32-bit sizes
-  if (c->d % 8 || c->latent % 8 || c->expert_inter % 8 || c->shared_inter % 8)
+  // the engine's K tiles (64) over d, L, I and I_s as K of stored operands;
+  // 16-byte rows chunks of K-outer operands (E columns of the router gradient)
+  if (c->d % 64 || c->latent % 64 || c->expert_inter % 64 ||
+      (c->n_shared && c->shared_inter % 64) || c->n_experts % 8)
     return MOE_ERR_UNSUPPORTED;
   const int64_t E = c->n_experts, L = c->latent, I = c->expert_inter, d = c->d;
   const int64_t SI = c->n_shared * c->shared_inter, P = bt * c->top_k;
+  // 32-bit element counts in the kernels; gathered rows addressed with 32-bit offsets
   if (P >= (int64_t)1 << 31 || P * std::max(L, I) >= (int64_t)1 << 31 ||
       bt * std::max({d, L, E, SI}) >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
   const int64_t nb = (bt + 63) / 64, nchunk = (bt + kColChunk - 1) / kColChunk;
+  p->e_pad = (E + 63) / 64 * 64;
   size_t off = 0;
   auto take = [&](int64_t bytes) {
     size_t o = off;
@@ -99,13 +104,16 @@ moe_status bwd_plan(const moe_config *c, int64_t bt, BwdPlan *p) {
   p->dg = take(2 * P * I);
   p->du = take(2 * P * I);
   p->dz = take(4 * bt * E);
-  p->dz16 = take(2 * bt * E);
+  p->dz16 = take(2 * bt * p->e_pad);
   p->dxg = take(4 * P * L);
   p->dxlat = take(2 * bt * L);
   p->dhs = take(4 * bt * SI);
   p->dgs = take(2 * bt * SI);
   p->dus = take(2 * bt * SI);
   p->part = take(4 * nchunk * std::max(L, E));
+  // split-K partial sums of the dense input-gradient GEMMs of short batches
+  if (bt > 0 && bt <= 256) p->split_cap = 16 * bt * std::max({d, L, SI, E});
+  p->split = take(4 * p->split_cap);
   p->total = off;
   return MOE_OK;
 }
@@ -119,86 +127,6 @@ T *at(void *ws, size_t off) {
   do {                                           \
     if ((expr) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
-#define MOE_TRY_BLAS(expr)                                     \
-  do {                                                         \
-    if ((expr) != rocblas_status_success) return MOE_ERR_HIP; \
-  } while (0)
-
-// ---- rocBLAS and the expert streams ---------------------------------------------------
-// One expert's GEMM (a few hundred rows at prefill, a few at decode) covers a
-// small part of the 256 CUs, so consecutive experts go round-robin to kSide
-// streams and run side by side.  Per device, created on first use with that
-// device current: a handle for the caller's stream, and a stream + handle +
-// event for each side; all at the default priority.
-constexpr int kSide = 4;
-struct Blas {
-  rocblas_handle main = nullptr;
-  rocblas_handle side[kSide] = {};
-  hipStream_t ss[kSide] = {};
-  hipEvent_t done[kSide] = {};
-  hipEvent_t fork = nullptr;
-  bool ok = false;
-};
-
-Blas *blas() {
-  static std::mutex mu;
-  static Blas per_dev[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lk(mu);
-  Blas &b = per_dev[dev];
-  if (!b.ok) {
-    if (!b.main && rocblas_create_handle(&b.main) != rocblas_status_success) return nullptr;
-    if (!b.fork && hipEventCreateWithFlags(&b.fork, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-    for (int i = 0; i < kSide; ++i) {
-      if (!b.ss[i] && hipStreamCreateWithFlags(&b.ss[i], hipStreamNonBlocking) != hipSuccess)
-        return nullptr;
-      if (!b.done[i] && hipEventCreateWithFlags(&b.done[i], hipEventDisableTiming) != hipSuccess)
-        return nullptr;
-      if (!b.side[i]) {
-        if (rocblas_create_handle(&b.side[i]) != rocblas_status_success) return nullptr;
-        if (rocblas_set_stream(b.side[i], b.ss[i]) != rocblas_status_success) return nullptr;
-      }
-    }
-    b.ok = true;
-  }
-  return &b;
-}
-
-// the side streams start after the work enqueued on s so far ...
-hipError_t fork_sides(const Blas &b, hipStream_t s) {
-  hipError_t e = hipEventRecord(b.fork, s);
-  for (int i = 0; i < kSide && e == hipSuccess; ++i) e = hipStreamWaitEvent(b.ss[i], b.fork, 0);
-  return e;
-}
-// ... and s continues after everything enqueued on them
-hipError_t join_sides(const Blas &b, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  for (int i = 0; i < kSide && e == hipSuccess; ++i) {
-    e = hipEventRecord(b.done[i], b.ss[i]);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, b.done[i], 0);
-  }
-  return e;
-}
-
-// Row-major C[M][N] = op(A) op(B) + beta C with op(A) [M][K], op(B) [K][N]; ta / tb
-// mean A is stored [K][M] / B is stored [N][K].  rocBLAS is column-major, where
-// the row-major C is C^T = op(B)^T op(A)^T: the operands swap and keep their flags.
-rocblas_status gemm_rm(rocblas_handle hd, bool ta, bool tb, int64_t M, int64_t N, int64_t K,
-                       const void *A, rocblas_datatype at_, int64_t lda, const void *B,
-                       rocblas_datatype bt_, int64_t ldb, float beta, void *C,
-                       rocblas_datatype ct, int64_t ldc) {
-  if (M == 0 || N == 0) return rocblas_status_success;
-  const float alpha = 1.0f;
-  return rocblas_gemm_ex(hd, tb ? rocblas_operation_transpose : rocblas_operation_none,
-                         ta ? rocblas_operation_transpose : rocblas_operation_none, (int)N,
-                         (int)M, (int)K, &alpha, B, bt_, (int)ldb, A, at_, (int)lda, &beta, C,
-                         ct, (int)ldc, C, ct, (int)ldc, rocblas_datatype_f32_r,
-                         rocblas_gemm_algo_standard, 0, 0);
-}
-constexpr rocblas_datatype BF = rocblas_datatype_bf16_r, F32 = rocblas_datatype_f32_r;
-
 // ---- elementwise and reduction kernels ------------------------------------------------
 struct Situ {
   float phi, dphi, psi, dpsi;
@@ -219,14 +147,17 @@ __device__ __forceinline__ Situ situ_parts(float g, float u, float beta, float i
   return r;
 }
 
-// dst[q][:] = src[perm[q] / k][:] (bf16 rows, 8 values a thread)
+// dst[q][:] = src[perm[q] / k][:] (bf16 rows, 8 values a thread) for the rows
+// q < *rows_end (the dispatched pairs)
 __global__ void gather_rows_kernel(const uint16_t *__restrict__ src,
                                    const int32_t *__restrict__ perm, int k, int64_t rows,
-                                   int64_t cols, uint16_t *__restrict__ dst) {
-  const int64_t c8 = cols / 8, n = rows * c8;
+                                   int64_t cols, const int32_t *__restrict__ rows_end,
+                                   uint16_t *__restrict__ dst) {
+  const int64_t c8 = cols / 8, n = rows * c8, q_end = *rows_end;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t q = i / c8, c = i % c8;
+    if (q >= q_end) continue;
     const int64_t t = perm[q] / k;
     reinterpret_cast<uint4 *>(dst + q * cols)[c] =
         reinterpret_cast<const uint4 *>(src + t * cols)[c];
@@ -328,12 +259,13 @@ __global__ void situ_bwd_kernel(const float *__restrict__ dh, const float *__res
                                 const float *__restrict__ U, const float *__restrict__ w,
                                 const int32_t *__restrict__ perm,
                                 const int32_t *__restrict__ idx, int k, int64_t E, int64_t rows,
-                                int64_t cols, float beta, float inv_beta, float beta_u,
-                                float inv_beta_u, uint16_t *__restrict__ dg,
-                                uint16_t *__restrict__ du, float *__restrict__ dz) {
+                                int64_t cols, const int32_t *__restrict__ rows_end, float beta,
+                                float inv_beta, float beta_u, float inv_beta_u,
+                                uint16_t *__restrict__ dg, uint16_t *__restrict__ du,
+                                float *__restrict__ dz) {
   const int lane = threadIdx.x & 63;
   const int64_t q = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (q >= rows) return;
+  if (q >= rows || (rows_end && q >= *rows_end)) return;
   const float wq = w ? w[q] : 1.0f;
   float dw = 0.0f;
   for (int64_t i = lane; i < cols; i += 64) {
@@ -371,10 +303,15 @@ __global__ void fill_f32_kernel(float *__restrict__ p, int64_t n) {
        i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.0f;
 }
-__global__ void cvt_bf16_kernel(const float *__restrict__ s, int64_t n, uint16_t *__restrict__ d) {
+// d[r][c] = bf16(s[r][c]) for c < cols, 0 for cols <= c < ld
+__global__ void cvt_bf16_pad_kernel(const float *__restrict__ s, int64_t rows, int64_t cols,
+                                    int64_t ld, uint16_t *__restrict__ d) {
+  const int64_t n = rows * ld;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    d[i] = f32_to_bf16(s[i]);
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / ld, c = i % ld;
+    d[i] = c < cols ? f32_to_bf16(s[r * cols + c]) : (uint16_t)0;
+  }
 }
 
 // grid-stride launches: at most 65536 blocks of 256
@@ -399,27 +336,69 @@ hipError_t colsum(const float *a, const float *b, const float *rs, int64_t rows,
                        (const float *)part, nchunk, cols, out);
 }
 
-// Runs fn(e, handle, stream) for every expert e, expert e on side e % kSide;
-// each side's experts are issued by a host thread of its own (a library call
-// per GEMM costs microseconds of host time, comparable to a small expert's
-// GEMM).  The sides start after the work on s so far, and s waits for them.
-template <typename Fn>
-moe_status for_experts(const Blas &b, hipStream_t s, int64_t E, Fn fn) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || fork_sides(b, s) != hipSuccess) return MOE_ERR_HIP;
-  std::atomic<int> status{MOE_OK};
-  std::thread th[kSide];
-  for (int i = 0; i < kSide; ++i)
-    th[i] = std::thread([&, i] {
-      if (hipSetDevice(dev) != hipSuccess) status.store(MOE_ERR_HIP);  // the caller's device
-      for (int64_t e = i; e < E && status.load() == MOE_OK; e += kSide) {
-        const moe_status st = fn(e, b.side[i], b.ss[i]);
-        if (st != MOE_OK) status.store(st);
-      }
-    });
-  for (auto &t : th) t.join();
-  if (join_sides(b, s) != hipSuccess) return MOE_ERR_HIP;
-  return static_cast<moe_status>(status.load());
+// ---- contractions on the GEMM engine ---------------------------------------------------
+// One contraction C = op(A) op(B) with fp32 output (the recomputations keep
+// the forward's bf16 kinds): A [M][K] as stored or K-outer [K][M], B [N][K]
+// or K-outer [K][N].
+struct Contraction {
+  GemmArgs a = {};
+  Contraction(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+              int64_t ldb, void *C, int64_t ldc) {
+    a.M = M;
+    a.N = N;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{A, lda, B, ldb, nullptr, K};
+    a.out = C;
+    a.ldo = ldc;
+    a.beta = a.inv_beta = a.beta_u = a.inv_beta_u = 1.0f;
+  }
+  // grouped by expert: rows offsets[e].. of A against expert e's B
+  Contraction &by_expert(const int32_t *offsets, const int32_t *tile_offsets, int64_t E,
+                         int64_t b_estride) {
+    a.offsets = offsets;
+    a.tile_offsets = tile_offsets;
+    a.n_experts = (int32_t)E;
+    a.b_estride = b_estride;
+    return *this;
+  }
+  Contraction &plus(const float *c_in) {  // C = c_in + op(A) op(B) (c_in may be C)
+    a.resid = c_in;
+    a.ldr = a.ldo;
+    return *this;
+  }
+  Contraction &split(float *partial, int64_t cap) {  // short batches: split K
+    a.partial = partial;
+    a.partial_cap = cap;
+    return *this;
+  }
+};
+
+// C = A B^T, fp32 (the stored layouts; dense or grouped)
+hipError_t nt_f32(const Contraction &c, int v, hipStream_t s) {
+  return launch_dma<EPI_STORE, false, false, float, false>(v, c.a, s);
+}
+// C = A B with B K-outer ([K][N], per expert when grouped): input gradients
+hipError_t nn_f32(const Contraction &c, int v, hipStream_t s) {
+  return launch_dma_ko<EPI_STORE, false, true, false, false, float>(v, c.a, s);
+}
+// C = A^T B with both operands K-outer (K = tokens): dense weight gradients
+hipError_t tn_f32(const Contraction &c, hipStream_t s) {
+  return launch_dma_ko<EPI_STORE, true, true, false, false, float>(kVDense, c.a, s);
+}
+// C_e = A_e^T B_e over the rows offsets[e].. of both: the routed experts' weight gradients
+hipError_t tn_experts_f32(Contraction c, const int32_t *offsets, int64_t E, hipStream_t s) {
+  c.a.offsets = offsets;
+  c.a.n_experts = (int32_t)E;
+  return launch_dma_ko<EPI_STORE, true, true, true, false, float>(kVDense, c.a, s);
+}
+
+GemmArgs base_args_bwd(const moe_config *c) {
+  GemmArgs a = {};
+  a.beta = c->beta;
+  a.inv_beta = 1.0f / c->beta;
+  a.beta_u = c->beta_u;
+  a.inv_beta_u = 1.0f / c->beta_u;
+  return a;
 }
 
 bool grads_complete(const moe_config *c, const moe_grads *g, int64_t bt) {
@@ -465,13 +444,10 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
       if (a.first) MOE_TRY(fill_f32(a.first, a.second, s));
     return MOE_OK;
   }
-  Blas *bl = blas();
-  if (!bl) return MOE_ERR_HIP;
-  rocblas_handle hd = bl->main;
-  MOE_TRY_BLAS(rocblas_set_stream(hd, s));
   const float beta = cfg->beta, ib = 1.0f / cfg->beta, bu = cfg->beta_u, ibu = 1.0f / cfg->beta_u;
 
   int32_t *counts = at<int32_t>(ws, p.counts), *offsets = at<int32_t>(ws, p.offsets);
+  int32_t *tile_offsets = at<int32_t>(ws, p.tile_offsets);
   int32_t *perm = at<int32_t>(ws, p.perm), *inv_perm = at<int32_t>(ws, p.inv_perm);
   float *w_sorted = at<float>(ws, p.w_sorted);
   uint16_t *xlat = at<uint16_t>(ws, p.xlat), *xg = at<uint16_t>(ws, p.xg);
@@ -485,68 +461,76 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
   uint16_t *dg = at<uint16_t>(ws, p.dg), *du = at<uint16_t>(ws, p.du);
   uint16_t *dz16 = at<uint16_t>(ws, p.dz16), *dxlat = at<uint16_t>(ws, p.dxlat);
   float *dxg = at<float>(ws, p.dxg), *dhs = at<float>(ws, p.dhs), *part = at<float>(ws, p.part);
+  float *split = at<float>(ws, p.split);
   uint16_t *dgs = at<uint16_t>(ws, p.dgs), *dus = at<uint16_t>(ws, p.dus);
-  const uint16_t *Wg = static_cast<const uint16_t *>(w->w_gate);
-  const uint16_t *Wu = static_cast<const uint16_t *>(w->w_up);
-  const uint16_t *Wd = static_cast<const uint16_t *>(w->w_down);
+  const int32_t *pairs_end = offsets + E;  // dispatched pairs (bt k for valid routing)
+  // tile shapes: the routed experts' GEMMs as the forward's, short batches' dense ones
+  const int vg = dma_variant(GK_EXPERT_SITU, P, E);
+  const int vd = bt <= 64 ? kVSmallM : kVDense;
+  const int64_t dense_mt = (bt + gemm_bm(PATH_BF16) - 1) / gemm_bm(PATH_BF16);
+  const int64_t grouped_mt = (P + gemm_bm(PATH_BF16) - 1) / gemm_bm(PATH_BF16) + E;
 
   // ---- recompute: dispatch, x_lat, the routed experts, y_lat and r -------------------
-  MOE_TRY(launch_dispatch(topk_idx, topk_w, bt, k, E, 64, at<uint64_t>(ws, p.masks), counts,
-                          offsets, at<int32_t>(ws, p.tile_offsets), perm, inv_perm, w_sorted,
-                          s));
-  std::vector<int32_t> off_h(E + 1);
-  MOE_TRY(hipMemcpyAsync(off_h.data(), offsets, 4 * (E + 1), hipMemcpyDeviceToHost, s));
-  MOE_TRY(hipStreamSynchronize(s));
-  MOE_TRY_BLAS(gemm_rm(hd, false, true, bt, L, d, x, BF, d, w->w_down_proj, BF, d, 0.0f, xlat,
-                       BF, L));
+  MOE_TRY(launch_dispatch(topk_idx, topk_w, bt, k, E, grouped_tile_rows(PATH_BF16, WF_BF16, P, E),
+                          at<uint64_t>(ws, p.masks), counts, offsets, tile_offsets, perm,
+                          inv_perm, w_sorted, s));
+  {
+    GemmArgs a = base_args_bwd(cfg);
+    a.M = bt;
+    a.N = L;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{x, d, w->w_down_proj, d, nullptr, d};
+    a.out = xlat;
+    a.ldo = L;
+    a.partial = split;
+    a.partial_cap = p.split_cap;
+    MOE_TRY(gemm_launch(a, PATH_BF16, GK_DENSE, WF_BF16, dense_mt, s));
+  }
   MOE_TRY(launch_kernel(gather_rows_kernel, grid_for(P * L / 8), dim3(256), 0, s,
-                        (const uint16_t *)xlat, (const int32_t *)perm, (int)k, P, L, xg));
-  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
-    (void)se;
-    const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) return MOE_OK;
-    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, I, L, xg + q0 * L, BF, L, Wg + e * I * L, BF, L,
-                         0.0f, G + q0 * I, F32, I));
-    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, I, L, xg + q0 * L, BF, L, Wu + e * I * L, BF, L,
-                         0.0f, U + q0 * I, F32, I));
-    return MOE_OK;
-  });
-  if (st != MOE_OK) return st;
+                        (const uint16_t *)xlat, (const int32_t *)perm, (int)k, P, L, pairs_end,
+                        xg));
+  MOE_TRY(nt_f32(Contraction(P, I, L, xg, L, w->w_gate, L, G, I)
+                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
+  MOE_TRY(nt_f32(Contraction(P, I, L, xg, L, w->w_up, L, U, I)
+                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
   MOE_TRY(launch_kernel(situ_h_kernel, grid_for(P * I), dim3(256), 0, s, (const float *)G,
                         (const float *)U, (const float *)w_sorted, P, I, beta, ib, bu, ibu, h));
-  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
-    (void)se;
-    const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) return MOE_OK;
-    MOE_TRY_BLAS(gemm_rm(he, false, true, ne, L, I, h + q0 * I, BF, I, Wd + e * L * I, BF, I,
-                         0.0f, o + q0 * L, BF, L));
-    return MOE_OK;
-  });
-  if (st != MOE_OK) return st;
+  {
+    GemmArgs a = base_args_bwd(cfg);
+    a.M = P;
+    a.N = L;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{h, I, w->w_down, I, nullptr, I};
+    a.offsets = offsets;
+    a.tile_offsets = tile_offsets;
+    a.n_experts = (int32_t)E;
+    a.b_estride = L * I;
+    a.out = o;
+    a.ldo = L;
+    MOE_TRY(gemm_launch(a, PATH_BF16, GK_EXPERT_DOWN, WF_BF16, grouped_mt, s));
+  }
   MOE_TRY(launch_kernel(combine_ylat_kernel, dim3((unsigned)bt), dim3(256), 0, s,
                         (const uint16_t *)o, (const int32_t *)inv_perm, (int)k, L,
                         w->latent_gamma, cfg->rms_eps, ylat, rinv, n));
-  const uint16_t *shg = static_cast<const uint16_t *>(w->sh_gate);
-  const uint16_t *shu = static_cast<const uint16_t *>(w->sh_up);
-  const uint16_t *shd = static_cast<const uint16_t *>(w->sh_down);
   if (S > 0) {  // the S shared experts' gate / up rows are one [S I_s][d] matrix each
-    MOE_TRY_BLAS(gemm_rm(hd, false, true, bt, SI, d, x, BF, d, shg, BF, d, 0.0f, Gs, F32, SI));
-    MOE_TRY_BLAS(gemm_rm(hd, false, true, bt, SI, d, x, BF, d, shu, BF, d, 0.0f, Us, F32, SI));
+    MOE_TRY(nt_f32(Contraction(bt, SI, d, x, d, w->sh_gate, d, Gs, SI).split(split, p.split_cap),
+                   vd, s));
+    MOE_TRY(nt_f32(Contraction(bt, SI, d, x, d, w->sh_up, d, Us, SI).split(split, p.split_cap),
+                   vd, s));
     MOE_TRY(launch_kernel(situ_h_kernel, grid_for(bt * SI), dim3(256), 0, s, (const float *)Gs,
                           (const float *)Us, (const float *)nullptr, bt, SI, beta, ib, bu, ibu,
                           hs));
   }
 
   // ---- y = W_up n + sum_s W_ds,s hs_s ----------------------------------------------
-  MOE_TRY_BLAS(gemm_rm(hd, true, false, d, L, bt, dy, BF, d, n, BF, L, 0.0f, g->w_up_proj, F32,
-                       L));
-  MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, L, d, dy, BF, d, w->w_up_proj, BF, L, 0.0f, dn, F32,
-                       L));
+  MOE_TRY(tn_f32(Contraction(d, L, bt, dy, d, n, L, g->w_up_proj, L), s));
+  MOE_TRY(nn_f32(Contraction(bt, L, d, dy, d, w->w_up_proj, L, dn, L).split(split, p.split_cap),
+                 vd, s));
+  const uint16_t *shd = static_cast<const uint16_t *>(w->sh_down);
   for (int64_t sx = 0; sx < S; ++sx) {
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, d, Is, bt, dy, BF, d, hs + sx * Is, BF, SI, 0.0f,
-                         g->sh_down + sx * d * Is, F32, Is));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, Is, d, dy, BF, d, shd + sx * d * Is, BF, Is, 0.0f,
-                         dhs + sx * Is, F32, SI));
+    MOE_TRY(tn_f32(Contraction(d, Is, bt, dy, d, hs + sx * Is, SI, g->sh_down + sx * d * Is, Is), s));
+    MOE_TRY(nn_f32(Contraction(bt, Is, d, dy, d, shd + sx * d * Is, Is, dhs + sx * Is, SI)
+                       .split(split, p.split_cap), vd, s));
   }
   // ---- n = y_lat r gamma ------------------------------------------------------------
   MOE_TRY(colsum(dn, ylat, rinv, bt, L, part, g->latent_gamma, s));
@@ -554,73 +538,49 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
                         (const float *)ylat, (const float *)rinv, w->latent_gamma, L, dylat));
   // ---- routed experts ---------------------------------------------------------------
   MOE_TRY(launch_kernel(gather_rows_kernel, grid_for(P * L / 8), dim3(256), 0, s,
-                        (const uint16_t *)dylat, (const int32_t *)perm, (int)k, P, L, dyg));
+                        (const uint16_t *)dylat, (const int32_t *)perm, (int)k, P, L, pairs_end,
+                        dyg));
+  // dW_d,e = dy_e^T h_e over expert e's pairs (zero for an expert no pair chose)
+  MOE_TRY(tn_experts_f32(Contraction(L, I, 0, dyg, L, h, I, g->w_down, I), offsets, E, s));
+  MOE_TRY(nn_f32(Contraction(P, I, L, dyg, L, w->w_down, I, dh, I)
+                     .by_expert(offsets, tile_offsets, E, L * I), vg, s));
   MOE_TRY(fill_f32(dz, bt * E, s));
-  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
-    (void)se;
-    const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) {  // no pair chose the expert
-      MOE_TRY(fill_f32(g->w_down + e * L * I, L * I, se));
-      return MOE_OK;
-    }
-    MOE_TRY_BLAS(gemm_rm(he, true, false, L, I, ne, dyg + q0 * L, BF, L, h + q0 * I, BF, I, 0.0f,
-                         g->w_down + e * L * I, F32, I));
-    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, I, L, dyg + q0 * L, BF, L, Wd + e * L * I, BF, I,
-                         0.0f, dh + q0 * I, F32, I));
-    return MOE_OK;
-  });
-  if (st != MOE_OK) return st;
-  MOE_TRY(launch_kernel(situ_bwd_kernel, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s, (const float *)dh,
-                        (const float *)G, (const float *)U, (const float *)w_sorted,
-                        (const int32_t *)perm, topk_idx, (int)k, E, P, I, beta, ib, bu, ibu, dg,
-                        du, dz));
-  st = for_experts(*bl, s, E, [&](int64_t e, rocblas_handle he, hipStream_t se) -> moe_status {
-    (void)se;
-    const int64_t q0 = off_h[e], ne = off_h[e + 1] - q0;
-    if (ne == 0) {
-      MOE_TRY(fill_f32(g->w_gate + e * I * L, I * L, se));
-      MOE_TRY(fill_f32(g->w_up + e * I * L, I * L, se));
-      return MOE_OK;
-    }
-    MOE_TRY_BLAS(gemm_rm(he, true, false, I, L, ne, dg + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
-                         g->w_gate + e * I * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(he, true, false, I, L, ne, du + q0 * I, BF, I, xg + q0 * L, BF, L, 0.0f,
-                         g->w_up + e * I * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, L, I, dg + q0 * I, BF, I, Wg + e * I * L, BF, L,
-                         0.0f, dxg + q0 * L, F32, L));
-    MOE_TRY_BLAS(gemm_rm(he, false, false, ne, L, I, du + q0 * I, BF, I, Wu + e * I * L, BF, L,
-                         1.0f, dxg + q0 * L, F32, L));
-    return MOE_OK;
-  });
-  if (st != MOE_OK) return st;
+  MOE_TRY(launch_kernel(situ_bwd_kernel, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s,
+                        (const float *)dh, (const float *)G, (const float *)U,
+                        (const float *)w_sorted, (const int32_t *)perm, topk_idx, (int)k, E, P,
+                        I, pairs_end, beta, ib, bu, ibu, dg, du, dz));
+  MOE_TRY(tn_experts_f32(Contraction(I, L, 0, dg, I, xg, L, g->w_gate, L), offsets, E, s));
+  MOE_TRY(tn_experts_f32(Contraction(I, L, 0, du, I, xg, L, g->w_up, L), offsets, E, s));
+  MOE_TRY(nn_f32(Contraction(P, L, I, dg, I, w->w_gate, L, dxg, L)
+                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
+  MOE_TRY(nn_f32(Contraction(P, L, I, du, I, w->w_up, L, dxg, L)
+                     .by_expert(offsets, tile_offsets, E, I * L).plus(dxg), vg, s));
   MOE_TRY(launch_kernel(combine_rows_kernel, grid_for(bt * L), dim3(256), 0, s,
                         (const float *)dxg, (const int32_t *)inv_perm, (int)k, bt, L, dxlat));
   // ---- x_lat = W_down_proj x, and the router ------------------------------------------
-  MOE_TRY_BLAS(gemm_rm(hd, true, false, L, d, bt, dxlat, BF, L, x, BF, d, 0.0f, g->w_down_proj,
-                       F32, d));
-  MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, d, L, dxlat, BF, L, w->w_down_proj, BF, d, 0.0f,
-                       g->dx, F32, d));
-  MOE_TRY(launch_kernel(cvt_bf16_kernel, grid_for(bt * E), dim3(256), 0, s, (const float *)dz,
-                        bt * E, dz16));
-  MOE_TRY_BLAS(gemm_rm(hd, true, false, E, d, bt, dz16, BF, E, x, BF, d, 0.0f, g->w_router, F32,
-                       d));
-  MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, d, E, dz16, BF, E, w->w_router, BF, d, 1.0f, g->dx,
-                       F32, d));
+  MOE_TRY(tn_f32(Contraction(L, d, bt, dxlat, L, x, d, g->w_down_proj, d), s));
+  MOE_TRY(nn_f32(Contraction(bt, d, L, dxlat, L, w->w_down_proj, d, g->dx, d)
+                     .split(split, p.split_cap), vd, s));
+  MOE_TRY(launch_kernel(cvt_bf16_pad_kernel, grid_for(bt * p.e_pad), dim3(256), 0, s,
+                        (const float *)dz, bt, E, p.e_pad, dz16));
+  MOE_TRY(tn_f32(Contraction(E, d, bt, dz16, p.e_pad, x, d, g->w_router, d), s));
+  // (K = E: the router rows past E are masked, the padded dz columns are zero)
+  MOE_TRY(nn_f32(Contraction(bt, d, E, dz16, p.e_pad, w->w_router, d, g->dx, d)
+                     .plus(g->dx).split(split, p.split_cap), vd, s));
   MOE_TRY(colsum(dz, nullptr, nullptr, bt, E, part, g->router_bias, s));
   // ---- shared experts ---------------------------------------------------------------
   if (S > 0) {
-    MOE_TRY(launch_kernel(situ_bwd_kernel, dim3((unsigned)((bt + 3) / 4)), dim3(256), 0, s, (const float *)dhs,
-                          (const float *)Gs, (const float *)Us, (const float *)nullptr,
-                          (const int32_t *)nullptr, (const int32_t *)nullptr, 1, E, bt, SI, beta,
+    MOE_TRY(launch_kernel(situ_bwd_kernel, dim3((unsigned)((bt + 3) / 4)), dim3(256), 0, s,
+                          (const float *)dhs, (const float *)Gs, (const float *)Us,
+                          (const float *)nullptr, (const int32_t *)nullptr,
+                          (const int32_t *)nullptr, 1, E, bt, SI, (const int32_t *)nullptr, beta,
                           ib, bu, ibu, dgs, dus, (float *)nullptr));
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, SI, d, bt, dgs, BF, SI, x, BF, d, 0.0f, g->sh_gate, F32,
-                         d));
-    MOE_TRY_BLAS(gemm_rm(hd, true, false, SI, d, bt, dus, BF, SI, x, BF, d, 0.0f, g->sh_up, F32,
-                         d));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, d, SI, dgs, BF, SI, shg, BF, d, 1.0f, g->dx, F32,
-                         d));
-    MOE_TRY_BLAS(gemm_rm(hd, false, false, bt, d, SI, dus, BF, SI, shu, BF, d, 1.0f, g->dx, F32,
-                         d));
+    MOE_TRY(tn_f32(Contraction(SI, d, bt, dgs, SI, x, d, g->sh_gate, d), s));
+    MOE_TRY(tn_f32(Contraction(SI, d, bt, dus, SI, x, d, g->sh_up, d), s));
+    MOE_TRY(nn_f32(Contraction(bt, d, SI, dgs, SI, w->sh_gate, d, g->dx, d)
+                       .plus(g->dx).split(split, p.split_cap), vd, s));
+    MOE_TRY(nn_f32(Contraction(bt, d, SI, dus, SI, w->sh_up, d, g->dx, d)
+                       .plus(g->dx).split(split, p.split_cap), vd, s));
   }
   return MOE_OK;
 }

@@ -368,7 +368,6 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int rsub = lane / CPR, slot = lane % CPR;
 
   // ---- per-row factors of the SiTU epilogue, into LDS past the ring --------
   // (older than every operand load, so the first tile's wait covers them)

@@ -29,6 +29,9 @@ enum WFmt { WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2, WF_MX4A8 = 3, WF_MX8A8 = 4 };
 // n_experts experts with weights in format wf (the dispatch lays its tile
 // table out in these units).
 int grouped_tile_rows(int path, int wf, int64_t rows, int64_t n_experts);
+// Tile shape (index into the direct-to-LDS engine's shape table) of a bf16
+// problem of this kind over `rows` rows (per expert: n_experts).
+int dma_variant(GemmKind kind, int64_t rows, int64_t n_experts);
 int gemm_bn_out(int path, bool dual);
 hipError_t gemm_launch(const GemmArgs &a, int path, GemmKind kind, int wf, int64_t m_tiles,
                        hipStream_t s);
