@@ -315,7 +315,7 @@ moe_status moe_cutoff_update(float *alpha, const float *zeta, int64_t n_experts,
                              void *stream);
 
 /* ---- Expert tiering: cold experts in host DRAM, hot ones cached in HBM -----
- * akashbajwa.co "稀疏设计" (the tiered-memory paragraphs near its end): at low
+ * bittide.aicompass.dev "稀疏设计" (the tiered-memory paragraphs near its end): at low
  * batch, the most used experts can sit in HBM and the rarely used ones in
  * cheaper DRAM, hot experts being loaded as needed -- worthwhile when routing
  * concentrates on popular experts (a power law), not when a large batch

@@ -389,7 +389,7 @@ hipError_t tn_f32(const Contraction &c, hipStream_t s) {
 hipError_t tn_experts_f32(Contraction c, const int32_t *offsets, int64_t E, hipStream_t s) {
   c.a.offsets = offsets;
   c.a.n_experts = (int32_t)E;
-  return launch_dma_ko<EPI_STORE, true, true, true, false, float>(kVDense, c.a, s);
+  return launch_dma_ko<EPI_STORE, true, true, true, false, float>(kgrp_variant(), c.a, s);
 }
 
 GemmArgs base_args_bwd(const moe_config *c) {

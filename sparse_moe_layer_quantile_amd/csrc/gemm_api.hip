@@ -55,7 +55,7 @@ MOE_API moe_status moe_gemm_bf16(const moe_gemm_desc *g, void *stream) {
     if (g->c_in) return MOE_ERR_UNSUPPORTED;
     a.offsets = g->k_offsets;
     a.n_experts = (int32_t)g->n_experts;
-    e = launch_dma_ko<EPI_STORE, true, true, true, false, float>(kVDense, a, s);
+    e = launch_dma_ko<EPI_STORE, true, true, true, false, float>(kgrp_variant(), a, s);
   } else if (ako) {
     e = launch_dma_ko<EPI_STORE, true, true, false, false, float>(kVDense, a, s);
   } else if (bko) {

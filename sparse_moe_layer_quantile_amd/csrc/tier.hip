@@ -1,6 +1,6 @@
 // tier.hip -- cold experts in host DRAM, hot ones cached in HBM (moe_tier_*).
 //
-// akashbajwa.co "稀疏设计", the tiered-memory paragraphs near its end: at low
+// bittide.aicompass.dev "稀疏设计", the tiered-memory paragraphs near its end: at low
 // batch the most used experts can live in HBM and the others in cheaper DRAM,
 // hot experts being loaded on demand; it pays when routing follows a power law
 // over experts.

@@ -63,12 +63,13 @@ def test_both_operands_k_outer(M, N, K):
            f"A^T B {M}x{N}x{K}")
 
 
-def test_expert_batched_k_ranges():
+@pytest.mark.parametrize("N", [136, 768])
+def test_expert_batched_k_ranges(N):
     """One output per expert over its rows: empty experts, 1 row, ragged tails,
-    several K tiles."""
+    several K tiles; N in whole N tiles (one workgroup walks them all) or not."""
     import sparse_moe_layer_quantile_amd as moe
     rng = np.random.default_rng(4)
-    M, N = 264, 136
+    M = 264
     off = np.array([0, 0, 3, 70, 70, 71, 200, 200], np.int32)
     P = int(off[-1])
     a, b = _bf16(rng, P + 8, M), _bf16(rng, P + 8, N)  # rows past P: never read
