@@ -95,16 +95,28 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
                                    16, 0, 0);
 }
 
-// Eight fp8 e4m3 codes (lo: codes 0-3, hi: codes 4-7, byte order) times a
-// block scale, rounded to bf16: the B operand of one bf16 MFMA.
+// Eight fp8 e4m3 codes (lo: codes 0-3, hi: codes 4-7, byte order) times the
+// power of two of a block scale s, 2^floor(log2 |s|), as bf16: the B operand
+// of one bf16 MFMA.  The gfx950 scaled conversion reads only the exponent of
+// s, and every such product is exact in bf16 (three significand bits); the
+// rest of s, its signed significand (scale_sig), multiplies the accumulators
+// once per 128-wide K block instead of every element.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float s) {
-  typedef __attribute__((ext_vector_type(2))) float f2;
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  bf16x8 r;
-  r[0] = (__bf16)(a.x * s); r[1] = (__bf16)(a.y * s); r[2] = (__bf16)(b.x * s); r[3] = (__bf16)(b.y * s);
-  r[4] = (__bf16)(c.x * s); r[5] = (__bf16)(c.y * s); r[6] = (__bf16)(d.x * s); r[7] = (__bf16)(d.y * s);
-  return r;
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  u32x4 v;
+  v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, false));
+  v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, true));
+  v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, false));
+  v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, true));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Signed significand of a block scale, in [1, 2) up to sign: s / 2^floor(log2 |s|).
+// (A zero or subnormal scale gives 1: its block then enters at 2^-127 times
+// its codes, which is zero to bf16 and fp32 accumulation alike.)
+__device__ __forceinline__ float scale_sig(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (b & 0x7F800000u) == 0 ? 1.0f : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
 }
 
 // Eight E2M1 codes (element 2i in the low nibble of byte i) times an E8M0
@@ -711,7 +723,11 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     }
     int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
     if constexpr (PN) kb += g < TA ? 0 : jn * nstep_b;
-    if constexpr (BF != BF_BF16) {
+    if constexpr (B8) {
+      // (the block-scale branch of the K loop leaves the base's uniformity to
+      // the compiler's guess: moved to scalar registers explicitly)
+      dma16_asm(uniform_ptr(base + kb), o, smem + st * STAGE_BYTES + g * 1024);
+    } else if constexpr (BF != BF_BF16) {
       dma16_asm(base + kb, o, smem + st * STAGE_BYTES + g * 1024);
     } else {
       asm volatile("" : "+v"(o));
@@ -1126,6 +1142,19 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
               bsc[j] = scale_b8(kt, j);
               read_b8(st, 0, j, braw);
             });
+            // the first K tile of a 128-wide block after another: the
+            // accumulators, in units of the previous block's scale significand,
+            // change to this block's
+            if (kt > 0 && ((k_begin + kt) & 1) == 0) {
+              static_for<FRN>([&](auto j_tag) G2_INL {
+                constexpr int j = decltype(j_tag)::value;
+                const float ratio = scale_sig(scale_b8(kt - 1, j_tag)) / scale_sig(bsc[j]);
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+#pragma unroll
+                  for (int r = 0; r < 16; ++r) acc[i][j][r] *= ratio;
+              });
+            }
             static_for<NF>([&](auto f) G2_INL {
               if constexpr (f >= FRN) read_frag(st, 0, f, fa[0], fb[0]);
             });
@@ -1237,6 +1266,17 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         }
       }
       wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
+      if constexpr (B8 && NS > 0) {
+        // the last block's scale significand
+        static_for<FRN>([&](auto j_tag) G2_INL {
+          constexpr int j = decltype(j_tag)::value;
+          const float sig = scale_sig(scale_b8(ktiles - 1, j_tag));
+#pragma unroll
+          for (int i = 0; i < NS; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] *= sig;
+        });
+      }
     }
   };
   // one specialised copy of the K loop per number of active sub-blocks
