@@ -86,11 +86,16 @@ constexpr DmaShape kDma[] = {
     // shape and 128 x 128 ones with two and four workgroups a CU: the
     // backward 3% faster at K3 prefill, 6% at decode)
     {2, 4, 2, 2, 32, 2, 2},  // 16: 128 x 256, 8 waves, BK 32, 2 stages (48 KB)
+    // fp8 B, grouped: one wave row of 8 waves along N, so each B element is
+    // widened by one wave only, with 5 x 2 MFMA blocks a wave (K3 fp8 prefill
+    // expert gate/up 6.90 ms against 7.50 ms on 192 x 256, 3 stages; 7.05 ms
+    // with 2 stages)
+    {1, 8, 5, 2, 64, 3, 1},  // 17: 160 x 512, BK 64, 3 stages (156 KB)
 };
 // the shapes the engine picks by default (gemm.hip, dma_variant)
 constexpr int kVGrouped = 0, kVGroupedShort = 1, kVDense = 2, kVSmallM = 3, kVSmallMX4 = 6,
               kVTinyMX4 = 7, kVTinyMX4W = 8, kVQ256 = 9, kVQ192 = 10, kVA8 = 11,
-              kVA8W = 12, kVA8S = 13, kVB8 = 14, kVB8S = 15, kVKgrp = 16;
+              kVA8W = 12, kVA8S = 13, kVB8 = 14, kVB8S = 15, kVKgrp = 16, kVF8W = 17;
 constexpr int kNumDma = sizeof(kDma) / sizeof(kDma[0]);
 // the shape of the expert-batched weight gradients (MOE_KGRP_V overrides it)
 inline int kgrp_variant() { return env_int("MOE_KGRP_V", kVKgrp); }
@@ -171,15 +176,16 @@ hipError_t launch_dma_v(const GemmArgs &a, hipStream_t s) {
 }
 
 // fp8 e4m3 B with block scales: the shape for the variant v the bf16 engine
-// would take (the 192-row grouped tiles with a third stage, which the half-size
-// B stage leaves room for; the other grouped and small-M ones as they are, the
-// dense one otherwise); MOE_GEMM_FP8 overrides the grouped shape
+// would take (for the short grouped tiles, 160 x 512 with a third stage, which
+// the half-size B stage leaves room for; the other grouped and small-M ones as
+// they are, the dense one otherwise); MOE_GEMM_FP8 overrides the grouped shape
 inline int fp8_shape(int v, bool grouped) {
-  const int dflt = v == kVGroupedShort                          ? kVQ192
+  const int dflt = v == kVGroupedShort                          ? kVF8W
                    : (v == kVGrouped || v == kVSmallM) ? v
                                                                 : kVDense;
   const int o = grouped ? env_int("MOE_GEMM_FP8", -1) : -1;
-  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallM || o == kVQ256 || o == kVQ192)
+  return (o == kVGrouped || o == kVGroupedShort || o == kVSmallM || o == kVQ256 || o == kVQ192 ||
+          o == kVF8W)
              ? o
              : dflt;
 }
@@ -195,6 +201,7 @@ hipError_t launch_dma_b8(int shape, const GemmArgs &a, hipStream_t s) {
     case kVSmallM: return launch_dma_impl<kVSmallM, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVQ256: return launch_dma_impl<kVQ256, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     case kVQ192: return launch_dma_impl<kVQ192, EPI, DUAL, GATHER, false, F, OutT>(a, s);
+    case kVF8W: return launch_dma_impl<kVF8W, EPI, DUAL, GATHER, false, F, OutT>(a, s);
     default: return launch_dma_impl<kVDense, EPI, DUAL, GATHER, false, F, OutT>(a, s);
   }
 }
