@@ -155,8 +155,8 @@ __device__ __forceinline__ void dma4(const void *g, void *lds_wave_base) {
 // nothing to registers, and the compiler's wait-count pass does not see them:
 // with the builtin it must assume that an LDS read may hit the bytes of any
 // load still in flight, and where it cannot prove otherwise (the quantised-B
-// operand reads) it drains every load (vmcnt(0)) before the read, which
-// undoes the ring.  The kernels order these loads themselves: wait_vmcnt
+// operand reads, the transposing reads of K-outer operands) it drains every
+// load (vmcnt(0)) before the read, which undoes the ring.  The kernels order these loads themselves: wait_vmcnt
 // before a stage is read and before the workgroup ends, and a barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
@@ -717,15 +717,17 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
         const int64_t ldx = g < TA ? cur_lda : cur_ldb;
         o = __umul24(kr, (uint32_t)(ldx * 2)) + (o & 0xFFFFu);
         asm volatile("" : "+v"(o));
-        dma16(base + (int64_t)kt * BK * ldx * 2 + o, smem + st * STAGE_BYTES + g * 1024);
+        dma16_asm(uniform_ptr(base + (int64_t)kt * BK * ldx * 2), o,
+                  smem + st * STAGE_BYTES + g * 1024);
         return;
       }
     }
     int64_t kb = (int64_t)kt * (g < TA ? RB : RB_B);
     if constexpr (PN) kb += g < TA ? 0 : jn * nstep_b;
-    if constexpr (B8) {
-      // (the block-scale branch of the K loop leaves the base's uniformity to
-      // the compiler's guess: moved to scalar registers explicitly)
+    if constexpr (B8 || AKO || BKO) {
+      // (the block-scale branch of the fp8 K loop, and the K-outer layouts'
+      // clamps, leave the base's uniformity to the compiler's guess: moved to
+      // scalar registers explicitly)
       dma16_asm(uniform_ptr(base + kb), o, smem + st * STAGE_BYTES + g * 1024);
     } else if constexpr (BF != BF_BF16) {
       dma16_asm(base + kb, o, smem + st * STAGE_BYTES + g * 1024);
