@@ -361,6 +361,13 @@ struct Contraction {
     a.b_estride = b_estride;
     return *this;
   }
+  // C = A B + A1 B1 (B K-outer, grouped): a second K segment with A's and B's
+  // strides and K (whole K tiles), in the same launch
+  Contraction &and_(const void *A1, const void *B1) {
+    a.nseg = 2;
+    a.seg[1] = GemmSeg{A1, a.seg[0].lda, B1, a.seg[0].ldb, nullptr, a.seg[0].k};
+    return *this;
+  }
   Contraction &plus(const float *c_in) {  // C = c_in + op(A) op(B) (c_in may be C)
     a.resid = c_in;
     a.ldr = a.ldo;
@@ -378,7 +385,11 @@ hipError_t nt_f32(const Contraction &c, int v, hipStream_t s) {
   return launch_dma<EPI_STORE, false, false, float, false>(v, c.a, s);
 }
 // C = A B with B K-outer ([K][N], per expert when grouped): input gradients
+// (two K segments: grouped, unsplit, whole 64-wide K tiles)
 hipError_t nn_f32(const Contraction &c, int v, hipStream_t s) {
+  if (c.a.nseg == 2 && (c.a.offsets == nullptr || c.a.partial != nullptr || c.a.seg[0].k % 64 ||
+                        c.a.seg[1].k != c.a.seg[0].k))
+    return hipErrorInvalidValue;
   return launch_dma_ko<EPI_STORE, false, true, false, false, float>(v, c.a, s);
 }
 // C = A^T B with both operands K-outer (K = tokens): dense weight gradients
@@ -551,10 +562,10 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
                         I, pairs_end, beta, ib, bu, ibu, dg, du, dz));
   MOE_TRY(tn_experts_f32(Contraction(I, L, 0, dg, I, xg, L, g->w_gate, L), offsets, E, s));
   MOE_TRY(tn_experts_f32(Contraction(I, L, 0, du, I, xg, L, g->w_up, L), offsets, E, s));
+  // dx_lat rows = dg W_g + du W_u: one launch over both K segments
   MOE_TRY(nn_f32(Contraction(P, L, I, dg, I, w->w_gate, L, dxg, L)
-                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
-  MOE_TRY(nn_f32(Contraction(P, L, I, du, I, w->w_up, L, dxg, L)
-                     .by_expert(offsets, tile_offsets, E, I * L).plus(dxg), vg, s));
+                     .by_expert(offsets, tile_offsets, E, I * L)
+                     .and_(du, w->w_up), vg, s));
   MOE_TRY(launch_kernel(combine_rows_kernel, grid_for(bt * L), dim3(256), 0, s,
                         (const float *)dxg, (const int32_t *)inv_perm, (int)k, bt, L, dxlat));
   // ---- x_lat = W_down_proj x, and the router ------------------------------------------

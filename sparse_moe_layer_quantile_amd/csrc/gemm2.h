@@ -478,6 +478,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     kr0 = args.offsets[tile.e];
     klen = args.offsets[tile.e + 1] - kr0;
   }
+  // B K-outer with two segments (C = A0 B0 + A1 B1, equal strides, whole K
+  // tiles): one K range over both, the second segment's sources a fixed
+  // distance from the first's (two-segment K-outer form)
+  constexpr bool KSEG2 = BKO && !AKO && !KGRP && !MSEG;
+  int kt_seg1 = INT32_MAX;
+  int64_t seg1_da = 0, seg1_db = 0;
+  if constexpr (KSEG2) {
+    if (args.nseg == 2) {
+      kt_seg1 = (int)(klen / BK);
+      klen += args.seg[1].k;
+      seg1_da = static_cast<const char *>(args.seg[1].a) - static_cast<const char *>(args.seg[0].a);
+      seg1_db = static_cast<const char *>(args.seg[1].b) - static_cast<const char *>(args.seg[0].b);
+    }
+  }
   int ktiles = (int)((klen + BK - 1) / BK);
   const int ktiles_all = ktiles;
   const int klast = (int)(klen - (int64_t)(ktiles - 1) * BK);  // k values in the last K tile
@@ -707,12 +721,20 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     // body, so the instruction selector sees uniform base + zext(offset) there
     // (SGPR-base form) instead of a 64-bit address hoisted out of the loop)
     uint32_t o = off[d];
+    const int kt_glob = kt;  // (K tile over both segments)
+    if constexpr (KSEG2) {
+      // K tiles of the second segment: its sources, from its own first K tile
+      if (k_begin + kt >= kt_seg1) {
+        base += g < TA ? seg1_da : seg1_db;
+        kt -= kt_seg1 - k_begin;
+      }
+    }
     if constexpr (AKO || BKO) {
       const bool ko = (AKO && g < TA) || (BKO && g >= TA);
       if (ko) {
         // k rows past the end of K (last tile) re-read the last row; the B
         // fragments mask those k
-        const int kv = k_begin + kt == ktiles_all - 1 ? klast : BK;
+        const int kv = k_begin + kt_glob == ktiles_all - 1 ? klast : BK;
         const uint32_t kr = min((int)(o >> 16), kv - 1);
         const int64_t ldx = g < TA ? cur_lda : cur_ldb;
         o = __umul24(kr, (uint32_t)(ldx * 2)) + (o & 0xFFFFu);
