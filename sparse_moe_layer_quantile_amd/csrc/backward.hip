@@ -164,20 +164,6 @@ __global__ void gather_rows_kernel(const uint16_t *__restrict__ src,
   }
 }
 
-// h[q][i] = bf16(w_q phi(g) psi(u)); w = NULL: weight 1
-__global__ void situ_h_kernel(const float *__restrict__ G, const float *__restrict__ U,
-                              const float *__restrict__ w, int64_t rows, int64_t cols,
-                              float beta, float inv_beta, float beta_u, float inv_beta_u,
-                              uint16_t *__restrict__ h) {
-  const int64_t n = rows * cols;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const Situ s = situ_parts(G[i], U[i], beta, inv_beta, beta_u, inv_beta_u);
-    const float wq = w ? w[i / cols] : 1.0f;
-    h[i] = f32_to_bf16(wq * (s.phi * s.psi));
-  }
-}
-
 __device__ __forceinline__ float block_sum(float v, float *red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -500,12 +486,29 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
   MOE_TRY(launch_kernel(gather_rows_kernel, grid_for(P * L / 8), dim3(256), 0, s,
                         (const uint16_t *)xlat, (const int32_t *)perm, (int)k, P, L, pairs_end,
                         xg));
-  MOE_TRY(nt_f32(Contraction(P, I, L, xg, L, w->w_gate, L, G, I)
-                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
-  MOE_TRY(nt_f32(Contraction(P, I, L, xg, L, w->w_up, L, U, I)
-                     .by_expert(offsets, tile_offsets, E, I * L), vg, s));
-  MOE_TRY(launch_kernel(situ_h_kernel, grid_for(P * I), dim3(256), 0, s, (const float *)G,
-                        (const float *)U, (const float *)w_sorted, P, I, beta, ib, bu, ibu, h));
+  {
+    // the forward's gate/up launch (gathered rows, h = w phi(g) psi(u)), also
+    // writing each pair's raw g and u in fp32
+    GemmArgs a = base_args_bwd(cfg);
+    a.M = P;
+    a.N = I;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{xlat, L, w->w_gate, L, nullptr, L};
+    a.b_up = w->w_up;
+    a.offsets = offsets;
+    a.tile_offsets = tile_offsets;
+    a.n_experts = (int32_t)E;
+    a.b_estride = I * L;
+    a.gather = perm;
+    a.gather_div = (int32_t)k;
+    a.row_scale = w_sorted;
+    a.out = h;
+    a.ldo = I;
+    a.out_g = G;
+    a.out_u = U;
+    a.ldgu = I;
+    MOE_TRY(gemm_launch(a, PATH_BF16, GK_EXPERT_SITU, WF_BF16, grouped_mt, s));
+  }
   {
     GemmArgs a = base_args_bwd(cfg);
     a.M = P;
@@ -524,13 +527,21 @@ MOE_API moe_status moe_backward(const moe_config *cfg, const moe_weights *w, con
                         (const uint16_t *)o, (const int32_t *)inv_perm, (int)k, L,
                         w->latent_gamma, cfg->rms_eps, ylat, rinv, n));
   if (S > 0) {  // the S shared experts' gate / up rows are one [S I_s][d] matrix each
-    MOE_TRY(nt_f32(Contraction(bt, SI, d, x, d, w->sh_gate, d, Gs, SI).split(split, p.split_cap),
-                   vd, s));
-    MOE_TRY(nt_f32(Contraction(bt, SI, d, x, d, w->sh_up, d, Us, SI).split(split, p.split_cap),
-                   vd, s));
-    MOE_TRY(launch_kernel(situ_h_kernel, grid_for(bt * SI), dim3(256), 0, s, (const float *)Gs,
-                          (const float *)Us, (const float *)nullptr, bt, SI, beta, ib, bu, ibu,
-                          hs));
+    // the forward's shared gate/up launch, also writing the raw g and u
+    GemmArgs a = base_args_bwd(cfg);
+    a.M = bt;
+    a.N = SI;
+    a.nseg = 1;
+    a.seg[0] = GemmSeg{x, d, w->sh_gate, d, nullptr, d};
+    a.b_up = w->sh_up;
+    a.partial = split;
+    a.partial_cap = p.split_cap;
+    a.out = hs;
+    a.ldo = SI;
+    a.out_g = Gs;
+    a.out_u = Us;
+    a.ldgu = SI;
+    MOE_TRY(gemm_launch(a, PATH_BF16, GK_DENSE_SITU, WF_BF16, dense_mt, s));
   }
 
   // ---- y = W_up n + sum_s W_ds,s hs_s ----------------------------------------------

@@ -51,6 +51,10 @@ struct GemmArgs {
   float *out_t;              // router: transposed copy [N][M] (may be NULL)
   const float *bias;         // router: [N] (may be NULL)
   const float *row_scale;    // SiTU and store: factor of output row m (NULL = 1)
+  // SiTU (direct-to-LDS engine and its split-K sum): also the raw gate and up
+  // sums, fp32 [M][ldgu] each (the backward's recompute; NULL = not written)
+  float *out_g, *out_u;
+  int64_t ldgu;
   const void *resid;         // store: out = acc + resid[m][ldr] (OutT; NULL = none; may be out)
   int64_t ldr;
   // MX FP8 A (direct-to-LDS engine, BF_MX4A8): E8M0 codes a_sc[row][lda_sc] of the A

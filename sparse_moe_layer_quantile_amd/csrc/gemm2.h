@@ -979,10 +979,15 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
             const float f = use_rs ? rs_lds[rr] : 1.0f;
 #pragma unroll
             for (int j = 0; j < JN; ++j)
-              if (col_ok[j])
+              if (col_ok[j]) {
                 store_out<OutT>(orow, col[j],
                                 f * situ(acc[i][j][r], acc[i][j + FRN / 2][r], args.beta,
                                          args.inv_beta, args.beta_u, args.inv_beta_u));
+                if constexpr (GEN) {  // and the raw gate and up sums
+                  args.out_g[row * args.ldgu + col[j]] = acc[i][j][r];
+                  args.out_u[row * args.ldgu + col[j]] = acc[i][j + FRN / 2][r];
+                }
+              }
           } else if constexpr (EPI == EPI_ROUTER) {
 #pragma unroll
             for (int j = 0; j < JN; ++j)
@@ -1010,6 +1015,9 @@ __global__ void __launch_bounds__(64 * WM * WN, OCC) gemm_dma_kernel(GemmArgs ar
     if constexpr (EPI == EPI_STORE) {
       if (plain_store) rows_loop(std::false_type{});
       else rows_loop(std::true_type{});
+    } else if constexpr (EPI == EPI_SITU) {
+      if (args.out_g != nullptr) rows_loop(std::true_type{});
+      else rows_loop(std::false_type{});
     } else {
       rows_loop(std::false_type{});
     }
@@ -1387,6 +1395,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a) {
       const float f = a.row_scale ? a.row_scale[row] : 1.0f;
       store_out<OutT>(a.out, row * a.ldo + col,
                       f * situ(g, u, a.beta, a.inv_beta, a.beta_u, a.inv_beta_u));
+      if (a.out_g != nullptr) {
+        a.out_g[row * a.ldgu + col] = g;
+        a.out_u[row * a.ldgu + col] = u;
+      }
     } else {
       if (a.row_scale) g *= a.row_scale[row];
       if (a.resid) g += load_in<OutT>(a.resid, row * a.ldr + col);
