@@ -9,7 +9,8 @@
 // TM = WM * SUBM * 32 A rows (or MA < 32 rows, see below), TN = WN * FRN * 32
 // B rows and BK = 32 or 64;
 // WM x WN waves, each wave SUBM x FRN blocks of
-// v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC workgroups per CU.
+// v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC is the launch
+// bound's minimum waves per SIMD (it caps the registers of a wave at 512 / OCC).
 //
 //  * Global -> LDS with global_load_lds_dwordx4 (gfx950): no staging
 //    registers; each wave instruction fills 1 KB = RPI tile rows of 2 BK

@@ -19,7 +19,7 @@ inline int env_int(const char *name, int dflt) {
 
 // ---- direct-to-LDS bf16 engine ----------------------------------------------------
 struct DmaShape {
-  int wm, wn, subm, frn, bk, stages, occ;
+  int wm, wn, subm, frn, bk, stages, occ;  // occ: minimum waves per SIMD (launch bound)
   int ma = 0;  // rows of a short tile (0: wm * subm * 32)
   constexpr int threads() const { return 64 * wm * wn; }
   constexpr int tm() const { return ma > 0 ? ma : wm * subm * 32; }
@@ -81,11 +81,11 @@ constexpr DmaShape kDma[] = {
     {2, 4, 4, 2, 128, 2, 1},  // 14: 256 x 256 (136 KB)
     {2, 4, 3, 2, 128, 2, 1},  // 15: 192 x 256 (120 KB)
     // expert-batched weight gradients (few K tiles, then a large fp32 store):
-    // a small ring, so that two workgroups share a CU and one's stores drain
-    // while the other loads and multiplies (measured against the 256 x 256
-    // shape and 128 x 128 ones with two and four workgroups a CU: the
-    // backward 3% faster at K3 prefill, 6% at decode)
-    {2, 4, 2, 2, 32, 2, 2},  // 16: 128 x 256, 8 waves, BK 32, 2 stages (48 KB)
+    // a small ring and at most 128 VGPRs, so that two workgroups share a CU
+    // and one's stores drain while the other loads and multiplies.  Against
+    // the 256 x 256 shape, 2-stage rings and 128 x 128 tiles with two or four
+    // workgroups a CU: the backward 2-3% faster at K3 prefill, 8-10% at decode
+    {2, 4, 2, 2, 32, 3, 4},  // 16: 128 x 256, 8 waves, BK 32, 3 stages (72 KB)
     // fp8 B, grouped: one wave row of 8 waves along N, so each B element is
     // widened by one wave only, with 5 x 2 MFMA blocks a wave (K3 fp8 prefill
     // expert gate/up 6.90 ms against 7.50 ms on 192 x 256, 3 stages; 7.05 ms
