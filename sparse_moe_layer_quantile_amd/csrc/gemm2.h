@@ -1,13 +1,16 @@
 // gemm2.h -- bf16 MFMA GEMM engine with direct-to-LDS loads.
 //
 // Same problem description as gemm.h (GemmArgs: dense / grouped / gathered /
-// dual gate-up / K-segmented), for bf16 A operands and B in one of three
-// formats (BFmt): bf16; fp8 e4m3 with 128 x 128 block scales; OCP MX FP4
-// (E2M1 codes, two per byte, with an E8M0 scale per 32 K elements of a row).
-// Quantised B tiles travel to LDS as stored and are widened to bf16 in
-// registers, times their scale, just before the MFMA.  Tile TM x TN x BK with
-// TM = WM * SUBM * 32 A rows (or MA < 32 rows, see below), TN = WN * FRN * 32
-// B rows and BK = 32 or 64;
+// dual gate-up / K-segmented), for bf16 A operands and B in one of the
+// formats of BFmt: bf16; fp8 e4m3 with 128 x 128 block scales; OCP MX FP4
+// (E2M1 codes, two per byte, with an E8M0 scale per 32 K elements of a row);
+// and, with MX FP8 A, MX FP4 or MX FP8 B on the block-scaled MFMA.  Quantised
+// B tiles travel to LDS as stored; for the bf16 MFMA they are widened in
+// registers just before it (fp8: exactly, times the power of two of the
+// block scale, the scale's significand going on the accumulators).  The
+// backward's layouts add operands stored K-outer and per-expert K ranges.
+// Tile TM x TN x BK with TM = WM * SUBM * 32 A rows (or MA < 32 rows, see
+// below), TN = WN * FRN * 32 B rows and BK = 32 to 256;
 // WM x WN waves, each wave SUBM x FRN blocks of
 // v_mfma_f32_32x32x16_bf16, with WM x WN = 4 or 8 waves; OCC is the launch
 // bound's minimum waves per SIMD (it caps the registers of a wave at 512 / OCC).
