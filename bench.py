@@ -442,6 +442,12 @@ def bench_backward(args, cfg) -> int:
     """moe_backward on the workload's batch: the routing from one route() call
     (outside the timed region, as a training step takes it from its forward),
     gradients into preallocated fp32 tensors."""
+    print(json.dumps(backward_line(args, cfg)), flush=True)
+    return 0
+
+
+def backward_line(args, cfg) -> dict:
+    """The JSON line of bench_backward."""
     import torch
     torch.cuda.set_device(0)
     layer, x = device_layer(cfg, args.seed)
@@ -486,8 +492,9 @@ def bench_backward(args, cfg) -> int:
         # the fp64 oracle would need the experts' 30 G parameters as fp64 on the host
         "cpu_baseline": None,
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    del grads, layer, x, dy, r
+    torch.cuda.empty_cache()
+    return line
 
 
 def main(argv=None):
@@ -545,12 +552,17 @@ def main(argv=None):
     line["routing"] = routing_stats(cfg, res)
     if not args.no_secondary and args.config == "k3_prefill_bf16":
         line["secondary"] = {}
-        for name, steps in (("k3_decode_bf16", args.steps), ("k3_prefill_fp8", args.steps)):
+        for name in ("k3_decode_bf16", "k3_prefill_fp8", "k3_decode_mxfp4"):
             c2 = synth.CONFIGS[name]
-            r2 = time_forward(c2, args.seed, steps, args.warmup, False)
+            r2 = time_forward(c2, args.seed, args.steps, args.warmup, False)
             l2 = forward_line(c2, args, r2)
             line["secondary"][name] = {k: l2[k] for k in ("value", "unit", "ms_per_step",
                                                            "roofline", "layer", "phases_ms")}
+        # the backward of the headline workload (gradients of x and every weight)
+        lb = backward_line(argparse.Namespace(seed=args.seed, steps=min(args.steps, 10),
+                                              warmup=min(args.warmup, 3)), cfg)
+        line["secondary"]["k3_prefill_bf16_backward"] = {
+            k: lb[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "roofline")}
     del res
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
