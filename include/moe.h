@@ -197,7 +197,12 @@ moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, int64_t 
  * they receive the routing and dispatch of this call.  The latent down
  * projection and the shared experts' gate/up do not depend on routing: they
  * run on shared_stream (NULL: on `stream`), joined into `stream` before the
- * routed experts and before the output projection respectively. */
+ * routed experts and before the output projection respectively.  The call
+ * enqueues kernels and event record / wait pairs only (no memset, copy or
+ * host wait), so it can be recorded into a HIP graph by capturing `stream`;
+ * shared_stream is then forked from and joined back into the capture by those
+ * events.  The first call on a device must run outside capture (it sets the
+ * kernels' LDS limits and fills the library's event pool). */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, int64_t bt,
                        void *y, moe_route_out *route, moe_dispatch_out *disp, void *ws,
                        size_t ws_bytes, void *stream, void *shared_stream);
