@@ -196,3 +196,46 @@ def test_backward_k3_prefill_sampled_tokens():
     err = parity.normwise_err(dx.astype(np.float64), ref["dx"])
     say(f"  dx normwise {err:.2e}")
     assert err <= TOL
+
+
+def test_backward_k3_widths_large_expert_groups():
+    """K3 widths (d 7168, L 3584, I 3072, two shared of 3072, Zipf(1.1)
+    offsets, batch cutoffs) with prefill-sized expert groups: 1024 tokens over
+    32 experts, top 16, about 512 pairs an expert (K3 prefill has about 293).
+    The least-loaded expert's gate / up / down / router gradients in full and
+    the dx of every token that chose it, against the oracle on those tokens
+    and the experts they touch."""
+    cfg = synth.CONFIGS["k3_prefill_bf16"].with_(bt=1024, n_experts=32)
+    seed = 0
+    say("backward K3 widths, 32 experts, 1024 tokens")
+    layer, x = parity.device_layer(cfg, seed=seed)
+    bits, dy64 = _bf16_dy(cfg, seed + 7)
+    dy = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    r = layer.route(x)
+    g = layer.backward(x, dy, route=r)
+    torch.cuda.synchronize()
+    idx = parity.to_np(r["idx"])
+    ref_route = parity.oracle_routing_full(cfg, seed=seed)
+    _, bad = parity.routing_mismatches(idx, ref_route["idx"], ref_route["z32"],
+                                       ref_route["alpha"])
+    assert not bad, f"tokens whose expert set is not a valid top-k: {bad[:8]}"
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_experts)
+    e_star = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
+    tokens = [int(t) for t in np.nonzero((idx == e_star).any(axis=1))[0]]
+    say("  expert", e_star, "tokens", len(tokens))
+    got = {"dx": parity.to_np(g["dx"][tokens])}
+    for n in ("w_gate", "w_up", "w_down", "w_router"):
+        got[n] = parity.to_np(g[n][e_star])
+    gb = float(g["router_bias"][e_star])
+    del g, layer
+    torch.cuda.empty_cache()
+    sub, lay, remap, sub_idx = _reduced_host_layer(cfg, tokens, idx, seed)
+    xs = oracle.decode(synth.host_rows(cfg, "x", tokens, seed))
+    ref = ob.backward(sub, ob.decode_layer(sub, lay), xs, sub_idx, dy64[tokens])
+    es = remap[e_star]
+    for name in got:
+        want = ref[name] if name == "dx" else ref[name][es]
+        err = parity.normwise_err(got[name].astype(np.float64), want)
+        say(f"  {name:9s} normwise {err:.2e}")
+        assert err <= TOL, (name, err)
+    assert abs(gb - ref["router_bias"][es]) <= TOL * max(1e-30, abs(ref["router_bias"][es]))
