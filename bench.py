@@ -525,8 +525,8 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one MI355X: the layer runs on a single GPU, with no "
+              "multi-GPU path (run with --gpus 1).", file=sys.stderr)
         return 2
 
     import synth
